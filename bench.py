@@ -1,0 +1,185 @@
+#!/usr/bin/env python3
+"""Benchmark of the compressed-KV hot path on one MI355X.
+
+Workload (1.3B-class video-DiT layer, 12 heads x d=128, bf16, centroid + INT2
+group-32 codec with 256 centroids per head, 1560 tokens per latent frame):
+one step =
+  1. encode one 3-frame chunk of keys and of values (4680 tokens each) into the
+     compressed history at its offset (nearest centroid, residual, group scale/zero,
+     quantize, pack), and
+  2. decode-fused attention of 4680 queries over all 32760 compressed keys/values.
+The history (chunks before the timed one) is encoded once before timing; all
+inputs are resident in HBM when the timed region starts.  The metric is query
+tokens per second (each query token covers all 12 heads).
+
+Prints ONE JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+def encode_bytes(n_tokens: int, heads: int, dim: int, bits: int, group: int, n_centroids: int,
+                 x_bytes: int = 2) -> int:
+    """Algorithmic bytes of one centroid-codec encode: read x once, read the centroid
+    table once, write codes + scale/zero + uint8 index once."""
+    per_th = dim * x_bytes + dim * bits // 8 + 4 * (dim // group) + (1 if n_centroids <= 256 else 2)
+    return n_tokens * heads * per_th + heads * n_centroids * dim * x_bytes
+
+
+def attention_flops(nq: int, nk: int, dim: int, heads: int) -> float:
+    """QK^T and PV: 2 * 2 * Nq * Nk * d per head."""
+    return 4.0 * nq * nk * dim * heads
+
+
+def cpu_baseline(d: dict, sample_heads=(0, 1), enc_frames: int = 1, q_sample: int = 512) -> dict:
+    """The oracle, as it stands, timed on this host on a bounded sample of one step.
+
+    Sample: encode of `enc_frames` latent frame(s) of keys and values (all heads), decode of
+    the full compressed history and attention of `q_sample` queries for `sample_heads`
+    (the history of those heads is encoded by the oracle before timing).  Each part is
+    scaled to the full step (4680-token chunk, 12 heads, 4680 queries)."""
+    import numpy as np
+    from oracle import attention as oatt, codec as ocodec, numerics as nm
+
+    H, D, T = d["heads"], d["dim"], d["tokens_per_frame"]
+    lo, hi = d["chunk"]
+    nq = d["Q"].shape[0]
+    hs = list(sample_heads)
+    Kf, Vf = nm.bf16_to_f32(d["K"]), nm.bf16_to_f32(d["V"])
+    Ck, Cv = nm.bf16_to_f32(d["Ck"]), nm.bf16_to_f32(d["Cv"])
+    # setup (untimed): the oracle's own compressed history for the sampled heads
+    hist_k = ocodec.encode_centroid(Kf[:, hs], Ck[hs], 2, 32)["store"]
+    hist_v = ocodec.encode_centroid(Vf[:, hs], Cv[hs], 2, 32)["store"]
+    t0 = time.perf_counter()
+    for x, C in ((Kf, Ck), (Vf, Cv)):
+        ocodec.encode_centroid(x[lo:lo + enc_frames * T], C, 2, 32)
+    t_enc = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    kh = oatt.cache_view(ocodec.decode_store(hist_k, 2, 32, D, C=Ck[hs]), "bf16")
+    vh = oatt.cache_view(ocodec.decode_store(hist_v, 2, 32, D, C=Cv[hs]), "bf16")
+    t_dec = time.perf_counter() - t0
+    q = nm.bf16_to_f32(d["Q"][:q_sample][:, hs])
+    t0 = time.perf_counter()
+    oatt.attention(q, kh, vh, d["scale"])
+    t_att = time.perf_counter() - t0
+    step = t_enc * (hi - lo) / (enc_frames * T) + t_dec * H / len(hs) \
+        + t_att * (nq / q_sample) * (H / len(hs))
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    return {
+        "value": nq / step, "unit": "query-tok/s", "cores": int(blas_threads), "kind": "oracle",
+        "sample": (f"oracle encode of {enc_frames} frame(s) x {H} heads (K and V, single-threaded "
+                   f"numpy), decode of the {d['K'].shape[0]}-token history and fp64 attention of "
+                   f"{q_sample} queries for {len(hs)} heads ({blas_threads} BLAS threads); "
+                   f"scaled to one full step"),
+        "seconds": {"encode": t_enc, "decode": t_dec, "attention": t_att, "step_estimate": step},
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              f"the multi-GPU sharding is described, not built", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import kv_cache_compression_02_amd as kvc
+    import synth
+
+    dev = torch.device("cuda:0")
+    d = synth.cfg1()
+    H, D, C = d["heads"], d["dim"], d["centroids"]
+    bits, group = d["bits"], d["group"]
+    lo, hi = d["chunk"]
+    nk, nq = d["K"].shape[0], d["Q"].shape[0]
+
+    def dev_bf16(a):
+        return torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
+
+    K, V, Q = dev_bf16(d["K"]), dev_bf16(d["V"]), dev_bf16(d["Q"])
+    codec = kvc.Codec(H, D, bits, group, kvc.BASE_CENTROID, C)
+    ks, vs = kvc.Store.allocate(codec, nk, dev), kvc.Store.allocate(codec, nk, dev)
+    kb = kvc.BaseParams(centroids=dev_bf16(d["Ck"]))
+    vb = kvc.BaseParams(centroids=dev_bf16(d["Cv"]))
+    out = torch.empty((nq, H, D), dtype=torch.float32, device=dev)
+    # history before the timed chunk, encoded once
+    if lo:
+        kvc.kvc_encode(codec, K[:lo], ks, 0, kb)
+        kvc.kvc_encode(codec, V[:lo], vs, 0, vb)
+    Kc, Vc = K[lo:hi].contiguous(), V[lo:hi].contiguous()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e: e[0].record()
+        kvc.kvc_encode(codec, Kc, ks, lo, kb)
+        kvc.kvc_encode(codec, Vc, vs, lo, vb)
+        if e: e[1].record()
+        kvc.kvc_attend_compressed(codec, ks, kb, codec, vs, vb, nk, Q, d["scale"], out=out)
+        if e: e[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    t_enc = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps * 1e-3
+    t_att = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps * 1e-3
+    flops = attention_flops(nq, nk, D, H)
+    enc_b = 2 * encode_bytes(hi - lo, H, D, bits, group, C)
+    achieved = flops / t_att / 1e12
+    line = {
+        "metric": "compressed-KV attention query-tok/s (encode 3-frame chunk + attention over history)",
+        "value": nq * args.steps / elapsed,
+        "unit": "query-tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded clustered AR(1) video-DiT KV, 1560 tokens/frame)",
+        "config": {"workload": "centroid+INT2 g32 codec, 12 heads x 128, 256 centroids/head; "
+                               "encode 4680-token chunk (K,V) + attention 4680 q x 32760 keys",
+                   "heads": H, "head_dim": D, "history_tokens": nk, "queries": nq,
+                   "chunk_tokens": hi - lo, "bits": bits, "group": group, "centroids": C},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "attend_bf16_kernel", "ms": t_att * 1e3},
+        "encode": {"ms": t_enc * 1e3, "bytes": enc_b, "GB/s": enc_b / t_enc / 1e9,
+                   "frac_hbm": enc_b / t_enc / 1e9 / HBM_PEAK_GBS},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(d)
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

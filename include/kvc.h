@@ -1,0 +1,212 @@
+/*
+ * kvc.h - C ABI of the compressed KV-cache codec and attention library (libkvc.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages: NanoKV project page and arXiv 2611.06377; Coral-KV arXiv
+ * 2610.12514; TempoKV arXiv 2610.15324): every cached key/value vector gets a
+ * base - its nearest cluster centroid (Coral-KV abstract, Fig. 2c; NanoKV
+ * abstract), a block-diagonal-plus-low-rank prediction from the reconstructed
+ * previous layer (Coral-KV Fig. 3), or a temporal prediction from the
+ * reconstructed previous frames (TempoKV Fig. 2b) - and only the residual is
+ * stored, quantized group-wise to INT2/INT4 with a shared scale per group
+ * (Coral-KV Fig. 5c) and bit-packed (Coral-KV Table 9 caption lists the stored
+ * state: residual codes and scales, assignments, codebooks or predictors).
+ * Attention then runs over the compressed history (NanoKV abstract), either by
+ * decoding K/V tiles on the fly or, NanoKV-Fast style, by scoring queries on the
+ * stored low-dimensional coefficients (NanoKV page, '03 / Measured results').
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Ownership: every buffer is owned by the caller.  The library never
+ *   allocates or frees device memory and keeps no mutable global state.
+ * - Pointers: all tensor pointers are DEVICE pointers and must be 16-byte
+ *   aligned; descriptors (kvc_codec, kvc_store, kvc_base_params) are HOST
+ *   structs read during the call only.  A call with nothing to process
+ *   (n_tokens == 0, n_queries == 0) may pass NULL for the empty tensors and
+ *   returns KVC_OK without launching anything.
+ * - Streams: `stream` is a hipStream_t (NULL = the default stream).  Every call
+ *   is asynchronous on that stream and never synchronizes.  Outputs must not
+ *   alias inputs.
+ * - Errors: arguments are validated on the host before anything is launched;
+ *   on failure the call returns a kvc_status and touches no output.  A launch
+ *   failure reported by the HIP runtime returns KVC_E_DEVICE.  Inputs must be
+ *   finite (not checked).
+ * - Layouts (element = x_dtype unless stated):
+ *     x, reconstructions, queries, outputs   [N][H][d], token-major; consecutive
+ *                                            tokens `token_stride` elements apart
+ *     store.codes        uint32 [H][capacity][d*bits/32]   (m*bits/32 for COEFF)
+ *     store.scale_zero   uint32 [H][capacity][d/group]     (m/group for COEFF)
+ *     store.index        uint8 (<= 256 centroids) or uint16, [H][capacity]
+ *     centroids          [H][C][d]
+ *   Code i of a vector sits in word floor(i*bits/32) at bit bits*(i mod 32/bits)
+ *   (little-endian).  A scale/zero word holds the fp16 bits of the scale in its
+ *   low half and those of the zero in its high half.
+ * - Arithmetic of the codec (bit-exact contract): residual r = x - base in fp32;
+ *   per group of `group` consecutive values: z = fp16(min r),
+ *   s = fp16(fp32(max r - min r) / (2^bits - 1)), code = clamp(rint((r - z)/s),
+ *   0, 2^bits - 1) (all codes 0 when s == 0), fp32 IEEE division, ties to even;
+ *   reconstruction = base + ((code * s) + z).  Groups whose scale or zero
+ *   overflows fp16 are outside the contract.  Nearest-centroid distances are
+ *   sum_i (x_i - c_i)^2 in fp32 in ascending channel order, ties to the lowest
+ *   index.
+ */
+#ifndef KVC_H_
+#define KVC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVC_ABI_VERSION 1
+
+typedef enum {
+  KVC_OK = 0,
+  KVC_E_NULL = 1,        /* a required pointer is NULL                          */
+  KVC_E_SHAPE = 2,       /* sizes inconsistent or out of range                  */
+  KVC_E_UNSUPPORTED = 3, /* valid request this build does not implement         */
+  KVC_E_ALIGN = 4,       /* a device pointer is not 16-byte aligned             */
+  KVC_E_WORKSPACE = 5,   /* workspace smaller than kvc_workspace_bytes()        */
+  KVC_E_DEVICE = 6       /* the HIP runtime reported an error                   */
+} kvc_status;
+
+typedef enum { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
+
+typedef enum {
+  KVC_BASE_NONE = 0,     /* base 0: anchors and plain group quantization          */
+  KVC_BASE_CENTROID = 1, /* base = C[h][a], a = nearest centroid                  */
+  KVC_BASE_DPLR = 2,     /* cross-layer block-diagonal + rank-r prediction        */
+  KVC_BASE_TEMPORAL = 3, /* per-channel AR(2) keys / key->value cross prediction  */
+  KVC_BASE_COEFF = 4     /* C[h][a] + B c: m coefficients of the centroid residual */
+} kvc_base_kind;
+
+/* Codec description (plain data). */
+typedef struct {
+  int32_t heads;       /* H >= 1                                                 */
+  int32_t head_dim;    /* d: 64 or 128                                           */
+  int32_t bits;        /* residual code width: 2 or 4                            */
+  int32_t group;       /* values per scale/zero group: 16, 32, 64 or 128; must
+                          divide d (or coeff_dim for KVC_BASE_COEFF)             */
+  int32_t base;        /* kvc_base_kind                                          */
+  int32_t n_centroids; /* CENTROID / COEFF: 1..65535                             */
+  int32_t rank;        /* DPLR: r, a multiple of 16, <= 256                      */
+  int32_t n_inputs;    /* DPLR: 1 (keys from K_{l-1}) or 2 (values from
+                          [K_l ; V_{l-1}])                                       */
+  int32_t coeff_dim;   /* COEFF: m = 16                                          */
+  int32_t x_dtype;     /* kvc_dtype of x, centroids, queries, reconstructions    */
+} kvc_codec;
+
+/* A compressed store (device buffers owned by the caller). */
+typedef struct {
+  uint32_t* codes;      /* [H][capacity][code words]                     */
+  uint32_t* scale_zero; /* [H][capacity][groups]                         */
+  void* index;          /* [H][capacity]; NULL unless CENTROID / COEFF   */
+  int64_t capacity;     /* tokens per head row                           */
+} kvc_store;
+
+/* Base parameters (device pointers; unused members may be NULL).
+ *   CENTROID: centroids.
+ *   COEFF:    centroids, basis [d][m] bf16 (orthonormal columns, shared by heads).
+ *   DPLR:     prev0 = first input reconstruction (K_{l-1} for keys, K_l for values),
+ *             prev1 = second input (V_{l-1}, values only), both bf16 [N][H][d];
+ *             w_block [H][d][n_inputs*d], u [H*d][r], v_lr [n_inputs*H*d][r], bf16.
+ *             prediction[h] = W_h [prev0_h ; prev1_h] + U (v_lr^T [prev0 ; prev1])[h].
+ *   TEMPORAL: keys:   prediction = (coef_a * prev0) + (coef_b * prev1) per channel,
+ *                     prev0 = K_{t-1}, prev1 = K_{t-2}, bf16 [N][H][d]; coef fp32 [H][d].
+ *             values: prediction = M_h aux + (coef_a * prev0), aux = aligned K_t,
+ *                     prev0 = V_{t-1}; M = w_block [H][d][d] bf16; coef_b = NULL.
+ *   prev_token_stride: elements between consecutive tokens of prev0/prev1/aux
+ *   (0 = H*d). */
+typedef struct {
+  const void* centroids;
+  const void* basis;
+  const void* prev0;
+  const void* prev1;
+  const void* aux;
+  const void* w_block;
+  const void* u;
+  const void* v_lr;
+  const float* coef_a;
+  const float* coef_b;
+  int64_t prev_token_stride;
+} kvc_base_params;
+
+/* Device bytes a store of `capacity` tokens needs (host-side helper). */
+kvc_status kvc_store_bytes(const kvc_codec* codec, int64_t capacity, size_t* codes_bytes,
+                           size_t* scale_zero_bytes, size_t* index_bytes);
+
+/* kvc_encode - compress n_tokens vectors x [n][H][d] into dst at token rows
+ * [token_offset, token_offset + n_tokens).
+ * Computes, per (token, head): the base (per codec->base), the residual, the
+ * group scale/zero, codes, and packs them (Coral-KV Fig. 3 and Fig. 5c; TempoKV
+ * Fig. 2b; NanoKV abstract).  For KVC_BASE_COEFF the quantized vector is the m
+ * coefficients B^T (x - C[a]).
+ *   x_token_stride: elements between consecutive tokens of x (0 = H*d).
+ *   recon_out: optional [n][H][d] x_dtype reconstruction (base + dequantized
+ *              residual, rounded to x_dtype) - the input of the next predictor step.
+ *   pred_out:  optional [n][H][d] fp32 copy of the base used (prediction).
+ *   workspace: unused by this version (pass NULL, 0).
+ * Errors: KVC_E_NULL, KVC_E_SHAPE (token_offset + n_tokens > capacity, bad
+ * codec), KVC_E_UNSUPPORTED, KVC_E_ALIGN, KVC_E_DEVICE. */
+kvc_status kvc_encode(const kvc_codec* codec, const void* x, int64_t n_tokens,
+                      int64_t x_token_stride, const kvc_base_params* base, const kvc_store* dst,
+                      int64_t token_offset, void* recon_out, float* pred_out, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* kvc_decode - reconstruct rows [token_offset, token_offset + n_tokens) of a store:
+ * out = base + ((code * s) + z), written as out_dtype [n][H][d] (bf16 output is the
+ * fp32 value rounded to nearest even).  Predictor bases read `base` exactly as
+ * kvc_encode did.  pred_out: optional fp32 base.
+ * Errors: as kvc_encode. */
+kvc_status kvc_decode(const kvc_codec* codec, const kvc_store* src, int64_t token_offset,
+                      int64_t n_tokens, const kvc_base_params* base, void* out, int32_t out_dtype,
+                      float* pred_out, void* stream);
+
+/* kvc_attend_compressed - O = softmax(Q K^T * softmax_scale) V per head, no mask,
+ * over n_keys keys held compressed in stores k and v (rows 0..n_keys-1); K and V
+ * tiles are decoded on the fly (NanoKV abstract: repeated attention over the
+ * compressed history).  K and V codecs: KVC_BASE_CENTROID or KVC_BASE_NONE with
+ * d = 128 and bf16 x_dtype (bf16 MFMA path; decoded values are rounded to bf16, as
+ * a bf16 cache would hold them), or any d in {64, 128} with f32 x_dtype (fp32 path).
+ *   q:   [n_queries][H][d] x_dtype, token stride H*d.
+ *   out: [n_queries][H][d] fp32.
+ *   lse: optional [H][n_queries] fp32 natural-log sum-exp of the scaled scores.
+ *   workspace: unused by this version (pass NULL, 0).
+ * Errors: KVC_E_NULL, KVC_E_SHAPE (n_keys > capacity, n_keys < 1, mismatched
+ * heads/d), KVC_E_UNSUPPORTED, KVC_E_ALIGN, KVC_E_DEVICE. */
+kvc_status kvc_attend_compressed(const kvc_codec* kc, const kvc_store* k,
+                                 const kvc_base_params* kp, const kvc_codec* vc,
+                                 const kvc_store* v, const kvc_base_params* vp, int64_t n_keys,
+                                 const void* q, int64_t n_queries, float softmax_scale,
+                                 float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/* kvc_attend_mixed_dim - NanoKV-Fast style attention from the stored representation
+ * without rebuilding keys (NanoKV page, '03 / Measured results'): the score of key n
+ * is (q . C_k[a_n] + (B^T q) . c_n) * softmax_scale, c_n = dequantized coefficients;
+ * softmax over all n_keys keys; values decoded from their centroid store.
+ *   kc: KVC_BASE_COEFF (bf16, d = 128, m = 16); kp: centroids + basis.
+ *   vc: KVC_BASE_CENTROID (bf16, d = 128); vp: centroids.
+ *   q, out, lse, workspace: as kvc_attend_compressed.
+ * Errors: as kvc_attend_compressed. */
+kvc_status kvc_attend_mixed_dim(const kvc_codec* kc, const kvc_store* k,
+                                const kvc_base_params* kp, const kvc_codec* vc,
+                                const kvc_store* v, const kvc_base_params* vp, int64_t n_keys,
+                                const void* q, int64_t n_queries, float softmax_scale,
+                                float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* Workspace bytes an entry point needs (0 for every entry point of this version). */
+size_t kvc_workspace_bytes(int32_t op, const kvc_codec* codec, int64_t n_tokens,
+                           int64_t n_queries);
+
+const char* kvc_status_str(kvc_status status);
+int32_t kvc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H_ */

@@ -1,0 +1,11 @@
+"""Compressed KV-cache codec and attention for AMD MI355X (gfx950).
+
+The compute path is libkvc.so (hand-written HIP kernels behind the C ABI in
+include/kvc.h); ``kvc`` is a thin ctypes binding that marshals torch tensors
+(device memory and the current stream) into it.
+"""
+from .kvc import (  # noqa: F401
+    BASE_CENTROID, BASE_COEFF, BASE_DPLR, BASE_NONE, BASE_TEMPORAL, BF16, F32, BaseParams,
+    Codec, KvcError, Store, kvc_attend_compressed, kvc_attend_mixed_dim, kvc_decode,
+    kvc_encode, kvc_store_bytes, kvc_workspace_bytes, lib,
+)

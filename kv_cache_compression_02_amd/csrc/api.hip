@@ -1,0 +1,302 @@
+// C-ABI entry points: host-side validation, then an asynchronous launch on the
+// caller's stream.  No device memory is allocated here; no exception crosses the
+// ABI.  See include/kvc.h for the contract of every call.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "kvc.h"
+#include "kvc_internal.h"
+
+using namespace kvc;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validate a codec and derive the per-vector layout.
+kvc_status resolve_codec(const kvc_codec* c, CodecArgs* out) {
+  if (!c) return KVC_E_NULL;
+  CodecArgs a;
+  a.H = c->heads;
+  a.D = c->head_dim;
+  a.bits = c->bits;
+  a.group = c->group;
+  a.base = c->base;
+  a.C = c->n_centroids;
+  a.rank = c->rank;
+  a.n_inputs = c->n_inputs;
+  a.m = c->coeff_dim;
+  a.x_dtype = c->x_dtype;
+  if (a.H < 1 || a.H > 4096) return KVC_E_SHAPE;
+  if (a.D != 64 && a.D != 128) return KVC_E_UNSUPPORTED;
+  if (a.bits != 2 && a.bits != 4) return KVC_E_UNSUPPORTED;
+  if (a.group != 16 && a.group != 32 && a.group != 64 && a.group != 128) return KVC_E_UNSUPPORTED;
+  if (a.x_dtype != KVC_F32 && a.x_dtype != KVC_BF16) return KVC_E_UNSUPPORTED;
+  a.vec_len = a.D;
+  switch (a.base) {
+    case KVC_BASE_NONE: break;
+    case KVC_BASE_CENTROID:
+      if (a.C < 1 || a.C > 65535) return KVC_E_SHAPE;
+      break;
+    case KVC_BASE_COEFF:
+      if (a.C < 1 || a.C > 65535) return KVC_E_SHAPE;
+      if (a.m != 16) return KVC_E_UNSUPPORTED;
+      a.vec_len = a.m;
+      break;
+    case KVC_BASE_TEMPORAL:
+      if (a.x_dtype != KVC_BF16) return KVC_E_UNSUPPORTED;
+      break;
+    case KVC_BASE_DPLR:
+      if (a.x_dtype != KVC_BF16 || a.D != 128) return KVC_E_UNSUPPORTED;
+      if (a.rank < 16 || a.rank > 256 || a.rank % 16) return KVC_E_SHAPE;
+      if (a.n_inputs != 1 && a.n_inputs != 2) return KVC_E_SHAPE;
+      break;
+    default: return KVC_E_UNSUPPORTED;
+  }
+  if ((a.base == KVC_BASE_DPLR || a.base == KVC_BASE_TEMPORAL) && !predict_available()) {
+    // temporal keys are elementwise and always available; the matrix-product
+    // predictors are checked again where the base parameters are known
+    if (a.base == KVC_BASE_DPLR) return KVC_E_UNSUPPORTED;
+  }
+  if (a.vec_len % a.group) return KVC_E_SHAPE;
+  a.code_words = a.vec_len * a.bits / 32;
+  a.groups = a.vec_len / a.group;
+  a.index_bytes = (a.base == KVC_BASE_CENTROID || a.base == KVC_BASE_COEFF) ? (a.C <= 256 ? 1 : 2) : 0;
+  *out = a;
+  return KVC_OK;
+}
+
+kvc_status resolve_store(const kvc_store* s, const CodecArgs& c, StoreArgs* out) {
+  if (!s) return KVC_E_NULL;
+  if (!s->codes || !s->scale_zero) return KVC_E_NULL;
+  if (c.index_bytes && !s->index) return KVC_E_NULL;
+  if (!aligned16(s->codes) || !aligned16(s->scale_zero)) return KVC_E_ALIGN;
+  if (c.index_bytes && !aligned16(s->index)) return KVC_E_ALIGN;
+  if (s->capacity < 0) return KVC_E_SHAPE;
+  out->codes = s->codes;
+  out->sz = s->scale_zero;
+  out->index = s->index;
+  out->capacity = s->capacity;
+  return KVC_OK;
+}
+
+kvc_status resolve_base(const kvc_base_params* b, const CodecArgs& c, BaseArgs* out, bool need_prev) {
+  if (c.base == KVC_BASE_NONE) return KVC_OK;
+  if (!b) return KVC_E_NULL;
+  BaseArgs a;
+  a.centroids = b->centroids;
+  a.basis = b->basis;
+  a.prev0 = b->prev0;
+  a.prev1 = b->prev1;
+  a.aux = b->aux;
+  a.w_block = b->w_block;
+  a.u = b->u;
+  a.v_lr = b->v_lr;
+  a.coef_a = b->coef_a;
+  a.coef_b = b->coef_b;
+  a.prev_stride = b->prev_token_stride ? b->prev_token_stride : (int64_t)c.H * c.D;
+  if (a.prev_stride < (int64_t)c.H * c.D) return KVC_E_SHAPE;
+  switch (c.base) {
+    case KVC_BASE_CENTROID:
+      if (!a.centroids) return KVC_E_NULL;
+      if (!aligned16(a.centroids)) return KVC_E_ALIGN;
+      break;
+    case KVC_BASE_COEFF:
+      if (!a.centroids || !a.basis) return KVC_E_NULL;
+      if (!aligned16(a.centroids) || !aligned16(a.basis)) return KVC_E_ALIGN;
+      break;
+    case KVC_BASE_TEMPORAL:
+      if (!need_prev) break;
+      if (!a.prev0 || !a.coef_a) return KVC_E_NULL;
+      if (a.w_block) {   // values: M aux + beta prev0
+        if (!predict_available()) return KVC_E_UNSUPPORTED;
+        if (!a.aux) return KVC_E_NULL;
+        if (a.coef_b) return KVC_E_SHAPE;
+      } else {           // keys: a prev0 + b prev1
+        if (!a.prev1 || !a.coef_b) return KVC_E_NULL;
+      }
+      break;
+    case KVC_BASE_DPLR:
+      if (!need_prev) break;
+      if (!a.prev0 || !a.w_block || !a.u || !a.v_lr) return KVC_E_NULL;
+      if (c.n_inputs == 2 && !a.prev1) return KVC_E_NULL;
+      break;
+    default: break;
+  }
+  const void* ptrs[] = {a.prev0, a.prev1, a.aux, a.w_block, a.u, a.v_lr, a.coef_a, a.coef_b};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return KVC_E_ALIGN;
+  *out = a;
+  return KVC_OK;
+}
+
+kvc_status from_hip(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_E_DEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvc_abi_version(void) { return KVC_ABI_VERSION; }
+
+const char* kvc_status_str(kvc_status s) {
+  switch (s) {
+    case KVC_OK: return "ok";
+    case KVC_E_NULL: return "a required pointer is NULL";
+    case KVC_E_SHAPE: return "sizes inconsistent or out of range";
+    case KVC_E_UNSUPPORTED: return "unsupported codec, dtype or size";
+    case KVC_E_ALIGN: return "device pointer not 16-byte aligned";
+    case KVC_E_WORKSPACE: return "workspace too small";
+    case KVC_E_DEVICE: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+kvc_status kvc_store_bytes(const kvc_codec* codec, int64_t capacity, size_t* codes_bytes,
+                           size_t* scale_zero_bytes, size_t* index_bytes) {
+  CodecArgs c;
+  kvc_status st = resolve_codec(codec, &c);
+  if (st != KVC_OK) return st;
+  if (capacity < 0) return KVC_E_SHAPE;
+  const size_t rows = (size_t)c.H * (size_t)capacity;
+  if (codes_bytes) *codes_bytes = rows * c.code_words * 4u;
+  if (scale_zero_bytes) *scale_zero_bytes = rows * c.groups * 4u;
+  if (index_bytes) *index_bytes = rows * c.index_bytes;
+  return KVC_OK;
+}
+
+size_t kvc_workspace_bytes(int32_t op, const kvc_codec* codec, int64_t n_tokens, int64_t n_queries) {
+  (void)n_queries;
+  CodecArgs c;
+  if (resolve_codec(codec, &c) != KVC_OK || n_tokens < 0) return 0;
+  if (op == 0 || op == 1) return encode_workspace_bytes(c, n_tokens);
+  return 0;
+}
+
+kvc_status kvc_encode(const kvc_codec* codec, const void* x, int64_t n_tokens,
+                      int64_t x_token_stride, const kvc_base_params* base, const kvc_store* dst,
+                      int64_t token_offset, void* recon_out, float* pred_out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  EncodeLaunch a;
+  kvc_status st = resolve_codec(codec, &a.c);
+  if (st != KVC_OK) return st;
+  if (n_tokens < 0 || token_offset < 0) return KVC_E_SHAPE;
+  if (!x && n_tokens > 0) return KVC_E_NULL;   // an empty call may pass NULL buffers
+  if (!aligned16(x) || (recon_out && !aligned16(recon_out)) || (pred_out && !aligned16(pred_out)))
+    return KVC_E_ALIGN;
+  const int64_t hd = (int64_t)a.c.H * a.c.D;
+  const int64_t stride = x_token_stride ? x_token_stride : hd;
+  if (stride < hd) return KVC_E_SHAPE;
+  st = resolve_store(dst, a.c, &a.st);
+  if (st != KVC_OK) return st;
+  if (token_offset + n_tokens > a.st.capacity) return KVC_E_SHAPE;
+  st = resolve_base(base, a.c, &a.b, true);
+  if (st != KVC_OK) return st;
+  if (a.c.base == KVC_BASE_COEFF && recon_out) return KVC_E_UNSUPPORTED;
+  const size_t need = encode_workspace_bytes(a.c, n_tokens);
+  if (need && !pred_out) {
+    if (!workspace) return KVC_E_WORKSPACE;
+    if (workspace_bytes < need) return KVC_E_WORKSPACE;
+    if (!aligned16(workspace)) return KVC_E_ALIGN;
+  }
+  a.x = x;
+  a.n_tokens = n_tokens;
+  a.x_stride = stride;
+  a.token_offset = token_offset;
+  a.recon = recon_out;
+  a.pred = pred_out;
+  a.workspace = workspace;
+  return from_hip(launch_encode(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+kvc_status kvc_decode(const kvc_codec* codec, const kvc_store* src, int64_t token_offset,
+                      int64_t n_tokens, const kvc_base_params* base, void* out, int32_t out_dtype,
+                      float* pred_out, void* stream) {
+  DecodeLaunch a;
+  kvc_status st = resolve_codec(codec, &a.c);
+  if (st != KVC_OK) return st;
+  if (a.c.base == KVC_BASE_COEFF) return KVC_E_UNSUPPORTED;
+  if (n_tokens < 0 || token_offset < 0) return KVC_E_SHAPE;
+  if (!out && n_tokens > 0) return KVC_E_NULL;
+  if (!aligned16(out) || (pred_out && !aligned16(pred_out))) return KVC_E_ALIGN;
+  if (out_dtype != KVC_F32 && out_dtype != KVC_BF16) return KVC_E_UNSUPPORTED;
+  st = resolve_store(src, a.c, &a.st);
+  if (st != KVC_OK) return st;
+  if (token_offset + n_tokens > a.st.capacity) return KVC_E_SHAPE;
+  st = resolve_base(base, a.c, &a.b, true);
+  if (st != KVC_OK) return st;
+  if (encode_workspace_bytes(a.c, n_tokens) && !pred_out) return KVC_E_UNSUPPORTED;
+  a.n_tokens = n_tokens;
+  a.token_offset = token_offset;
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.pred = pred_out;
+  return from_hip(launch_decode(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+static kvc_status check_attend(const kvc_codec* kc, const kvc_store* k, const kvc_base_params* kp,
+                               const kvc_codec* vc, const kvc_store* v, const kvc_base_params* vp,
+                               int64_t n_keys, const void* q, int64_t n_queries, float* out,
+                               float* lse, AttendLaunch* a) {
+  kvc_status st = resolve_codec(kc, &a->kc);
+  if (st != KVC_OK) return st;
+  st = resolve_codec(vc, &a->vc);
+  if (st != KVC_OK) return st;
+  if (n_keys < 1 || n_queries < 0) return KVC_E_SHAPE;
+  if ((!q || !out) && n_queries > 0) return KVC_E_NULL;
+  if (!aligned16(q) || !aligned16(out) || (lse && !aligned16(lse))) return KVC_E_ALIGN;
+  if (a->kc.H != a->vc.H || a->kc.D != a->vc.D || a->kc.x_dtype != a->vc.x_dtype) return KVC_E_SHAPE;
+  st = resolve_store(k, a->kc, &a->ks);
+  if (st != KVC_OK) return st;
+  st = resolve_store(v, a->vc, &a->vs);
+  if (st != KVC_OK) return st;
+  if (n_keys > a->ks.capacity || n_keys > a->vs.capacity) return KVC_E_SHAPE;
+  st = resolve_base(kp, a->kc, &a->kb, false);
+  if (st != KVC_OK) return st;
+  st = resolve_base(vp, a->vc, &a->vb, false);
+  if (st != KVC_OK) return st;
+  a->n_keys = n_keys;
+  a->n_queries = n_queries;
+  a->q = q;
+  a->out = out;
+  a->lse = lse;
+  return KVC_OK;
+}
+
+kvc_status kvc_attend_compressed(const kvc_codec* kc, const kvc_store* k,
+                                 const kvc_base_params* kp, const kvc_codec* vc,
+                                 const kvc_store* v, const kvc_base_params* vp, int64_t n_keys,
+                                 const void* q, int64_t n_queries, float softmax_scale,
+                                 float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  AttendLaunch a;
+  kvc_status st = check_attend(kc, k, kp, vc, v, vp, n_keys, q, n_queries, out, lse, &a);
+  if (st != KVC_OK) return st;
+  for (const CodecArgs* c : {&a.kc, &a.vc})
+    if (c->base != KVC_BASE_NONE && c->base != KVC_BASE_CENTROID) return KVC_E_UNSUPPORTED;
+  if (a.kc.x_dtype == KVC_BF16 && a.kc.D != 128) return KVC_E_UNSUPPORTED;
+  a.scale = softmax_scale;
+  return from_hip(launch_attend(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+kvc_status kvc_attend_mixed_dim(const kvc_codec* kc, const kvc_store* k,
+                                const kvc_base_params* kp, const kvc_codec* vc,
+                                const kvc_store* v, const kvc_base_params* vp, int64_t n_keys,
+                                const void* q, int64_t n_queries, float softmax_scale,
+                                float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  AttendLaunch a;
+  kvc_status st = check_attend(kc, k, kp, vc, v, vp, n_keys, q, n_queries, out, lse, &a);
+  if (st != KVC_OK) return st;
+  if (a.kc.base != KVC_BASE_COEFF || a.vc.base != KVC_BASE_CENTROID) return KVC_E_UNSUPPORTED;
+  if (a.kc.x_dtype != KVC_BF16 || a.kc.D != 128) return KVC_E_UNSUPPORTED;
+  a.scale = softmax_scale;
+  return from_hip(launch_attend_mixed(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

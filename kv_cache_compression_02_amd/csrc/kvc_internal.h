@@ -1,0 +1,89 @@
+// Internal interface between the C-ABI entry points (api.hip) and the kernel
+// translation units.  Host-side plain structs; no torch types anywhere.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kvc.h"
+
+namespace kvc {
+
+// Everything a codec kernel needs, resolved and validated on the host.
+struct CodecArgs {
+  int H = 0, D = 0, bits = 0, group = 0, base = 0, C = 0, rank = 0, n_inputs = 0, m = 0;
+  int x_dtype = 0;
+  int vec_len = 0;     // values quantized per token-head (D, or m for COEFF)
+  int code_words = 0;  // uint32 words per token-head
+  int groups = 0;      // scale/zero words per token-head
+  int index_bytes = 0; // 1 or 2 (0 when no index)
+};
+
+struct StoreArgs {
+  uint32_t* codes = nullptr;
+  uint32_t* sz = nullptr;
+  void* index = nullptr;
+  int64_t capacity = 0;
+};
+
+struct BaseArgs {
+  const void* centroids = nullptr;
+  const void* basis = nullptr;
+  const void* prev0 = nullptr;
+  const void* prev1 = nullptr;
+  const void* aux = nullptr;
+  const void* w_block = nullptr;
+  const void* u = nullptr;
+  const void* v_lr = nullptr;
+  const float* coef_a = nullptr;
+  const float* coef_b = nullptr;
+  int64_t prev_stride = 0;
+};
+
+struct EncodeLaunch {
+  CodecArgs c;
+  StoreArgs st;
+  BaseArgs b;
+  const void* x = nullptr;
+  int64_t n_tokens = 0, x_stride = 0, token_offset = 0;
+  void* recon = nullptr;
+  float* pred = nullptr;
+  void* workspace = nullptr;
+};
+
+struct DecodeLaunch {
+  CodecArgs c;
+  StoreArgs st;
+  BaseArgs b;
+  int64_t n_tokens = 0, token_offset = 0;
+  void* out = nullptr;
+  int out_dtype = 0;
+  float* pred = nullptr;
+  void* workspace = nullptr;
+};
+
+struct AttendLaunch {
+  CodecArgs kc, vc;
+  StoreArgs ks, vs;
+  BaseArgs kb, vb;
+  int64_t n_keys = 0, n_queries = 0;
+  const void* q = nullptr;
+  float scale = 0.f;
+  float* out = nullptr;
+  float* lse = nullptr;
+};
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s);
+hipError_t launch_decode(const DecodeLaunch& a, hipStream_t s);
+hipError_t launch_attend(const AttendLaunch& a, hipStream_t s);
+hipError_t launch_attend_mixed(const AttendLaunch& a, hipStream_t s);
+
+// Whether the matrix-product predictor bases (DPLR, temporal values) are built.
+bool predict_available();
+
+// Workspace bytes of the predictor paths (0 otherwise).
+size_t encode_workspace_bytes(const CodecArgs& c, int64_t n_tokens);
+
+}  // namespace kvc
