@@ -6,9 +6,11 @@
 // bf16 (or fp32) cache would hold: every decoded value is rounded to the cache
 // dtype before it meets a query.
 //
-// bf16 path (d = 128), one workgroup = 4 wave64 = 128 queries of one head:
-//   per 64-key tile: all 256 threads decode K (row-major) and V (transposed) into
-//   LDS as bf16, then each wave computes S^T = K Q^T for its 32 queries with
+// bf16 path (d = 128), one workgroup = 8 wave64 = 256 queries of one head:
+//   per 64-key tile: all 512 threads decode K (row-major bf16) and V (transposed
+//   fp16) into one of two LDS buffers from compressed rows prefetched a tile earlier
+//   with buffer loads (indices two tiles earlier), while the other buffer is consumed:
+//   each wave computes S^T = K Q^T for its 32 queries with
 //   v_mfma_f32_32x32x16_bf16 (a lane owns one query column, so the softmax row
 //   reductions are in-lane plus one cross-half exchange), runs the online
 //   softmax in fp32 with exp2, rounds P to fp16 (nearest even) and accumulates
@@ -92,27 +94,241 @@ __device__ __forceinline__ void decode8(const Src& s, int h, int64_t key, int ch
 // bf16 MFMA path
 // ----------------------------------------------------------------------------
 constexpr int BK = 64;           // keys per tile
-constexpr int NW = 4;            // waves per workgroup
+constexpr int NW = 8;            // waves per workgroup (two per SIMD)
 constexpr int QW = 32;           // queries per wave
 constexpr int BQ = NW * QW;      // queries per workgroup
+constexpr int NT = NW * 64;      // threads per workgroup
 constexpr int DM = 128;          // head dim of the MFMA path
 constexpr int KROW = DM + 8;     // K tile row (bf16 elements), padded
-constexpr int VROW = BK + 4;     // V^T tile row (bf16 elements), padded
+constexpr int VROW = BK + 8;     // V^T tile row (fp16 elements), padded
 
-__global__ __launch_bounds__(NW * 64, 2) void attend_bf16_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[BK * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[DM * VROW];   // fp16 bits
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float byte_f(uint32_t x, int k) { return (float)((x >> (8 * k)) & 0xFFu); }
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  bf2 v = {(__bf16)a, (__bf16)b};   // v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+// packed bf16 pair -> packed fp16 pair holding the same values (exact for |v| in
+// 2^-14..65504; nearest even otherwise)
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  h2 v = {(_Float16)lo_bf16(w), (_Float16)hi_bf16(w)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Value held by lane l ^ 32 (v_permlane32_swap: the upper half of the first operand
+// and the lower half of the second trade places).
+__device__ __forceinline__ float other_half(float x, int half) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(half ? r[0] : r[1]);
+}
+
+// Registers a thread prefetches for one tile.
+template <int BITS>
+struct KPre {                     // key kk, channels 16w..16w+15
+  uint32_t code[BITS / 2];
+  uint32_t sz;
+  uint4 c0, c1;
+};
+struct VPre {                     // keys 2kp, 2kp+1, channels 8c8..8c8+7
+  uint32_t code[2];
+  uint32_t sz[2];
+  uint4 c[2];
+};
+
+// V^T tile swizzle: row r keeps its keys in groups of 4, XOR-permuted by (r/8) mod 8
+// so that the transposed writes of 16 lanes (rows 8 apart) and the MFMA operand reads
+// spread over the LDS banks.
+__device__ __forceinline__ int vswz(int row, int key) { return key ^ (((row >> 3) & 7) << 2); }
+
+template <int BITS, int VBITS, bool KCEN, bool VCEN>
+__global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BK * KROW];   // bf16
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][DM * VROW];   // fp16 bits
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int half = lane >> 5;     // which 8-wide k-slice of an MFMA operand
-  const int col = lane & 31;      // query (S^T column) / row index of an operand
+  const int half = lane >> 5;
+  const int col = lane & 31;
   const int nqb = (int)((p.nq + BQ - 1) / BQ);
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int h = tile / nqb;
-  const int64_t q0 = (int64_t)(tile % nqb) * BQ + wave * QW;
-  const int64_t myq = q0 + col;
+  const int64_t myq = (int64_t)(tile % nqb) * BQ + wave * QW + col;
+  const int nk = (int)p.nk;
+  const int ntiles = (nk + BK - 1) / BK;
+
+  // Per-head buffer resources (SGPRs): every prefetch is a buffer load with a 32-bit
+  // byte offset, and the descriptor's record count bounds it - a read past the head's
+  // rows (the tail of the last tile) returns zeros instead of touching other memory.
+  auto rsrc = [](const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+  };
+  const int kwb = p.k.words * 4, kgb = p.k.groups * 4;   // bytes per key row
+  const int vwb = p.v.words * 4, vgb = p.v.groups * 4;
+  const int64_t khrow = (int64_t)h * p.k.cap, vhrow = (int64_t)h * p.v.cap;
+  const auto rk_code = rsrc(p.k.codes + khrow * p.k.words, p.k.cap * kwb);
+  const auto rk_sz = rsrc(p.k.sz + khrow * p.k.groups, p.k.cap * kgb);
+  const auto rv_code = rsrc(p.v.codes + vhrow * p.v.words, p.v.cap * vwb);
+  const auto rv_sz = rsrc(p.v.sz + vhrow * p.v.groups, p.v.cap * vgb);
+  const auto rk_idx = rsrc(reinterpret_cast<const uint8_t*>(p.k.index) + khrow * p.k.idxb,
+                           KCEN ? p.k.cap * p.k.idxb : 0);
+  const auto rv_idx = rsrc(reinterpret_cast<const uint8_t*>(p.v.index) + vhrow * p.v.idxb,
+                           VCEN ? p.v.cap * p.v.idxb : 0);
+  const auto rk_cen = rsrc(reinterpret_cast<const uint16_t*>(p.k.cen) + (int64_t)h * p.k.C * DM,
+                           KCEN ? (int64_t)p.k.C * DM * 2 : 0);
+  const auto rv_cen = rsrc(reinterpret_cast<const uint16_t*>(p.v.cen) + (int64_t)h * p.v.C * DM,
+                           VCEN ? (int64_t)p.v.C * DM * 2 : 0);
+
+  // decode roles: 8 lanes share a K row (16 channels each), 16 lanes share a V row (8
+  // channels each), so every load instruction reads whole contiguous rows
+  const int kk = tid >> 3, kw = tid & 7;          // K: key kk, channels 16kw..16kw+15
+  const int c8 = tid & 15, kp = tid >> 4;         // V: keys 2kp, 2kp+1, channels 8c8..8c8+7
+  const int kword = (16 * kw * BITS) >> 5;        // first code word of the 16 channels
+  const int kgrp = (16 * kw) / p.k.group;
+  const int vword = (8 * c8 * VBITS) >> 5;
+  const int vgrp = (8 * c8) / p.v.group;
+  const int vsh = (8 * c8 * VBITS) & 31;          // bit offset of the 8 codes in their word
+  // index entries are read as the aligned dword holding them (k0 is a multiple of 64, so
+  // the shift within the dword depends on the thread only)
+  const uint32_t kimask = p.k.idxb == 1 ? 0xFFu : 0xFFFFu, vimask = p.v.idxb == 1 ? 0xFFu : 0xFFFFu;
+  const uint32_t kish = 8u * ((uint32_t)(kk * p.k.idxb) & 3u);
+  const uint32_t vish0 = 8u * ((uint32_t)(2 * kp * p.v.idxb) & 3u);
+  const uint32_t vish1 = 8u * ((uint32_t)((2 * kp + 1) * p.v.idxb) & 3u);
+
+  auto idx_of = [](uint32_t word, uint32_t sh, uint32_t mask, int C) -> uint32_t {
+    return min((word >> sh) & mask, (uint32_t)(C - 1));
+  };
+  // the raw index words are kept in registers; shift, mask and clamp happen at use
+  auto load_idx = [&](int t, int& ki, int (&vi)[2]) {
+    const uint32_t k0 = (uint32_t)(t * BK);
+    if constexpr (KCEN)
+      ki = (int)__builtin_amdgcn_raw_buffer_load_b32(rk_idx, ((k0 + kk) * p.k.idxb) & ~3u, 0, 0);
+    else
+      ki = 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if constexpr (VCEN)
+        vi[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(
+            rv_idx, ((k0 + 2 * kp + j) * p.v.idxb) & ~3u, 0, 0);
+      else
+        vi[j] = 0;
+    }
+  };
+  auto load_data = [&](int t, int ki, const int (&vi)[2], KPre<BITS>& kpr, VPre& vp) {
+    const uint32_t k0 = (uint32_t)(t * BK);
+    const uint32_t n = k0 + kk;
+    if constexpr (BITS == 2) {
+      kpr.code[0] = __builtin_amdgcn_raw_buffer_load_b32(rk_code, n * kwb + kword * 4, 0, 0);
+    } else {
+      typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+      const u2 c = __builtin_amdgcn_raw_buffer_load_b64(rk_code, n * kwb + kword * 4, 0, 0);
+      kpr.code[0] = c.x;
+      kpr.code[1] = c.y;
+    }
+    kpr.sz = __builtin_amdgcn_raw_buffer_load_b32(rk_sz, n * kgb + kgrp * 4, 0, 0);
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    if constexpr (KCEN) {
+      const uint32_t off = idx_of((uint32_t)ki, kish, kimask, p.k.C) * (DM * 2) + 32 * kw;
+      const u4 a0 = __builtin_amdgcn_raw_buffer_load_b128(rk_cen, off, 0, 0);
+      const u4 a1 = __builtin_amdgcn_raw_buffer_load_b128(rk_cen, off + 16, 0, 0);
+      kpr.c0 = uint4{a0.x, a0.y, a0.z, a0.w};
+      kpr.c1 = uint4{a1.x, a1.y, a1.z, a1.w};
+    } else {
+      kpr.c0 = uint4{0u, 0u, 0u, 0u};
+      kpr.c1 = kpr.c0;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t m = k0 + 2 * kp + j;
+      vp.code[j] = __builtin_amdgcn_raw_buffer_load_b32(rv_code, m * vwb + vword * 4, 0, 0);
+      vp.sz[j] = __builtin_amdgcn_raw_buffer_load_b32(rv_sz, m * vgb + vgrp * 4, 0, 0);
+      if constexpr (VCEN) {
+        const uint32_t off =
+            idx_of((uint32_t)vi[j], j ? vish1 : vish0, vimask, p.v.C) * (DM * 2) + 16 * c8;
+        const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rv_cen, off, 0, 0);
+        vp.c[j] = uint4{a.x, a.y, a.z, a.w};
+      } else {
+        vp.c[j] = uint4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto dequant = [&](const KPre<BITS>& kpr, const VPre& vp, int buf) {
+    // ---- K: 16 consecutive channels of key kk -> row-major bf16
+    {
+      const float sc = f16_bits_to_f32(kpr.sz & 0xFFFFu), ze = f16_bits_to_f32(kpr.sz >> 16);
+      float q[16];
+      if constexpr (BITS == 2) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t b = (kpr.code[0] >> (2 * r)) & 0x03030303u;   // codes r, r+4, r+8, r+12
+#pragma unroll
+          for (int k = 0; k < 4; ++k) q[r + 4 * k] = byte_f(b, k);
+        }
+      } else {
+#pragma unroll
+        for (int wd = 0; wd < 2; ++wd)
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            const uint32_t b = (kpr.code[wd] >> (4 * r)) & 0x0F0F0F0Fu;  // codes r, r+2, r+4, r+6
+#pragma unroll
+            for (int k = 0; k < 4; ++k) q[8 * wd + r + 2 * k] = byte_f(b, k);
+          }
+      }
+      const uint32_t cw[8] = {kpr.c0.x, kpr.c0.y, kpr.c0.z, kpr.c0.w, kpr.c1.x, kpr.c1.y, kpr.c1.z, kpr.c1.w};
+      uint32_t o[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x0 = lo_bf16(cw[i]) + __builtin_fmaf(q[2 * i], sc, ze);
+        const float x1 = hi_bf16(cw[i]) + __builtin_fmaf(q[2 * i + 1], sc, ze);
+        o[i] = pk_bf16(x0, x1);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(&k_lds[buf][kk * KROW + 16 * kw]);
+      dst[0] = uint4{o[0], o[1], o[2], o[3]};
+      dst[1] = uint4{o[4], o[5], o[6], o[7]};
+    }
+    // ---- V: channels 8c8..8c8+7 of keys 2kp, 2kp+1 -> transposed fp16 (swizzled)
+    {
+      float x[2][8];   // [key j][channel c]
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float sc = f16_bits_to_f32(vp.sz[j] & 0xFFFFu), ze = f16_bits_to_f32(vp.sz[j] >> 16);
+        float q[8];
+        if constexpr (VBITS == 2) {
+          const uint32_t w = vp.code[j] >> vsh;               // 8 codes in bits 0..15
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t b = (w >> (2 * r)) & 0x0303u;       // codes r, r+4
+            q[r] = byte_f(b, 0);
+            q[r + 4] = byte_f(b, 1);
+          }
+        } else {
+          const uint32_t w = vp.code[j];                       // 8 codes in bits 0..31
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            const uint32_t b = (w >> (4 * r)) & 0x0F0F0F0Fu;   // codes r, r+2, r+4, r+6
+#pragma unroll
+            for (int k = 0; k < 4; ++k) q[r + 2 * k] = byte_f(b, k);
+          }
+        }
+        const uint32_t cw[4] = {vp.c[j].x, vp.c[j].y, vp.c[j].z, vp.c[j].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[j][2 * i] = lo_bf16(cw[i]) + __builtin_fmaf(q[2 * i], sc, ze);
+          x[j][2 * i + 1] = hi_bf16(cw[i]) + __builtin_fmaf(q[2 * i + 1], sc, ze);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int row = 8 * c8 + c;
+        const uint32_t w = bf16x2_to_f16x2(pk_bf16(x[0][c], x[1][c]));   // keys 2kp, 2kp+1
+        *reinterpret_cast<uint32_t*>(&v_lds[buf][row * VROW + vswz(row, 2 * kp)]) = w;
+      }
+    }
+  };
 
   // Q^T operand: lane holds Q[myq][16*ks + 8*half .. +7] for ks = 0..7
   bf16x8_t qreg[8];
@@ -132,127 +348,128 @@ __global__ __launch_bounds__(NW * 64, 2) void attend_bf16_kernel(AttnParams p) {
     for (int r = 0; r < 16; ++r) oacc[d][r] = 0.0f;
   float m_run = -__builtin_inff();
   float l_run = 0.0f;
+  const float c2 = p.scale_log2;
 
-  for (int64_t k0 = 0; k0 < p.nk; k0 += BK) {
-    __syncthreads();
-    // ---- decode K tile: item -> (key = item / 16, chunk = item % 16), row-major
-#pragma unroll
-    for (int it = 0; it < (BK * DM / 8) / (NW * 64); ++it) {
-      const int item = tid + it * NW * 64;
-      const int kk = item >> 4, c8 = item & 15;
-      const int64_t key = k0 + kk;
-      uint4 w = {0u, 0u, 0u, 0u};
-      if (key < p.nk) {
-        float v[8];
-        decode8<uint16_t, DM>(p.k, h, key, c8 * 8, v);
-        w.x = pack_bf16x2(v[0], v[1]);
-        w.y = pack_bf16x2(v[2], v[3]);
-        w.z = pack_bf16x2(v[4], v[5]);
-        w.w = pack_bf16x2(v[6], v[7]);
-      }
-      *reinterpret_cast<uint4*>(&k_lds[kk * KROW + c8 * 8]) = w;
-    }
-    // ---- decode V tile transposed: thread -> (chunk = tid / 16, keys 4*(tid%16)..+3)
-    {
-      const int c8 = tid >> 4;
-      const int kq = tid & 15;
-      float v[4][8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t key = k0 + 4 * kq + j;
-        if (key < p.nk) decode8<uint16_t, DM>(p.v, h, key, c8 * 8, v[j]);
-        else {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) v[j][k] = 0.0f;
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        // bf16 cache value, held exactly in fp16 (round-toward-zero is exact here)
-        uint2 w;
-        w.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(round_bf16_f32(v[0][c]),
-                                                                      round_bf16_f32(v[1][c])));
-        w.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(round_bf16_f32(v[2][c]),
-                                                                      round_bf16_f32(v[3][c])));
-        *reinterpret_cast<uint2*>(&v_lds[(c8 * 8 + c) * VROW + 4 * kq]) = w;
-      }
-    }
-    __syncthreads();
-
-    // ---- S^T = K Q^T for 64 keys (two 32-key blocks)
+  auto compute = [&](int t, int buf) {
+    const int k0 = t * BK;
+    // S^T = K Q^T (raw scores)
+    // K fragments stream through two groups of 4 registers: the reads of group g+1
+    // are in flight while the 4 MFMAs of group g run
     f32x16_t sacc[2];
+    const uint16_t* krow = &k_lds[buf][col * KROW + 8 * half];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+    bf16x8_t kf[2][4];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8_t a =
-            *reinterpret_cast<const bf16x8_t*>(&k_lds[(kb * 32 + col) * KROW + 16 * ks + 8 * half]);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc[kb], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) kf[0][i] = *reinterpret_cast<const bf16x8_t*>(krow + 16 * i);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {   // g: (kb, ks half) = (g >> 1, g & 1)
+      if (g + 1 < 4) {
+        const int kb1 = (g + 1) >> 1, k1 = 4 * ((g + 1) & 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          kf[(g + 1) & 1][i] =
+              *reinterpret_cast<const bf16x8_t*>(krow + kb1 * 32 * KROW + 16 * (k1 + i));
       }
+      const int kb = g >> 1, k0s = 4 * (g & 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[g & 1][i], qreg[k0s + i], sacc[kb], 0, 0, 0);
     }
-
-    // ---- online softmax (log2 domain); lane = query `col`, 32 of the tile's keys
-    float s[32];
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int g = 0; g < 3; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      if (g < 2) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    if (k0 + BK > nk) {   // last, partial tile: mask keys >= nk
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= nk) sacc[kb][r] = -__builtin_inff();
+    }
     float mloc = -__builtin_inff();
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t key = k0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        float x = sacc[kb][r] * p.scale_log2;
-        x = (key < p.nk) ? x : -__builtin_inff();
-        s[kb * 16 + r] = x;
-        mloc = fmaxf(mloc, x);
-      }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
+      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[kb][r]);
+    mloc = fmaxf(mloc, other_half(mloc, half));
+    const float m_new = fmaxf(m_run, mloc * c2);     // log2 domain (scale > 0)
     const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float negm = -m_new;
     float lsum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      s[i] = __builtin_amdgcn_exp2f(s[i] - m_new);
-      lsum += s[i];
-    }
-    lsum += __shfl_xor(lsum, 32);
-    l_run = l_run * corr + lsum;
-    m_run = m_new;
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[d][r] *= corr;
-
-    // ---- P^T operands (fp16, nearest even): (kb, hf) covers keys
-    //      32*kb + 16*hf + {4*half+0..3, 8+4*half+0..3}
     f16x8_t pb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const float* sp = &s[kb * 16 + hf * 8];
-        f16x8_t t;
+        f16x8_t t8;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) t[j] = (_Float16)sp[j];
-        pb[kb][hf] = t;
+        for (int j = 0; j < 8; ++j) {
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * hf + j], c2, negm));
+          lsum += e;
+          t8[j] = (_Float16)e;
+        }
+        pb[kb][hf] = t8;
       }
-
-    // ---- O^T += V^T P^T
+    lsum += other_half(lsum, half);
+    l_run = l_run * corr + lsum;
+    m_run = m_new;
+    if (!__all(corr == 1.0f)) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[d][r] *= corr;
+    }
+    // O^T += V^T P^T; (kb, hf) covers keys 32*kb + 16*hf + {4*half+0..3, 8+4*half+0..3}
+    f16x8_t vf[4];
+    auto load_v = [&](int d, f16x8_t (&dst)[4]) {
+      const int row = d * 32 + col;
+      const uint16_t* vrow = &v_lds[buf][row * VROW];
+#pragma unroll
+      for (int kh = 0; kh < 4; ++kh) {   // kh = 2*kb + hf
+        const int kb0 = 16 * kh + 4 * half;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + vswz(row, kb0));
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + vswz(row, kb0 + 8));
+        dst[kh] = __builtin_bit_cast(f16x8_t, uint4{lo.x, lo.y, hi.x, hi.y});
+      }
+    };
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const uint16_t* vrow = &v_lds[(d * 32 + col) * VROW];
+      load_v(d, vf);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int kbase = kb * 32 + hf * 16 + 4 * half;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + kbase);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + kbase + 8);
-          const uint4 w = {lo.x, lo.y, hi.x, hi.y};
-          const f16x8_t a = __builtin_bit_cast(f16x8_t, w);
-          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[kb][hf], oacc[d], 0, 0, 0);
-        }
+      for (int kh = 0; kh < 4; ++kh)
+        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[kh], pb[kh >> 1][kh & 1], oacc[d], 0, 0, 0);
     }
+  };
+
+  // ---- prologue: tile 0 decoded into buffer 0, tile 1 prefetched, indices of tile 2
+  KPre<BITS> kpre;
+  VPre vpre;
+  int kidx, vidx[2];
+  load_idx(0, kidx, vidx);
+  load_data(0, kidx, vidx, kpre, vpre);
+  if (ntiles > 1) load_idx(1, kidx, vidx);
+  dequant(kpre, vpre, 0);
+  if (ntiles > 1) load_data(1, kidx, vidx, kpre, vpre);
+  if (ntiles > 2) load_idx(2, kidx, vidx);
+  __syncthreads();
+
+  // ---- main loop: decode tile t+1 into the other buffer, prefetch tile t+2's
+  //      compressed rows (and t+3's indices), then attend tile t
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) {
+      dequant(kpre, vpre, buf ^ 1);
+      if (t + 2 < ntiles) load_data(t + 2, kidx, vidx, kpre, vpre);
+      if (t + 3 < ntiles) load_idx(t + 3, kidx, vidx);
+    }
+    compute(t, buf);
+    __syncthreads();
   }
 
   // ---- epilogue: O[q][h][c] = O^T[c][q] / l
@@ -381,7 +598,24 @@ hipError_t launch_attend(const AttendLaunch& a, hipStream_t s) {
   p.v = make_src(a.vc, a.vs, a.vb);
   if (a.kc.x_dtype == KVC_BF16) {
     const int nqb = (int)((a.n_queries + BQ - 1) / BQ);
-    hipLaunchKernelGGL(attend_bf16_kernel, dim3(nqb * a.kc.H), dim3(NW * 64), 0, s, p);
+    const dim3 grid(nqb * a.kc.H), block(NT);
+    const bool kc = p.k.mode == SRC_CENTROID, vc = p.v.mode == SRC_CENTROID;
+    // every (K bits, V bits, K base, V base) combination is its own kernel so the
+    // prefetch loads stay branch-free
+#define KVC_ATT(KB_, VB_, KC_, VC_)                                                       \
+  if (a.kc.bits == KB_ && a.vc.bits == VB_ && kc == KC_ && vc == VC_) {                 \
+    hipLaunchKernelGGL((attend_bf16_kernel<KB_, VB_, KC_, VC_>), grid, block, 0, s, p); \
+    return hipGetLastError();                                                            \
+  }
+#define KVC_ATT_BITS(KC_, VC_) \
+  KVC_ATT(2, 2, KC_, VC_) KVC_ATT(2, 4, KC_, VC_) KVC_ATT(4, 2, KC_, VC_) KVC_ATT(4, 4, KC_, VC_)
+    KVC_ATT_BITS(true, true)
+    KVC_ATT_BITS(true, false)
+    KVC_ATT_BITS(false, true)
+    KVC_ATT_BITS(false, false)
+#undef KVC_ATT_BITS
+#undef KVC_ATT
+    return hipErrorInvalidValue;
   } else {
     const int nqb = (int)((a.n_queries + 63) / 64);
     if (a.kc.D == 128)
