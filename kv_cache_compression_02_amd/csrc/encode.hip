@@ -206,6 +206,269 @@ __global__ __launch_bounds__(NTHREADS) void encode_kernel(EncodeParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Nearest centroid with an MFMA shortlist (bf16, d = 128).
+//
+// x . c_j for every centroid runs on v_mfma_f32_32x32x16_bf16 (bf16 products are
+// exact; fp32 accumulation).  With n_j = ||c_j||^2 and the token norm, the expanded
+// distance A_j = n_j - 2 x.c_j differs from the exact D_j - ||x||^2 by at most
+// E_j = 2 (d + 4) u (n_j + 2 ||x|| ||c_j||), u = 2^-24 (both sums carry at most d
+// rounding errors of relative size u; the factor 2 is slack).  U = min_j (A_j + E_j)
+// bounds the best exact distance from above; every centroid whose lower bound
+// A_j - E_j lies within U + 8 (d + 4) u (|U| + ||x||^2) - a margin covering the
+// oracle's own fp32 rounding of the direct-form sums - is rescored with exactly
+// the oracle's arithmetic (fp32, ascending channels, ties to the lowest index).
+// Every centroid outside that set is provably farther in the oracle's arithmetic,
+// so the index equals the oracle's bit for bit.
+// ---------------------------------------------------------------------------
+template <int TOK>
+__global__ __launch_bounds__(NTHREADS, 1) void encode_shortlist_kernel(EncodeParams p) {
+  constexpr int D = 128;
+  constexpr int XROW = D + 8;                 // bf16 elements per staged token row
+  constexpr int CCH = 256;                    // centroid rows per staged chunk
+  constexpr int CROW = D + 8;
+  constexpr int CMAX = TOK == 64 ? 256 : 512;
+  constexpr int SROW = CMAX + 1;              // fp32 expanded distances per token
+  constexpr int PARTS = NTHREADS / TOK;       // threads cooperating on one token
+  __shared__ __attribute__((aligned(16))) uint16_t xs[TOK * XROW];
+  __shared__ __attribute__((aligned(16))) uint16_t ct[CCH * CROW];
+  __shared__ float sm[TOK * SROW];
+  __shared__ float cn2[CMAX], cn1[CMAX];
+  __shared__ float xn2[TOK], xn1[TOK];
+  __shared__ int aidx[TOK];
+  // after the argmin the distance buffer holds the coefficients and the chosen rows
+  float (*cbuf)[17] = reinterpret_cast<float (*)[17]>(sm);
+  uint16_t* brow = reinterpret_cast<uint16_t*>(sm + TOK * 17);   // [TOK][XROW] bf16
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ntiles = (int)((p.n_tokens + TOK - 1) / TOK);
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = tile / ntiles;
+  const int64_t n0 = (int64_t)(tile % ntiles) * TOK;
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(p.x);
+  const uint16_t* cen = reinterpret_cast<const uint16_t*>(p.centroids) + (int64_t)h * p.C * D;
+
+  // 1. token tile (16-byte rows pieces), zero rows past the end
+  for (int e = tid; e < TOK * (D / 8); e += NTHREADS) {
+    const int t = e / (D / 8), c = e % (D / 8);
+    const int64_t n = n0 + t;
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (n < p.n_tokens) v = *reinterpret_cast<const uint4*>(x + n * p.x_stride + (int64_t)h * D + 8 * c);
+    *reinterpret_cast<uint4*>(&xs[t * XROW + 8 * c]) = v;
+  }
+  __syncthreads();
+  // squared norm of a staged bf16 row (any order: it only feeds the error bound)
+  auto row_norm2 = [](const uint16_t* row) {
+    float s2 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < D; i += 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(row + i);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float lo = bf16_bits_to_f32(w[k] & 0xFFFFu), hi = bf16_bits_to_f32(w[k] >> 16);
+        s2 = __builtin_fmaf(lo, lo, s2);
+        s2 = __builtin_fmaf(hi, hi, s2);
+      }
+    }
+    return s2;
+  };
+  if (tid < TOK) {
+    const float s2 = row_norm2(&xs[tid * XROW]);
+    xn2[tid] = s2;
+    xn1[tid] = sqrtf(s2);
+  }
+
+  // 2. expanded distances, one staged chunk of centroids at a time
+  const int col = lane & 31, half = lane >> 5;
+  int last_c0 = 0, last_nc = 0;
+  for (int c0 = 0; c0 < p.C; c0 += CCH) {
+    const int nc = min(CCH, p.C - c0);
+    __syncthreads();
+    for (int e = tid; e < CCH * (D / 8); e += NTHREADS) {
+      const int j = e / (D / 8), c = e % (D / 8);
+      uint4 v = {0u, 0u, 0u, 0u};
+      if (j < nc) v = *reinterpret_cast<const uint4*>(cen + (int64_t)(c0 + j) * D + 8 * c);
+      *reinterpret_cast<uint4*>(&ct[j * CROW + 8 * c]) = v;
+    }
+    __syncthreads();
+    for (int j = tid; j < nc; j += NTHREADS) {
+      const float s2 = row_norm2(&ct[j * CROW]);
+      cn2[c0 + j] = s2;
+      cn1[c0 + j] = sqrtf(s2);
+    }
+    __syncthreads();
+    constexpr int NB = (TOK / 32) * (CCH / 32);      // 32x32 output blocks
+    for (int b = wave; b < NB; b += NTHREADS / 64) {
+      const int tb = b / (CCH / 32), cb = b % (CCH / 32);
+      if (cb * 32 >= nc) continue;
+      f32x16_t acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&xs[(32 * tb + col) * XROW + 16 * ks + 8 * half]);
+        const bf16x8_t bb = *reinterpret_cast<const bf16x8_t*>(&ct[(32 * cb + col) * CROW + 16 * ks + 8 * half]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc, 0, 0, 0);
+      }
+      const int j = 32 * cb + col;
+      if (j < nc) {
+        const float nj = cn2[c0 + j];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 32 * tb + 8 * (r >> 2) + 4 * half + (r & 3);
+          sm[t * SROW + c0 + j] = nj - 2.0f * acc[r];
+        }
+      }
+    }
+    last_c0 = c0;
+    last_nc = nc;
+  }
+  __syncthreads();
+
+  // 3. shortlist bound per token: PARTS consecutive lanes share a token, each owning a
+  //    contiguous run of SPAN centroids read as 16-byte LDS vectors
+  constexpr int SPAN = CMAX / PARTS;     // 64 in both configurations
+  const int t = tid / PARTS, q = tid % PARTS;
+  const int j0 = q * SPAN;
+  const float g = 2.0f * (float)(D + 4) * 5.9604645e-8f;   // 2 (d + 4) 2^-24
+  const float xn2x = 2.0f * xn1[t], xx = xn2[t];
+  float lbv[SPAN];
+  float ub = __builtin_inff();
+#pragma unroll
+  for (int i = 0; i < SPAN; i += 4) {
+    const float4 a4 = *reinterpret_cast<const float4*>(&sm[t * SROW + j0 + i]);
+    const float4 n2 = *reinterpret_cast<const float4*>(&cn2[j0 + i]);
+    const float4 n1 = *reinterpret_cast<const float4*>(&cn1[j0 + i]);
+    const float av[4] = {a4.x, a4.y, a4.z, a4.w}, nv2[4] = {n2.x, n2.y, n2.z, n2.w},
+                nv1[4] = {n1.x, n1.y, n1.z, n1.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bool valid = j0 + i + k < p.C;
+      const float e = g * __builtin_fmaf(xn2x, nv1[k], nv2[k]);
+      ub = valid ? fminf(ub, av[k] + e) : ub;
+      lbv[i + k] = valid ? av[k] - e : __builtin_inff();
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < PARTS; o <<= 1) ub = fminf(ub, __shfl_xor(ub, o));
+  const float T = ub + 4.0f * g * (fabsf(ub) + xx);
+  uint64_t cand = 0;
+#pragma unroll
+  for (int i = 0; i < SPAN; ++i) cand |= (uint64_t)(lbv[i] <= T) << i;
+
+  // 4. exact rescoring of the shortlist (the oracle's fp32 direct form), ascending j
+  float best = __builtin_inff();
+  int bestj = 0x7FFFFFFF;
+  while (cand) {
+    const int i = __builtin_ctzll(cand);
+    cand &= cand - 1;
+    const int j = j0 + i;
+    const bool resident = j >= last_c0 && j < last_c0 + last_nc;
+    const uint16_t* crow = resident ? &ct[(j - last_c0) * CROW] : cen + (int64_t)j * D;
+    float acc = 0.0f;
+    for (int ii = 0; ii < D; ii += 8) {
+      const uint4 xv = *reinterpret_cast<const uint4*>(&xs[t * XROW + ii]);
+      const uint4 cv = *reinterpret_cast<const uint4*>(crow + ii);
+      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, cw[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float d0 = bf16_bits_to_f32(xw[k] & 0xFFFFu) - bf16_bits_to_f32(cw[k] & 0xFFFFu);
+        float sq0 = d0 * d0;
+        acc = acc + sq0;
+        float d1 = bf16_bits_to_f32(xw[k] >> 16) - bf16_bits_to_f32(cw[k] >> 16);
+        float sq1 = d1 * d1;
+        acc = acc + sq1;
+      }
+    }
+    if (acc < best) { best = acc; bestj = j; }   // ascending j: first minimum wins ties
+  }
+#pragma unroll
+  for (int o = 1; o < PARTS; o <<= 1) {
+    const float ob = __shfl_xor(best, o);
+    const int oj = __shfl_xor(bestj, o);
+    if (ob < best || (ob == best && oj < bestj)) { best = ob; bestj = oj; }
+  }
+  if (q == 0) {
+    aidx[t] = bestj;
+    const int64_t n = n0 + t;
+    if (n < p.n_tokens) {
+      const int64_t row = (int64_t)h * p.capacity + p.token_offset + n;
+      if (p.index_bytes == 1) reinterpret_cast<uint8_t*>(p.index)[row] = (uint8_t)bestj;
+      else reinterpret_cast<uint16_t*>(p.index)[row] = (uint16_t)bestj;
+    }
+  }
+  __syncthreads();
+  // stage each token's centroid row (16-byte pieces)
+  for (int e = tid; e < TOK * (D / 8); e += NTHREADS) {
+    const int tt = e / (D / 8), c = e % (D / 8);
+    *reinterpret_cast<uint4*>(&brow[tt * XROW + 8 * c]) =
+        *reinterpret_cast<const uint4*>(cen + (int64_t)aidx[tt] * D + 8 * c);
+  }
+  __syncthreads();
+
+  // 5. coefficients of the centroid residual (fp32, ascending channels)
+  if (p.mode == MODE_COEFF) {
+    for (int e = tid; e < TOK * p.m; e += NTHREADS) {
+      const int tt = e / p.m, j = e % p.m;
+      const uint16_t* crow = &brow[tt * XROW];
+      float acc = 0.0f;
+      for (int i = 0; i < D; ++i) {
+        const float r = bf16_bits_to_f32(xs[tt * XROW + i]) - bf16_bits_to_f32(crow[i]);
+        const float b = bf16_bits_to_f32(p.basis[i * p.m + j]);
+        const float prod = r * b;
+        acc = acc + prod;
+      }
+      cbuf[tt][j] = acc;
+    }
+    __syncthreads();
+  }
+
+  // 6. quantize + pack, one thread per (token, group)
+  const int levels = (1 << p.bits) - 1;
+  const int per_word = 32 / p.bits;
+  const int gsz = p.group;
+  for (int item = tid; item < TOK * p.groups; item += NTHREADS) {
+    const int tt = item / p.groups, gi = item % p.groups;
+    const int64_t n = n0 + tt;
+    if (n >= p.n_tokens) continue;
+    const int i0 = gi * gsz;
+    const uint16_t* crow = &brow[tt * XROW];
+    const int64_t xrow = (n * p.H + h) * (int64_t)D;
+    auto value_at = [&](int i) -> float {
+      if (p.mode == MODE_COEFF) return cbuf[tt][i];
+      return bf16_bits_to_f32(xs[tt * XROW + i]) - bf16_bits_to_f32(crow[i]);
+    };
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+    for (int i = 0; i < gsz; ++i) {
+      const float r = value_at(i0 + i);
+      mn = fminf(mn, r);
+      mx = fmaxf(mx, r);
+    }
+    const GroupQ gq = group_scale_zero(mn, mx, levels);
+    const int64_t row = (int64_t)h * p.capacity + p.token_offset + n;
+    p.sz[row * p.groups + gi] = gq.word;
+    const int words = gsz / per_word;
+    for (int wd = 0; wd < words; ++wd) {
+      uint32_t word = 0;
+      for (int k = 0; k < per_word; ++k) {
+        const int i = i0 + wd * per_word + k;
+        const uint32_t code = quantize_one(value_at(i), gq, levels);
+        word |= code << (p.bits * k);
+        if (p.mode != MODE_COEFF && (p.recon || p.pred)) {
+          const float bsv = bf16_bits_to_f32(crow[i]);
+          if (p.pred) p.pred[xrow + i] = bsv;
+          if (p.recon) {
+            const float xh = bsv + dequant_one(code, gq.s, gq.z);
+            reinterpret_cast<uint16_t*>(p.recon)[xrow + i] = (uint16_t)f32_to_bf16_bits(xh);
+          }
+        }
+      }
+      p.codes[row * p.code_words + (i0 / per_word) + wd] = word;
+    }
+  }
+}
+
 template <typename XT, int D>
 hipError_t launch_encode_t(const EncodeParams& p, int H, hipStream_t s) {
   const int ntiles = (int)((p.n_tokens + TOK - 1) / TOK);
@@ -267,6 +530,18 @@ hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   const bool bf16 = a.c.x_dtype == KVC_BF16;
+  // centroid and coefficient bases on bf16 d = 128 data: MFMA shortlist + exact rescoring
+  if (bf16 && a.c.D == 128 && (p.mode == MODE_CENTROID || p.mode == MODE_COEFF) &&
+      p.x_stride % 8 == 0 && a.c.C <= 512) {
+    if (a.c.C <= 256) {
+      const int ntiles = (int)((p.n_tokens + 63) / 64);
+      hipLaunchKernelGGL(encode_shortlist_kernel<64>, dim3(ntiles * a.c.H), dim3(NTHREADS), 0, s, p);
+    } else {
+      const int ntiles = (int)((p.n_tokens + 31) / 32);
+      hipLaunchKernelGGL(encode_shortlist_kernel<32>, dim3(ntiles * a.c.H), dim3(NTHREADS), 0, s, p);
+    }
+    return hipGetLastError();
+  }
   if (a.c.D == 128) {
     return bf16 ? launch_encode_t<uint16_t, 128>(p, a.c.H, s) : launch_encode_t<float, 128>(p, a.c.H, s);
   }
