@@ -294,7 +294,9 @@ kvc_status kvc_attend_mixed_dim(const kvc_codec* kc, const kvc_store* k,
   kvc_status st = check_attend(kc, k, kp, vc, v, vp, n_keys, q, n_queries, out, lse, &a);
   if (st != KVC_OK) return st;
   if (a.kc.base != KVC_BASE_COEFF || a.vc.base != KVC_BASE_CENTROID) return KVC_E_UNSUPPORTED;
-  if (a.kc.x_dtype != KVC_BF16 || a.kc.D != 128) return KVC_E_UNSUPPORTED;
+  if (a.kc.x_dtype != KVC_BF16 || a.kc.D != 128 || a.kc.m != 16 || a.kc.groups != 1)
+    return KVC_E_UNSUPPORTED;
+  if (!a.kb.basis) return KVC_E_NULL;
   a.scale = softmax_scale;
   return from_hip(launch_attend_mixed(a, reinterpret_cast<hipStream_t>(stream)));
 }

@@ -49,6 +49,7 @@ struct AttnParams {
   float* out;
   float* lse;
   Src k, v;
+  const uint16_t* basis;   // mixed-dimensional keys: [d][m] bf16
 };
 
 // Decode channels ch0..ch0+7 of key `key` (head h) as fp32 (cache dtype XT rounding
@@ -143,9 +144,15 @@ struct VPre {                     // keys 2kp, 2kp+1, channels 8c8..8c8+7
 // spread over the LDS banks.
 __device__ __forceinline__ int vswz(int row, int key) { return key ^ (((row >> 3) & 7) << 2); }
 
-template <int BITS, int VBITS, bool KCEN, bool VCEN>
+// MIXED: keys are NanoKV-Fast coefficient records.  The K tile then holds, per key,
+// the centroid row C[a] (128 bf16) followed by the dequantized coefficients c split
+// into bf16 high and low parts (16 + 16); the queries carry B^T q split the same way,
+// and three extra MFMA steps add (B^T q) . c to q . C[a] with about 2^-16 relative
+// error - the score is formed without reconstructing the key.
+template <int BITS, int VBITS, bool KCEN, bool VCEN, bool MIXED>
 __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BK * KROW];   // bf16
+  constexpr int KR = MIXED ? DM + 32 + 8 : KROW;   // K tile row (bf16 elements)
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BK * KR];     // bf16
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][DM * VROW];   // fp16 bits
 
   const int tid = threadIdx.x;
@@ -187,8 +194,10 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
   // channels each), so every load instruction reads whole contiguous rows
   const int kk = tid >> 3, kw = tid & 7;          // K: key kk, channels 16kw..16kw+15
   const int c8 = tid & 15, kp = tid >> 4;         // V: keys 2kp, 2kp+1, channels 8c8..8c8+7
-  const int kword = (16 * kw * BITS) >> 5;        // first code word of the 16 channels
-  const int kgrp = (16 * kw) / p.k.group;
+  // first code word of the thread's 16 channels (MIXED: of coefficients 8kw..8kw+7)
+  const int kword = MIXED ? (8 * min(kw, 1) * BITS) >> 5 : (16 * kw * BITS) >> 5;
+  const int kcsh = MIXED ? (8 * min(kw, 1) * BITS) & 31 : 0;
+  const int kgrp = MIXED ? 0 : (16 * kw) / p.k.group;   // coefficients: one group per key
   const int vword = (8 * c8 * VBITS) >> 5;
   const int vgrp = (8 * c8) / p.v.group;
   const int vsh = (8 * c8 * VBITS) & 31;          // bit offset of the 8 codes in their word
@@ -221,7 +230,7 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
   auto load_data = [&](int t, int ki, const int (&vi)[2], KPre<BITS>& kpr, VPre& vp) {
     const uint32_t k0 = (uint32_t)(t * BK);
     const uint32_t n = k0 + kk;
-    if constexpr (BITS == 2) {
+    if constexpr (BITS == 2 || MIXED) {
       kpr.code[0] = __builtin_amdgcn_raw_buffer_load_b32(rk_code, n * kwb + kword * 4, 0, 0);
     } else {
       typedef uint32_t u2 __attribute__((ext_vector_type(2)));
@@ -257,8 +266,28 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
     }
   };
   auto dequant = [&](const KPre<BITS>& kpr, const VPre& vp, int buf) {
+    if constexpr (MIXED) {
+      // ---- K: centroid row chunk as is; lanes kw < 2 add 8 coefficients (hi, lo)
+      uint4* dst = reinterpret_cast<uint4*>(&k_lds[buf][kk * KR + 16 * kw]);
+      dst[0] = kpr.c0;
+      dst[1] = kpr.c1;
+      if (kw < 2) {
+        const float sc = f16_bits_to_f32(kpr.sz & 0xFFFFu), ze = f16_bits_to_f32(kpr.sz >> 16);
+        const uint32_t w = kpr.code[0] >> kcsh;
+        float cv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) cv[i] = __builtin_fmaf((float)((w >> (BITS * i)) & ((1u << BITS) - 1u)), sc, ze);
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          hi[i] = pk_bf16(cv[2 * i], cv[2 * i + 1]);
+          lo[i] = pk_bf16(cv[2 * i] - lo_bf16(hi[i]), cv[2 * i + 1] - hi_bf16(hi[i]));
+        }
+        *reinterpret_cast<uint4*>(&k_lds[buf][kk * KR + DM + 8 * kw]) = uint4{hi[0], hi[1], hi[2], hi[3]};
+        *reinterpret_cast<uint4*>(&k_lds[buf][kk * KR + DM + 16 + 8 * kw]) = uint4{lo[0], lo[1], lo[2], lo[3]};
+      }
+    } else {
     // ---- K: 16 consecutive channels of key kk -> row-major bf16
-    {
       const float sc = f16_bits_to_f32(kpr.sz & 0xFFFFu), ze = f16_bits_to_f32(kpr.sz >> 16);
       float q[16];
       if constexpr (BITS == 2) {
@@ -286,7 +315,7 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
         const float x1 = hi_bf16(cw[i]) + __builtin_fmaf(q[2 * i + 1], sc, ze);
         o[i] = pk_bf16(x0, x1);
       }
-      uint4* dst = reinterpret_cast<uint4*>(&k_lds[buf][kk * KROW + 16 * kw]);
+      uint4* dst = reinterpret_cast<uint4*>(&k_lds[buf][kk * KR + 16 * kw]);
       dst[0] = uint4{o[0], o[1], o[2], o[3]};
       dst[1] = uint4{o[4], o[5], o[6], o[7]};
     }
@@ -341,6 +370,47 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
     }
   }
 
+  // MIXED: (B^T q) for the lane's query as bf16 high / low parts, k-slice 8*half..+7
+  bf16x8_t phi = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0}, plo = phi;
+  if constexpr (MIXED) {
+    uint16_t* bst = &v_lds[1][0];   // the basis is staged in the not yet used V buffer
+    for (int e = tid; e < DM * 16 / 8; e += NT)
+      *reinterpret_cast<uint4*>(&bst[8 * e]) = *reinterpret_cast<const uint4*>(p.basis + 8 * e);
+    __syncthreads();
+    float part[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) part[j] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = 16 * ks + 8 * half + e;
+        const float qv = bf16_bits_to_f32((uint16_t)qreg[ks][e]);
+        const uint4 b0 = *reinterpret_cast<const uint4*>(&bst[16 * i]);
+        const uint4 b1 = *reinterpret_cast<const uint4*>(&bst[16 * i + 8]);
+        const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          part[2 * jj] = __builtin_fmaf(qv, lo_bf16(bw[jj]), part[2 * jj]);
+          part[2 * jj + 1] = __builtin_fmaf(qv, hi_bf16(bw[jj]), part[2 * jj + 1]);
+        }
+      }
+    float pj[8];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float full = part[j] + other_half(part[j], half);
+      if ((j >> 3) == half) pj[j & 7] = full;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t h2 = pk_bf16(pj[2 * i], pj[2 * i + 1]);
+      const uint32_t l2 = pk_bf16(pj[2 * i] - lo_bf16(h2), pj[2 * i + 1] - hi_bf16(h2));
+      phi[2 * i] = (short)(h2 & 0xFFFFu); phi[2 * i + 1] = (short)(h2 >> 16);
+      plo[2 * i] = (short)(l2 & 0xFFFFu); plo[2 * i + 1] = (short)(l2 >> 16);
+    }
+    __syncthreads();
+  }
+
   f32x16_t oacc[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d)
@@ -356,7 +426,7 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
     // K fragments stream through two groups of 4 registers: the reads of group g+1
     // are in flight while the 4 MFMAs of group g run
     f32x16_t sacc[2];
-    const uint16_t* krow = &k_lds[buf][col * KROW + 8 * half];
+    const uint16_t* krow = &k_lds[buf][col * KR + 8 * half];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -371,7 +441,7 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           kf[(g + 1) & 1][i] =
-              *reinterpret_cast<const bf16x8_t*>(krow + kb1 * 32 * KROW + 16 * (k1 + i));
+              *reinterpret_cast<const bf16x8_t*>(krow + kb1 * 32 * KR + 16 * (k1 + i));
       }
       const int kb = g >> 1, k0s = 4 * (g & 1);
 #pragma unroll
@@ -385,6 +455,17 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
       if (g < 2) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    if constexpr (MIXED) {   // + (B^T q) . c: hi*hi + hi*lo + lo*hi
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint16_t* r0 = &k_lds[buf][(kb * 32 + col) * KR + DM + 8 * half];
+        const bf16x8_t ch = *reinterpret_cast<const bf16x8_t*>(r0);
+        const bf16x8_t cl = *reinterpret_cast<const bf16x8_t*>(r0 + 16);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ch, phi, sacc[kb], 0, 0, 0);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ch, plo, sacc[kb], 0, 0, 0);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cl, phi, sacc[kb], 0, 0, 0);
+      }
+    }
     if (k0 + BK > nk) {   // last, partial tile: mask keys >= nk
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -577,7 +658,7 @@ Src make_src(const CodecArgs& c, const StoreArgs& st, const BaseArgs& b) {
   s.words = c.code_words;
   s.idxb = c.index_bytes;
   s.C = c.C;
-  s.mode = c.base == KVC_BASE_CENTROID ? SRC_CENTROID : SRC_NONE;
+  s.mode = (c.base == KVC_BASE_CENTROID || c.base == KVC_BASE_COEFF) ? SRC_CENTROID : SRC_NONE;
   return s;
 }
 
@@ -604,7 +685,7 @@ hipError_t launch_attend(const AttendLaunch& a, hipStream_t s) {
     // prefetch loads stay branch-free
 #define KVC_ATT(KB_, VB_, KC_, VC_)                                                       \
   if (a.kc.bits == KB_ && a.vc.bits == VB_ && kc == KC_ && vc == VC_) {                 \
-    hipLaunchKernelGGL((attend_bf16_kernel<KB_, VB_, KC_, VC_>), grid, block, 0, s, p); \
+    hipLaunchKernelGGL((attend_bf16_kernel<KB_, VB_, KC_, VC_, false>), grid, block, 0, s, p); \
     return hipGetLastError();                                                            \
   }
 #define KVC_ATT_BITS(KC_, VC_) \
@@ -624,6 +705,34 @@ hipError_t launch_attend(const AttendLaunch& a, hipStream_t s) {
       hipLaunchKernelGGL(attend_f32_kernel<64>, dim3(nqb * a.kc.H), dim3(64), 0, s, p);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_attend_mixed(const AttendLaunch& a, hipStream_t s) {
+  if (a.n_queries == 0) return hipSuccess;
+  if (a.kc.m != 16 || a.kc.groups != 1) return hipErrorInvalidValue;
+  AttnParams p{};
+  p.q = a.q;
+  p.nq = a.n_queries;
+  p.nk = a.n_keys;
+  p.H = a.kc.H;
+  p.scale = a.scale;
+  p.scale_log2 = a.scale * 1.4426950408889634f;
+  p.out = a.out;
+  p.lse = a.lse;
+  p.k = make_src(a.kc, a.ks, a.kb);
+  p.v = make_src(a.vc, a.vs, a.vb);
+  p.basis = reinterpret_cast<const uint16_t*>(a.kb.basis);
+  const int nqb = (int)((a.n_queries + BQ - 1) / BQ);
+  const dim3 grid(nqb * a.kc.H), block(NT);
+  const bool vc = p.v.mode == SRC_CENTROID;
+#define KVC_MIX(KB_, VB_, VC_)                                                           \
+  if (a.kc.bits == KB_ && a.vc.bits == VB_ && vc == VC_) {                              \
+    hipLaunchKernelGGL((attend_bf16_kernel<KB_, VB_, true, VC_, true>), grid, block, 0, s, p); \
+    return hipGetLastError();                                                            \
+  }
+  KVC_MIX(4, 2, true) KVC_MIX(4, 4, true) KVC_MIX(2, 2, true) KVC_MIX(2, 4, true)
+#undef KVC_MIX
+  return hipErrorInvalidValue;
 }
 
 }  // namespace kvc
