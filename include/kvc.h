@@ -111,14 +111,19 @@ typedef struct {
  *   COEFF:    centroids, basis [d][m] bf16 (orthonormal columns, shared by heads).
  *   DPLR:     prev0 = first input reconstruction (K_{l-1} for keys, K_l for values),
  *             prev1 = second input (V_{l-1}, values only), both bf16 [N][H][d];
- *             w_block [H][d][n_inputs*d], u [H*d][r], v_lr [n_inputs*H*d][r], bf16.
- *             prediction[h] = W_h [prev0_h ; prev1_h] + U (v_lr^T [prev0 ; prev1])[h].
+ *             w_block [H][d][n_inputs*d], u [H*d][r], v_lr [r][n_inputs*H*d], bf16
+ *             (every matrix is stored with its contraction index contiguous).
+ *             prediction[h] = W_h [prev0_h ; prev1_h] + U (v_lr [prev0 ; prev1])[h],
+ *             where [prev0 ; prev1] stacks all heads of prev0, then all of prev1.
  *   TEMPORAL: keys:   prediction = (coef_a * prev0) + (coef_b * prev1) per channel,
  *                     prev0 = K_{t-1}, prev1 = K_{t-2}, bf16 [N][H][d]; coef fp32 [H][d].
  *             values: prediction = M_h aux + (coef_a * prev0), aux = aligned K_t,
  *                     prev0 = V_{t-1}; M = w_block [H][d][d] bf16; coef_b = NULL.
  *   prev_token_stride: elements between consecutive tokens of prev0/prev1/aux
- *   (0 = H*d). */
+ *   (0 = H*d; a multiple of 8 for the matrix-product bases).
+ * Matrix-product bases (DPLR, temporal values) compute an fp32 prediction first: it
+ * goes to pred_out when given, else to the workspace; DPLR always needs the workspace
+ * (kvc_workspace_bytes) for its rank-r intermediate. */
 typedef struct {
   const void* centroids;
   const void* basis;
@@ -147,9 +152,11 @@ kvc_status kvc_store_bytes(const kvc_codec* codec, int64_t capacity, size_t* cod
  *   recon_out: optional [n][H][d] x_dtype reconstruction (base + dequantized
  *              residual, rounded to x_dtype) - the input of the next predictor step.
  *   pred_out:  optional [n][H][d] fp32 copy of the base used (prediction).
- *   workspace: unused by this version (pass NULL, 0).
+ *   workspace: device scratch of kvc_workspace_bytes(KVC_OP_ENCODE, ...) bytes for
+ *              the matrix-product bases (DPLR; temporal values without pred_out); the
+ *              contents on return are unspecified.  NULL, 0 otherwise.
  * Errors: KVC_E_NULL, KVC_E_SHAPE (token_offset + n_tokens > capacity, bad
- * codec), KVC_E_UNSUPPORTED, KVC_E_ALIGN, KVC_E_DEVICE. */
+ * codec), KVC_E_UNSUPPORTED, KVC_E_ALIGN, KVC_E_WORKSPACE, KVC_E_DEVICE. */
 kvc_status kvc_encode(const kvc_codec* codec, const void* x, int64_t n_tokens,
                       int64_t x_token_stride, const kvc_base_params* base, const kvc_store* dst,
                       int64_t token_offset, void* recon_out, float* pred_out, void* workspace,
@@ -158,11 +165,13 @@ kvc_status kvc_encode(const kvc_codec* codec, const void* x, int64_t n_tokens,
 /* kvc_decode - reconstruct rows [token_offset, token_offset + n_tokens) of a store:
  * out = base + ((code * s) + z), written as out_dtype [n][H][d] (bf16 output is the
  * fp32 value rounded to nearest even).  Predictor bases read `base` exactly as
- * kvc_encode did.  pred_out: optional fp32 base.
- * Errors: as kvc_encode. */
+ * kvc_encode did (so a chain decodes in the order it was encoded); pred_out:
+ * optional fp32 base; workspace: as kvc_encode.
+ * Errors: as kvc_encode; KVC_E_UNSUPPORTED for KVC_BASE_COEFF (those keys are only
+ * read by kvc_attend_mixed_dim). */
 kvc_status kvc_decode(const kvc_codec* codec, const kvc_store* src, int64_t token_offset,
                       int64_t n_tokens, const kvc_base_params* base, void* out, int32_t out_dtype,
-                      float* pred_out, void* stream);
+                      float* pred_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* kvc_attend_compressed - O = softmax(Q K^T * softmax_scale) V per head, no mask,
  * over n_keys keys held compressed in stores k and v (rows 0..n_keys-1); K and V
@@ -198,7 +207,9 @@ kvc_status kvc_attend_mixed_dim(const kvc_codec* kc, const kvc_store* k,
                                 float* out, float* lse, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
-/* Workspace bytes an entry point needs (0 for every entry point of this version). */
+/* Workspace bytes an entry point needs for n_tokens tokens (op: KVC_OP_*).  Nonzero
+ * only for encode / decode with the DPLR or temporal bases. */
+enum { KVC_OP_ENCODE = 0, KVC_OP_DECODE = 1, KVC_OP_ATTEND = 2, KVC_OP_ATTEND_MIXED = 3 };
 size_t kvc_workspace_bytes(int32_t op, const kvc_codec* codec, int64_t n_tokens,
                            int64_t n_queries);
 

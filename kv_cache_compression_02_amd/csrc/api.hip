@@ -134,6 +134,22 @@ kvc_status resolve_base(const kvc_base_params* b, const CodecArgs& c, BaseArgs* 
 
 kvc_status from_hip(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_E_DEVICE; }
 
+// Matrix-product bases need a buffer for the fp32 prediction (pred_out or the
+// workspace) and, for DPLR, the workspace for the rank-r intermediate.
+kvc_status check_predict_workspace(const CodecArgs& c, const BaseArgs& b, int64_t n_tokens,
+                                   const float* pred_out, const void* workspace,
+                                   size_t workspace_bytes) {
+  const bool matrix = c.base == KVC_BASE_DPLR || (c.base == KVC_BASE_TEMPORAL && b.w_block);
+  if (!matrix || n_tokens == 0) return KVC_OK;
+  if (b.prev_stride % 8) return KVC_E_ALIGN;   // 16-byte fragments of the inputs
+  const size_t need = encode_workspace_bytes(c, n_tokens);
+  if (c.base == KVC_BASE_DPLR || !pred_out) {
+    if (!workspace || workspace_bytes < need) return KVC_E_WORKSPACE;
+    if (!aligned16(workspace)) return KVC_E_ALIGN;
+  }
+  return KVC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -194,12 +210,8 @@ kvc_status kvc_encode(const kvc_codec* codec, const void* x, int64_t n_tokens,
   st = resolve_base(base, a.c, &a.b, true);
   if (st != KVC_OK) return st;
   if (a.c.base == KVC_BASE_COEFF && recon_out) return KVC_E_UNSUPPORTED;
-  const size_t need = encode_workspace_bytes(a.c, n_tokens);
-  if (need && !pred_out) {
-    if (!workspace) return KVC_E_WORKSPACE;
-    if (workspace_bytes < need) return KVC_E_WORKSPACE;
-    if (!aligned16(workspace)) return KVC_E_ALIGN;
-  }
+  st = check_predict_workspace(a.c, a.b, n_tokens, pred_out, workspace, workspace_bytes);
+  if (st != KVC_OK) return st;
   a.x = x;
   a.n_tokens = n_tokens;
   a.x_stride = stride;
@@ -212,7 +224,7 @@ kvc_status kvc_encode(const kvc_codec* codec, const void* x, int64_t n_tokens,
 
 kvc_status kvc_decode(const kvc_codec* codec, const kvc_store* src, int64_t token_offset,
                       int64_t n_tokens, const kvc_base_params* base, void* out, int32_t out_dtype,
-                      float* pred_out, void* stream) {
+                      float* pred_out, void* workspace, size_t workspace_bytes, void* stream) {
   DecodeLaunch a;
   kvc_status st = resolve_codec(codec, &a.c);
   if (st != KVC_OK) return st;
@@ -226,7 +238,9 @@ kvc_status kvc_decode(const kvc_codec* codec, const kvc_store* src, int64_t toke
   if (token_offset + n_tokens > a.st.capacity) return KVC_E_SHAPE;
   st = resolve_base(base, a.c, &a.b, true);
   if (st != KVC_OK) return st;
-  if (encode_workspace_bytes(a.c, n_tokens) && !pred_out) return KVC_E_UNSUPPORTED;
+  st = check_predict_workspace(a.c, a.b, n_tokens, pred_out, workspace, workspace_bytes);
+  if (st != KVC_OK) return st;
+  a.workspace = workspace;
   a.n_tokens = n_tokens;
   a.token_offset = token_offset;
   a.out = out;

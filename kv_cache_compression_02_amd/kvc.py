@@ -70,7 +70,7 @@ def lib():
     L.kvc_store_bytes.restype = I32
     L.kvc_encode.argtypes = [P(_Codec), VP, I64, I64, P(_Base), P(_Store), I64, VP, VP, VP, SZ, VP]
     L.kvc_encode.restype = I32
-    L.kvc_decode.argtypes = [P(_Codec), P(_Store), I64, I64, P(_Base), VP, I32, VP, VP]
+    L.kvc_decode.argtypes = [P(_Codec), P(_Store), I64, I64, P(_Base), VP, I32, VP, VP, SZ, VP]
     L.kvc_decode.restype = I32
     att = [P(_Codec), P(_Store), P(_Base), P(_Codec), P(_Store), P(_Base), I64, VP, I64,
            ctypes.c_float, VP, VP, VP, SZ, VP]
@@ -203,17 +203,27 @@ def kvc_encode(codec: Codec, x: torch.Tensor, store: Store, token_offset: int = 
 
 def kvc_decode(codec: Codec, store: Store, token_offset: int, n_tokens: int,
                base: Optional[BaseParams] = None, out: Optional[torch.Tensor] = None,
-               out_dtype: int = F32, pred_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+               out_dtype: int = F32, pred_out: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Reconstruct store rows [token_offset, token_offset + n_tokens) as [n][H][d]."""
     if out is None:
         dt = torch.float32 if out_dtype == F32 else torch.bfloat16
         out = torch.empty((n_tokens, codec.heads, codec.head_dim), dtype=dt,
                           device=store.codes.device)
     b = (base or BaseParams()).c()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().kvc_decode(ctypes.byref(codec.c()), ctypes.byref(store.c()), token_offset,
                             n_tokens, ctypes.byref(b), _p(out), out_dtype, _p(pred_out),
-                            _stream()), "kvc_decode")
+                            _p(workspace), ws_bytes, _stream()), "kvc_decode")
     return out
+
+
+def workspace_for(op: int, codec: Codec, n_tokens: int, device) -> Optional[torch.Tensor]:
+    """A device workspace of the size kvc_workspace_bytes reports (None when 0)."""
+    nbytes = kvc_workspace_bytes(op, codec, n_tokens)
+    if nbytes == 0:
+        return None
+    return torch.empty(((nbytes + 15) // 16) * 16, dtype=torch.uint8, device=device)
 
 
 def _attend(fn, name, kc, kstore, kbase, vc, vstore, vbase, n_keys, q, softmax_scale, out, lse,

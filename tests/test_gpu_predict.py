@@ -1,0 +1,191 @@
+"""GPU parity of the predictor bases through the C ABI: TempoKV-style temporal chains
+and Coral-KV-style cross-layer block-DPLR chains.
+
+Contract:
+* temporal keys: prediction (a * K_{t-1}) + (b * K_{t-2}) bit-exact, codes bit-exact;
+* matrix-product predictions (M_h K_t + beta V_{t-1}; block-DPLR): within the fp32
+  accumulation bound 2 (n + 4) 2^-24 sum|terms| of the fp64 oracle (n = length of the
+  longest sum; the rank-r intermediate adds its own bound and a 2^-15 relative term
+  for its bf16 high/low split), and codes bit-exact against the oracle quantizer run on
+  the GPU's own prediction (conditional bit-exactness);
+* chains are teacher-forced: every step reads the oracle's reconstructions, so
+  differences cannot compound; a free-running GPU chain is checked against the
+  quantizer's error bound per step."""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compression_02_amd as kvc
+import synth
+from oracle import codec as ocodec, numerics as nm, predict as opred
+from gpu_util import device, store_np, to_dev
+
+pytestmark = pytest.mark.gpu
+U = 2.0 ** -24
+
+
+def _bf16_dev(x_f32, dev):
+    return to_dev(nm.f32_to_bf16(x_f32), dev)
+
+
+def _enc(codec, x_bits, dev, base=None, ws=True):
+    n = x_bits.shape[0]
+    st = kvc.Store.allocate(codec, n, dev)
+    x = to_dev(x_bits, dev)
+    rec = torch.empty_like(x)
+    pred = torch.empty(x.shape, dtype=torch.float32, device=dev)
+    w = kvc.kvc.workspace_for(kvc.kvc.OP_ENCODE, codec, n, dev) if ws else None
+    kvc.kvc_encode(codec, x, st, 0, base, recon_out=rec, pred_out=pred, workspace=w)
+    torch.cuda.synchronize()
+    return st, rec, pred
+
+
+def _cond_exact(st, x_f32, pred_gpu, bits, group):
+    """Codes and scale/zero equal the oracle quantizer applied to the GPU prediction."""
+    want = opred.encode_with_prediction(x_f32, pred_gpu.astype(np.float64), bits, group)["store"]
+    got = store_np(st)
+    assert np.array_equal(got["codes"], want["codes"])
+    assert np.array_equal(got["scale_zero"], want["scale_zero"])
+
+
+def _quant_bound_ok(x, xhat, st, bits, group, base):
+    """|x - xhat| within the quantizer bound of each group (loose, per element)."""
+    got = store_np(st)
+    s16, z16 = ocodec.unpack_scale_zero(np.transpose(got["scale_zero"], (1, 0, 2)))
+    s = np.repeat(s16.astype(np.float64), group, axis=2)
+    r = (x.astype(np.float64) - base)
+    err = np.abs(xhat.astype(np.float64) - x)
+    # rounding of the reconstruction to bf16 adds up to half a bf16 ulp of |xhat|
+    assert np.all(err <= s * 0.5 + np.abs(r).max() * 1e-6 + np.abs(xhat) * 2.0 ** -8 + 1e-6)
+
+
+def test_temporal_chain_teacher_forced_and_free_running():
+    dev = device()
+    d = synth.cfg3(n_frames=5, query_frames=1, tokens=100, heads=4, dim=128)
+    H, T = d["heads"], d["tokens_per_frame"]
+    bits, g, ab = d["bits"], d["group"], d["anchor_bits"]
+    K = nm.bf16_to_f32(d["K"]).reshape(-1, T, H, 128)
+    V = nm.bf16_to_f32(d["V"]).reshape(-1, T, H, 128)
+    a, b, beta = d["a"], d["b"], d["beta"]
+    M = nm.bf16_to_f32(d["M"])
+    a_d, b_d, beta_d = (torch.from_numpy(v).to(dev) for v in (a, b, beta))
+    M_d = to_dev(d["M"], dev)
+    anchor = kvc.Codec(H, 128, ab, g, kvc.BASE_NONE)
+    kcod = kvc.Codec(H, 128, bits, g, kvc.BASE_TEMPORAL)
+    vcod = kvc.Codec(H, 128, bits, g, kvc.BASE_TEMPORAL)
+    oracle = list(opred.temporal_chain(list(K), list(V), a, b, M, beta, bits, g, ab))
+    gk = [None] * len(oracle)   # free-running GPU reconstructions (bf16 tensors)
+    gv = [None] * len(oracle)
+    for t, o in enumerate(oracle):
+        kx, vx = nm.f32_to_bf16(K[t]), nm.f32_to_bf16(V[t])
+        if t == 0:
+            st, rk, _ = _enc(anchor, kx, dev)
+            assert np.array_equal(store_np(st)["codes"], o["k"]["store"]["codes"])
+            st, rv, _ = _enc(anchor, vx, dev)
+            assert np.array_equal(store_np(st)["codes"], o["v"]["store"]["codes"])
+            gk[0], gv[0] = rk, rv
+            continue
+        prev = oracle[t - 1]
+        prev2 = oracle[t - 2] if t > 1 else prev
+        # keys, teacher-forced: bit-exact prediction and codes
+        base = kvc.BaseParams(prev0=_bf16_dev(prev["k"]["xhat"], dev),
+                              prev1=_bf16_dev(prev2["k"]["xhat"], dev), coef_a=a_d, coef_b=b_d)
+        st, _, pk = _enc(kcod, kx, dev, base)
+        assert np.array_equal(pk.cpu().numpy(), o["k"]["base"])
+        assert np.array_equal(store_np(st)["codes"], o["k"]["store"]["codes"])
+        assert np.array_equal(store_np(st)["scale_zero"], o["k"]["store"]["scale_zero"])
+        # values, teacher-forced: M_h K_t + beta V_{t-1}
+        kt = nm.round_bf16(o["k"]["xhat"]).astype(np.float64)
+        vp = nm.round_bf16(prev["v"]["xhat"]).astype(np.float64)
+        base = kvc.BaseParams(aux=_bf16_dev(o["k"]["xhat"], dev), prev0=_bf16_dev(prev["v"]["xhat"], dev),
+                              w_block=M_d, coef_a=beta_d)
+        st, _, pv = _enc(vcod, vx, dev, base)
+        pv = pv.cpu().numpy()
+        exact = opred.temporal_predict_v(o["k"]["xhat"], prev["v"]["xhat"], M, beta)
+        mag = np.stack([np.abs(kt[:, h]) @ np.abs(M[h]).T for h in range(H)], axis=1) \
+            + np.abs(beta) * np.abs(vp)
+        assert np.all(np.abs(pv - exact) <= 2 * (128 + 4) * U * mag + 1e-30)
+        _cond_exact(st, V[t], pv, bits, g)
+        # free-running GPU chain
+        base = kvc.BaseParams(prev0=gk[t - 1], prev1=gk[t - 2] if t > 1 else gk[t - 1],
+                              coef_a=a_d, coef_b=b_d)
+        st, rk, pk = _enc(kcod, kx, dev, base)
+        _quant_bound_ok(K[t], rk.float().cpu().numpy(), st, bits, g, pk.cpu().numpy())
+        base = kvc.BaseParams(aux=rk, prev0=gv[t - 1], w_block=M_d, coef_a=beta_d)
+        st, rv, pv = _enc(vcod, vx, dev, base)
+        _quant_bound_ok(V[t], rv.float().cpu().numpy(), st, bits, g, pv.cpu().numpy())
+        gk[t], gv[t] = rk, rv
+        # decode of the free-running store reproduces the encoder's reconstruction
+        w = kvc.kvc.workspace_for(kvc.kvc.OP_DECODE, vcod, vx.shape[0], dev)
+        out = kvc.kvc_decode(vcod, st, 0, vx.shape[0], base, out_dtype=kvc.BF16,
+                             pred_out=torch.empty(vx.shape, dtype=torch.float32, device=dev),
+                             workspace=w)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), rv.view(torch.int16))
+
+
+def _dplr_bound(xs, W, Uf, Vt, r):
+    """2 (n + 4) u sum|terms| for the block and low-rank sums (fp64 magnitudes)."""
+    n, H, D = xs[0].shape
+    nin = len(xs)
+    ax = np.concatenate([np.abs(x) for x in xs], axis=2)
+    blk = np.stack([ax[:, h] @ np.abs(W[h]).T for h in range(H)], axis=1)
+    alr = np.concatenate([np.abs(x).reshape(n, H * D) for x in xs], axis=1)
+    tmag = alr @ np.abs(Vt).T                                   # |V||x|, [n][r]
+    texact = np.concatenate([x.reshape(n, H * D) for x in xs], axis=1) @ Vt.T
+    terr = 2 * (nin * H * D + 4) * U * tmag + 2.0 ** -15 * np.abs(texact)
+    low = (terr @ np.abs(Uf).T + 2 * (r + 4) * U * (np.abs(texact) @ np.abs(Uf).T)).reshape(n, H, D)
+    return 2 * (nin * D + 4) * U * blk + low
+
+
+def test_dplr_chain_teacher_forced_and_free_running():
+    dev = device()
+    H, D, r, L, n = 3, 128, 16, 4, 100
+    prm = synth.cfg2_params(heads=H, dim=D, rank=r)
+    layers = [(nm.bf16_to_f32(k), nm.bf16_to_f32(v))
+              for k, v in synth.cfg2_layers(params=prm, n_tokens=n, n_layers=L, chunk=50)]
+    f = {k: nm.bf16_to_f32(prm[k]).astype(np.float64) for k in ("WK", "UK", "VK", "WV", "UV", "VV")}
+    oparams = dict(WK=f["WK"], UK=f["UK"], VK=f["VK"], WV=f["WV"], UV=f["UV"], VV=f["VV"])
+    oracle = list(opred.dplr_chain(layers, oparams, 2, 32, 4))
+    dv = {k: to_dev(prm[k], dev) for k in ("WK", "UK", "WV", "UV")}
+    # v_lr is stored [r][n_in*H*d] (contraction index contiguous)
+    vk_t = to_dev(np.ascontiguousarray(prm["VK"].T), dev)
+    vv_t = to_dev(np.ascontiguousarray(prm["VV"].T), dev)
+    anchor = kvc.Codec(H, D, 4, 32, kvc.BASE_NONE)
+    kcod = kvc.Codec(H, D, 2, 32, kvc.BASE_DPLR, rank=r, n_inputs=1)
+    vcod = kvc.Codec(H, D, 2, 32, kvc.BASE_DPLR, rank=r, n_inputs=2)
+    gk = gv = None
+    for l, ((kx, vx), o) in enumerate(zip(layers, oracle)):
+        kb, vb = nm.f32_to_bf16(kx), nm.f32_to_bf16(vx)
+        if l == 0:
+            st, gk, _ = _enc(anchor, kb, dev)
+            assert np.array_equal(store_np(st)["codes"], o["k"]["store"]["codes"])
+            st, gv, _ = _enc(anchor, vb, dev)
+            assert np.array_equal(store_np(st)["codes"], o["v"]["store"]["codes"])
+            continue
+        prev = oracle[l - 1]
+        kin = [nm.round_bf16(prev["k"]["xhat"]).astype(np.float64)]
+        base = kvc.BaseParams(prev0=_bf16_dev(prev["k"]["xhat"], dev), w_block=dv["WK"], u=dv["UK"],
+                              v_lr=vk_t)
+        st, _, pk = _enc(kcod, kb, dev, base)
+        pk = pk.cpu().numpy()
+        exact = opred.dplr_predict([prev["k"]["xhat"]], f["WK"], f["UK"], f["VK"])
+        assert np.all(np.abs(pk - exact) <= _dplr_bound(kin, f["WK"], f["UK"], f["VK"].T, r))
+        _cond_exact(st, kx, pk, 2, 32)
+        vin = [nm.round_bf16(o["k"]["xhat"]).astype(np.float64),
+               nm.round_bf16(prev["v"]["xhat"]).astype(np.float64)]
+        base = kvc.BaseParams(prev0=_bf16_dev(o["k"]["xhat"], dev), prev1=_bf16_dev(prev["v"]["xhat"], dev),
+                              w_block=dv["WV"], u=dv["UV"], v_lr=vv_t)
+        st, _, pv = _enc(vcod, vb, dev, base)
+        pv = pv.cpu().numpy()
+        exact = opred.dplr_predict([o["k"]["xhat"], prev["v"]["xhat"]], f["WV"], f["UV"], f["VV"])
+        assert np.all(np.abs(pv - exact) <= _dplr_bound(vin, f["WV"], f["UV"], f["VV"].T, r))
+        _cond_exact(st, vx, pv, 2, 32)
+        # free-running GPU chain
+        base = kvc.BaseParams(prev0=gk, w_block=dv["WK"], u=dv["UK"], v_lr=vk_t)
+        st, nk_, pk = _enc(kcod, kb, dev, base)
+        _quant_bound_ok(kx, nk_.float().cpu().numpy(), st, 2, 32, pk.cpu().numpy())
+        base = kvc.BaseParams(prev0=nk_, prev1=gv, w_block=dv["WV"], u=dv["UV"], v_lr=vv_t)
+        st, nv_, pv = _enc(vcod, vb, dev, base)
+        _quant_bound_ok(vx, nv_.float().cpu().numpy(), st, 2, 32, pv.cpu().numpy())
+        gk, gv = nk_, nv_
