@@ -86,7 +86,10 @@ typedef enum {
 typedef struct {
   int32_t heads;       /* H >= 1                                                 */
   int32_t head_dim;    /* d: 64 or 128                                           */
-  int32_t bits;        /* residual code width: 2 or 4                            */
+  int32_t bits;        /* residual code width: 2 or 4; 16 with KVC_BASE_NONE and
+                          bf16 marks an uncompressed cache (attention input only:
+                          store.codes then points to bf16 [capacity][H][d],
+                          token-major, and scale_zero / index are unused)       */
   int32_t group;       /* values per scale/zero group: 16, 32, 64 or 128; must
                           divide d (or coeff_dim for KVC_BASE_COEFF)             */
   int32_t base;        /* kvc_base_kind                                          */
@@ -179,6 +182,8 @@ kvc_status kvc_decode(const kvc_codec* codec, const kvc_store* src, int64_t toke
  * compressed history).  K and V codecs: KVC_BASE_CENTROID or KVC_BASE_NONE with
  * d = 128 and bf16 x_dtype (bf16 MFMA path; decoded values are rounded to bf16, as
  * a bf16 cache would hold them), or any d in {64, 128} with f32 x_dtype (fp32 path).
+ * bits = 16 on both K and V attends over uncompressed bf16 caches (for example the
+ * reconstructions a predictor chain decodes; each cache below 2 GiB).
  *   q:   [n_queries][H][d] x_dtype, token stride H*d.
  *   out: [n_queries][H][d] fp32.
  *   lse: optional [H][n_queries] fp32 natural-log sum-exp of the scaled scores.

@@ -31,6 +31,16 @@ kvc_status resolve_codec(const kvc_codec* c, CodecArgs* out) {
   a.x_dtype = c->x_dtype;
   if (a.H < 1 || a.H > 4096) return KVC_E_SHAPE;
   if (a.D != 64 && a.D != 128) return KVC_E_UNSUPPORTED;
+  if (a.bits == 16) {   // uncompressed bf16 cache, token-major (attention inputs only)
+    if (a.base != KVC_BASE_NONE || a.x_dtype != KVC_BF16) return KVC_E_UNSUPPORTED;
+    a.vec_len = a.D;
+    a.group = a.D;
+    a.code_words = a.D / 2;
+    a.groups = 0;
+    a.index_bytes = 0;
+    *out = a;
+    return KVC_OK;
+  }
   if (a.bits != 2 && a.bits != 4) return KVC_E_UNSUPPORTED;
   if (a.group != 16 && a.group != 32 && a.group != 64 && a.group != 128) return KVC_E_UNSUPPORTED;
   if (a.x_dtype != KVC_F32 && a.x_dtype != KVC_BF16) return KVC_E_UNSUPPORTED;
@@ -70,9 +80,9 @@ kvc_status resolve_codec(const kvc_codec* c, CodecArgs* out) {
 
 kvc_status resolve_store(const kvc_store* s, const CodecArgs& c, StoreArgs* out) {
   if (!s) return KVC_E_NULL;
-  if (!s->codes || !s->scale_zero) return KVC_E_NULL;
+  if (!s->codes || (c.groups && !s->scale_zero)) return KVC_E_NULL;
   if (c.index_bytes && !s->index) return KVC_E_NULL;
-  if (!aligned16(s->codes) || !aligned16(s->scale_zero)) return KVC_E_ALIGN;
+  if (!aligned16(s->codes) || (c.groups && !aligned16(s->scale_zero))) return KVC_E_ALIGN;
   if (c.index_bytes && !aligned16(s->index)) return KVC_E_ALIGN;
   if (s->capacity < 0) return KVC_E_SHAPE;
   out->codes = s->codes;
@@ -176,7 +186,7 @@ kvc_status kvc_store_bytes(const kvc_codec* codec, int64_t capacity, size_t* cod
   if (st != KVC_OK) return st;
   if (capacity < 0) return KVC_E_SHAPE;
   const size_t rows = (size_t)c.H * (size_t)capacity;
-  if (codes_bytes) *codes_bytes = rows * c.code_words * 4u;
+  if (codes_bytes) *codes_bytes = rows * c.code_words * 4u;   // bits 16: the bf16 cache
   if (scale_zero_bytes) *scale_zero_bytes = rows * c.groups * 4u;
   if (index_bytes) *index_bytes = rows * c.index_bytes;
   return KVC_OK;
@@ -197,6 +207,7 @@ kvc_status kvc_encode(const kvc_codec* codec, const void* x, int64_t n_tokens,
   EncodeLaunch a;
   kvc_status st = resolve_codec(codec, &a.c);
   if (st != KVC_OK) return st;
+  if (a.c.bits == 16) return KVC_E_UNSUPPORTED;
   if (n_tokens < 0 || token_offset < 0) return KVC_E_SHAPE;
   if (!x && n_tokens > 0) return KVC_E_NULL;   // an empty call may pass NULL buffers
   if (!aligned16(x) || (recon_out && !aligned16(recon_out)) || (pred_out && !aligned16(pred_out)))
@@ -228,7 +239,7 @@ kvc_status kvc_decode(const kvc_codec* codec, const kvc_store* src, int64_t toke
   DecodeLaunch a;
   kvc_status st = resolve_codec(codec, &a.c);
   if (st != KVC_OK) return st;
-  if (a.c.base == KVC_BASE_COEFF) return KVC_E_UNSUPPORTED;
+  if (a.c.base == KVC_BASE_COEFF || a.c.bits == 16) return KVC_E_UNSUPPORTED;
   if (n_tokens < 0 || token_offset < 0) return KVC_E_SHAPE;
   if (!out && n_tokens > 0) return KVC_E_NULL;
   if (!aligned16(out) || (pred_out && !aligned16(pred_out))) return KVC_E_ALIGN;
@@ -292,6 +303,9 @@ kvc_status kvc_attend_compressed(const kvc_codec* kc, const kvc_store* k,
   for (const CodecArgs* c : {&a.kc, &a.vc})
     if (c->base != KVC_BASE_NONE && c->base != KVC_BASE_CENTROID) return KVC_E_UNSUPPORTED;
   if (a.kc.x_dtype == KVC_BF16 && a.kc.D != 128) return KVC_E_UNSUPPORTED;
+  if ((a.kc.bits == 16) != (a.vc.bits == 16)) return KVC_E_UNSUPPORTED;   // both dense or neither
+  if (a.kc.bits == 16 && (int64_t)a.ks.capacity * a.kc.H * a.kc.D * 2 >= (int64_t)1 << 31)
+    return KVC_E_SHAPE;   // one 32-bit buffer range per dense cache
   a.scale = softmax_scale;
   return from_hip(launch_attend(a, reinterpret_cast<hipStream_t>(stream)));
 }

@@ -144,12 +144,14 @@ struct VPre {                     // keys 2kp, 2kp+1, channels 8c8..8c8+7
 // spread over the LDS banks.
 __device__ __forceinline__ int vswz(int row, int key) { return key ^ (((row >> 3) & 7) << 2); }
 
+// DENSE: K and V are uncompressed bf16 caches [capacity][H][d] (e.g. what kvc_decode
+// writes for a predictor chain); the tile loaders copy rows instead of decoding.
 // MIXED: keys are NanoKV-Fast coefficient records.  The K tile then holds, per key,
 // the centroid row C[a] (128 bf16) followed by the dequantized coefficients c split
 // into bf16 high and low parts (16 + 16); the queries carry B^T q split the same way,
 // and three extra MFMA steps add (B^T q) . c to q . C[a] with about 2^-16 relative
 // error - the score is formed without reconstructing the key.
-template <int BITS, int VBITS, bool KCEN, bool VCEN, bool MIXED>
+template <int BITS, int VBITS, bool KCEN, bool VCEN, bool MIXED, bool DENSE = false>
 __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
   constexpr int KR = MIXED ? DM + 32 + 8 : KROW;   // K tile row (bf16 elements)
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BK * KR];     // bf16
@@ -189,6 +191,11 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
                            KCEN ? (int64_t)p.k.C * DM * 2 : 0);
   const auto rv_cen = rsrc(reinterpret_cast<const uint16_t*>(p.v.cen) + (int64_t)h * p.v.C * DM,
                            VCEN ? (int64_t)p.v.C * DM * 2 : 0);
+
+  // DENSE: one resource over the whole token-major cache, rows H*d apart
+  const int hdb = p.H * DM * 2;
+  const auto rk_dense = rsrc(p.k.codes, DENSE ? p.k.cap * hdb : 0);
+  const auto rv_dense = rsrc(p.v.codes, DENSE ? p.v.cap * hdb : 0);
 
   // decode roles: 8 lanes share a K row (16 channels each), 16 lanes share a V row (8
   // channels each), so every load instruction reads whole contiguous rows
@@ -230,6 +237,21 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
   auto load_data = [&](int t, int ki, const int (&vi)[2], KPre<BITS>& kpr, VPre& vp) {
     const uint32_t k0 = (uint32_t)(t * BK);
     const uint32_t n = k0 + kk;
+    if constexpr (DENSE) {
+      typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+      const uint32_t ko = n * hdb + h * DM * 2 + 32 * kw;
+      const u4 a0 = __builtin_amdgcn_raw_buffer_load_b128(rk_dense, ko, 0, 0);
+      const u4 a1 = __builtin_amdgcn_raw_buffer_load_b128(rk_dense, ko + 16, 0, 0);
+      kpr.c0 = uint4{a0.x, a0.y, a0.z, a0.w};
+      kpr.c1 = uint4{a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u4 a = __builtin_amdgcn_raw_buffer_load_b128(
+            rv_dense, (k0 + 2 * kp + j) * hdb + h * DM * 2 + 16 * c8, 0, 0);
+        vp.c[j] = uint4{a.x, a.y, a.z, a.w};
+      }
+      return;
+    }
     if constexpr (BITS == 2 || MIXED) {
       kpr.code[0] = __builtin_amdgcn_raw_buffer_load_b32(rk_code, n * kwb + kword * 4, 0, 0);
     } else {
@@ -266,6 +288,22 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
     }
   };
   auto dequant = [&](const KPre<BITS>& kpr, const VPre& vp, int buf) {
+    if constexpr (DENSE) {
+      uint4* dst = reinterpret_cast<uint4*>(&k_lds[buf][kk * KR + 16 * kw]);
+      dst[0] = kpr.c0;
+      dst[1] = kpr.c1;
+      const uint32_t v0[4] = {vp.c[0].x, vp.c[0].y, vp.c[0].z, vp.c[0].w};
+      const uint32_t v1[4] = {vp.c[1].x, vp.c[1].y, vp.c[1].z, vp.c[1].w};
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int row = 8 * c8 + c;
+        const uint32_t a = (c & 1) ? (v0[c >> 1] >> 16) : (v0[c >> 1] & 0xFFFFu);
+        const uint32_t b = (c & 1) ? (v1[c >> 1] >> 16) : (v1[c >> 1] & 0xFFFFu);
+        *reinterpret_cast<uint32_t*>(&v_lds[buf][row * VROW + vswz(row, 2 * kp)]) =
+            bf16x2_to_f16x2(a | (b << 16));
+      }
+      return;
+    }
     if constexpr (MIXED) {
       // ---- K: centroid row chunk as is; lanes kw < 2 add 8 coefficients (hi, lo)
       uint4* dst = reinterpret_cast<uint4*>(&k_lds[buf][kk * KR + 16 * kw]);
@@ -680,6 +718,10 @@ hipError_t launch_attend(const AttendLaunch& a, hipStream_t s) {
   if (a.kc.x_dtype == KVC_BF16) {
     const int nqb = (int)((a.n_queries + BQ - 1) / BQ);
     const dim3 grid(nqb * a.kc.H), block(NT);
+    if (a.kc.bits == 16) {   // uncompressed bf16 caches (validated: both K and V)
+      hipLaunchKernelGGL((attend_bf16_kernel<2, 2, false, false, false, true>), grid, block, 0, s, p);
+      return hipGetLastError();
+    }
     const bool kc = p.k.mode == SRC_CENTROID, vc = p.v.mode == SRC_CENTROID;
     // every (K bits, V bits, K base, V base) combination is its own kernel so the
     // prefetch loads stay branch-free

@@ -152,7 +152,7 @@ class Store:
     """Compressed store: codes int32 [H][cap][words], scale_zero int32 [H][cap][groups],
     index uint8 / int16 [H][cap] (bit patterns of the C layout's uint32 / uint16)."""
     codes: torch.Tensor
-    scale_zero: torch.Tensor
+    scale_zero: Optional[torch.Tensor]
     index: Optional[torch.Tensor]
     capacity: int
 
@@ -173,8 +173,14 @@ class Store:
             index = torch.empty((H, capacity), dtype=dt, device=device)
         return Store(codes, sz, index, capacity)
 
+    @staticmethod
+    def dense(cache: torch.Tensor) -> "Store":
+        """An uncompressed bf16 cache [N][H][d] (codec bits = 16) for the attention calls."""
+        return Store(cache, None, None, cache.shape[0])
+
     def c(self) -> _Store:
-        return _Store(self.codes.data_ptr(), self.scale_zero.data_ptr(),
+        return _Store(self.codes.data_ptr(),
+                      None if self.scale_zero is None else self.scale_zero.data_ptr(),
                       None if self.index is None else self.index.data_ptr(), self.capacity)
 
 
