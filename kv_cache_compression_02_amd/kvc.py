@@ -97,8 +97,23 @@ def _check(status: int, where: str):
         raise KvcError(status, where)
 
 
-def _p(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+def _p(t: Optional[torch.Tensor], name: str = "tensor"):
+    """Pointer of a tensor the C layout reads as densely packed."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous: the C layout is dense")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _row_stride(t: torch.Tensor, name: str) -> int:
+    """Token stride (elements) of a [n][...] tensor whose rows are each dense."""
+    expect = 1
+    for size, st in reversed(list(zip(t.shape[1:], t.stride()[1:]))):
+        if size != 1 and st != expect:
+            raise ValueError(f"{name}: each token row must be dense")
+        expect *= size
+    return t.stride(0) if t.shape[0] > 1 else expect
 
 
 def _stream():
@@ -139,11 +154,22 @@ class BaseParams:
 
     def c(self) -> _Base:
         b = _Base()
-        for name in ("centroids", "basis", "prev0", "prev1", "aux", "w_block", "u", "v_lr",
-                     "coef_a", "coef_b"):
+        for name in ("centroids", "basis", "w_block", "u", "v_lr", "coef_a", "coef_b"):
             t = getattr(self, name)
-            setattr(b, name, None if t is None else t.data_ptr())
-        b.prev_token_stride = self.prev_token_stride
+            setattr(b, name, None if t is None else _p(t, name).value)
+        # prev0, prev1 and aux share one token stride
+        strides = set()
+        for name in ("prev0", "prev1", "aux"):
+            t = getattr(self, name)
+            if t is not None:
+                strides.add(_row_stride(t, name))
+                setattr(b, name, t.data_ptr())
+        stride = self.prev_token_stride
+        if not stride and strides:
+            if len(strides) > 1:
+                raise ValueError("prev0, prev1 and aux must share one token stride")
+            stride = strides.pop()
+        b.prev_token_stride = stride
         return b
 
 
@@ -179,9 +205,9 @@ class Store:
         return Store(cache, None, None, cache.shape[0])
 
     def c(self) -> _Store:
-        return _Store(self.codes.data_ptr(),
-                      None if self.scale_zero is None else self.scale_zero.data_ptr(),
-                      None if self.index is None else self.index.data_ptr(), self.capacity)
+        return _Store(_p(self.codes, "codes").value,
+                      None if self.scale_zero is None else _p(self.scale_zero, "scale_zero").value,
+                      None if self.index is None else _p(self.index, "index").value, self.capacity)
 
 
 def kvc_store_bytes(codec: Codec, capacity: int):
@@ -202,9 +228,12 @@ def kvc_encode(codec: Codec, x: torch.Tensor, store: Store, token_offset: int = 
     """Compress x [n][H][d] into store rows [token_offset, token_offset + n)."""
     b = (base or BaseParams()).c()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().kvc_encode(ctypes.byref(codec.c()), _p(x), x.shape[0], x_token_stride,
-                            ctypes.byref(b), ctypes.byref(store.c()), token_offset, _p(recon_out),
-                            _p(pred_out), _p(workspace), ws_bytes, _stream()), "kvc_encode")
+    if not x_token_stride:
+        x_token_stride = _row_stride(x, "x")
+    _check(lib().kvc_encode(ctypes.byref(codec.c()), ctypes.c_void_p(x.data_ptr()), x.shape[0],
+                            x_token_stride, ctypes.byref(b), ctypes.byref(store.c()), token_offset,
+                            _p(recon_out, "recon_out"), _p(pred_out, "pred_out"),
+                            _p(workspace, "workspace"), ws_bytes, _stream()), "kvc_encode")
 
 
 def kvc_decode(codec: Codec, store: Store, token_offset: int, n_tokens: int,
@@ -219,8 +248,8 @@ def kvc_decode(codec: Codec, store: Store, token_offset: int, n_tokens: int,
     b = (base or BaseParams()).c()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().kvc_decode(ctypes.byref(codec.c()), ctypes.byref(store.c()), token_offset,
-                            n_tokens, ctypes.byref(b), _p(out), out_dtype, _p(pred_out),
-                            _p(workspace), ws_bytes, _stream()), "kvc_decode")
+                            n_tokens, ctypes.byref(b), _p(out, "out"), out_dtype,
+                            _p(pred_out, "pred_out"), _p(workspace, "workspace"), ws_bytes, _stream()), "kvc_decode")
     return out
 
 
@@ -243,8 +272,9 @@ def _attend(fn, name, kc, kstore, kbase, vc, vstore, vbase, n_keys, q, softmax_s
     vb = (vbase or BaseParams()).c()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(fn(ctypes.byref(kc.c()), ctypes.byref(kstore.c()), ctypes.byref(kb),
-              ctypes.byref(vc.c()), ctypes.byref(vstore.c()), ctypes.byref(vb), n_keys, _p(q),
-              nq, ctypes.c_float(softmax_scale), _p(out), _p(lse), _p(workspace), ws_bytes,
+              ctypes.byref(vc.c()), ctypes.byref(vstore.c()), ctypes.byref(vb), n_keys, _p(q, "q"),
+              nq, ctypes.c_float(softmax_scale), _p(out, "out"), _p(lse, "lse"),
+              _p(workspace, "workspace"), ws_bytes,
               _stream()), name)
     return (out, lse) if want_lse else out
 

@@ -174,6 +174,11 @@ def _bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def _per_head(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """out[n, h] = w[h] @ x[n, h] for x [n][H][k], w [H][d][k] (per-head matrix products)."""
+    return np.stack([x[:, h] @ w[h].T for h in range(w.shape[0])], axis=1)
+
+
 def cfg2_layers(seed: int = 1236, params: dict | None = None, n_tokens: int = 21 * TOKENS_PER_FRAME,
                 n_layers: int = 30, chunk_ids=None, chunk: int = TOKENS_PER_FRAME,
                 noise: float = 0.2):
@@ -203,12 +208,12 @@ def cfg2_layers(seed: int = 1236, params: dict | None = None, n_tokens: int = 21
                 v = pv.draw(rng, m)
             else:
                 kp, vp = k_prev[j], v_prev[j]
-                k = np.einsum("hij,nhj->nhi", wk, kp) \
+                k = _per_head(kp, wk) \
                     + ((kp.reshape(m, D) @ vk) @ uk.T).reshape(m, heads, dim) \
                     + noise * rng.standard_normal((m, heads, dim))
                 kv = np.concatenate([k, vp], axis=2)  # per head [K_l,h ; V_{l-1},h]
                 lr_in = np.concatenate([k.reshape(m, D), vp.reshape(m, D)], axis=1)
-                v = np.einsum("hij,nhj->nhi", wv, kv) \
+                v = _per_head(kv, wv) \
                     + ((lr_in @ vv) @ uv.T).reshape(m, heads, dim) \
                     + noise * rng.standard_normal((m, heads, dim))
             ks.append(k)
@@ -249,7 +254,7 @@ def cfg3(seed: int = 1237, n_frames: int = 16, query_frames: int = 3,
             k = a * k1 + b * k2 + 0.3 * r.standard_t(4, size=k0.shape)
         K[t * tokens:(t + 1) * tokens] = k
         if t < n_frames:
-            v = np.einsum("hij,nhj->nhi", m, k) + beta * vprev \
+            v = _per_head(k, m) + beta * vprev \
                 + 0.3 * r.standard_t(4, size=k0.shape)
             V[t * tokens:(t + 1) * tokens] = v
             vprev = v
@@ -259,3 +264,45 @@ def cfg3(seed: int = 1237, n_frames: int = 16, query_frames: int = 3,
                 n_frames=n_frames, K=bf16_bits(K[:nh]), V=bf16_bits(V), Q=bf16_bits(K[nh:]),
                 a=a, b=b, beta=beta, M=m_bits, bits=2, group=64, anchor_bits=4,
                 scale=1.0 / np.sqrt(dim))
+
+
+def cfg2_layers_device(device, seed: int = 1236, params: dict | None = None,
+                       n_tokens: int = 21 * TOKENS_PER_FRAME, n_layers: int = 30,
+                       noise: float = 0.2):
+    """The block-DPLR layer process of cfg2_layers drawn with torch's generator on
+    `device` (full-size runs); yields (K_l, V_l) as bf16 tensors [n][H][d].  Same recipe,
+    different random stream: use cfg2_layers where values must match the oracle's."""
+    import torch
+
+    if params is None:
+        params = cfg2_params(seed)
+    heads, dim = params["heads"], params["dim"]
+    D = heads * dim
+
+    def f(name):
+        b = torch.from_numpy(params[name].view(np.int16)).view(torch.bfloat16)
+        return b.to(device=device, dtype=torch.float32)
+
+    wk, uk, vk, wv, uv, vv = (f(n) for n in ("WK", "UK", "VK", "WV", "UV", "VV"))
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    proc = ClusterProcess(rng_for(seed, 101), heads, dim)
+    centers = torch.from_numpy(proc.centers).to(device=device, dtype=torch.float32)
+
+    def cluster(n):
+        z = torch.randint(0, proc.n_centers, (n, heads), generator=gen, device=device)
+        x = centers[torch.arange(heads, device=device)[None, :], z]
+        return x + proc.noise * torch.randn((n, heads, dim), generator=gen, device=device)
+
+    k = cluster(n_tokens)
+    v = cluster(n_tokens)
+    for layer in range(n_layers):
+        if layer:
+            kp, vp = k, v
+            k = torch.einsum("hij,nhj->nhi", wk, kp).contiguous() + ((kp.reshape(-1, D) @ vk) @ uk.T).reshape(
+                -1, heads, dim) + noise * torch.randn(kp.shape, generator=gen, device=device)
+            kv = torch.cat([k, vp], dim=2)
+            lr = torch.cat([k.reshape(-1, D), vp.reshape(-1, D)], dim=1)
+            v = torch.einsum("hij,nhj->nhi", wv, kv).contiguous() + ((lr @ vv) @ uv.T).reshape(
+                -1, heads, dim) + noise * torch.randn(vp.shape, generator=gen, device=device)
+        yield k.to(torch.bfloat16).contiguous(), v.to(torch.bfloat16).contiguous()

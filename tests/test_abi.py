@@ -106,3 +106,26 @@ def test_python_binding_raises_on_status():
     with pytest.raises(kvc.KvcError) as e:
         kvc._check(kvc.KVC_E_SHAPE, "x")
     assert e.value.status == kvc.KVC_E_SHAPE
+
+
+def test_python_binding_checks_tensor_layouts():
+    """The C layouts are dense (or dense rows with a token stride for x and the
+    predictor inputs): the binding refuses any other strides instead of handing a
+    permuted view's pointer to the library."""
+    import torch
+    permuted = torch.zeros(4, 3, 8).permute(1, 0, 2)
+    with pytest.raises(ValueError):
+        kvc._row_stride(permuted, "x")
+    with pytest.raises(ValueError):
+        kvc._row_stride(torch.zeros(5, 3, 8)[:, :, :4], "x")
+    every_other = torch.zeros(6, 3, 8)[::2]
+    assert kvc._row_stride(every_other, "x") == 48
+    assert kvc._row_stride(torch.zeros(6, 3, 8), "x") == 24
+    assert kvc._row_stride(torch.zeros(1, 3, 8), "x") == 24
+    with pytest.raises(ValueError):
+        kvc._p(every_other, "q")
+    with pytest.raises(ValueError):
+        kvc.BaseParams(w_block=torch.zeros(4, 4).t()).c()
+    with pytest.raises(ValueError):
+        kvc.BaseParams(prev0=torch.zeros(4, 2, 8), prev1=torch.zeros(8, 2, 8)[::2]).c()
+    assert kvc.BaseParams(prev0=every_other).c().prev_token_stride == 48
