@@ -469,6 +469,384 @@ __global__ __launch_bounds__(NTHREADS, 1) void encode_shortlist_kernel(EncodePar
   }
 }
 
+// ---------------------------------------------------------------------------
+// Centroid codec for bf16 d = 128 data with at most 256 centroids per head.
+//
+// One wave encodes 32 tokens of one head; lane (t, hf) owns channels 64 hf ..
+// 64 hf + 63 of token t in registers for the whole kernel.  The head's centroid
+// table sits in LDS, once per workgroup of four waves (128 tokens).
+//
+// Assignment.  v_j = x.c_j - |c_j|^2 / 2 comes out of v_mfma_f32_32x32x16_bf16
+// (accumulator seeded with -|c_j|^2 / 2; the contraction index is permuted so that
+// every lane feeds its own half row), one lane per (token, half) holding 128 of the
+// 256 values.  A lane keeps the top three of its values with the centroid's
+// position packed into the low 8 mantissa bits, and merges them with its partner
+// half.  With E >= |v_j - V_j| (the MFMA error, counted at two units in the last
+// place per addition), g = (d + 3) 2^-24 the relative error of the exact fp32
+// distance, and V the true values, d_j > d_w for the exact fp32 distances whenever
+//     (v_w - v_j) - g (|x|^2 - v_w - v_j) > 2 E,
+// since |x - c_j|^2 = |x|^2 - 2 V_j.  If that holds between the best and the second
+// best value, the best centroid is the nearest one; if it holds between the best
+// and the third, the nearest is one of the top two, and both are rescored in the
+// exact fp32 order; otherwise every centroid the test cannot exclude is rescored.
+// Ties in the exact distance go to the lower index.
+//
+// Quantization.  code = clamp(rint(fl(fl(r - z) / s))) is evaluated as
+// rint(r * rcp(s) - z * rcp(s)); the two agree unless the product lies within
+// (|z / s| + L + 2) 2^-19 of a half-integer, and a group with such an element is
+// redone with the IEEE division.
+__device__ __forceinline__ uint32_t swap_halves(uint32_t v, int hf) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return hf ? r[0] : r[1];
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <int BITS, int G>
+__global__ __launch_bounds__(256, 2) void encode_centroid_kernel(EncodeParams p) {
+  constexpr int D = 128, ROW = D + 8, CM = 256;
+  constexpr int L = (1 << BITS) - 1;
+  constexpr int NG = 64 / G;          // groups in a half row
+  constexpr int PER = 32 / BITS;      // codes per word
+  constexpr int WPL = 64 / PER;       // code words per half row
+  constexpr int GW = G / PER;         // code words per group
+  __shared__ __attribute__((aligned(16))) uint16_t tab[CM * ROW];
+  __shared__ __attribute__((aligned(16))) float hn[CM];
+  __shared__ float cnu[CM];   // |c_j| (upper bound), 0 beyond C
+  __shared__ float wmax[4];
+  __shared__ uint32_t tq[4][64];   // rescoring tasks of each wave: lane << 8 | centroid
+  __shared__ float tqd[4][64];
+  __shared__ uint32_t tqn[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = lane & 31, hf = lane >> 5;
+  const int nblk = (int)((p.n_tokens + 127) / 128);
+  const int b = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = b / nblk;
+  const int64_t n = (int64_t)(b % nblk) * 128 + wave * 32 + t;
+  const bool live = n < p.n_tokens;
+  const int C = p.C;
+  const int nb = (C + 31) >> 5;
+  const uint16_t* cen = reinterpret_cast<const uint16_t*>(p.centroids) + (int64_t)h * C * D;
+
+  // 1. this lane's half row, and the head's centroid table (rows C .. 32 nb - 1 zero)
+  uint4 xv[8];
+  {
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(p.x) + (live ? n : 0) * p.x_stride +
+                          (int64_t)h * D + 64 * hf;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      xv[i] = live ? *reinterpret_cast<const uint4*>(src + 8 * i) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  {
+    // all sixteen 16-byte pieces of this thread in flight at once
+    uint4 v[16];
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int j = 16 * it + (tid >> 4), c = tid & 15;
+      v[it] = make_uint4(0u, 0u, 0u, 0u);
+      if (j < C) v[it] = *reinterpret_cast<const uint4*>(cen + (int64_t)j * D + 8 * c);
+    }
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int j = 16 * it + (tid >> 4), c = tid & 15;
+      if (j < 32 * nb) *reinterpret_cast<uint4*>(&tab[j * ROW + 8 * c]) = v[it];
+    }
+  }
+  __syncthreads();
+  {
+    const int j = tid;
+    float s2 = 0.0f;
+    if (j < C) {
+#pragma unroll
+      for (int i = 0; i < D; i += 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(&tab[j * ROW + i]);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          s2 = __builtin_fmaf(lo_bf16(w[k]), lo_bf16(w[k]), s2);
+          s2 = __builtin_fmaf(hi_bf16(w[k]), hi_bf16(w[k]), s2);
+        }
+      }
+    }
+    hn[j] = j < C ? -0.5f * s2 : -1e30f;
+    float cn = sqrtf(s2) * (1.0f + 0x1p-10f);
+    cnu[j] = cn;
+#pragma unroll
+    for (int o = 32; o; o >>= 1) cn = fmaxf(cn, __shfl_xor(cn, o));
+    if (lane == 0) wmax[wave] = cn;
+  }
+  __syncthreads();
+  const float cmax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+
+  // 2. v_j for the 128 centroids of this half; top three with packed positions
+  float m1 = -3.0e38f, m2 = -3.0e38f, m3 = -3.0e38f;
+  auto block_values = [&](int cb, f32x16_t& acc) {
+    const float4* hp = reinterpret_cast<const float4*>(&hn[32 * cb + 4 * hf]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = hp[2 * q];
+      acc[4 * q] = v.x; acc[4 * q + 1] = v.y; acc[4 * q + 2] = v.z; acc[4 * q + 3] = v.w;
+    }
+    const uint16_t* arow = &tab[(32 * cb + t) * ROW + 64 * hf];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(arow + 8 * ks);
+      bf16x8_t bx;
+      __builtin_memcpy(&bx, &xv[ks], 16);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bx, acc, 0, 0, 0);
+    }
+  };
+  for (int cb = 0; cb < nb; ++cb) {
+    f32x16_t acc;
+    block_values(cb, acc);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pv = __uint_as_float((__float_as_uint(acc[r]) & 0xFFFFFF00u) | (uint32_t)(16 * cb + r));
+      m3 = __builtin_amdgcn_fmed3f(m2, m3, pv);
+      m2 = __builtin_amdgcn_fmed3f(m1, m2, pv);
+      m1 = fmaxf(m1, pv);
+    }
+  }
+  // tag the half in bit 7, merge the two halves' top three
+  m1 = __uint_as_float(__float_as_uint(m1) | ((uint32_t)hf << 7));
+  m2 = __uint_as_float(__float_as_uint(m2) | ((uint32_t)hf << 7));
+  m3 = __uint_as_float(__float_as_uint(m3) | ((uint32_t)hf << 7));
+  auto swf = [&](float v) { return __uint_as_float(swap_halves(__float_as_uint(v), hf)); };
+  const float b1 = swf(m1), b2 = swf(m2), b3 = swf(m3);
+  const float t1 = fmaxf(m1, b1);
+  const float t2 = fmaxf(fmaxf(m2, b2), fminf(m1, b1));
+  const float t3 = fmaxf(fmaxf(m3, b3), fmaxf(fminf(m2, b1), fminf(m1, b2)));
+
+  // |x|^2 (upper bound) and the separation test
+  float xs = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t w[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      xs = __builtin_fmaf(lo_bf16(w[k]), lo_bf16(w[k]), xs);
+      xs = __builtin_fmaf(hi_bf16(w[k]), hi_bf16(w[k]), xs);
+    }
+  }
+  const float xxu = (xs + swf(xs)) * (1.0f + 0x1p-10f);
+  const float xn = sqrtf(xxu) * (1.0f + 0x1p-10f);
+  // error bound of one value v_j, from |c_j| (and E for any row: |c_j| <= cmax)
+  auto erow = [&](float cj) {
+    return (2.0f * (D + 2) * 0x1p-24f) * cj * (cj + xn) * (1.0f + 0x1p-10f) + 1e-30f;
+  };
+  const float E = erow(cmax);
+  const float go = (D + 3) * 0x1p-24f * (1.0f + 0x1p-10f);
+  // a (packed best) beats every centroid whose value is at most c, given the sum of
+  // the two values' error bounds
+  auto separated = [&](float a, float c, float esum) {
+    const float va = a - 0x1p-15f * fabsf(a), vc = c + 0x1p-15f * fabsf(c);
+    const float rhs = esum + go * (xxu - va - vc) + 0x1p-20f * (fabsf(va) + fabsf(vc) + xxu);
+    return va - vc > rhs;
+  };
+  auto cidx = [](float v) {
+    const uint32_t tg = __float_as_uint(v) & 0xFFu;
+    const int hw = (int)(tg >> 7), loc = (int)(tg & 0x7Fu), cb = loc >> 4, r = loc & 15;
+    return 32 * cb + 8 * (r >> 2) + 4 * hw + (r & 3);
+  };
+  int best = cidx(t1);
+  // with every error at its largest (E) most tokens are settled; the rest are
+  // tested again with the row bounds of the best (and second) centroid
+  bool uniq = !live || separated(t1, t2, 2.0f * E), pair = false;
+  if (!uniq) {
+    const float e1 = erow(cnu[best]), e2 = erow(cnu[cidx(t2)]);
+    const bool beats_rest = separated(t1, t3, e1 + E);
+    uniq = beats_rest && separated(t1, t2, e1 + e2);
+    pair = beats_rest && !uniq;
+  }
+
+  // 3. exact rescoring: every (token, candidate) pair is a task in this wave's LDS
+  //    queue; lane i computes task i in the exact fp32 order from the token's row
+  if (__any(!uniq)) {
+    uint32_t* q = &tq[wave][0];
+    float* qd = &tqd[wave][0];
+    int single = pair ? cidx(hf ? t2 : t1) : -1;   // one candidate per lane of a pair token
+    uint32_t mask[4] = {0u, 0u, 0u, 0u};            // bit 16 cb + r: candidate value of this lane
+    const bool full = !uniq && !pair;
+    if (__any(full)) {
+      // every value below tau is separated from the best one (the right-hand side of
+      // the test grows far slower than the gap), so the values >= tau are a superset of
+      // the centroids that can still be nearest; all of them are rescored
+      const float va = t1 - 0x1p-15f * fabsf(t1);
+      const float tau = va - 2.0f * (2.0f * E + go * (xxu + 2.0f * fabsf(va)) +
+                                     0x1p-20f * (2.0f * fabsf(va) + xxu) + 0x1p-14f * fabsf(va));
+      for (int cb = 0; cb < nb; ++cb) {
+        f32x16_t acc;
+        block_values(cb, acc);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = 32 * cb + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (full && j < C && acc[r] >= tau) mask[cb >> 1] |= 1u << (16 * (cb & 1) + r);
+        }
+      }
+    }
+    const int64_t nw0 = n - t;   // first token of this wave
+    float bd = __builtin_inff();
+    int bj = 0x7FFFFFFF;
+    bool pending = single >= 0 || (mask[0] | mask[1] | mask[2] | mask[3]) != 0u;
+    while (__any(pending)) {
+      if (lane == 0) tqn[wave] = 0;
+      __builtin_amdgcn_wave_barrier();
+      if (pending) {
+        if (single >= 0) {
+          const uint32_t slot = atomicAdd(&tqn[wave], 1u);
+          if (slot < 64u) { q[slot] = ((uint32_t)lane << 8) | (uint32_t)single; single = -1; }
+        }
+        for (int w = 0; w < 4; ++w) {
+          while (mask[w]) {
+            const int bit = __builtin_ctz(mask[w]);
+            const uint32_t slot = atomicAdd(&tqn[wave], 1u);
+            if (slot >= 64u) break;
+            const int cb = 2 * w + (bit >> 4), r = bit & 15;
+            const int j = 32 * cb + 8 * (r >> 2) + 4 * hf + (r & 3);
+            q[slot] = ((uint32_t)lane << 8) | (uint32_t)j;
+            mask[w] &= mask[w] - 1u;
+          }
+        }
+        pending = single >= 0 || (mask[0] | mask[1] | mask[2] | mask[3]) != 0u;
+      }
+      __builtin_amdgcn_wave_barrier();
+      const int ntask = min((int)tqn[wave], 64);
+      if (lane < ntask) {
+        const uint32_t tk = q[lane];
+        const int j = (int)(tk & 0xFFu);
+        const int64_t nt = nw0 + (int)((tk >> 8) & 31u);
+        const uint16_t* xr = reinterpret_cast<const uint16_t*>(p.x) + nt * p.x_stride + (int64_t)h * D;
+        const uint16_t* crow = &tab[j * ROW];
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint4 xw = *reinterpret_cast<const uint4*>(xr + 8 * i);
+          const uint4 cw = *reinterpret_cast<const uint4*>(crow + 8 * i);
+          const uint32_t xa[4] = {xw.x, xw.y, xw.z, xw.w}, ca[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float d0 = lo_bf16(xa[k]) - lo_bf16(ca[k]);
+            const float q0 = d0 * d0;
+            acc = acc + q0;
+            const float d1 = hi_bf16(xa[k]) - hi_bf16(ca[k]);
+            const float q1 = d1 * d1;
+            acc = acc + q1;
+          }
+        }
+        qd[lane] = acc;
+      }
+      __builtin_amdgcn_wave_barrier();
+      for (int i = 0; i < ntask; ++i) {
+        const uint32_t tk = q[i];
+        if ((int)(tk >> 8) == lane) {
+          const float d = qd[i];
+          const int j = (int)(tk & 0xFFu);
+          if (d < bd || (d == bd && j < bj)) { bd = d; bj = j; }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    const float od = swf(bd);
+    const int oj = (int)swap_halves((uint32_t)bj, hf);
+    if (!uniq) best = (od < bd || (od == bd && oj < bj)) ? oj : bj;
+  }
+
+  // 4. residual, group scale/zero, codes
+  const uint16_t* crow = &tab[best * ROW + 64 * hf];
+  uint32_t words[WPL], szw[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    float r[G];
+#pragma unroll
+    for (int i = 0; i < G / 8; ++i) {
+      const uint4 cw = *reinterpret_cast<const uint4*>(crow + G * gi + 8 * i);
+      const uint4 xw = xv[(G * gi) / 8 + i];
+      const uint32_t xa[4] = {xw.x, xw.y, xw.z, xw.w}, ca[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        r[8 * i + 2 * k] = lo_bf16(xa[k]) - lo_bf16(ca[k]);
+        r[8 * i + 2 * k + 1] = hi_bf16(xa[k]) - hi_bf16(ca[k]);
+      }
+    }
+    float mn = r[0], mx = r[0];
+#pragma unroll
+    for (int i = 1; i < G; ++i) { mn = fminf(mn, r[i]); mx = fmaxf(mx, r[i]); }
+    const GroupQ q = group_scale_zero(mn, mx, L);
+    szw[gi] = q.word;
+    uint32_t cw[GW];
+#pragma unroll
+    for (int w = 0; w < GW; ++w) cw[w] = 0u;
+    if (q.s != 0.0f) {
+      const float rinv = __builtin_amdgcn_rcpf(q.s);
+      const float nzr = -(q.z * rinv);
+      const float thr = 0.5f - (fabsf(nzr) + (float)(L + 2)) * 0x1p-19f;
+      bool bad = false;
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        const float y = __builtin_fmaf(r[i], rinv, nzr);
+        const float k = __builtin_rintf(y);
+        bad |= fabsf(y - k) > thr;
+        const uint32_t code = (uint32_t)__builtin_amdgcn_fmed3f(k, 0.0f, (float)L);
+        cw[i / PER] |= code << (BITS * (i % PER));
+      }
+      if (bad) {
+#pragma unroll
+        for (int w = 0; w < GW; ++w) cw[w] = 0u;
+#pragma unroll
+        for (int i = 0; i < G; ++i) cw[i / PER] |= quantize_one(r[i], q, L) << (BITS * (i % PER));
+      }
+    }
+#pragma unroll
+    for (int w = 0; w < GW; ++w) words[gi * GW + w] = cw[w];
+    if (live && (p.recon || p.pred)) {
+      const int64_t xrow = (n * p.H + h) * (int64_t)D + 64 * hf + G * gi;
+      if (p.recon) {
+        uint16_t* rec = reinterpret_cast<uint16_t*>(p.recon) + xrow;
+#pragma unroll
+        for (int i = 0; i < G; i += 8) {
+          uint32_t o[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int i0 = i + 2 * k, i1 = i0 + 1;
+            const uint32_t c0 = (cw[i0 / PER] >> (BITS * (i0 % PER))) & L;
+            const uint32_t c1 = (cw[i1 / PER] >> (BITS * (i1 % PER))) & L;
+            const uint32_t cw2 = crow[G * gi + i0] | ((uint32_t)crow[G * gi + i1] << 16);
+            const float e0 = lo_bf16(cw2) + dequant_one(c0, q.s, q.z);
+            const float e1 = hi_bf16(cw2) + dequant_one(c1, q.s, q.z);
+            o[k] = f32_to_bf16_bits(e0) | (f32_to_bf16_bits(e1) << 16);
+          }
+          *reinterpret_cast<uint4*>(rec + i) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+      }
+      if (p.pred) {
+        float* pd = p.pred + xrow;
+#pragma unroll
+        for (int i = 0; i < G; i += 4) {
+          const uint2 cw2 = *reinterpret_cast<const uint2*>(crow + G * gi + i);
+          *reinterpret_cast<float4*>(pd + i) =
+              make_float4(lo_bf16(cw2.x), hi_bf16(cw2.x), lo_bf16(cw2.y), hi_bf16(cw2.y));
+        }
+      }
+    }
+  }
+
+  // 5. stores: whole 16-byte pieces of the token's code and scale/zero rows
+  if (live) {
+    const int64_t row = (int64_t)h * p.capacity + p.token_offset + n;
+    uint32_t* cd = p.codes + row * (2 * WPL) + WPL * hf;
+#pragma unroll
+    for (int w = 0; w < WPL; w += 4)
+      *reinterpret_cast<uint4*>(cd + w) = make_uint4(words[w], words[w + 1], words[w + 2], words[w + 3]);
+    uint32_t* sd = p.sz + row * (2 * NG) + NG * hf;
+    if constexpr (NG == 4) *reinterpret_cast<uint4*>(sd) = make_uint4(szw[0], szw[1], szw[2], szw[3]);
+    else if constexpr (NG == 2) *reinterpret_cast<uint2*>(sd) = make_uint2(szw[0], szw[1]);
+    else sd[0] = szw[0];
+    if (hf == 0) reinterpret_cast<uint8_t*>(p.index)[row] = (uint8_t)best;
+  }
+}
+
 template <typename XT, int D>
 hipError_t launch_encode_t(const EncodeParams& p, int H, hipStream_t s) {
   const int ntiles = (int)((p.n_tokens + TOK - 1) / TOK);
@@ -530,6 +908,19 @@ hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   const bool bf16 = a.c.x_dtype == KVC_BF16;
+  // centroid base, bf16 d = 128, <= 256 centroids: register-resident MFMA assignment
+  if (bf16 && a.c.D == 128 && p.mode == MODE_CENTROID && a.c.C <= 256 && p.x_stride % 8 == 0 &&
+      (a.c.group == 16 || a.c.group == 32 || a.c.group == 64)) {
+    const dim3 grid((unsigned)(((p.n_tokens + 127) / 128) * a.c.H));
+#define KVC_ENC_CEN(B, G) \
+    if (a.c.bits == B && a.c.group == G) { \
+      hipLaunchKernelGGL((encode_centroid_kernel<B, G>), grid, dim3(256), 0, s, p); \
+      return hipGetLastError(); \
+    }
+    KVC_ENC_CEN(2, 16) KVC_ENC_CEN(2, 32) KVC_ENC_CEN(2, 64)
+    KVC_ENC_CEN(4, 16) KVC_ENC_CEN(4, 32) KVC_ENC_CEN(4, 64)
+#undef KVC_ENC_CEN
+  }
   // centroid and coefficient bases on bf16 d = 128 data: MFMA shortlist + exact rescoring
   if (bf16 && a.c.D == 128 && (p.mode == MODE_CENTROID || p.mode == MODE_COEFF) &&
       p.x_stride % 8 == 0 && a.c.C <= 512) {
