@@ -13,6 +13,9 @@ inputs are resident in HBM when the timed region starts.  The metric is query
 tokens per second (each query token covers all 12 heads).
 
 Prints ONE JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
+`--workload dplr|temporal|mixed` measures the other paths instead (the 30-layer
+cross-layer chain, the temporal chain + attention over its reconstruction, and
+mixed-dimensional attention); the default line is the one above.
 """
 from __future__ import annotations
 
@@ -21,6 +24,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -90,6 +95,223 @@ def cpu_baseline(d: dict, sample_heads=(0, 1), enc_frames: int = 1, q_sample: in
     }
 
 
+def copy_reference(torch, dev):
+    """One plain 256 MiB device-to-device copy (its HBM counters calibrate the others)."""
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def log(msg: str):
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+def _timed(torch, step, steps: int, warmup: int):
+    """Warm up, then time `steps` calls of step(i) between device synchronizations;
+    returns (seconds per step, per-step event pairs)."""
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        step(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps, ev
+
+
+def _line(metric, value, unit, args, t_step, dtype, config, roofline, **extra):
+    out = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": t_step * 1e3, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+           "data": "synthetic (seeded, shapes of the video-DiT caches)", "config": config,
+           "roofline": roofline}
+    out.update(extra)
+    return out
+
+
+def bench_dplr(args, torch, kvc, synth, dev):
+    """30-layer cross-layer chain (12 heads x 128, 32760 tokens, rank 64): per layer the
+    keys are predicted from the reconstructed keys of the layer before and the values from
+    [keys of this layer ; reconstructed values of the layer before] (block-diagonal + rank
+    64), the residual is quantized INT2 g32; layer 0 is an INT4 g32 anchor.  One step =
+    encoding all 30 layers of K and V.  Roofline: algorithmic HBM bytes (inputs read once,
+    codes and scale/zero written once, predictor parameters read once)."""
+    n, H, D, r, layers = 32760, 12, 128, 64, 30
+    prm = synth.cfg2_params()
+
+    def f(name, t=False):
+        b = torch.from_numpy(prm[name].view("int16")).view(torch.bfloat16)
+        return (b.t() if t else b).contiguous().to(dev)
+
+    WK, UK, WV, UV, VKt, VVt = f("WK"), f("UK"), f("WV"), f("UV"), f("VK", True), f("VV", True)
+    log("drawing 30 layers on the device")
+    xs = [(k, v) for k, v in synth.cfg2_layers_device(dev, params=prm)]
+    anchor = kvc.Codec(H, D, 4, 32, kvc.BASE_NONE)
+    kcod = kvc.Codec(H, D, 2, 32, kvc.BASE_DPLR, rank=r, n_inputs=1)
+    vcod = kvc.Codec(H, D, 2, 32, kvc.BASE_DPLR, rank=r, n_inputs=2)
+    stores = [(kvc.Store.allocate(anchor if l == 0 else kcod, n, dev),
+               kvc.Store.allocate(anchor if l == 0 else vcod, n, dev)) for l in range(layers)]
+    rec = [[torch.empty((n, H, D), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+           for _ in range(2)]
+    ws = kvc.kvc.workspace_for(kvc.kvc.OP_ENCODE, vcod, n, dev)
+
+    def step(_):
+        for l in range(layers):
+            k, v = xs[l]
+            rk, rv = rec[l & 1]
+            pk, pv = rec[(l + 1) & 1]
+            if l == 0:
+                kvc.kvc_encode(anchor, k, stores[l][0], 0, None, recon_out=rk)
+                kvc.kvc_encode(anchor, v, stores[l][1], 0, None, recon_out=rv)
+            else:
+                kvc.kvc_encode(kcod, k, stores[l][0], 0,
+                               kvc.BaseParams(prev0=pk, w_block=WK, u=UK, v_lr=VKt),
+                               recon_out=rk, workspace=ws)
+                kvc.kvc_encode(vcod, v, stores[l][1], 0,
+                               kvc.BaseParams(prev0=rk, prev1=pv, w_block=WV, u=UV, v_lr=VVt),
+                               recon_out=rv, workspace=ws)
+
+    log("timing")
+    t_step, ev = _timed(torch, step, args.steps, args.warmup)
+    t_ev = sum(a.elapsed_time(b) for a, b in ev) / len(ev) * 1e-3
+    x_bytes = layers * 2 * n * H * D * 2
+    code_bytes = 2 * n * H * (D * 4 // 8 + 4 * D // 32) + 2 * (layers - 1) * n * H * (D * 2 // 8 + 4 * D // 32)
+    param_bytes = (layers - 1) * sum(int(np.prod(prm[k].shape)) * 2 for k in ("WK", "UK", "VK", "WV", "UV", "VV"))
+    alg = x_bytes + code_bytes + param_bytes
+    flops = (layers - 1) * n * 2 * (H * D * r + H * D * D + H * D * r          # keys
+                                    + 2 * H * D * r + 2 * H * D * D + H * D * r)  # values
+    gbs = alg / t_ev / 1e9
+    return _line("cross-layer block-DPLR chain encode GB/s (30 layers K+V)", gbs, "GB/s", args,
+                 t_step, "bf16", {"workload": "block-DPLR cross-layer chain, 30 layers x 12 heads "
+                                  "x 128, 32760 tokens, rank 64, INT2 g32 (INT4 g32 layer 0)",
+                                  "layers": layers, "tokens": n, "heads": H, "rank": r},
+                 {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "chain", "ms": t_ev * 1e3},
+                 predictor_tflops=flops / t_ev / 1e12, algorithmic_bytes=alg, flops=flops)
+
+
+def bench_temporal(args, torch, kvc, synth, dev):
+    """Temporal chain (40 heads x 128, 16 frames x 1560 tokens, INT2 g64 after an INT4
+    g64 anchor frame): keys predicted per channel from the two previous reconstructed
+    frames, values from the aligned reconstructed keys and the previous values; then
+    attention of the next 3 frames' 4680 queries over the 24960 reconstructed tokens.
+    One step = the 16-frame encode of K and V + the attention."""
+    log("drawing the temporal workload (numpy, about 1.5 minutes)")
+    d = synth.cfg3()
+    H, T, F, D = d["heads"], d["tokens_per_frame"], d["n_frames"], d["dim"]
+    nk, nq = F * T, d["Q"].shape[0]
+
+    def b16(a):
+        return torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
+
+    K, V, Q, M = b16(d["K"]), b16(d["V"]), b16(d["Q"]), b16(d["M"])
+    a_d, b_d, be_d = (torch.from_numpy(x).to(dev) for x in (d["a"], d["b"], d["beta"]))
+    kcod = kvc.Codec(H, D, d["bits"], d["group"], kvc.BASE_TEMPORAL)
+    anchor = kvc.Codec(H, D, d["anchor_bits"], d["group"], kvc.BASE_NONE)
+    dense = kvc.Codec(H, D, 16, 128, kvc.BASE_NONE)
+    khat = torch.empty((nk, H, D), dtype=torch.bfloat16, device=dev)
+    vhat = torch.empty_like(khat)
+    ks = [kvc.Store.allocate(anchor if t == 0 else kcod, T, dev) for t in range(F)]
+    vs = [kvc.Store.allocate(anchor if t == 0 else kcod, T, dev) for t in range(F)]
+    ws = kvc.kvc.workspace_for(kvc.kvc.OP_ENCODE, kcod, T, dev)
+    out = torch.empty((nq, H, D), dtype=torch.float32, device=dev)
+    ev_att = []
+
+    def fr(x, t):
+        return x[t * T:(t + 1) * T]
+
+    def step(i):
+        for t in range(F):
+            if t == 0:
+                kvc.kvc_encode(anchor, fr(K, 0), ks[0], 0, None, recon_out=fr(khat, 0))
+                kvc.kvc_encode(anchor, fr(V, 0), vs[0], 0, None, recon_out=fr(vhat, 0))
+                continue
+            p2 = fr(khat, t - 2) if t > 1 else fr(khat, t - 1)
+            kvc.kvc_encode(kcod, fr(K, t), ks[t], 0,
+                           kvc.BaseParams(prev0=fr(khat, t - 1), prev1=p2, coef_a=a_d, coef_b=b_d),
+                           recon_out=fr(khat, t))
+            kvc.kvc_encode(kcod, fr(V, t), vs[t], 0,
+                           kvc.BaseParams(aux=fr(khat, t), prev0=fr(vhat, t - 1), w_block=M,
+                                          coef_a=be_d), recon_out=fr(vhat, t), workspace=ws)
+        if i is not None:
+            e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            e[0].record()
+        kvc.kvc_attend_compressed(dense, kvc.Store.dense(khat), None, dense, kvc.Store.dense(vhat),
+                                  None, nk, Q, d["scale"], out=out)
+        if i is not None:
+            e[1].record()
+            ev_att.append(e)
+
+    log("timing")
+    t_step, ev = _timed(torch, step, args.steps, args.warmup)
+    t_ev = sum(a.elapsed_time(b) for a, b in ev) / len(ev) * 1e-3
+    t_att = sum(a.elapsed_time(b) for a, b in ev_att) / len(ev_att) * 1e-3
+    flops = attention_flops(nq, nk, D, H)
+    achieved = flops / t_att / 1e12
+    enc_bytes = 2 * nk * H * D * 2 + 2 * T * H * (D * 4 // 8 + 4 * D // 64) \
+        + 2 * (F - 1) * T * H * (D * 2 // 8 + 4 * D // 64)
+    t_enc = t_ev - t_att
+    return _line("temporal chain: attention query-tok/s (16-frame K+V encode + attention)",
+                 nq / t_ev, "query-tok/s", args, t_step, "bf16",
+                 {"workload": "temporal AR(2) keys + key->value cross predictor, 40 heads x 128, "
+                              "16 frames x 1560 tokens, INT2 g64 (INT4 g64 frame 0); attention "
+                              "4680 q x 24960 keys", "heads": H, "frames": F, "tokens": nk,
+                  "queries": nq},
+                 {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                  "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None, "kernel": "attend_bf16_kernel",
+                  "ms": t_att * 1e3},
+                 encode={"ms": t_enc * 1e3, "bytes": enc_bytes, "GB/s": enc_bytes / t_enc / 1e9,
+                         "frac_hbm": enc_bytes / t_enc / 1e9 / HBM_PEAK_GBS})
+
+
+def bench_mixed(args, torch, kvc, synth, dev):
+    """NanoKV-Fast style attention: 12 heads x 128, 65520 keys with 512 centroids per
+    head, INT4 key coefficients on a 16-dim basis, INT2 g32 values; 4680 queries scored as
+    q.C[a] + (B^T q).c without rebuilding keys.  One step = the attention.  Roofline: the
+    method's algorithmic flops (Q C^T table + projection + scores + PV)."""
+    log("drawing the mixed-dimensional workload")
+    d = synth.cfg4()
+    H, C, m, D = d["heads"], d["centroids"], d["coeff_dim"], d["dim"]
+    nk, nq = d["K"].shape[0], d["Q"].shape[0]
+
+    def b16(a):
+        return torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
+
+    kc = kvc.Codec(H, D, d["k_bits"], m, kvc.BASE_COEFF, C, coeff_dim=m)
+    vc = kvc.Codec(H, D, d["v_bits"], d["v_group"], kvc.BASE_CENTROID, C)
+    ks, vs = kvc.Store.allocate(kc, nk, dev), kvc.Store.allocate(vc, nk, dev)
+    kb = kvc.BaseParams(centroids=b16(d["Ck"]), basis=b16(d["B"]))
+    vb = kvc.BaseParams(centroids=b16(d["Cv"]))
+    kvc.kvc_encode(kc, b16(d["K"]), ks, 0, kb)
+    kvc.kvc_encode(vc, b16(d["V"]), vs, 0, vb)
+    Q = b16(d["Q"])
+    out = torch.empty((nq, H, D), dtype=torch.float32, device=dev)
+
+    def step(_):
+        kvc.kvc_attend_mixed_dim(kc, ks, kb, vc, vs, vb, nk, Q, d["scale"], out=out)
+
+    log("timing")
+    t_step, ev = _timed(torch, step, args.steps, args.warmup)
+    t_ev = sum(a.elapsed_time(b) for a, b in ev) / len(ev) * 1e-3
+    flops = H * (2.0 * nq * C * D + 2.0 * nq * D * m + 2.0 * nq * nk * m + 2.0 * nq * nk * D)
+    achieved = flops / t_ev / 1e12
+    return _line("mixed-dimensional attention query-tok/s", nq / t_ev, "query-tok/s", args, t_step,
+                 "bf16", {"workload": "NanoKV-Fast style mixed-dimensional attention, 12 heads x "
+                                      "128, 65520 keys, 512 centroids/head, INT4 m=16 key "
+                                      "coefficients, INT2 g32 values, 4680 queries",
+                          "heads": H, "keys": nk, "queries": nq, "centroids": C, "coeff_dim": m},
+                 {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                  "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                  "kernel": "attend_bf16_kernel (mixed)", "ms": t_ev * 1e3},
+                 full_attention_equivalent_tflops=attention_flops(nq, nk, D, H) / t_ev / 1e12)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,6 +320,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-ref", action="store_true",
                     help="run one plain 256 MiB device copy first (calibrates HBM counters)")
+    ap.add_argument("--workload", default="centroid",
+                    choices=("centroid", "dplr", "temporal", "mixed"),
+                    help="centroid: the default line; the others measure the cross-layer "
+                         "chain, the temporal chain + attention, mixed-dimensional attention")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -110,6 +336,13 @@ def main() -> int:
     import synth
 
     dev = torch.device("cuda:0")
+    if args.copy_ref:
+        copy_reference(torch, dev)
+    if args.workload != "centroid":
+        line = {"dplr": bench_dplr, "temporal": bench_temporal, "mixed": bench_mixed}[args.workload](
+            args, torch, kvc, synth, dev)
+        print(json.dumps(line))
+        return 0
     d = synth.cfg1()
     H, D, C = d["heads"], d["dim"], d["centroids"]
     bits, group = d["bits"], d["group"]
@@ -125,12 +358,6 @@ def main() -> int:
     kb = kvc.BaseParams(centroids=dev_bf16(d["Ck"]))
     vb = kvc.BaseParams(centroids=dev_bf16(d["Cv"]))
     out = torch.empty((nq, H, D), dtype=torch.float32, device=dev)
-    if args.copy_ref:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
     # history before the timed chunk, encoded once
     if lo:
         kvc.kvc_encode(codec, K[:lo], ks, 0, kb)

@@ -495,14 +495,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void encode_shortlist_kernel(EncodePar
 // rint(r * rcp(s) - z * rcp(s)); the two agree unless the product lies within
 // (|z / s| + L + 2) 2^-19 of a half-integer, and a group with such an element is
 // redone with the IEEE division.
-__device__ __forceinline__ uint32_t swap_halves(uint32_t v, int hf) {
-  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return hf ? r[0] : r[1];
-}
-
-__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
 template <int BITS, int G>
 __global__ __launch_bounds__(256, 2) void encode_centroid_kernel(EncodeParams p) {
   constexpr int D = 128, ROW = D + 8, CM = 256;
@@ -761,43 +753,18 @@ __global__ __launch_bounds__(256, 2) void encode_centroid_kernel(EncodeParams p)
     float r[G];
 #pragma unroll
     for (int i = 0; i < G / 8; ++i) {
-      const uint4 cw = *reinterpret_cast<const uint4*>(crow + G * gi + 8 * i);
+      const uint4 cv = *reinterpret_cast<const uint4*>(crow + G * gi + 8 * i);
       const uint4 xw = xv[(G * gi) / 8 + i];
-      const uint32_t xa[4] = {xw.x, xw.y, xw.z, xw.w}, ca[4] = {cw.x, cw.y, cw.z, cw.w};
+      const uint32_t xa[4] = {xw.x, xw.y, xw.z, xw.w}, ca[4] = {cv.x, cv.y, cv.z, cv.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         r[8 * i + 2 * k] = lo_bf16(xa[k]) - lo_bf16(ca[k]);
         r[8 * i + 2 * k + 1] = hi_bf16(xa[k]) - hi_bf16(ca[k]);
       }
     }
-    float mn = r[0], mx = r[0];
-#pragma unroll
-    for (int i = 1; i < G; ++i) { mn = fminf(mn, r[i]); mx = fmaxf(mx, r[i]); }
-    const GroupQ q = group_scale_zero(mn, mx, L);
-    szw[gi] = q.word;
     uint32_t cw[GW];
-#pragma unroll
-    for (int w = 0; w < GW; ++w) cw[w] = 0u;
-    if (q.s != 0.0f) {
-      const float rinv = __builtin_amdgcn_rcpf(q.s);
-      const float nzr = -(q.z * rinv);
-      const float thr = 0.5f - (fabsf(nzr) + (float)(L + 2)) * 0x1p-19f;
-      bool bad = false;
-#pragma unroll
-      for (int i = 0; i < G; ++i) {
-        const float y = __builtin_fmaf(r[i], rinv, nzr);
-        const float k = __builtin_rintf(y);
-        bad |= fabsf(y - k) > thr;
-        const uint32_t code = (uint32_t)__builtin_amdgcn_fmed3f(k, 0.0f, (float)L);
-        cw[i / PER] |= code << (BITS * (i % PER));
-      }
-      if (bad) {
-#pragma unroll
-        for (int w = 0; w < GW; ++w) cw[w] = 0u;
-#pragma unroll
-        for (int i = 0; i < G; ++i) cw[i / PER] |= quantize_one(r[i], q, L) << (BITS * (i % PER));
-      }
-    }
+    const GroupQ q = quantize_group<BITS, G>(r, cw);
+    szw[gi] = q.word;
 #pragma unroll
     for (int w = 0; w < GW; ++w) words[gi * GW + w] = cw[w];
     if (live && (p.recon || p.pred)) {
@@ -810,8 +777,8 @@ __global__ __launch_bounds__(256, 2) void encode_centroid_kernel(EncodeParams p)
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const int i0 = i + 2 * k, i1 = i0 + 1;
-            const uint32_t c0 = (cw[i0 / PER] >> (BITS * (i0 % PER))) & L;
-            const uint32_t c1 = (cw[i1 / PER] >> (BITS * (i1 % PER))) & L;
+            const uint32_t c0 = group_code<BITS, G>(cw, i0);
+            const uint32_t c1 = group_code<BITS, G>(cw, i1);
             const uint32_t cw2 = crow[G * gi + i0] | ((uint32_t)crow[G * gi + i1] << 16);
             const float e0 = lo_bf16(cw2) + dequant_one(c0, q.s, q.z);
             const float e1 = hi_bf16(cw2) + dequant_one(c1, q.s, q.z);
@@ -861,6 +828,10 @@ hipError_t launch_predict(const EncodeLaunch& a, float* base_out, hipStream_t s)
 
 hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s) {
   if (a.n_tokens == 0) return hipSuccess;
+  {
+    hipError_t e = hipSuccess;
+    if (launch_encode_fused(a, s, &e)) return e;
+  }
   EncodeParams p{};
   p.x = a.x;
   p.n_tokens = a.n_tokens;

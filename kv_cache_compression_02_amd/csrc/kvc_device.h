@@ -111,6 +111,61 @@ __device__ __forceinline__ float dequant_one(uint32_t code, float s, float z) {
   return __builtin_fmaf((float)code, s, z);
 }
 
+// Lanes l and l ^ 32 exchange a 32-bit value (v_permlane32_swap); hf = lane >> 5.
+__device__ __forceinline__ uint32_t swap_halves(uint32_t v, int hf) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return hf ? r[0] : r[1];
+}
+
+// The two bf16 values of a packed word, widened exactly to fp32.
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Group quantizer of the codec contract on G residuals: scale/zero as
+// group_scale_zero, codes clamp(rint(fl(fl(r - z) / s)), 0, L) packed BITS-wide into
+// cw.  The quotient is taken as r * rcp(s) - z * rcp(s), which rounds to the same
+// integer unless it lies within (|z / s| + L + 2) 2^-19 of a half-integer (the two
+// forms differ by at most a quarter of that for the values that the clamp keeps); a
+// group with such a value is redone with the IEEE division.
+template <int BITS, int G>
+__device__ __forceinline__ GroupQ quantize_group(const float (&r)[G], uint32_t (&cw)[G * BITS / 32]) {
+  constexpr int L = (1 << BITS) - 1, PER = 32 / BITS, GW = G / PER;
+  float mn = r[0], mx = r[0];
+#pragma unroll
+  for (int i = 1; i < G; ++i) { mn = fminf(mn, r[i]); mx = fmaxf(mx, r[i]); }
+  const GroupQ q = group_scale_zero(mn, mx, L);
+#pragma unroll
+  for (int w = 0; w < GW; ++w) cw[w] = 0u;
+  if (q.s != 0.0f) {
+    const float rinv = __builtin_amdgcn_rcpf(q.s);
+    const float nzr = -(q.z * rinv);
+    const float thr = 0.5f - (fabsf(nzr) + (float)(L + 2)) * 0x1p-19f;
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const float y = __builtin_fmaf(r[i], rinv, nzr);
+      const float k = __builtin_rintf(y);
+      bad |= fabsf(y - k) > thr;
+      const uint32_t code = (uint32_t)__builtin_amdgcn_fmed3f(k, 0.0f, (float)L);
+      cw[i / PER] |= code << (BITS * (i % PER));
+    }
+    if (bad) {
+#pragma unroll
+      for (int w = 0; w < GW; ++w) cw[w] = 0u;
+#pragma unroll
+      for (int i = 0; i < G; ++i) cw[i / PER] |= quantize_one(r[i], q, L) << (BITS * (i % PER));
+    }
+  }
+  return q;
+}
+
+// Code i of a group packed by quantize_group.
+template <int BITS, int G>
+__device__ __forceinline__ uint32_t group_code(const uint32_t (&cw)[G * BITS / 32], int i) {
+  constexpr int PER = 32 / BITS;
+  return (cw[i / PER] >> (BITS * (i % PER))) & ((1u << BITS) - 1u);
+}
+
 // XCD-aware remap of a linear workgroup id: hardware dispatches consecutive ids
 // round-robin over the 8 XCDs; this gives each XCD a contiguous range of tiles so
 // tiles that share data (same head) share that XCD's L2.

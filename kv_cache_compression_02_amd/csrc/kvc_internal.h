@@ -80,6 +80,13 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t s);
 hipError_t launch_attend(const AttendLaunch& a, hipStream_t s);
 hipError_t launch_attend_mixed(const AttendLaunch& a, hipStream_t s);
 
+// Fused predictor + quantizer for bf16 d = 128 (anchors, temporal keys and values,
+// block-DPLR): returns false when a call is outside its shapes, else launches and
+// stores the launch status in *err.  launch_predict_fused writes the prediction only
+// (the decoder's base), with the same kernels and arithmetic as the encoder.
+bool launch_encode_fused(const EncodeLaunch& a, hipStream_t s, hipError_t* err);
+bool launch_predict_fused(const EncodeLaunch& a, float* out, hipStream_t s, hipError_t* err);
+
 // Whether the matrix-product predictor bases (DPLR, temporal values) are built.
 bool predict_available();
 

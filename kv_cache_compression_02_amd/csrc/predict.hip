@@ -128,6 +128,7 @@ hipError_t launch_predict(const EncodeLaunch& a, float* base_out, hipStream_t s)
   const int M = (int)N;
   if (N == 0) return hipSuccess;
   hipError_t e;
+  if (launch_predict_fused(a, base_out, s, &e)) return e;
   if (a.c.base == KVC_BASE_TEMPORAL) {
     // M_h aux_h, then + beta_h * prev0_h
     e = gemm(false, a.b.aux, ps, D, reinterpret_cast<const uint16_t*>(a.b.w_block), D,

@@ -1,0 +1,503 @@
+// Fused predictor + quantizer for bf16 d = 128 data.
+//
+// * Cross-layer block-DPLR (Coral-KV arXiv 2610.12514, Fig. 3):
+//       pred[h] = W_h [in0_h ; in1_h] + U_h t,   t = v_lr [in0 ; in1]   (rank r)
+// * Temporal values (TempoKV arXiv 2610.15324, Fig. 2b): pred[h] = M_h aux_h + beta_h * in0_h.
+// * Temporal keys: pred = (a * in0) + (b * in1) per channel; anchors: pred = 0.
+//
+// rank_kernel forms t (fp32) for 64 tokens per workgroup, the contraction split over
+// four waves and the partial sums added in a fixed order, so every call with the same
+// inputs gives the same t.  pred_kernel keeps one head's W_h and U_h in LDS and walks
+// that head's 32-token tiles; in a wave, lane (t, hf) owns channels 64 hf .. 64 hf + 63 of
+// token t.  The MFMA rows of the weight operand are permuted (row 8q + 4hf + s of block
+// ob holds output channel 64 hf + 16 ob + 4 q + s) so that accumulator r of block ob is
+// channel 64 hf + 16 ob + r of the lane's own token: the prediction reaches the group
+// quantizer from registers.  The contraction index is permuted the same way on both
+// operands, so each lane also feeds only its own half rows.  t enters as bf16 high and
+// low parts (about 2^-16 relative).  With no input to encode the same kernel only
+// writes the prediction, for the decoder: encoder and decoder see identical bases.
+#include "kvc_device.h"
+#include "kvc_internal.h"
+
+namespace kvc {
+
+namespace {
+
+constexpr int D = 128;
+
+struct RankParams {
+  const uint16_t* in0;
+  const uint16_t* in1;
+  int64_t ps;            // token stride of the inputs (elements)
+  const uint16_t* vlr;   // [r][nin * hd]
+  float* t;              // [n][r]
+  int n, r, hd, nin;
+};
+
+template <int RB>        // r <= 32 RB
+__global__ __launch_bounds__(256) void rank_kernel(RankParams p) {
+  __shared__ float red[3][2 * RB][16][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, hf = lane >> 5;
+  const int n0 = blockIdx.x * 64;
+  const int K = p.nin * p.hd;
+  const int slice = K / 4;
+  f32x16_t acc[2][RB];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+  int64_t trow[2];
+  bool tok[2];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    const int n = n0 + 32 * tb + col;
+    tok[tb] = n < p.n;
+    trow[tb] = (int64_t)(tok[tb] ? n : 0) * p.ps;
+  }
+  const uint16_t* arow[RB];
+  bool rok[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int rr = 32 * rb + col;
+    rok[rb] = rr < p.r;
+    arow[rb] = p.vlr + (int64_t)(rok[rb] ? rr : 0) * K;
+  }
+  const bf16x8_t zero = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll 2
+  for (int k = wave * slice; k < (wave + 1) * slice; k += 16) {
+    const int kk = k + 8 * hf;
+    const int j = kk >= p.hd ? 1 : 0;
+    const uint16_t* src = (j ? p.in1 : p.in0) + (kk - j * p.hd);
+    bf16x8_t bx[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+      bx[tb] = tok[tb] ? *reinterpret_cast<const bf16x8_t*>(src + trow[tb]) : zero;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const bf16x8_t a = rok[rb] ? *reinterpret_cast<const bf16x8_t*>(arow[rb] + kk) : zero;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+        acc[tb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bx[tb], acc[tb][rb], 0, 0, 0);
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) red[wave - 1][tb * RB + rb][i][lane] = acc[tb][rb][i];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w)
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[tb][rb][i] = acc[tb][rb][i] + red[w][tb * RB + rb][i][lane];
+  // acc[tb][rb][4q + s] = t[n][32 rb + 8 q + 4 hf + s], n = n0 + 32 tb + col
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    if (!tok[tb]) continue;
+    float* trow_out = p.t + (int64_t)(n0 + 32 * tb + col) * p.r;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = 32 * rb + 8 * q + 4 * hf;
+        if (c < p.r)
+          *reinterpret_cast<float4*>(trow_out + c) =
+              make_float4(acc[tb][rb][4 * q], acc[tb][rb][4 * q + 1], acc[tb][rb][4 * q + 2],
+                          acc[tb][rb][4 * q + 3]);
+      }
+  }
+}
+
+enum { PM_NONE = 0, PM_TEMPORAL_K = 1, PM_DPLR = 2, PM_TEMPORAL_V = 3 };
+
+struct PredParams {
+  const uint16_t* x;       // encode input [n][H][D] (token stride x_stride)
+  int64_t x_stride;
+  const uint16_t* g0;      // matrix-product inputs (DPLR: in0, in1; temporal V: aux)
+  const uint16_t* g1;
+  const uint16_t* e0;      // element-wise inputs (temporal K: K_{t-1}, K_{t-2}; temporal V: V_{t-1})
+  const uint16_t* e1;
+  int64_t ps;              // token stride of g0 / g1 / e0 / e1
+  const uint16_t* w;       // [H][D][nin D]
+  const uint16_t* u;       // [H D][r]
+  const float* t;          // [n][r]
+  const float* ca;         // [H][D]
+  const float* cb;
+  int n, H, r, segs;
+  int64_t token_offset, capacity;
+  uint32_t* codes;
+  uint32_t* sz;
+  uint16_t* recon;         // [n][H][D] bf16 or null
+  float* pred;             // [n][H][D] fp32 or null
+};
+
+// LDS row of MFMA row i of output block ob (the permutation described above)
+__device__ __forceinline__ int out_channel(int ob, int i) {
+  return 64 * ((i >> 2) & 1) + 16 * ob + 4 * (i >> 3) + (i & 3);
+}
+
+template <int BITS, int G, int PM, int NIN>
+__global__ __launch_bounds__(512) void pred_kernel(PredParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  constexpr bool MAT = PM == PM_DPLR || PM == PM_TEMPORAL_V;
+  constexpr bool LR = PM == PM_DPLR;
+  constexpr int WROW = NIN * D + 8;          // padded weight row (bf16)
+  constexpr int NG = 64 / G, PER = 32 / BITS, GW = G / PER, WPL = 64 / PER;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = lane & 31, hf = lane >> 5;
+  const int h = blockIdx.x / p.segs, seg = blockIdx.x % p.segs;
+  const int urow = p.r + 8;
+  uint16_t* wl = lds;                        // [128][WROW]
+  uint16_t* ul = lds + 128 * WROW;           // [128][r + 8]
+  if constexpr (MAT) {
+    const uint16_t* wh = p.w + (int64_t)h * D * (NIN * D);
+    for (int e = tid; e < 128 * NIN * 16; e += 512) {
+      const int i2 = e / (NIN * 16), c = e % (NIN * 16);
+      const int ch = out_channel(i2 >> 5, i2 & 31);
+      *reinterpret_cast<uint4*>(&wl[i2 * WROW + 8 * c]) =
+          *reinterpret_cast<const uint4*>(wh + (int64_t)ch * (NIN * D) + 8 * c);
+    }
+    if constexpr (LR) {
+      const int rc = p.r / 8;
+      for (int e = tid; e < 128 * rc; e += 512) {
+        const int i2 = e / rc, c = e % rc;
+        const int ch = out_channel(i2 >> 5, i2 & 31);
+        *reinterpret_cast<uint4*>(&ul[i2 * urow + 8 * c]) =
+            *reinterpret_cast<const uint4*>(p.u + ((int64_t)h * D + ch) * p.r + 8 * c);
+      }
+    }
+    __syncthreads();
+  }
+  const int tiles = (p.n + 31) / 32;
+  const bf16x8_t zero = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll 1
+  for (int tile = seg * 8 + wave; tile < tiles; tile += p.segs * 8) {
+    const int n = tile * 32 + t;
+    const bool live = n < p.n;
+    const int64_t hrow = (int64_t)(live ? n : 0) * p.ps + (int64_t)h * D + 64 * hf;
+    float pred[64];
+    if constexpr (PM == PM_NONE) {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) pred[i] = 0.0f;
+    } else if constexpr (PM == PM_TEMPORAL_K) {
+      const float* ca = p.ca + h * D + 64 * hf;
+      const float* cb = p.cb + h * D + 64 * hf;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint4 v0 = live ? *reinterpret_cast<const uint4*>(p.e0 + hrow + 8 * i) : make_uint4(0u, 0u, 0u, 0u);
+        const uint4 v1 = live ? *reinterpret_cast<const uint4*>(p.e1 + hrow + 8 * i) : make_uint4(0u, 0u, 0u, 0u);
+        const uint32_t a0[4] = {v0.x, v0.y, v0.z, v0.w}, a1[4] = {v1.x, v1.y, v1.z, v1.w};
+        const float4 ca0 = *reinterpret_cast<const float4*>(ca + 8 * i);
+        const float4 ca1 = *reinterpret_cast<const float4*>(ca + 8 * i + 4);
+        const float4 cb0 = *reinterpret_cast<const float4*>(cb + 8 * i);
+        const float4 cb1 = *reinterpret_cast<const float4*>(cb + 8 * i + 4);
+        const float av[8] = {ca0.x, ca0.y, ca0.z, ca0.w, ca1.x, ca1.y, ca1.z, ca1.w};
+        const float bv[8] = {cb0.x, cb0.y, cb0.z, cb0.w, cb1.x, cb1.y, cb1.z, cb1.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float p0 = av[2 * k] * lo_bf16(a0[k]), q0 = bv[2 * k] * lo_bf16(a1[k]);
+          const float p1 = av[2 * k + 1] * hi_bf16(a0[k]), q1 = bv[2 * k + 1] * hi_bf16(a1[k]);
+          pred[8 * i + 2 * k] = p0 + q0;
+          pred[8 * i + 2 * k + 1] = p1 + q1;
+        }
+      }
+    } else {
+      // matrix products, one input at a time: B operand = this lane's half rows
+      const uint16_t* gsrc[2] = {p.g0, p.g1};
+      f32x16_t acc[4];
+#pragma unroll
+      for (int ob = 0; ob < 4; ++ob)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[ob][i] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NIN; ++j) {
+        bf16x8_t gin[8];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+          gin[ks] = live ? *reinterpret_cast<const bf16x8_t*>(gsrc[j] + hrow + 8 * ks) : zero;
+#pragma unroll
+        for (int ob = 0; ob < 4; ++ob) {
+          const uint16_t* arow = wl + (32 * ob + t) * WROW + j * D + 64 * hf;
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) {
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(arow + 8 * ks);
+            acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, gin[ks], acc[ob], 0, 0, 0);
+          }
+        }
+      }
+      if constexpr (LR) {
+        // rank part: t as bf16 high + low, its own accumulator, added at the end
+        const int rsteps = p.r / 16;
+        bf16x8_t thi[4], tlo[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          float tv[8];
+          if (live && ks < rsteps) {
+            const float4* tp = reinterpret_cast<const float4*>(p.t + (int64_t)n * p.r + 16 * ks + 8 * hf);
+            const float4 a = tp[0], b = tp[1];
+            tv[0] = a.x; tv[1] = a.y; tv[2] = a.z; tv[3] = a.w;
+            tv[4] = b.x; tv[5] = b.y; tv[6] = b.z; tv[7] = b.w;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) tv[i] = 0.0f;
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t hb = f32_to_bf16_bits(tv[i]);
+            thi[ks][i] = (short)hb;
+            tlo[ks][i] = (short)f32_to_bf16_bits(tv[i] - bf16_bits_to_f32(hb));
+          }
+        }
+#pragma unroll
+        for (int ob = 0; ob < 4; ++ob) {
+          const uint16_t* urw = ul + (32 * ob + t) * urow + 8 * hf;
+          f32x16_t au;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) au[i] = 0.0f;
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            if (ks < rsteps) {
+              const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(urw + 16 * ks);
+              au = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, thi[ks], au, 0, 0, 0);
+              au = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, tlo[ks], au, 0, 0, 0);
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) pred[16 * ob + i] = acc[ob][i] + au[i];
+        }
+      } else {
+#pragma unroll
+        for (int ob = 0; ob < 4; ++ob)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) pred[16 * ob + i] = acc[ob][i];
+      }
+      if constexpr (PM == PM_TEMPORAL_V) {
+        const float* ca = p.ca + h * D + 64 * hf;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint4 v0 = live ? *reinterpret_cast<const uint4*>(p.e0 + hrow + 8 * i) : make_uint4(0u, 0u, 0u, 0u);
+          const uint32_t a0[4] = {v0.x, v0.y, v0.z, v0.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int c = 8 * i + 2 * k;
+            const float b0 = ca[c] * lo_bf16(a0[k]), b1 = ca[c + 1] * hi_bf16(a0[k]);
+            pred[c] = pred[c] + b0;
+            pred[c + 1] = pred[c + 1] + b1;
+          }
+        }
+      }
+    }
+    if (!live) continue;
+    const int64_t orow = ((int64_t)n * p.H + h) * D + 64 * hf;   // [n][H][D] outputs
+    if (p.pred) {
+#pragma unroll
+      for (int i = 0; i < 64; i += 4)
+        *reinterpret_cast<float4*>(p.pred + orow + i) = make_float4(pred[i], pred[i + 1], pred[i + 2], pred[i + 3]);
+    }
+    if (p.x) {
+      uint4 xv[8];
+      const uint16_t* xs = p.x + (int64_t)n * p.x_stride + (int64_t)h * D + 64 * hf;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xv[i] = *reinterpret_cast<const uint4*>(xs + 8 * i);
+      uint32_t words[WPL], szw[NG];
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        float r[G];
+#pragma unroll
+        for (int i = 0; i < G / 8; ++i) {
+          const uint4 xw = xv[(G * gi) / 8 + i];
+          const uint32_t xa[4] = {xw.x, xw.y, xw.z, xw.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int c = G * gi + 8 * i + 2 * k;
+            r[8 * i + 2 * k] = lo_bf16(xa[k]) - pred[c];
+            r[8 * i + 2 * k + 1] = hi_bf16(xa[k]) - pred[c + 1];
+          }
+        }
+        uint32_t cw[GW];
+        const GroupQ q = quantize_group<BITS, G>(r, cw);
+        szw[gi] = q.word;
+#pragma unroll
+        for (int w = 0; w < GW; ++w) words[gi * GW + w] = cw[w];
+        if (p.recon) {
+#pragma unroll
+          for (int i = 0; i < G; i += 8) {
+            uint32_t o[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int i0 = i + 2 * k;
+              const float v0 = pred[G * gi + i0] + dequant_one(group_code<BITS, G>(cw, i0), q.s, q.z);
+              const float v1 = pred[G * gi + i0 + 1] + dequant_one(group_code<BITS, G>(cw, i0 + 1), q.s, q.z);
+              o[k] = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
+            }
+            *reinterpret_cast<uint4*>(p.recon + orow + G * gi + i) = make_uint4(o[0], o[1], o[2], o[3]);
+          }
+        }
+      }
+      const int64_t row = (int64_t)h * p.capacity + p.token_offset + n;
+      uint32_t* cd = p.codes + row * (2 * WPL) + WPL * hf;
+#pragma unroll
+      for (int w = 0; w < WPL; w += 4)
+        *reinterpret_cast<uint4*>(cd + w) = make_uint4(words[w], words[w + 1], words[w + 2], words[w + 3]);
+      uint32_t* sd = p.sz + row * (2 * NG) + NG * hf;
+      if constexpr (NG == 2) *reinterpret_cast<uint2*>(sd) = make_uint2(szw[0], szw[1]);
+      else sd[0] = szw[0];
+    }
+  }
+}
+
+template <int BITS, int G, int PM, int NIN>
+hipError_t launch_pred_t(const PredParams& p, int grid, size_t lds, hipStream_t s) {
+  auto k = pred_kernel<BITS, G, PM, NIN>;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k, dim3(grid), dim3(512), lds, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_rank(const EncodeLaunch& a, float* t, hipStream_t s) {
+  RankParams r{};
+  r.in0 = reinterpret_cast<const uint16_t*>(a.b.prev0);
+  r.in1 = reinterpret_cast<const uint16_t*>(a.b.prev1);
+  r.ps = a.b.prev_stride;
+  r.vlr = reinterpret_cast<const uint16_t*>(a.b.v_lr);
+  r.t = t;
+  r.n = (int)a.n_tokens;
+  r.r = a.c.rank;
+  r.hd = a.c.H * D;
+  r.nin = a.c.n_inputs;
+  const dim3 grid((unsigned)((a.n_tokens + 63) / 64));
+  if (r.r <= 32) hipLaunchKernelGGL(rank_kernel<1>, grid, dim3(256), 0, s, r);
+  else hipLaunchKernelGGL(rank_kernel<2>, grid, dim3(256), 0, s, r);
+  return hipGetLastError();
+}
+
+// Which fused mode a call maps to (-1: none).
+int fused_mode(const EncodeLaunch& a) {
+  const CodecArgs& c = a.c;
+  if (c.x_dtype != KVC_BF16 || c.D != D || a.n_tokens >= (1ll << 31)) return -1;
+  if ((a.b.prev_stride % 8) != 0) return -1;
+  switch (c.base) {
+    case KVC_BASE_NONE: return PM_NONE;
+    case KVC_BASE_TEMPORAL: return a.b.w_block ? PM_TEMPORAL_V : PM_TEMPORAL_K;
+    case KVC_BASE_DPLR:
+      if (c.rank % 16 != 0 || c.rank > 64 || c.n_inputs < 1 || c.n_inputs > 2) return -1;
+      return PM_DPLR;
+    default: return -1;
+  }
+}
+
+PredParams make_params(const EncodeLaunch& a, int mode, float* pred) {
+  PredParams p{};
+  p.x = reinterpret_cast<const uint16_t*>(a.x);
+  p.x_stride = a.x_stride;
+  p.ps = a.b.prev_stride;
+  if (mode == PM_DPLR) {
+    p.g0 = reinterpret_cast<const uint16_t*>(a.b.prev0);
+    p.g1 = reinterpret_cast<const uint16_t*>(a.b.prev1);
+    p.u = reinterpret_cast<const uint16_t*>(a.b.u);
+    p.t = reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.workspace) +
+                                         (size_t)a.n_tokens * a.c.H * D * sizeof(float));
+  } else if (mode == PM_TEMPORAL_V) {
+    p.g0 = reinterpret_cast<const uint16_t*>(a.b.aux);
+    p.e0 = reinterpret_cast<const uint16_t*>(a.b.prev0);
+  } else if (mode == PM_TEMPORAL_K) {
+    p.e0 = reinterpret_cast<const uint16_t*>(a.b.prev0);
+    p.e1 = reinterpret_cast<const uint16_t*>(a.b.prev1);
+  }
+  p.w = reinterpret_cast<const uint16_t*>(a.b.w_block);
+  p.ca = a.b.coef_a;
+  p.cb = a.b.coef_b;
+  p.n = (int)a.n_tokens;
+  p.H = a.c.H;
+  p.r = a.c.rank;
+  p.token_offset = a.token_offset;
+  p.capacity = a.st.capacity;
+  p.codes = a.st.codes;
+  p.sz = a.st.sz;
+  p.recon = reinterpret_cast<uint16_t*>(a.recon);
+  p.pred = pred;
+  const int tiles = (int)((a.n_tokens + 31) / 32);
+  const int per_head = (tiles + 7) / 8;
+  const bool mat = mode == PM_DPLR || mode == PM_TEMPORAL_V;
+  p.segs = mat ? std::max(1, std::min(per_head, 256 / std::max(1, a.c.H))) : per_head;
+  return p;
+}
+
+size_t lds_bytes(int mode, int nin, int r) {
+  if (mode != PM_DPLR && mode != PM_TEMPORAL_V) return 0;
+  size_t b = (size_t)128 * (nin * D + 8) * 2;
+  if (mode == PM_DPLR) b += (size_t)128 * (r + 8) * 2;
+  return b;
+}
+
+// One dispatch for the encoder and the decoder's prediction, so the two always run the
+// same instantiation on the same calls.
+hipError_t dispatch(const EncodeLaunch& a, int mode, const PredParams& p, hipStream_t s) {
+  const int bits = a.c.bits, g = a.c.group, grid = p.segs * a.c.H;
+  // the temporal value map has one matrix input whatever n_inputs says
+  const size_t lds = lds_bytes(mode, mode == PM_DPLR ? a.c.n_inputs : 1, a.c.rank);
+#define KVC_PRED(B, G_, M, N)                                                       \
+  if (bits == B && g == G_ && mode == M && (M != PM_DPLR || a.c.n_inputs == N))   \
+    return launch_pred_t<B, G_, M, N>(p, grid, lds, s);
+#define KVC_PRED_ALL(B, G_)                                                        \
+  KVC_PRED(B, G_, PM_NONE, 1) KVC_PRED(B, G_, PM_TEMPORAL_K, 1)                    \
+  KVC_PRED(B, G_, PM_TEMPORAL_V, 1) KVC_PRED(B, G_, PM_DPLR, 1) KVC_PRED(B, G_, PM_DPLR, 2)
+  KVC_PRED_ALL(2, 32) KVC_PRED_ALL(2, 64) KVC_PRED_ALL(4, 32) KVC_PRED_ALL(4, 64)
+#undef KVC_PRED_ALL
+#undef KVC_PRED
+  return hipErrorInvalidValue;
+}
+
+bool fused_codec(const EncodeLaunch& a) {
+  const int bits = a.c.bits, g = a.c.group;
+  return (bits == 2 || bits == 4) && (g == 32 || g == 64);
+}
+
+}  // namespace
+
+bool launch_encode_fused(const EncodeLaunch& a, hipStream_t s, hipError_t* err) {
+  const int mode = fused_mode(a);
+  if (mode < 0 || !fused_codec(a) || a.x_stride % 8 != 0) return false;
+  if (a.n_tokens == 0) { *err = hipSuccess; return true; }
+  if (mode == PM_DPLR) {
+    float* t = reinterpret_cast<float*>(reinterpret_cast<char*>(a.workspace) +
+                                        (size_t)a.n_tokens * a.c.H * D * sizeof(float));
+    const hipError_t e = launch_rank(a, t, s);
+    if (e != hipSuccess) { *err = e; return true; }
+  }
+  *err = dispatch(a, mode, make_params(a, mode, a.pred), s);
+  return true;
+}
+
+bool launch_predict_fused(const EncodeLaunch& a, float* out, hipStream_t s, hipError_t* err) {
+  const int mode = fused_mode(a);
+  if ((mode != PM_DPLR && mode != PM_TEMPORAL_V) || !fused_codec(a)) return false;
+  if (a.n_tokens == 0) { *err = hipSuccess; return true; }
+  if (mode == PM_DPLR) {
+    float* t = reinterpret_cast<float*>(reinterpret_cast<char*>(a.workspace) +
+                                        (size_t)a.n_tokens * a.c.H * D * sizeof(float));
+    const hipError_t e = launch_rank(a, t, s);
+    if (e != hipSuccess) { *err = e; return true; }
+  }
+  PredParams p = make_params(a, mode, out);
+  p.x = nullptr;   // prediction only
+  *err = dispatch(a, mode, p, s);
+  return true;
+}
+
+}  // namespace kvc
