@@ -121,18 +121,16 @@ __device__ __forceinline__ uint32_t swap_halves(uint32_t v, int hf) {
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Group quantizer of the codec contract on G residuals: scale/zero as
-// group_scale_zero, codes clamp(rint(fl(fl(r - z) / s)), 0, L) packed BITS-wide into
-// cw.  The quotient is taken as r * rcp(s) - z * rcp(s), which rounds to the same
+// Group quantizer of the codec contract on G residuals whose group min and max are
+// mn and mx (a group may span lanes): scale/zero as group_scale_zero, codes
+// clamp(rint(fl(fl(r - z) / s)), 0, L) packed BITS-wide into cw.  The quotient is taken as r * rcp(s) - z * rcp(s), which rounds to the same
 // integer unless it lies within (|z / s| + L + 2) 2^-19 of a half-integer (the two
 // forms differ by at most a quarter of that for the values that the clamp keeps); a
 // group with such a value is redone with the IEEE division.
 template <int BITS, int G>
-__device__ __forceinline__ GroupQ quantize_group(const float (&r)[G], uint32_t (&cw)[G * BITS / 32]) {
+__device__ __forceinline__ GroupQ quantize_with(const float (&r)[G], float mn, float mx,
+                                                uint32_t (&cw)[G * BITS / 32]) {
   constexpr int L = (1 << BITS) - 1, PER = 32 / BITS, GW = G / PER;
-  float mn = r[0], mx = r[0];
-#pragma unroll
-  for (int i = 1; i < G; ++i) { mn = fminf(mn, r[i]); mx = fmaxf(mx, r[i]); }
   const GroupQ q = group_scale_zero(mn, mx, L);
 #pragma unroll
   for (int w = 0; w < GW; ++w) cw[w] = 0u;
@@ -157,6 +155,15 @@ __device__ __forceinline__ GroupQ quantize_group(const float (&r)[G], uint32_t (
     }
   }
   return q;
+}
+
+// The same with the group's min and max taken over r itself.
+template <int BITS, int G>
+__device__ __forceinline__ GroupQ quantize_group(const float (&r)[G], uint32_t (&cw)[G * BITS / 32]) {
+  float mn = r[0], mx = r[0];
+#pragma unroll
+  for (int i = 1; i < G; ++i) { mn = fminf(mn, r[i]); mx = fmaxf(mx, r[i]); }
+  return quantize_with<BITS, G>(r, mn, mx, cw);
 }
 
 // Code i of a group packed by quantize_group.

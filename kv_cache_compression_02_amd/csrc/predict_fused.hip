@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void rank_kernel(RankParams p) {
     arow[rb] = p.vlr + (int64_t)(rok[rb] ? rr : 0) * K;
   }
   const bf16x8_t zero = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll 2
+#pragma unroll 4
   for (int k = wave * slice; k < (wave + 1) * slice; k += 16) {
     const int kk = k + 8 * hf;
     const int j = kk >= p.hd ? 1 : 0;
@@ -142,10 +142,11 @@ struct PredParams {
   float* pred;             // [n][H][D] fp32 or null
 };
 
-// LDS row of MFMA row i of output block ob (the permutation described above)
-__device__ __forceinline__ int out_channel(int ob, int i) {
-  return 64 * ((i >> 2) & 1) + 16 * ob + 4 * (i >> 3) + (i & 3);
-}
+// Output channel held by MFMA row i of output block ob (16 x 16 blocks): row 4 q + s
+// of block ob is channel 32 q + 4 ob + s, so lane (t, q) receives channels 32 q + 4 ob + s.
+__device__ __forceinline__ int out_channel(int ob, int i) { return 32 * (i >> 2) + 4 * ob + (i & 3); }
+
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 
 template <int BITS, int G, int PM, int NIN>
 __global__ __launch_bounds__(512) void pred_kernel(PredParams p) {
@@ -153,18 +154,21 @@ __global__ __launch_bounds__(512) void pred_kernel(PredParams p) {
   constexpr bool MAT = PM == PM_DPLR || PM == PM_TEMPORAL_V;
   constexpr bool LR = PM == PM_DPLR;
   constexpr int WROW = NIN * D + 8;          // padded weight row (bf16)
-  constexpr int NG = 64 / G, PER = 32 / BITS, GW = G / PER, WPL = 64 / PER;
+  constexpr int PER = 32 / BITS;             // codes per word
+  constexpr int LW = 32 / PER;               // code words of a lane (32 values)
+  constexpr int GL = G < 32 ? G : 32;        // values of one group in a lane
+  constexpr int NGL = 32 / GL;               // groups (or group halves) in a lane
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t = lane & 31, hf = lane >> 5;
+  const int t = lane & 15, q = lane >> 4;
   const int h = blockIdx.x / p.segs, seg = blockIdx.x % p.segs;
   const int urow = p.r + 8;
-  uint16_t* wl = lds;                        // [128][WROW]
-  uint16_t* ul = lds + 128 * WROW;           // [128][r + 8]
+  uint16_t* wl = lds;                        // [128][WROW], permuted rows
+  uint16_t* ul = lds + 128 * WROW;           // [128][r + 8], permuted rows
   if constexpr (MAT) {
     const uint16_t* wh = p.w + (int64_t)h * D * (NIN * D);
     for (int e = tid; e < 128 * NIN * 16; e += 512) {
       const int i2 = e / (NIN * 16), c = e % (NIN * 16);
-      const int ch = out_channel(i2 >> 5, i2 & 31);
+      const int ch = out_channel(i2 >> 4, i2 & 15);
       *reinterpret_cast<uint4*>(&wl[i2 * WROW + 8 * c]) =
           *reinterpret_cast<const uint4*>(wh + (int64_t)ch * (NIN * D) + 8 * c);
     }
@@ -172,38 +176,46 @@ __global__ __launch_bounds__(512) void pred_kernel(PredParams p) {
       const int rc = p.r / 8;
       for (int e = tid; e < 128 * rc; e += 512) {
         const int i2 = e / rc, c = e % rc;
-        const int ch = out_channel(i2 >> 5, i2 & 31);
+        const int ch = out_channel(i2 >> 4, i2 & 15);
         *reinterpret_cast<uint4*>(&ul[i2 * urow + 8 * c]) =
             *reinterpret_cast<const uint4*>(p.u + ((int64_t)h * D + ch) * p.r + 8 * c);
       }
     }
     __syncthreads();
   }
-  const int tiles = (p.n + 31) / 32;
+  const int tiles = (p.n + 15) / 16;
   const bf16x8_t zero = {0, 0, 0, 0, 0, 0, 0, 0};
+  const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll 1
   for (int tile = seg * 8 + wave; tile < tiles; tile += p.segs * 8) {
-    const int n = tile * 32 + t;
+    const int n = tile * 16 + t;
     const bool live = n < p.n;
-    const int64_t hrow = (int64_t)(live ? n : 0) * p.ps + (int64_t)h * D + 64 * hf;
-    float pred[64];
+    const int64_t qrow = (int64_t)(live ? n : 0) * p.ps + (int64_t)h * D + 32 * q;
+    // the quarter row to encode, in flight while the prediction is formed
+    uint4 xv[4];
+    if (p.x) {
+      const uint16_t* xs = p.x + (int64_t)(live ? n : 0) * p.x_stride + (int64_t)h * D + 32 * q;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xv[i] = live ? *reinterpret_cast<const uint4*>(xs + 8 * i) : z4;
+    }
+    float pred[32];
     if constexpr (PM == PM_NONE) {
 #pragma unroll
-      for (int i = 0; i < 64; ++i) pred[i] = 0.0f;
+      for (int i = 0; i < 32; ++i) pred[i] = 0.0f;
     } else if constexpr (PM == PM_TEMPORAL_K) {
-      const float* ca = p.ca + h * D + 64 * hf;
-      const float* cb = p.cb + h * D + 64 * hf;
+      const float* ca = p.ca + h * D + 32 * q;
+      const float* cb = p.cb + h * D + 32 * q;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint4 v0 = live ? *reinterpret_cast<const uint4*>(p.e0 + hrow + 8 * i) : make_uint4(0u, 0u, 0u, 0u);
-        const uint4 v1 = live ? *reinterpret_cast<const uint4*>(p.e1 + hrow + 8 * i) : make_uint4(0u, 0u, 0u, 0u);
-        const uint32_t a0[4] = {v0.x, v0.y, v0.z, v0.w}, a1[4] = {v1.x, v1.y, v1.z, v1.w};
+      for (int i = 0; i < 4; ++i) {
+        const uint4 v0 = live ? *reinterpret_cast<const uint4*>(p.e0 + qrow + 8 * i) : z4;
+        const uint4 v1 = live ? *reinterpret_cast<const uint4*>(p.e1 + qrow + 8 * i) : z4;
         const float4 ca0 = *reinterpret_cast<const float4*>(ca + 8 * i);
         const float4 ca1 = *reinterpret_cast<const float4*>(ca + 8 * i + 4);
         const float4 cb0 = *reinterpret_cast<const float4*>(cb + 8 * i);
         const float4 cb1 = *reinterpret_cast<const float4*>(cb + 8 * i + 4);
         const float av[8] = {ca0.x, ca0.y, ca0.z, ca0.w, ca1.x, ca1.y, ca1.z, ca1.w};
         const float bv[8] = {cb0.x, cb0.y, cb0.z, cb0.w, cb1.x, cb1.y, cb1.z, cb1.w};
+        const uint32_t a0[4] = {v0.x, v0.y, v0.z, v0.w}, a1[4] = {v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const float p0 = av[2 * k] * lo_bf16(a0[k]), q0 = bv[2 * k] * lo_bf16(a1[k]);
@@ -213,38 +225,41 @@ __global__ __launch_bounds__(512) void pred_kernel(PredParams p) {
         }
       }
     } else {
-      // matrix products, one input at a time: B operand = this lane's half rows
+      // matrix products, one input at a time: B operand = this lane's quarter rows
       const uint16_t* gsrc[2] = {p.g0, p.g1};
-      f32x16_t acc[4];
+      f32x4_t acc[8];
 #pragma unroll
-      for (int ob = 0; ob < 4; ++ob)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[ob][i] = 0.0f;
+      for (int ob = 0; ob < 8; ++ob) acc[ob] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int j = 0; j < NIN; ++j) {
-        bf16x8_t gin[8];
+        bf16x8_t gin[4];
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-          gin[ks] = live ? *reinterpret_cast<const bf16x8_t*>(gsrc[j] + hrow + 8 * ks) : zero;
+        for (int ks = 0; ks < 4; ++ks)
+          gin[ks] = live ? *reinterpret_cast<const bf16x8_t*>(gsrc[j] + qrow + 8 * ks) : zero;
 #pragma unroll
-        for (int ob = 0; ob < 4; ++ob) {
-          const uint16_t* arow = wl + (32 * ob + t) * WROW + j * D + 64 * hf;
+        for (int ob = 0; ob < 8; ++ob) {
+          const uint16_t* arow = wl + (16 * ob + t) * WROW + j * D + 32 * q;
 #pragma unroll
-          for (int ks = 0; ks < 8; ++ks) {
+          for (int ks = 0; ks < 4; ++ks) {
             const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(arow + 8 * ks);
-            acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, gin[ks], acc[ob], 0, 0, 0);
+            acc[ob] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, gin[ks], acc[ob], 0, 0, 0);
           }
+          // keep one block's weight fragments live at a time
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       if constexpr (LR) {
-        // rank part: t as bf16 high + low, its own accumulator, added at the end
-        const int rsteps = p.r / 16;
-        bf16x8_t thi[4], tlo[4];
+        // rank part: t as bf16 high + low parts, its own accumulator, added at the end;
+        // k-step ks covers t[32 ks .. 32 ks + 31], lane q feeding t[32 ks + 8 q ..]
+        constexpr int RS = 2;                  // r <= 64
+        const int rsteps = (p.r + 31) / 32;
+        bf16x8_t thi[RS], tlo[RS];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        for (int ks = 0; ks < RS; ++ks) {
           float tv[8];
-          if (live && ks < rsteps) {
-            const float4* tp = reinterpret_cast<const float4*>(p.t + (int64_t)n * p.r + 16 * ks + 8 * hf);
+          const int c0 = 32 * ks + 8 * q;
+          if (live && c0 < p.r) {
+            const float4* tp = reinterpret_cast<const float4*>(p.t + (int64_t)n * p.r + c0);
             const float4 a = tp[0], b = tp[1];
             tv[0] = a.x; tv[1] = a.y; tv[2] = a.z; tv[3] = a.w;
             tv[4] = b.x; tv[5] = b.y; tv[6] = b.z; tv[7] = b.w;
@@ -260,99 +275,109 @@ __global__ __launch_bounds__(512) void pred_kernel(PredParams p) {
           }
         }
 #pragma unroll
-        for (int ob = 0; ob < 4; ++ob) {
-          const uint16_t* urw = ul + (32 * ob + t) * urow + 8 * hf;
-          f32x16_t au;
+        for (int ob = 0; ob < 8; ++ob) {
+          f32x4_t au = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int i = 0; i < 16; ++i) au[i] = 0.0f;
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
+          for (int ks = 0; ks < RS; ++ks) {
             if (ks < rsteps) {
-              const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(urw + 16 * ks);
-              au = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, thi[ks], au, 0, 0, 0);
-              au = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, tlo[ks], au, 0, 0, 0);
+              const int c0 = 32 * ks + 8 * q;
+              const bf16x8_t a = c0 < p.r
+                  ? *reinterpret_cast<const bf16x8_t*>(ul + (16 * ob + t) * urow + c0) : zero;
+              au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, thi[ks], au, 0, 0, 0);
+              au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, tlo[ks], au, 0, 0, 0);
             }
           }
 #pragma unroll
-          for (int i = 0; i < 16; ++i) pred[16 * ob + i] = acc[ob][i] + au[i];
+          for (int s2 = 0; s2 < 4; ++s2) pred[4 * ob + s2] = acc[ob][s2] + au[s2];
+          __builtin_amdgcn_sched_barrier(0);
         }
       } else {
 #pragma unroll
-        for (int ob = 0; ob < 4; ++ob)
+        for (int ob = 0; ob < 8; ++ob)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) pred[16 * ob + i] = acc[ob][i];
+          for (int s2 = 0; s2 < 4; ++s2) pred[4 * ob + s2] = acc[ob][s2];
       }
       if constexpr (PM == PM_TEMPORAL_V) {
-        const float* ca = p.ca + h * D + 64 * hf;
+        const float* ca = p.ca + h * D + 32 * q;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint4 v0 = live ? *reinterpret_cast<const uint4*>(p.e0 + hrow + 8 * i) : make_uint4(0u, 0u, 0u, 0u);
+        for (int i = 0; i < 4; ++i) {
+          const uint4 v0 = live ? *reinterpret_cast<const uint4*>(p.e0 + qrow + 8 * i) : z4;
+          const float4 ca0 = *reinterpret_cast<const float4*>(ca + 8 * i);
+          const float4 ca1 = *reinterpret_cast<const float4*>(ca + 8 * i + 4);
+          const float av[8] = {ca0.x, ca0.y, ca0.z, ca0.w, ca1.x, ca1.y, ca1.z, ca1.w};
           const uint32_t a0[4] = {v0.x, v0.y, v0.z, v0.w};
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            const int c = 8 * i + 2 * k;
-            const float b0 = ca[c] * lo_bf16(a0[k]), b1 = ca[c + 1] * hi_bf16(a0[k]);
-            pred[c] = pred[c] + b0;
-            pred[c + 1] = pred[c + 1] + b1;
+            const float b0 = av[2 * k] * lo_bf16(a0[k]), b1 = av[2 * k + 1] * hi_bf16(a0[k]);
+            pred[8 * i + 2 * k] = pred[8 * i + 2 * k] + b0;
+            pred[8 * i + 2 * k + 1] = pred[8 * i + 2 * k + 1] + b1;
           }
         }
       }
     }
-    if (!live) continue;
-    const int64_t orow = ((int64_t)n * p.H + h) * D + 64 * hf;   // [n][H][D] outputs
-    if (p.pred) {
+    const int64_t orow = ((int64_t)(live ? n : 0) * p.H + h) * D + 32 * q;   // [n][H][D]
+    if (live && p.pred) {
 #pragma unroll
-      for (int i = 0; i < 64; i += 4)
+      for (int i = 0; i < 32; i += 4)
         *reinterpret_cast<float4*>(p.pred + orow + i) = make_float4(pred[i], pred[i + 1], pred[i + 2], pred[i + 3]);
     }
     if (p.x) {
-      uint4 xv[8];
-      const uint16_t* xs = p.x + (int64_t)n * p.x_stride + (int64_t)h * D + 64 * hf;
+      uint32_t words[LW], szw[NGL];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) xv[i] = *reinterpret_cast<const uint4*>(xs + 8 * i);
-      uint32_t words[WPL], szw[NG];
+      for (int gi = 0; gi < NGL; ++gi) {
+        float r[GL];
 #pragma unroll
-      for (int gi = 0; gi < NG; ++gi) {
-        float r[G];
-#pragma unroll
-        for (int i = 0; i < G / 8; ++i) {
-          const uint4 xw = xv[(G * gi) / 8 + i];
+        for (int i = 0; i < GL / 8; ++i) {
+          const uint4 xw = xv[(GL * gi) / 8 + i];
           const uint32_t xa[4] = {xw.x, xw.y, xw.z, xw.w};
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            const int c = G * gi + 8 * i + 2 * k;
+            const int c = GL * gi + 8 * i + 2 * k;
             r[8 * i + 2 * k] = lo_bf16(xa[k]) - pred[c];
             r[8 * i + 2 * k + 1] = hi_bf16(xa[k]) - pred[c + 1];
           }
         }
-        uint32_t cw[GW];
-        const GroupQ q = quantize_group<BITS, G>(r, cw);
-        szw[gi] = q.word;
+        uint32_t cw[GL * BITS / 32];
+        GroupQ gq;
+        if constexpr (G == 64) {
+          // the group spans this lane and lane ^ 16: combine min and max first
+          float mn = r[0], mx = r[0];
 #pragma unroll
-        for (int w = 0; w < GW; ++w) words[gi * GW + w] = cw[w];
-        if (p.recon) {
+          for (int i = 1; i < GL; ++i) { mn = fminf(mn, r[i]); mx = fmaxf(mx, r[i]); }
+          mn = fminf(mn, __shfl_xor(mn, 16));
+          mx = fmaxf(mx, __shfl_xor(mx, 16));
+          gq = quantize_with<BITS, GL>(r, mn, mx, cw);
+        } else {
+          gq = quantize_group<BITS, GL>(r, cw);
+        }
+        szw[gi] = gq.word;
 #pragma unroll
-          for (int i = 0; i < G; i += 8) {
+        for (int w = 0; w < GL * BITS / 32; ++w) words[gi * (GL * BITS / 32) + w] = cw[w];
+        if (live && p.recon) {
+#pragma unroll
+          for (int i = 0; i < GL; i += 8) {
             uint32_t o[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
               const int i0 = i + 2 * k;
-              const float v0 = pred[G * gi + i0] + dequant_one(group_code<BITS, G>(cw, i0), q.s, q.z);
-              const float v1 = pred[G * gi + i0 + 1] + dequant_one(group_code<BITS, G>(cw, i0 + 1), q.s, q.z);
+              const float v0 = pred[GL * gi + i0] + dequant_one(group_code<BITS, GL>(cw, i0), gq.s, gq.z);
+              const float v1 = pred[GL * gi + i0 + 1] + dequant_one(group_code<BITS, GL>(cw, i0 + 1), gq.s, gq.z);
               o[k] = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
             }
-            *reinterpret_cast<uint4*>(p.recon + orow + G * gi + i) = make_uint4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<uint4*>(p.recon + orow + GL * gi + i) = make_uint4(o[0], o[1], o[2], o[3]);
           }
         }
       }
-      const int64_t row = (int64_t)h * p.capacity + p.token_offset + n;
-      uint32_t* cd = p.codes + row * (2 * WPL) + WPL * hf;
-#pragma unroll
-      for (int w = 0; w < WPL; w += 4)
-        *reinterpret_cast<uint4*>(cd + w) = make_uint4(words[w], words[w + 1], words[w + 2], words[w + 3]);
-      uint32_t* sd = p.sz + row * (2 * NG) + NG * hf;
-      if constexpr (NG == 2) *reinterpret_cast<uint2*>(sd) = make_uint2(szw[0], szw[1]);
-      else sd[0] = szw[0];
+      if (live) {
+        const int64_t row = (int64_t)h * p.capacity + p.token_offset + n;
+        uint32_t* cd = p.codes + row * (4 * LW) + LW * q;
+        if constexpr (LW == 4) *reinterpret_cast<uint4*>(cd) = make_uint4(words[0], words[1], words[2], words[3]);
+        else *reinterpret_cast<uint2*>(cd) = make_uint2(words[0], words[1]);
+        uint32_t* sd = p.sz + row * (D / G);
+        if constexpr (G == 16) *reinterpret_cast<uint2*>(sd + 2 * q) = make_uint2(szw[0], szw[1]);
+        else if constexpr (G == 32) sd[q] = szw[0];
+        else if ((q & 1) == 0) sd[q >> 1] = szw[0];
+      }
     }
   }
 }
@@ -401,6 +426,13 @@ int fused_mode(const EncodeLaunch& a) {
   }
 }
 
+size_t lds_bytes(int mode, int nin, int r) {
+  if (mode != PM_DPLR && mode != PM_TEMPORAL_V) return 0;
+  size_t b = (size_t)128 * (nin * D + 8) * 2;
+  if (mode == PM_DPLR) b += (size_t)128 * (r + 8) * 2;
+  return b;
+}
+
 PredParams make_params(const EncodeLaunch& a, int mode, float* pred) {
   PredParams p{};
   p.x = reinterpret_cast<const uint16_t*>(a.x);
@@ -431,19 +463,17 @@ PredParams make_params(const EncodeLaunch& a, int mode, float* pred) {
   p.sz = a.st.sz;
   p.recon = reinterpret_cast<uint16_t*>(a.recon);
   p.pred = pred;
-  const int tiles = (int)((a.n_tokens + 31) / 32);
+  const int tiles = (int)((a.n_tokens + 15) / 16);
   const int per_head = (tiles + 7) / 8;
   const bool mat = mode == PM_DPLR || mode == PM_TEMPORAL_V;
-  p.segs = mat ? std::max(1, std::min(per_head, 256 / std::max(1, a.c.H))) : per_head;
+  // persistent workgroups for the matrix modes: as many as fit at once (the weights
+  // then load once per workgroup), two per CU when they leave LDS room for it
+  const size_t lds = lds_bytes(mode, mode == PM_DPLR ? a.c.n_inputs : 1, a.c.rank);
+  const int per_cu = lds <= 72 * 1024 ? 2 : 1;
+  p.segs = mat ? std::max(1, std::min(per_head, per_cu * 256 / std::max(1, a.c.H))) : per_head;
   return p;
 }
 
-size_t lds_bytes(int mode, int nin, int r) {
-  if (mode != PM_DPLR && mode != PM_TEMPORAL_V) return 0;
-  size_t b = (size_t)128 * (nin * D + 8) * 2;
-  if (mode == PM_DPLR) b += (size_t)128 * (r + 8) * 2;
-  return b;
-}
 
 // One dispatch for the encoder and the decoder's prediction, so the two always run the
 // same instantiation on the same calls.
@@ -457,7 +487,8 @@ hipError_t dispatch(const EncodeLaunch& a, int mode, const PredParams& p, hipStr
 #define KVC_PRED_ALL(B, G_)                                                        \
   KVC_PRED(B, G_, PM_NONE, 1) KVC_PRED(B, G_, PM_TEMPORAL_K, 1)                    \
   KVC_PRED(B, G_, PM_TEMPORAL_V, 1) KVC_PRED(B, G_, PM_DPLR, 1) KVC_PRED(B, G_, PM_DPLR, 2)
-  KVC_PRED_ALL(2, 32) KVC_PRED_ALL(2, 64) KVC_PRED_ALL(4, 32) KVC_PRED_ALL(4, 64)
+  KVC_PRED_ALL(2, 16) KVC_PRED_ALL(2, 32) KVC_PRED_ALL(2, 64)
+  KVC_PRED_ALL(4, 16) KVC_PRED_ALL(4, 32) KVC_PRED_ALL(4, 64)
 #undef KVC_PRED_ALL
 #undef KVC_PRED
   return hipErrorInvalidValue;
@@ -465,7 +496,7 @@ hipError_t dispatch(const EncodeLaunch& a, int mode, const PredParams& p, hipStr
 
 bool fused_codec(const EncodeLaunch& a) {
   const int bits = a.c.bits, g = a.c.group;
-  return (bits == 2 || bits == 4) && (g == 32 || g == 64);
+  return (bits == 2 || bits == 4) && (g == 16 || g == 32 || g == 64);
 }
 
 }  // namespace
