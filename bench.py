@@ -221,6 +221,7 @@ def bench_temporal(args, torch, kvc, synth, dev):
     vs = [kvc.Store.allocate(anchor if t == 0 else kcod, T, dev) for t in range(F)]
     ws = kvc.kvc.workspace_for(kvc.kvc.OP_ENCODE, kcod, T, dev)
     out = torch.empty((nq, H, D), dtype=torch.float32, device=dev)
+    att_ws = kvc.kvc.workspace_for(kvc.kvc.OP_ATTEND, dense, nk, dev, n_queries=nq)
     ev_att = []
 
     def fr(x, t):
@@ -243,7 +244,7 @@ def bench_temporal(args, torch, kvc, synth, dev):
             e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             e[0].record()
         kvc.kvc_attend_compressed(dense, kvc.Store.dense(khat), None, dense, kvc.Store.dense(vhat),
-                                  None, nk, Q, d["scale"], out=out)
+                                  None, nk, Q, d["scale"], out=out, workspace=att_ws)
         if i is not None:
             e[1].record()
             ev_att.append(e)
@@ -292,9 +293,10 @@ def bench_mixed(args, torch, kvc, synth, dev):
     kvc.kvc_encode(vc, b16(d["V"]), vs, 0, vb)
     Q = b16(d["Q"])
     out = torch.empty((nq, H, D), dtype=torch.float32, device=dev)
+    ws = kvc.kvc.workspace_for(kvc.kvc.OP_ATTEND_MIXED, kc, nk, dev, n_queries=nq)
 
     def step(_):
-        kvc.kvc_attend_mixed_dim(kc, ks, kb, vc, vs, vb, nk, Q, d["scale"], out=out)
+        kvc.kvc_attend_mixed_dim(kc, ks, kb, vc, vs, vb, nk, Q, d["scale"], out=out, workspace=ws)
 
     log("timing")
     t_step, ev = _timed(torch, step, args.steps, args.warmup)
@@ -363,6 +365,7 @@ def main() -> int:
         kvc.kvc_encode(codec, K[:lo], ks, 0, kb)
         kvc.kvc_encode(codec, V[:lo], vs, 0, vb)
     Kc, Vc = K[lo:hi].contiguous(), V[lo:hi].contiguous()
+    att_ws = kvc.kvc.workspace_for(kvc.kvc.OP_ATTEND, codec, nk, dev, n_queries=nq)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
 
     def step(e=None):
@@ -370,7 +373,8 @@ def main() -> int:
         kvc.kvc_encode(codec, Kc, ks, lo, kb)
         kvc.kvc_encode(codec, Vc, vs, lo, vb)
         if e: e[1].record()
-        kvc.kvc_attend_compressed(codec, ks, kb, codec, vs, vb, nk, Q, d["scale"], out=out)
+        kvc.kvc_attend_compressed(codec, ks, kb, codec, vs, vb, nk, Q, d["scale"], out=out,
+                                  workspace=att_ws)
         if e: e[2].record()
 
     for _ in range(args.warmup):

@@ -187,7 +187,11 @@ kvc_status kvc_decode(const kvc_codec* codec, const kvc_store* src, int64_t toke
  *   q:   [n_queries][H][d] x_dtype, token stride H*d.
  *   out: [n_queries][H][d] fp32.
  *   lse: optional [H][n_queries] fp32 natural-log sum-exp of the scaled scores.
- *   workspace: unused by this version (pass NULL, 0).
+ *   workspace: optional device scratch.  With kvc_workspace_bytes(KVC_OP_ATTEND, kc,
+ *     n_keys, n_queries) bytes (when that is nonzero) the bf16 path splits the keys
+ *     across workgroups and merges the partial results by their log-sum-exp (the
+ *     same softmax, summed in another order); NULL, or a smaller workspace, runs one
+ *     pass over the keys.  The contents are overwritten.
  * Errors: KVC_E_NULL, KVC_E_SHAPE (n_keys > capacity, n_keys < 1, mismatched
  * heads/d), KVC_E_UNSUPPORTED, KVC_E_ALIGN, KVC_E_DEVICE. */
 kvc_status kvc_attend_compressed(const kvc_codec* kc, const kvc_store* k,
@@ -212,8 +216,10 @@ kvc_status kvc_attend_mixed_dim(const kvc_codec* kc, const kvc_store* k,
                                 float* out, float* lse, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
-/* Workspace bytes an entry point needs for n_tokens tokens (op: KVC_OP_*).  Nonzero
- * only for encode / decode with the DPLR or temporal bases. */
+/* Workspace bytes of an entry point (op: KVC_OP_*) for n_tokens tokens (the keys for
+ * the attention ops) and n_queries queries.  Encode / decode: required by the DPLR
+ * and temporal-value bases, 0 otherwise.  Attention: the optional workspace that
+ * enables key splitting (0 when a single pass is used anyway). */
 enum { KVC_OP_ENCODE = 0, KVC_OP_DECODE = 1, KVC_OP_ATTEND = 2, KVC_OP_ATTEND_MIXED = 3 };
 size_t kvc_workspace_bytes(int32_t op, const kvc_codec* codec, int64_t n_tokens,
                            int64_t n_queries);

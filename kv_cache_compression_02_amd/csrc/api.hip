@@ -193,10 +193,10 @@ kvc_status kvc_store_bytes(const kvc_codec* codec, int64_t capacity, size_t* cod
 }
 
 size_t kvc_workspace_bytes(int32_t op, const kvc_codec* codec, int64_t n_tokens, int64_t n_queries) {
-  (void)n_queries;
   CodecArgs c;
   if (resolve_codec(codec, &c) != KVC_OK || n_tokens < 0) return 0;
-  if (op == 0 || op == 1) return encode_workspace_bytes(c, n_tokens);
+  if (op == KVC_OP_ENCODE || op == KVC_OP_DECODE) return encode_workspace_bytes(c, n_tokens);
+  if (op == KVC_OP_ATTEND || op == KVC_OP_ATTEND_MIXED) return attend_workspace_bytes(c, n_tokens, n_queries);
   return 0;
 }
 
@@ -295,11 +295,12 @@ kvc_status kvc_attend_compressed(const kvc_codec* kc, const kvc_store* k,
                                  const void* q, int64_t n_queries, float softmax_scale,
                                  float* out, float* lse, void* workspace, size_t workspace_bytes,
                                  void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   AttendLaunch a;
   kvc_status st = check_attend(kc, k, kp, vc, v, vp, n_keys, q, n_queries, out, lse, &a);
   if (st != KVC_OK) return st;
+  if (workspace && !aligned16(workspace)) return KVC_E_ALIGN;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace ? workspace_bytes : 0;
   for (const CodecArgs* c : {&a.kc, &a.vc})
     if (c->base != KVC_BASE_NONE && c->base != KVC_BASE_CENTROID) return KVC_E_UNSUPPORTED;
   if (a.kc.x_dtype == KVC_BF16 && a.kc.D != 128) return KVC_E_UNSUPPORTED;
@@ -316,11 +317,12 @@ kvc_status kvc_attend_mixed_dim(const kvc_codec* kc, const kvc_store* k,
                                 const void* q, int64_t n_queries, float softmax_scale,
                                 float* out, float* lse, void* workspace, size_t workspace_bytes,
                                 void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   AttendLaunch a;
   kvc_status st = check_attend(kc, k, kp, vc, v, vp, n_keys, q, n_queries, out, lse, &a);
   if (st != KVC_OK) return st;
+  if (workspace && !aligned16(workspace)) return KVC_E_ALIGN;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace ? workspace_bytes : 0;
   if (a.kc.base != KVC_BASE_COEFF || a.vc.base != KVC_BASE_CENTROID) return KVC_E_UNSUPPORTED;
   if (a.kc.x_dtype != KVC_BF16 || a.kc.D != 128 || a.kc.m != 16 || a.kc.groups != 1)
     return KVC_E_UNSUPPORTED;

@@ -22,6 +22,8 @@
 //   the S^T tile produces is used directly as the B operand: the key order inside
 //   each 16-key MFMA step is permuted, and V^T is read from LDS in the same order.
 // fp32 path (d = 64 or 128): one lane per query, fp32 dot products and softmax.
+#include <type_traits>
+
 #include "kvc_device.h"
 #include "kvc_internal.h"
 
@@ -50,6 +52,12 @@ struct AttnParams {
   float* lse;
   Src k, v;
   const uint16_t* basis;   // mixed-dimensional keys: [d][m] bf16
+  // key splitting: workgroup (head, query block, split) covers key tiles
+  // [split * tps, min(ntiles, (split + 1) * tps)) and writes its normalized partial
+  // output and log-sum-exp to part_o [splits][nq][H][D] / part_lse [splits][H][nq]
+  int splits, tps;
+  float* part_o;
+  float* part_lse;
 };
 
 // Decode channels ch0..ch0+7 of key `key` (head h) as fp32 (cache dtype XT rounding
@@ -139,10 +147,17 @@ struct VPre {                     // keys 2kp, 2kp+1, channels 8c8..8c8+7
   uint4 c[2];
 };
 
-// V^T tile swizzle: row r keeps its keys in groups of 4, XOR-permuted by (r/8) mod 8
-// so that the transposed writes of 16 lanes (rows 8 apart) and the MFMA operand reads
-// spread over the LDS banks.
-__device__ __forceinline__ int vswz(int row, int key) { return key ^ (((row >> 3) & 7) << 2); }
+// V^T tile layout: row r (a channel) holds the tile's 64 keys as fp16.  Inside each
+// group of 16 keys, bits 2 and 3 of the key index are swapped, so the 8 keys one lane
+// feeds to a PV MFMA ({4 h .. 4 h + 3, 8 + 4 h .. 8 + 4 h + 3} of the group, h = lane's
+// half) are 8 consecutive elements: one 16-byte read.  The 8-element blocks of row r
+// are XOR-permuted by (r / 16) mod 8, which keeps those reads free of bank conflicts
+// and the transposed decode writes (16 lanes, rows 8 apart) at most two-way.
+__device__ __forceinline__ int vpos(int row, int key) {
+  const int k16 = key & 15;
+  const int p = (key & ~15) | (k16 & 3) | ((k16 & 4) << 1) | ((k16 & 8) >> 1);
+  return (((p >> 3) ^ ((row >> 4) & 7)) << 3) | (p & 7);
+}
 
 // DENSE: K and V are uncompressed bf16 caches [capacity][H][d] (e.g. what kvc_decode
 // writes for a predictor chain); the tile loaders copy rows instead of decoding.
@@ -164,10 +179,12 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
   const int col = lane & 31;
   const int nqb = (int)((p.nq + BQ - 1) / BQ);
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = tile / nqb;
-  const int64_t myq = (int64_t)(tile % nqb) * BQ + wave * QW + col;
+  const int split = tile % p.splits, hq = tile / p.splits;
+  const int h = hq / nqb;
+  const int64_t myq = (int64_t)(hq % nqb) * BQ + wave * QW + col;
   const int nk = (int)p.nk;
   const int ntiles = (nk + BK - 1) / BK;
+  const int tb = split * p.tps, te = min(ntiles, tb + p.tps);   // this split's key tiles
 
   // Per-head buffer resources (SGPRs): every prefetch is a buffer load with a 32-bit
   // byte offset, and the descriptor's record count bounds it - a read past the head's
@@ -299,7 +316,7 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
         const int row = 8 * c8 + c;
         const uint32_t a = (c & 1) ? (v0[c >> 1] >> 16) : (v0[c >> 1] & 0xFFFFu);
         const uint32_t b = (c & 1) ? (v1[c >> 1] >> 16) : (v1[c >> 1] & 0xFFFFu);
-        *reinterpret_cast<uint32_t*>(&v_lds[buf][row * VROW + vswz(row, 2 * kp)]) =
+        *reinterpret_cast<uint32_t*>(&v_lds[buf][row * VROW + vpos(row, 2 * kp)]) =
             bf16x2_to_f16x2(a | (b << 16));
       }
       return;
@@ -392,7 +409,7 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
       for (int c = 0; c < 8; ++c) {
         const int row = 8 * c8 + c;
         const uint32_t w = bf16x2_to_f16x2(pk_bf16(x[0][c], x[1][c]));   // keys 2kp, 2kp+1
-        *reinterpret_cast<uint32_t*>(&v_lds[buf][row * VROW + vswz(row, 2 * kp)]) = w;
+        *reinterpret_cast<uint32_t*>(&v_lds[buf][row * VROW + vpos(row, 2 * kp)]) = w;
       }
     }
   };
@@ -458,7 +475,9 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
   float l_run = 0.0f;
   const float c2 = p.scale_log2;
 
-  auto compute = [&](int t, int buf) {
+  // MASK: the tile runs past the last key (only the final tile of a ragged history)
+  auto compute = [&](int t, int buf, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int k0 = t * BK;
     // S^T = K Q^T (raw scores)
     // K fragments stream through two groups of 4 registers: the reads of group g+1
@@ -493,6 +512,20 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
       if (g < 2) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    // all V^T fragments of the tile are read now, so they arrive during the softmax
+    // (one 16-byte read each: row 32 d + col, block (2 kh + half) ^ (2 d + col / 16) =
+    // 2 (kh ^ d) + (half ^ col / 16)); (kb, hf) = kh covers keys 32*kb + 16*hf +
+    // {4*half+0..3, 8+4*half+0..3}
+    f16x8_t vf[4][4];
+    {
+      const uint16_t* vbase = &v_lds[buf][col * VROW + 8 * (half ^ (col >> 4))];
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int kh = 0; kh < 4; ++kh)
+          vf[d][kh] = *reinterpret_cast<const f16x8_t*>(vbase + 32 * d * VROW + 16 * (kh ^ d));
+    }
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (MIXED) {   // + (B^T q) . c: hi*hi + hi*lo + lo*hi
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -504,7 +537,7 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cl, phi, sacc[kb], 0, 0, 0);
       }
     }
-    if (k0 + BK > nk) {   // last, partial tile: mask keys >= nk
+    if constexpr (MASK) {   // last, partial tile: mask keys >= nk
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -517,9 +550,20 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[kb][r]);
     mloc = fmaxf(mloc, other_half(mloc, half));
-    const float m_new = fmaxf(m_run, mloc * c2);     // log2 domain (scale > 0)
-    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
-    const float negm = -m_new;
+    // Lazy rescaling: the reference max moves only when a lane's scores exceed it by
+    // more than 2^8 (log2 domain, scale > 0), so P stays <= 256 - exact range for
+    // fp16 - and the output accumulators are rescaled on a few tiles only.
+    if (__builtin_expect(__any(mloc * c2 > m_run + 8.0f), 0)) {
+      const float m_new = fmaxf(m_run, mloc * c2);
+      const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= corr;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[d][r] *= corr;
+      m_run = m_new;
+    }
+    const float negm = -m_run;
     float lsum = 0.0f;
     f16x8_t pb[2][2];
 #pragma unroll
@@ -536,65 +580,52 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
         pb[kb][hf] = t8;
       }
     lsum += other_half(lsum, half);
-    l_run = l_run * corr + lsum;
-    m_run = m_new;
-    if (!__all(corr == 1.0f)) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[d][r] *= corr;
-    }
-    // O^T += V^T P^T; (kb, hf) covers keys 32*kb + 16*hf + {4*half+0..3, 8+4*half+0..3}
-    f16x8_t vf[4];
-    auto load_v = [&](int d, f16x8_t (&dst)[4]) {
-      const int row = d * 32 + col;
-      const uint16_t* vrow = &v_lds[buf][row * VROW];
-#pragma unroll
-      for (int kh = 0; kh < 4; ++kh) {   // kh = 2*kb + hf
-        const int kb0 = 16 * kh + 4 * half;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + vswz(row, kb0));
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + vswz(row, kb0 + 8));
-        dst[kh] = __builtin_bit_cast(f16x8_t, uint4{lo.x, lo.y, hi.x, hi.y});
-      }
-    };
+    l_run = l_run + lsum;
+    // O^T += V^T P^T
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      load_v(d, vf);
 #pragma unroll
       for (int kh = 0; kh < 4; ++kh)
-        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[kh], pb[kh >> 1][kh & 1], oacc[d], 0, 0, 0);
+        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[d][kh], pb[kh >> 1][kh & 1], oacc[d], 0, 0, 0);
     }
   };
 
-  // ---- prologue: tile 0 decoded into buffer 0, tile 1 prefetched, indices of tile 2
+  // ---- prologue: first tile decoded into buffer 0, the next prefetched, indices of
+  //      the one after
   KPre<BITS> kpre;
   VPre vpre;
   int kidx, vidx[2];
-  load_idx(0, kidx, vidx);
-  load_data(0, kidx, vidx, kpre, vpre);
-  if (ntiles > 1) load_idx(1, kidx, vidx);
+  load_idx(tb, kidx, vidx);
+  load_data(tb, kidx, vidx, kpre, vpre);
+  if (tb + 1 < te) load_idx(tb + 1, kidx, vidx);
   dequant(kpre, vpre, 0);
-  if (ntiles > 1) load_data(1, kidx, vidx, kpre, vpre);
-  if (ntiles > 2) load_idx(2, kidx, vidx);
+  if (tb + 1 < te) load_data(tb + 1, kidx, vidx, kpre, vpre);
+  if (tb + 2 < te) load_idx(tb + 2, kidx, vidx);
   __syncthreads();
 
   // ---- main loop: decode tile t+1 into the other buffer, prefetch tile t+2's
   //      compressed rows (and t+3's indices), then attend tile t
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) {
+  // the final tile of a ragged history (the only one that masks keys) runs after the
+  // loop, so the loop body has one variant
+  const int tfull = (te * BK > nk) ? te - 1 : te;
+  for (int t = tb; t < tfull; ++t) {
+    const int buf = (t - tb) & 1;
+    if (t + 1 < te) {
       dequant(kpre, vpre, buf ^ 1);
-      if (t + 2 < ntiles) load_data(t + 2, kidx, vidx, kpre, vpre);
-      if (t + 3 < ntiles) load_idx(t + 3, kidx, vidx);
+      if (t + 2 < te) load_data(t + 2, kidx, vidx, kpre, vpre);
+      if (t + 3 < te) load_idx(t + 3, kidx, vidx);
     }
-    compute(t, buf);
+    compute(t, buf, std::false_type{});
     __syncthreads();
   }
+  if (tfull < te) compute(tfull, (tfull - tb) & 1, std::true_type{});
 
-  // ---- epilogue: O[q][h][c] = O^T[c][q] / l
+  // ---- epilogue: O[q][h][c] = O^T[c][q] / l (a split's partial output when splitting)
+  float* const outp = p.splits > 1 ? p.part_o + (int64_t)split * p.nq * p.H * DM : p.out;
+  float* const lsep = p.splits > 1 ? p.part_lse + (int64_t)split * p.H * p.nq : p.lse;
   if (myq < p.nq) {
     const float inv = 1.0f / l_run;
-    float* op = p.out + (myq * p.H + h) * DM;
+    float* op = outp + (myq * p.H + h) * DM;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
@@ -606,9 +637,41 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
         o.w = oacc[d][4 * g + 3] * inv;
         *reinterpret_cast<float4*>(op + d * 32 + 8 * g + 4 * half) = o;
       }
-    if (p.lse && half == 0)
-      p.lse[(int64_t)h * p.nq + myq] = (m_run + __log2f(l_run)) * 0.69314718055994531f;
+    if (lsep && half == 0)
+      lsep[(int64_t)h * p.nq + myq] = (m_run + __log2f(l_run)) * 0.69314718055994531f;
   }
+}
+
+// Merge of the key splits: O = sum_s w_s O_s, w_s = exp(lse_s - lse) with
+// lse = log sum_s exp(lse_s); one thread per (query, head, 4 channels).
+__global__ __launch_bounds__(256) void attend_combine_kernel(AttnParams p) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nqh = p.nq * p.H;
+  if (i >= nqh * (DM / 4)) return;
+  const int64_t qh = i / (DM / 4);
+  const int c4 = (int)(i % (DM / 4));
+  const int64_t q = qh / p.H;
+  const int h = (int)(qh % p.H);
+  float ls[8];
+  float m = -__builtin_inff();
+  for (int s = 0; s < p.splits; ++s) {
+    ls[s] = p.part_lse[((int64_t)s * p.H + h) * p.nq + q];
+    m = fmaxf(m, ls[s]);
+  }
+  float wsum = 0.0f;
+  float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int s = 0; s < p.splits; ++s) {
+    const float w = __expf(ls[s] - m);
+    wsum += w;
+    const float4 v = *reinterpret_cast<const float4*>(p.part_o + ((int64_t)s * nqh + qh) * DM + 4 * c4);
+    o.x = __builtin_fmaf(w, v.x, o.x);
+    o.y = __builtin_fmaf(w, v.y, o.y);
+    o.z = __builtin_fmaf(w, v.z, o.z);
+    o.w = __builtin_fmaf(w, v.w, o.w);
+  }
+  const float inv = 1.0f / wsum;
+  *reinterpret_cast<float4*>(p.out + qh * DM + 4 * c4) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+  if (p.lse && c4 == 0) p.lse[(int64_t)h * p.nq + q] = m + __logf(wsum);
 }
 
 // ----------------------------------------------------------------------------
@@ -700,7 +763,47 @@ Src make_src(const CodecArgs& c, const StoreArgs& st, const BaseArgs& b) {
   return s;
 }
 
+// Key splits of the bf16 path: about two workgroups per CU when the (head, query
+// block) grid alone is smaller, at least 8 key tiles per split, at most 8 splits, and
+// no empty split.
+int choose_splits(int H, int64_t nq, int64_t nk) {
+  const int64_t base = (int64_t)H * ((nq + BQ - 1) / BQ);
+  const int ntiles = (int)((nk + BK - 1) / BK);
+  int sp = (int)std::min<int64_t>(8, (512 + base - 1) / base);
+  sp = std::max(1, std::min(sp, ntiles / 8));
+  const int tps = (ntiles + sp - 1) / sp;
+  return (ntiles + tps - 1) / tps;
+}
+
+// Sets p.splits / p.tps / partial buffers (one split when the workspace is too small).
+void plan_splits(const AttendLaunch& a, AttnParams& p) {
+  const int ntiles = (int)((a.n_keys + BK - 1) / BK);
+  p.splits = 1;
+  p.tps = ntiles;
+  const int sp = choose_splits(a.kc.H, a.n_queries, a.n_keys);
+  if (sp > 1 && a.workspace && a.workspace_bytes >= attend_workspace_bytes(a.kc, a.n_keys, a.n_queries)) {
+    p.splits = sp;
+    p.tps = (ntiles + sp - 1) / sp;
+    p.part_o = reinterpret_cast<float*>(a.workspace);
+    p.part_lse = p.part_o + (int64_t)sp * a.n_queries * a.kc.H * DM;
+  }
+}
+
+hipError_t launch_combine(const AttnParams& p, hipStream_t s) {
+  if (p.splits <= 1) return hipGetLastError();
+  const int64_t n = p.nq * p.H * (DM / 4);
+  hipLaunchKernelGGL(attend_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+size_t attend_workspace_bytes(const CodecArgs& kc, int64_t n_keys, int64_t n_queries) {
+  if (kc.x_dtype != KVC_BF16 || kc.D != DM || n_queries <= 0 || n_keys <= 0) return 0;
+  const int sp = choose_splits(kc.H, n_queries, n_keys);
+  if (sp <= 1) return 0;
+  return (size_t)sp * n_queries * kc.H * (DM + 1) * sizeof(float);
+}
 
 hipError_t launch_attend(const AttendLaunch& a, hipStream_t s) {
   if (a.n_queries == 0) return hipSuccess;
@@ -716,11 +819,12 @@ hipError_t launch_attend(const AttendLaunch& a, hipStream_t s) {
   p.k = make_src(a.kc, a.ks, a.kb);
   p.v = make_src(a.vc, a.vs, a.vb);
   if (a.kc.x_dtype == KVC_BF16) {
+    plan_splits(a, p);
     const int nqb = (int)((a.n_queries + BQ - 1) / BQ);
-    const dim3 grid(nqb * a.kc.H), block(NT);
+    const dim3 grid(nqb * a.kc.H * p.splits), block(NT);
     if (a.kc.bits == 16) {   // uncompressed bf16 caches (validated: both K and V)
       hipLaunchKernelGGL((attend_bf16_kernel<2, 2, false, false, false, true>), grid, block, 0, s, p);
-      return hipGetLastError();
+      return launch_combine(p, s);
     }
     const bool kc = p.k.mode == SRC_CENTROID, vc = p.v.mode == SRC_CENTROID;
     // every (K bits, V bits, K base, V base) combination is its own kernel so the
@@ -728,7 +832,7 @@ hipError_t launch_attend(const AttendLaunch& a, hipStream_t s) {
 #define KVC_ATT(KB_, VB_, KC_, VC_)                                                       \
   if (a.kc.bits == KB_ && a.vc.bits == VB_ && kc == KC_ && vc == VC_) {                 \
     hipLaunchKernelGGL((attend_bf16_kernel<KB_, VB_, KC_, VC_, false>), grid, block, 0, s, p); \
-    return hipGetLastError();                                                            \
+    return launch_combine(p, s);                                                         \
   }
 #define KVC_ATT_BITS(KC_, VC_) \
   KVC_ATT(2, 2, KC_, VC_) KVC_ATT(2, 4, KC_, VC_) KVC_ATT(4, 2, KC_, VC_) KVC_ATT(4, 4, KC_, VC_)
@@ -740,6 +844,7 @@ hipError_t launch_attend(const AttendLaunch& a, hipStream_t s) {
 #undef KVC_ATT
     return hipErrorInvalidValue;
   } else {
+    p.splits = 1;
     const int nqb = (int)((a.n_queries + 63) / 64);
     if (a.kc.D == 128)
       hipLaunchKernelGGL(attend_f32_kernel<128>, dim3(nqb * a.kc.H), dim3(64), 0, s, p);
@@ -764,13 +869,14 @@ hipError_t launch_attend_mixed(const AttendLaunch& a, hipStream_t s) {
   p.k = make_src(a.kc, a.ks, a.kb);
   p.v = make_src(a.vc, a.vs, a.vb);
   p.basis = reinterpret_cast<const uint16_t*>(a.kb.basis);
+  plan_splits(a, p);
   const int nqb = (int)((a.n_queries + BQ - 1) / BQ);
-  const dim3 grid(nqb * a.kc.H), block(NT);
+  const dim3 grid(nqb * a.kc.H * p.splits), block(NT);
   const bool vc = p.v.mode == SRC_CENTROID;
 #define KVC_MIX(KB_, VB_, VC_)                                                           \
   if (a.kc.bits == KB_ && a.vc.bits == VB_ && vc == VC_) {                              \
     hipLaunchKernelGGL((attend_bf16_kernel<KB_, VB_, true, VC_, true>), grid, block, 0, s, p); \
-    return hipGetLastError();                                                            \
+    return launch_combine(p, s);                                                         \
   }
   KVC_MIX(4, 2, true) KVC_MIX(4, 4, true) KVC_MIX(2, 2, true) KVC_MIX(2, 4, true)
 #undef KVC_MIX

@@ -72,6 +72,8 @@ struct AttendLaunch {
   float scale = 0.f;
   float* out = nullptr;
   float* lse = nullptr;
+  void* workspace = nullptr;      // optional: enables splitting the keys across workgroups
+  size_t workspace_bytes = 0;
 };
 
 // Launchers (return hipSuccess or the launch error).
@@ -89,6 +91,10 @@ bool launch_predict_fused(const EncodeLaunch& a, float* out, hipStream_t s, hipE
 
 // Whether the matrix-product predictor bases (DPLR, temporal values) are built.
 bool predict_available();
+
+// Workspace bytes that let attention split the keys across workgroups (0 when one
+// pass is used anyway).
+size_t attend_workspace_bytes(const CodecArgs& kc, int64_t n_keys, int64_t n_queries);
 
 // Workspace bytes of the predictor paths (0 otherwise).
 size_t encode_workspace_bytes(const CodecArgs& c, int64_t n_tokens);

@@ -253,9 +253,10 @@ def kvc_decode(codec: Codec, store: Store, token_offset: int, n_tokens: int,
     return out
 
 
-def workspace_for(op: int, codec: Codec, n_tokens: int, device) -> Optional[torch.Tensor]:
+def workspace_for(op: int, codec: Codec, n_tokens: int, device, n_queries: int = 0
+                  ) -> Optional[torch.Tensor]:
     """A device workspace of the size kvc_workspace_bytes reports (None when 0)."""
-    nbytes = kvc_workspace_bytes(op, codec, n_tokens)
+    nbytes = kvc_workspace_bytes(op, codec, n_tokens, n_queries)
     if nbytes == 0:
         return None
     return torch.empty(((nbytes + 15) // 16) * 16, dtype=torch.uint8, device=device)

@@ -75,6 +75,33 @@ def test_bf16_attention_small_ragged(n_keys):
         assert np.allclose(out.cpu().numpy(), np.broadcast_to(vh[:1], out.shape), atol=1e-6)
 
 
+@pytest.mark.parametrize("n_keys", [2000, 1100])
+def test_bf16_attention_key_splits(n_keys):
+    """With a workspace the keys are split across workgroups (here 4 or 2 splits, the
+    last one ragged) and merged by log-sum-exp.  The two paths round P to fp16
+    relative to different running maxima, so they agree to about fp16 resolution of
+    the output (2e-3 here), and each meets the oracle bar."""
+    dev = device()
+    d = synth.cfg1(seed=13, hist_frames=20, query_frames=3, tokens=100, heads=2, dim=128,
+                   n_centroids=64)
+    (kc, ks, kb), (vc, vs, vb) = _compress(d, 2, 128, 2, 32, 64, kvc.BF16, dev)
+    q = to_dev(d["Q"], dev)                                # 300 queries
+    ws = kvc.kvc.workspace_for(kvc.kvc.OP_ATTEND, kc, n_keys, dev, n_queries=q.shape[0])
+    assert ws is not None
+    one, lse1 = kvc.kvc_attend_compressed(kc, ks, kb, vc, vs, vb, n_keys, q, d["scale"],
+                                          want_lse=True)
+    split, lse2 = kvc.kvc_attend_compressed(kc, ks, kb, vc, vs, vb, n_keys, q, d["scale"],
+                                            want_lse=True, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.abs(split.cpu().numpy() - one.cpu().numpy()).max() <= 2e-3
+    assert np.abs(lse2.cpu().numpy() - lse1.cpu().numpy()).max() <= 1e-4
+    kh, vh = _oracle_cache(d, 2, 32, "bf16")
+    ref, rlse = oatt.attention(nm.bf16_to_f32(d["Q"]), kh[:n_keys], vh[:n_keys], d["scale"],
+                               return_lse=True)
+    assert np.abs(split.cpu().numpy() - ref).max() <= 2e-2
+    assert np.abs(lse2.cpu().numpy() - rlse).max() <= 2e-2
+
+
 def test_bf16_zero_queries_average_values():
     dev = device()
     d = synth.cfg1(seed=12, hist_frames=2, query_frames=1, tokens=96, heads=2, dim=128,
@@ -102,7 +129,10 @@ def test_cfg1_full_size_attention_sampled():
     d, kh, vh = _cfg1_full()
     (kc, ks, kb), (vc, vs, vb) = _compress(d, 12, 128, 2, 32, 256, kvc.BF16, dev)
     q = to_dev(d["Q"], dev)
-    out = kvc.kvc_attend_compressed(kc, ks, kb, vc, vs, vb, d["K"].shape[0], q, d["scale"])
+    ws = kvc.kvc.workspace_for(kvc.kvc.OP_ATTEND, kc, d["K"].shape[0], dev, n_queries=q.shape[0])
+    assert ws is not None   # the benchmark's configuration splits the keys
+    out = kvc.kvc_attend_compressed(kc, ks, kb, vc, vs, vb, d["K"].shape[0], q, d["scale"],
+                                    workspace=ws)
     torch.cuda.synchronize()
     o = out.cpu().numpy()
     assert np.all(np.isfinite(o))

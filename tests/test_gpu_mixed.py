@@ -114,7 +114,9 @@ def test_cfg4_full_size_sampled():
     kc, ks, kb = _encode_keys(d, dev)
     vc, vs, vb = _encode_values(d, dev)
     q = to_dev(d["Q"], dev)
-    out = kvc.kvc_attend_mixed_dim(kc, ks, kb, vc, vs, vb, d["K"].shape[0], q, d["scale"])
+    ws = kvc.kvc.workspace_for(kvc.kvc.OP_ATTEND_MIXED, kc, d["K"].shape[0], dev, n_queries=q.shape[0])
+    out = kvc.kvc_attend_mixed_dim(kc, ks, kb, vc, vs, vb, d["K"].shape[0], q, d["scale"],
+                                   workspace=ws)
     torch.cuda.synchronize()
     got = store_np(ks)
     rng = np.random.default_rng(3)
