@@ -95,6 +95,24 @@ def cpu_baseline(d: dict, sample_heads=(0, 1), enc_frames: int = 1, q_sample: in
     }
 
 
+def recorded_traffic(profile: str, source: str):
+    """HBM bytes per launch of a kernel, as measured by the FETCH_SIZE and WRITE_SIZE
+    passes summarized in `profile` (scaled by the reference copy's readings), or None.
+    The summary records the sha256 of the kernel source it measured; once that source
+    has changed the numbers no longer describe the kernel and None is returned."""
+    import hashlib
+    import re
+    try:
+        text = open(os.path.join(ROOT, "profiles", profile)).read()
+        sha = hashlib.sha256(open(os.path.join(ROOT, source), "rb").read()).hexdigest()
+    except OSError:
+        return None
+    m = re.search(r"traffic_per_launch: read_bytes=(\d+) write_bytes=(\d+) source_sha256=([0-9a-f]+)", text)
+    if not m or m.group(3) != sha:
+        return None
+    return int(m.group(1)) + int(m.group(2))
+
+
 def copy_reference(torch, dev):
     """One plain 256 MiB device-to-device copy (its HBM counters calibrate the others)."""
     src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -409,7 +427,9 @@ def main() -> int:
                    "heads": H, "head_dim": D, "history_tokens": nk, "queries": nq,
                    "chunk_tokens": hi - lo, "bits": bits, "group": group, "centroids": C},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
+                     "traffic": recorded_traffic("attend_bf16_kernel_centroid_int2_12x128_4680q_32760k.md",
+                                                 "kv_cache_compression_02_amd/csrc/attend.hip"),
                      "kernel": "attend_bf16_kernel", "ms": t_att * 1e3},
         "encode": {"ms": t_enc * 1e3, "bytes": enc_b, "GB/s": enc_b / t_enc / 1e9,
                    "frac_hbm": enc_b / t_enc / 1e9 / HBM_PEAK_GBS},
