@@ -148,6 +148,28 @@ __device__ __forceinline__ int out_channel(int ob, int i) { return 32 * (i >> 2)
 
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 
+// LDS geometry: permuted weight rows, U with permuted columns (always 64 + 8 wide,
+// zero past r), then one 16-token staging tile per wave.
+constexpr int URW = 64 + 8;
+constexpr int STG = 16 * D;                  // staging tile (bf16 elements)
+__host__ __device__ constexpr int w_elems(int nin) { return 128 * (nin * D + 8); }
+
+// 16-byte loads that give zeros when `ok` is false (a branch, not a select of addresses)
+__device__ __forceinline__ uint4 ld_u4(const void* p, bool ok) {
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (ok) v = *reinterpret_cast<const uint4*>(p);
+  return v;
+}
+__device__ __forceinline__ float4 ld_f4(const float* p, bool ok) {
+  float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (ok) v = *reinterpret_cast<const float4*>(p);
+  return v;
+}
+
+// Staging tile slot (16-byte units) of chunk c (8 channels) of token tok: chunk index
+// XOR token spreads both access patterns below over all 16 bank groups.
+__device__ __forceinline__ int stg_slot(int tok, int c) { return tok * 16 + (c ^ tok); }
+
 template <int BITS, int G, int PM, int NIN>
 __global__ __launch_bounds__(512) void pred_kernel(PredParams p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -160,12 +182,17 @@ __global__ __launch_bounds__(512) void pred_kernel(PredParams p) {
   constexpr int NGL = 32 / GL;               // groups (or group halves) in a lane
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = lane & 15, q = lane >> 4;
-  const int h = blockIdx.x / p.segs, seg = blockIdx.x % p.segs;
-  const int urow = p.r + 8;
-  uint16_t* wl = lds;                        // [128][WROW], permuted rows
-  uint16_t* ul = lds + 128 * WROW;           // [128][r + 8], permuted rows
+  // coalesced role of the lane: token 4 i + ct of a 16-token tile in instruction i,
+  // channel chunk cc (16 lanes cover one token's 256-byte row)
+  const int ct = lane >> 4, cc = lane & 15;
+  // matrix modes: workgroup = (head, segment) with the head's weights in LDS, its waves
+  // walking that head's tiles; other modes walk the flattened (head, tile) list
+  const int hw = MAT ? blockIdx.x / p.segs : 0, seg = blockIdx.x % p.segs;
+  uint16_t* wl = lds;                                   // [128][WROW], permuted rows
+  uint16_t* ul = lds + (MAT ? w_elems(NIN) : 0);        // [128][URW]
+  uint16_t* stg = lds + (MAT ? w_elems(NIN) : 0) + (LR ? 128 * URW : 0) + wave * STG;
   if constexpr (MAT) {
-    const uint16_t* wh = p.w + (int64_t)h * D * (NIN * D);
+    const uint16_t* wh = p.w + (int64_t)hw * D * (NIN * D);
     for (int e = tid; e < 128 * NIN * 16; e += 512) {
       const int i2 = e / (NIN * 16), c = e % (NIN * 16);
       const int ch = out_channel(i2 >> 4, i2 & 15);
@@ -173,42 +200,106 @@ __global__ __launch_bounds__(512) void pred_kernel(PredParams p) {
           *reinterpret_cast<const uint4*>(wh + (int64_t)ch * (NIN * D) + 8 * c);
     }
     if constexpr (LR) {
-      const int rc = p.r / 8;
-      for (int e = tid; e < 128 * rc; e += 512) {
-        const int i2 = e / rc, c = e % rc;
+      // U row ch in permuted row order; its 4-column piece m of 32-block kb goes to
+      // position 32 kb + 8 (m & 3) + 4 (m >> 2), matching how a lane reads t below
+      for (int e = tid; e < 128 * 16; e += 512) {
+        const int i2 = e >> 4, piece = e & 15, kb = piece >> 3, m = piece & 7;
         const int ch = out_channel(i2 >> 4, i2 & 15);
-        *reinterpret_cast<uint4*>(&ul[i2 * urow + 8 * c]) =
-            *reinterpret_cast<const uint4*>(p.u + ((int64_t)h * D + ch) * p.r + 8 * c);
+        const int col = 32 * kb + 4 * m;
+        uint2 v = make_uint2(0u, 0u);
+        if (col < p.r) v = *reinterpret_cast<const uint2*>(p.u + ((int64_t)hw * D + ch) * p.r + col);
+        *reinterpret_cast<uint2*>(&ul[i2 * URW + 32 * kb + 8 * (m & 3) + 4 * (m >> 2)]) = v;
       }
     }
     __syncthreads();
   }
   const int tiles = (p.n + 15) / 16;
-  const bf16x8_t zero = {0, 0, 0, 0, 0, 0, 0, 0};
-  const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+  constexpr int NG = MAT ? NIN : 0;                                 // matrix inputs
+  constexpr int NE = PM == PM_TEMPORAL_K ? 2 : (PM == PM_TEMPORAL_V ? 1 : 0);   // element-wise
+  constexpr int NT = LR ? 2 : 0;                                    // t k-steps (r <= 64)
+  // everything a tile reads, so the next tile's reads are in flight while this one computes
+  struct TileIn {
+    uint4 xv[4];                       // row to encode, coalesced layout
+    bf16x8_t gin[NG > 0 ? NG : 1][4];  // matrix-product inputs, k-step ks = chunk 4 ks + q
+    uint4 ev[NE > 0 ? NE : 1][4];      // element-wise inputs, coalesced layout
+    float4 tv[NT > 0 ? NT : 1][2];     // t[32 ks + 4 q ..], t[32 ks + 16 + 4 q ..]
+  };
+  const int items = MAT ? tiles : tiles * p.H;
+  const int istride = MAT ? p.segs * 8 : gridDim.x * 8;
+  auto load_tile = [&](int item, TileIn& in) __attribute__((always_inline)) {
+    const bool ok = item < items;
+    const int h = MAT ? hw : (ok ? item / tiles : 0), tile = MAT ? item : (ok ? item % tiles : 0);
+    const int n = tile * 16 + t;
+    const bool live = ok && n < p.n;
+    // coalesced: instruction i reads tokens 4 i .. 4 i + 3 whole
+    if (p.x) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int nc = tile * 16 + 4 * i + ct;
+        in.xv[i] = ld_u4(p.x + (int64_t)nc * p.x_stride + (int64_t)h * D + 8 * cc, ok && nc < p.n);
+      }
+    }
+    const uint16_t* esrc[2] = {p.e0, p.e1};
+#pragma unroll
+    for (int j = 0; j < NE; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int nc = tile * 16 + 4 * i + ct;
+        in.ev[j][i] = ld_u4(esrc[j] + (int64_t)nc * p.ps + (int64_t)h * D + 8 * cc, ok && nc < p.n);
+      }
+    const int64_t grow = (int64_t)(live ? n : 0) * p.ps + (int64_t)h * D;
+    const uint16_t* gsrc[2] = {p.g0, p.g1};
+#pragma unroll
+    for (int j = 0; j < NG; ++j)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        in.gin[j][ks] = __builtin_bit_cast(bf16x8_t, ld_u4(gsrc[j] + grow + 32 * ks + 8 * q, live));
+#pragma unroll
+    for (int ks = 0; ks < NT; ++ks) {
+      const float* tp = p.t + (int64_t)(live ? n : 0) * p.r + 32 * ks + 4 * q;
+      in.tv[ks][0] = ld_f4(tp, live && 32 * ks + 4 * q < p.r);
+      in.tv[ks][1] = ld_f4(tp + 16, live && 32 * ks + 16 + 4 * q < p.r);
+    }
+  };
+  // coalesced rows -> this lane's quarter row (channels 32 q .. 32 q + 31), through the
+  // wave's staging tile (a wave's LDS operations complete in order)
+  auto to_quarter = [&](const uint4 (&v)[4], uint4 (&o)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint4*>(&stg[8 * stg_slot(4 * i + ct, cc)]) = v[i];
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = *reinterpret_cast<const uint4*>(&stg[8 * stg_slot(t, 4 * q + i)]);
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  TileIn cur;
+  const int first = (MAT ? seg : (int)blockIdx.x) * 8 + wave;
+  load_tile(first, cur);
 #pragma unroll 1
-  for (int tile = seg * 8 + wave; tile < tiles; tile += p.segs * 8) {
+  for (int item = first; item < items; item += istride) {
+    TileIn nxt;
+    load_tile(item + istride, nxt);   // past the last item: no reads (zeros)
+    const int h = MAT ? hw : item / tiles, tile = MAT ? item : item % tiles;
     const int n = tile * 16 + t;
     const bool live = n < p.n;
-    const int64_t qrow = (int64_t)(live ? n : 0) * p.ps + (int64_t)h * D + 32 * q;
-    // the quarter row to encode, in flight while the prediction is formed
     uint4 xv[4];
-    if (p.x) {
-      const uint16_t* xs = p.x + (int64_t)(live ? n : 0) * p.x_stride + (int64_t)h * D + 32 * q;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xv[i] = live ? *reinterpret_cast<const uint4*>(xs + 8 * i) : z4;
-    }
+    if (p.x) to_quarter(cur.xv, xv);
     float pred[32];
     if constexpr (PM == PM_NONE) {
 #pragma unroll
       for (int i = 0; i < 32; ++i) pred[i] = 0.0f;
     } else if constexpr (PM == PM_TEMPORAL_K) {
+      uint4 e0[4], e1[4];
+      to_quarter(cur.ev[0], e0);
+      to_quarter(cur.ev[NE - 1], e1);
       const float* ca = p.ca + h * D + 32 * q;
       const float* cb = p.cb + h * D + 32 * q;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint4 v0 = live ? *reinterpret_cast<const uint4*>(p.e0 + qrow + 8 * i) : z4;
-        const uint4 v1 = live ? *reinterpret_cast<const uint4*>(p.e1 + qrow + 8 * i) : z4;
+        const uint4 v0 = e0[i];
+        const uint4 v1 = e1[i];
         const float4 ca0 = *reinterpret_cast<const float4*>(ca + 8 * i);
         const float4 ca1 = *reinterpret_cast<const float4*>(ca + 8 * i + 4);
         const float4 cb0 = *reinterpret_cast<const float4*>(cb + 8 * i);
@@ -225,48 +316,32 @@ __global__ __launch_bounds__(512) void pred_kernel(PredParams p) {
         }
       }
     } else {
-      // matrix products, one input at a time: B operand = this lane's quarter rows
-      const uint16_t* gsrc[2] = {p.g0, p.g1};
+      // matrix products, one input at a time; k-step ks: lane q feeds channels
+      // 32 ks + 8 q .. + 7 (its part of a contiguous 64-byte read per token)
       f32x4_t acc[8];
 #pragma unroll
       for (int ob = 0; ob < 8; ++ob) acc[ob] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int j = 0; j < NIN; ++j) {
-        bf16x8_t gin[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          gin[ks] = live ? *reinterpret_cast<const bf16x8_t*>(gsrc[j] + qrow + 8 * ks) : zero;
+      for (int j = 0; j < NG; ++j) {
 #pragma unroll
         for (int ob = 0; ob < 8; ++ob) {
-          const uint16_t* arow = wl + (16 * ob + t) * WROW + j * D + 32 * q;
+          const uint16_t* arow = wl + (16 * ob + t) * WROW + j * D + 8 * q;
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(arow + 8 * ks);
-            acc[ob] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, gin[ks], acc[ob], 0, 0, 0);
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(arow + 32 * ks);
+            acc[ob] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, cur.gin[j][ks], acc[ob], 0, 0, 0);
           }
           // keep one block's weight fragments live at a time
           __builtin_amdgcn_sched_barrier(0);
         }
       }
       if constexpr (LR) {
-        // rank part: t as bf16 high + low parts, its own accumulator, added at the end;
-        // k-step ks covers t[32 ks .. 32 ks + 31], lane q feeding t[32 ks + 8 q ..]
-        constexpr int RS = 2;                  // r <= 64
-        const int rsteps = (p.r + 31) / 32;
-        bf16x8_t thi[RS], tlo[RS];
+        // rank part: t as bf16 high + low parts, its own accumulator, added at the end
+        bf16x8_t thi[NT], tlo[NT];
 #pragma unroll
-        for (int ks = 0; ks < RS; ++ks) {
-          float tv[8];
-          const int c0 = 32 * ks + 8 * q;
-          if (live && c0 < p.r) {
-            const float4* tp = reinterpret_cast<const float4*>(p.t + (int64_t)n * p.r + c0);
-            const float4 a = tp[0], b = tp[1];
-            tv[0] = a.x; tv[1] = a.y; tv[2] = a.z; tv[3] = a.w;
-            tv[4] = b.x; tv[5] = b.y; tv[6] = b.z; tv[7] = b.w;
-          } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) tv[i] = 0.0f;
-          }
+        for (int ks = 0; ks < NT; ++ks) {
+          const float4 a = cur.tv[ks][0], b = cur.tv[ks][1];
+          const float tv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const uint32_t hb = f32_to_bf16_bits(tv[i]);
@@ -274,15 +349,14 @@ __global__ __launch_bounds__(512) void pred_kernel(PredParams p) {
             tlo[ks][i] = (short)f32_to_bf16_bits(tv[i] - bf16_bits_to_f32(hb));
           }
         }
+        const int rsteps = (p.r + 31) / 32;
 #pragma unroll
         for (int ob = 0; ob < 8; ++ob) {
           f32x4_t au = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int ks = 0; ks < RS; ++ks) {
+          for (int ks = 0; ks < NT; ++ks) {
             if (ks < rsteps) {
-              const int c0 = 32 * ks + 8 * q;
-              const bf16x8_t a = c0 < p.r
-                  ? *reinterpret_cast<const bf16x8_t*>(ul + (16 * ob + t) * urow + c0) : zero;
+              const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ul + (16 * ob + t) * URW + 32 * ks + 8 * q);
               au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, thi[ks], au, 0, 0, 0);
               au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, tlo[ks], au, 0, 0, 0);
             }
@@ -298,10 +372,12 @@ __global__ __launch_bounds__(512) void pred_kernel(PredParams p) {
           for (int s2 = 0; s2 < 4; ++s2) pred[4 * ob + s2] = acc[ob][s2];
       }
       if constexpr (PM == PM_TEMPORAL_V) {
+        uint4 e0[4];
+        to_quarter(cur.ev[0], e0);
         const float* ca = p.ca + h * D + 32 * q;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint4 v0 = live ? *reinterpret_cast<const uint4*>(p.e0 + qrow + 8 * i) : z4;
+          const uint4 v0 = e0[i];
           const float4 ca0 = *reinterpret_cast<const float4*>(ca + 8 * i);
           const float4 ca1 = *reinterpret_cast<const float4*>(ca + 8 * i + 4);
           const float av[8] = {ca0.x, ca0.y, ca0.z, ca0.w, ca1.x, ca1.y, ca1.z, ca1.w};
@@ -323,6 +399,7 @@ __global__ __launch_bounds__(512) void pred_kernel(PredParams p) {
     }
     if (p.x) {
       uint32_t words[LW], szw[NGL];
+      uint4 rq[4];   // reconstructed quarter row (bf16)
 #pragma unroll
       for (int gi = 0; gi < NGL; ++gi) {
         float r[GL];
@@ -353,7 +430,7 @@ __global__ __launch_bounds__(512) void pred_kernel(PredParams p) {
         szw[gi] = gq.word;
 #pragma unroll
         for (int w = 0; w < GL * BITS / 32; ++w) words[gi * (GL * BITS / 32) + w] = cw[w];
-        if (live && p.recon) {
+        if (p.recon) {
 #pragma unroll
           for (int i = 0; i < GL; i += 8) {
             uint32_t o[4];
@@ -364,9 +441,23 @@ __global__ __launch_bounds__(512) void pred_kernel(PredParams p) {
               const float v1 = pred[GL * gi + i0 + 1] + dequant_one(group_code<BITS, GL>(cw, i0 + 1), gq.s, gq.z);
               o[k] = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
             }
-            *reinterpret_cast<uint4*>(p.recon + orow + GL * gi + i) = make_uint4(o[0], o[1], o[2], o[3]);
+            rq[(GL * gi + i) / 8] = make_uint4(o[0], o[1], o[2], o[3]);
           }
         }
+      }
+      if (p.recon) {
+        // quarter rows -> whole rows through the staging tile, stored 1 KB at a time
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<uint4*>(&stg[8 * stg_slot(t, 4 * q + i)]) = rq[i];
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 v = *reinterpret_cast<const uint4*>(&stg[8 * stg_slot(4 * i + ct, cc)]);
+          const int nc = tile * 16 + 4 * i + ct;
+          if (nc < p.n) *reinterpret_cast<uint4*>(p.recon + ((int64_t)nc * p.H + h) * D + 8 * cc) = v;
+        }
+        __builtin_amdgcn_wave_barrier();
       }
       if (live) {
         const int64_t row = (int64_t)h * p.capacity + p.token_offset + n;
@@ -379,16 +470,41 @@ __global__ __launch_bounds__(512) void pred_kernel(PredParams p) {
         else if ((q & 1) == 0) sd[q >> 1] = szw[0];
       }
     }
+    cur = nxt;
   }
 }
 
+int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+// Persistent grid: as many workgroups as are resident at once (the kernel's register and
+// LDS use decide how many per CU), matrix modes split evenly over the heads.
 template <int BITS, int G, int PM, int NIN>
-hipError_t launch_pred_t(const PredParams& p, int grid, size_t lds, hipStream_t s) {
+hipError_t launch_pred_t(PredParams p, size_t lds, hipStream_t s) {
   auto k = pred_kernel<BITS, G, PM, NIN>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
+  }
+  int occ = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(k), 512, lds);
+  if (e != hipSuccess) return e;
+  const int64_t resident = (int64_t)std::max(1, occ) * cu_count();
+  const int64_t tiles = (p.n + 15) / 16;
+  int grid;
+  if (PM == PM_DPLR || PM == PM_TEMPORAL_V) {
+    const int64_t per_head = (tiles + 7) / 8;
+    p.segs = (int)std::max<int64_t>(1, std::min<int64_t>(per_head, resident / p.H));
+    grid = p.segs * p.H;
+  } else {
+    grid = (int)std::max<int64_t>(1, std::min<int64_t>((tiles * p.H + 7) / 8, resident));
+    p.segs = grid;
   }
   hipLaunchKernelGGL(k, dim3(grid), dim3(512), lds, s, p);
   return hipGetLastError();
@@ -427,9 +543,10 @@ int fused_mode(const EncodeLaunch& a) {
 }
 
 size_t lds_bytes(int mode, int nin, int r) {
-  if (mode != PM_DPLR && mode != PM_TEMPORAL_V) return 0;
-  size_t b = (size_t)128 * (nin * D + 8) * 2;
-  if (mode == PM_DPLR) b += (size_t)128 * (r + 8) * 2;
+  (void)r;
+  size_t b = (size_t)8 * STG * 2;   // staging tiles
+  if (mode == PM_DPLR || mode == PM_TEMPORAL_V) b += (size_t)w_elems(nin) * 2;
+  if (mode == PM_DPLR) b += (size_t)128 * URW * 2;
   return b;
 }
 
@@ -463,14 +580,7 @@ PredParams make_params(const EncodeLaunch& a, int mode, float* pred) {
   p.sz = a.st.sz;
   p.recon = reinterpret_cast<uint16_t*>(a.recon);
   p.pred = pred;
-  const int tiles = (int)((a.n_tokens + 15) / 16);
-  const int per_head = (tiles + 7) / 8;
-  const bool mat = mode == PM_DPLR || mode == PM_TEMPORAL_V;
-  // persistent workgroups for the matrix modes: as many as fit at once (the weights
-  // then load once per workgroup), two per CU when they leave LDS room for it
-  const size_t lds = lds_bytes(mode, mode == PM_DPLR ? a.c.n_inputs : 1, a.c.rank);
-  const int per_cu = lds <= 72 * 1024 ? 2 : 1;
-  p.segs = mat ? std::max(1, std::min(per_head, per_cu * 256 / std::max(1, a.c.H))) : per_head;
+  p.segs = 1;   // set at launch
   return p;
 }
 
@@ -478,12 +588,12 @@ PredParams make_params(const EncodeLaunch& a, int mode, float* pred) {
 // One dispatch for the encoder and the decoder's prediction, so the two always run the
 // same instantiation on the same calls.
 hipError_t dispatch(const EncodeLaunch& a, int mode, const PredParams& p, hipStream_t s) {
-  const int bits = a.c.bits, g = a.c.group, grid = p.segs * a.c.H;
+  const int bits = a.c.bits, g = a.c.group;
   // the temporal value map has one matrix input whatever n_inputs says
   const size_t lds = lds_bytes(mode, mode == PM_DPLR ? a.c.n_inputs : 1, a.c.rank);
 #define KVC_PRED(B, G_, M, N)                                                       \
   if (bits == B && g == G_ && mode == M && (M != PM_DPLR || a.c.n_inputs == N))   \
-    return launch_pred_t<B, G_, M, N>(p, grid, lds, s);
+    return launch_pred_t<B, G_, M, N>(p, lds, s);
 #define KVC_PRED_ALL(B, G_)                                                        \
   KVC_PRED(B, G_, PM_NONE, 1) KVC_PRED(B, G_, PM_TEMPORAL_K, 1)                    \
   KVC_PRED(B, G_, PM_TEMPORAL_V, 1) KVC_PRED(B, G_, PM_DPLR, 1) KVC_PRED(B, G_, PM_DPLR, 2)
