@@ -348,7 +348,10 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
       if constexpr (BITS == 2) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const uint32_t b = (kpr.code[0] >> (2 * r)) & 0x03030303u;   // codes r, r+4, r+8, r+12
+          uint32_t b = (kpr.code[0] >> (2 * r)) & 0x03030303u;   // codes r, r+4, r+8, r+12
+          // keep b opaque so each code converts with one v_cvt_f32_ubyteN (rather than
+          // a bit-field extract per code followed by a conversion)
+          asm volatile("" : "+v"(b));
 #pragma unroll
           for (int k = 0; k < 4; ++k) q[r + 4 * k] = byte_f(b, k);
         }
@@ -408,6 +411,7 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const int row = 8 * c8 + c;
+        // the decoded value is the codec's bf16 reconstruction; fp16 holds it exactly
         const uint32_t w = bf16x2_to_f16x2(pk_bf16(x[0][c], x[1][c]));   // keys 2kp, 2kp+1
         *reinterpret_cast<uint32_t*>(&v_lds[buf][row * VROW + vpos(row, 2 * kp)]) = w;
       }
@@ -564,7 +568,6 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
       m_run = m_new;
     }
     const float negm = -m_run;
-    float lsum = 0.0f;
     f16x8_t pb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -572,13 +575,23 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
       for (int hf = 0; hf < 2; ++hf) {
         f16x8_t t8;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * hf + j], c2, negm));
-          lsum += e;
-          t8[j] = (_Float16)e;
-        }
+        for (int j = 0; j < 8; ++j)
+          t8[j] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * hf + j], c2, negm));
         pb[kb][hf] = t8;
       }
+    // row sums of the fp16 P that the MFMAs use (two products per v_dot2_f32_f16,
+    // fp32 accumulation), so numerator and denominator see the same weights
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kh = 0; kh < 4; ++kh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const h2 pr = {pb[kh >> 1][kh & 1][2 * i], pb[kh >> 1][kh & 1][2 * i + 1]};
+        ls[kh] = __builtin_amdgcn_fdot2(pr, one2, ls[kh], false);
+      }
+    float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
     lsum += other_half(lsum, half);
     l_run = l_run + lsum;
     // O^T += V^T P^T
