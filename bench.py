@@ -307,8 +307,22 @@ def bench_mixed(args, torch, kvc, synth, dev):
     ks, vs = kvc.Store.allocate(kc, nk, dev), kvc.Store.allocate(vc, nk, dev)
     kb = kvc.BaseParams(centroids=b16(d["Ck"]), basis=b16(d["B"]))
     vb = kvc.BaseParams(centroids=b16(d["Cv"]))
-    kvc.kvc_encode(kc, b16(d["K"]), ks, 0, kb)
-    kvc.kvc_encode(vc, b16(d["V"]), vs, 0, vb)
+    Kx, Vx = b16(d["K"]), b16(d["V"])
+    kvc.kvc_encode(kc, Kx, ks, 0, kb)
+    kvc.kvc_encode(vc, Vx, vs, 0, vb)
+    # the encode of the whole 65520-token history (K: nearest of 512 centroids + INT4
+    # coefficients of the residual on the basis; V: nearest centroid + INT2 g32), timed
+    # with events apart from the attention steps
+    log("timing the history encode")
+    reps = max(1, min(args.steps, 5))
+    _, ev_k = _timed(torch, lambda _: kvc.kvc_encode(kc, Kx, ks, 0, kb), reps, 1)
+    _, ev_v = _timed(torch, lambda _: kvc.kvc_encode(vc, Vx, vs, 0, vb), reps, 1)
+    t_k = sum(a.elapsed_time(b) for a, b in ev_k) / reps * 1e-3
+    t_v = sum(a.elapsed_time(b) for a, b in ev_v) / reps * 1e-3
+    x_b = nk * H * D * 2
+    cen_b = H * C * D * 2
+    enc_k = x_b + cen_b + D * m * 2 + nk * H * (m * d["k_bits"] // 8 + 4 + 2)
+    enc_v = x_b + cen_b + nk * H * (D * d["v_bits"] // 8 + 4 * D // d["v_group"] + 2)
     Q = b16(d["Q"])
     out = torch.empty((nq, H, D), dtype=torch.float32, device=dev)
     ws = kvc.kvc.workspace_for(kvc.kvc.OP_ATTEND_MIXED, kc, nk, dev, n_queries=nq)
@@ -329,7 +343,10 @@ def bench_mixed(args, torch, kvc, synth, dev):
                  {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                   "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
                   "kernel": "attend_bf16_kernel (mixed)", "ms": t_ev * 1e3},
-                 full_attention_equivalent_tflops=attention_flops(nq, nk, D, H) / t_ev / 1e12)
+                 full_attention_equivalent_tflops=attention_flops(nq, nk, D, H) / t_ev / 1e12,
+                 encode={"keys_ms": t_k * 1e3, "values_ms": t_v * 1e3, "bytes": enc_k + enc_v,
+                         "GB/s": (enc_k + enc_v) / (t_k + t_v) / 1e9,
+                         "frac_hbm": (enc_k + enc_v) / (t_k + t_v) / 1e9 / HBM_PEAK_GBS})
 
 
 def main() -> int:

@@ -470,17 +470,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void encode_shortlist_kernel(EncodePar
 }
 
 // ---------------------------------------------------------------------------
-// Centroid codec for bf16 d = 128 data with at most 256 centroids per head.
+// Centroid and coefficient codecs for bf16 d = 128 data with at most CM (256 or 512)
+// centroids per head.
 //
-// One wave encodes 32 tokens of one head; lane (t, hf) owns channels 64 hf ..
-// 64 hf + 63 of token t in registers for the whole kernel.  The head's centroid
-// table sits in LDS, once per workgroup of four waves (128 tokens).
+// One wave encodes 32 tokens of one head at a time; lane (t, hf) owns channels 64 hf ..
+// 64 hf + 63 of token t in registers.  The head's centroid table sits in LDS, loaded
+// once per workgroup of NW waves (four, or eight when one workgroup fills the CU's LDS),
+// which then walks the head's tiles of 32 NW tokens.
 //
 // Assignment.  v_j = x.c_j - |c_j|^2 / 2 comes out of v_mfma_f32_32x32x16_bf16
 // (accumulator seeded with -|c_j|^2 / 2; the contraction index is permuted so that
 // every lane feeds its own half row), one lane per (token, half) holding 128 of the
-// 256 values.  A lane keeps the top three of its values with the centroid's
-// position packed into the low 8 mantissa bits, and merges them with its partner
+// CM values.  A lane keeps the top three of its values with the centroid's
+// position packed into the low 8 (CM = 256) or 9 (CM = 512) mantissa bits, and merges
+// them with its partner
 // half.  With E >= |v_j - V_j| (the MFMA error, counted at two units in the last
 // place per addition), g = (d + 3) 2^-24 the relative error of the exact fp32
 // distance, and V the true values, d_j > d_w for the exact fp32 distances whenever
@@ -491,13 +494,26 @@ __global__ __launch_bounds__(NTHREADS, 1) void encode_shortlist_kernel(EncodePar
 // exact fp32 order; otherwise every centroid the test cannot exclude is rescored.
 // Ties in the exact distance go to the lower index.
 //
+// Coefficients (COEFF).  c_j = sum_i B_ij r_i over the full residual row in ascending
+// i, multiply and add rounded separately; lane hf forms c_8hf .. c_8hf+7, and the m = 16
+// coefficients are one quantization group spanning the two lanes.
+//
 // Quantization.  code = clamp(rint(fl(fl(r - z) / s))) is evaluated as
 // rint(r * rcp(s) - z * rcp(s)); the two agree unless the product lies within
 // (|z / s| + L + 2) 2^-19 of a half-integer, and a group with such an element is
 // redone with the IEEE division.
-template <int BITS, int G>
-__global__ __launch_bounds__(256, 2) void encode_centroid_kernel(EncodeParams p) {
-  constexpr int D = 128, ROW = D + 8, CM = 256;
+// waves per workgroup of the centroid codec: eight when the LDS allows one workgroup
+// per CU (two waves per SIMD either way)
+__host__ __device__ constexpr int cen_waves(int cm, bool coeff) { return (cm == 512 || coeff) ? 8 : 4; }
+
+template <int BITS, int G, int CM, bool COEFF>
+__global__ __launch_bounds__(64 * cen_waves(CM, COEFF), 2 * 4 / cen_waves(CM, COEFF)) void encode_centroid_kernel(EncodeParams p) {
+  constexpr int D = 128, ROW = D + 8;
+  constexpr int NW = cen_waves(CM, COEFF), NT = 64 * NW, TT = 32 * NW;   // waves, threads, tokens
+  constexpr int NBM = CM / 32;                 // centroid blocks at most
+  constexpr int LOCB = CM == 256 ? 7 : 8;      // bits of a value's position in a half
+  constexpr uint32_t TAGM = (2u << LOCB) - 1u; // position + half bit
+  constexpr float TSLACK = CM == 256 ? 0x1p-15f : 0x1p-14f;   // relative change by the tag
   constexpr int L = (1 << BITS) - 1;
   constexpr int NG = 64 / G;          // groups in a half row
   constexpr int PER = 32 / BITS;      // codes per word
@@ -506,23 +522,81 @@ __global__ __launch_bounds__(256, 2) void encode_centroid_kernel(EncodeParams p)
   __shared__ __attribute__((aligned(16))) uint16_t tab[CM * ROW];
   __shared__ __attribute__((aligned(16))) float hn[CM];
   __shared__ float cnu[CM];   // |c_j| (upper bound), 0 beyond C
-  __shared__ float wmax[4];
-  __shared__ uint32_t tq[4][64];   // rescoring tasks of each wave: lane << 8 | centroid
-  __shared__ float tqd[4][64];
-  __shared__ uint32_t tqn[4];
+  __shared__ float wmax[NW];
+  __shared__ uint32_t tq[NW][64];   // rescoring tasks of each wave: lane << 10 | centroid
+  __shared__ float tqd[NW][64];
+  __shared__ uint32_t tqn[NW];
+  __shared__ __attribute__((aligned(16))) float bt[COEFF ? D * 16 : 4];   // basis [i][j], fp32
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = lane & 31, hf = lane >> 5;
-  const int nblk = (int)((p.n_tokens + 127) / 128);
+  const int ntile = (int)((p.n_tokens + TT - 1) / TT);
+  const int wph = (int)gridDim.x / p.H;   // workgroups per head
   const int b = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = b / nblk;
-  const int64_t n = (int64_t)(b % nblk) * 128 + wave * 32 + t;
-  const bool live = n < p.n_tokens;
+  const int h = b / wph, first = b % wph;
   const int C = p.C;
   const int nb = (C + 31) >> 5;
   const uint16_t* cen = reinterpret_cast<const uint16_t*>(p.centroids) + (int64_t)h * C * D;
 
-  // 1. this lane's half row, and the head's centroid table (rows C .. 32 nb - 1 zero)
+  // 1. the head's centroid table (rows C .. 32 nb - 1 zero), row norms, the basis
+#pragma unroll
+  for (int half16 = 0; half16 < (CM + NT - 1) / NT; ++half16) {   // rounds of 16 pieces a thread
+    // sixteen 16-byte pieces of this thread in flight at once
+    uint4 v[16];
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int j = (NT / 16) * (16 * half16 + it) + (tid >> 4), c = tid & 15;
+      v[it] = make_uint4(0u, 0u, 0u, 0u);
+      if (j < C) v[it] = *reinterpret_cast<const uint4*>(cen + (int64_t)j * D + 8 * c);
+    }
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int j = (NT / 16) * (16 * half16 + it) + (tid >> 4), c = tid & 15;
+      if (j < 32 * nb) *reinterpret_cast<uint4*>(&tab[j * ROW + 8 * c]) = v[it];
+    }
+  }
+  if constexpr (COEFF) {
+    for (int e = tid; e < D * 16; e += NT) bt[e] = bf16_bits_to_f32(p.basis[e]);
+  }
+  __syncthreads();
+  {
+    float cnw = 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < (CM + NT - 1) / NT; ++jj) {
+      const int j = tid + NT * jj;
+      if (j >= CM) break;
+      float s2 = 0.0f;
+      if (j < C) {
+#pragma unroll
+        for (int i = 0; i < D; i += 8) {
+          const uint4 v = *reinterpret_cast<const uint4*>(&tab[j * ROW + i]);
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            s2 = __builtin_fmaf(lo_bf16(w[k]), lo_bf16(w[k]), s2);
+            s2 = __builtin_fmaf(hi_bf16(w[k]), hi_bf16(w[k]), s2);
+          }
+        }
+      }
+      hn[j] = j < C ? -0.5f * s2 : -1e30f;
+      const float cn = sqrtf(s2) * (1.0f + 0x1p-10f);
+      cnu[j] = cn;
+      cnw = fmaxf(cnw, cn);
+    }
+#pragma unroll
+    for (int o = 32; o; o >>= 1) cnw = fmaxf(cnw, __shfl_xor(cnw, o));
+    if (lane == 0) wmax[wave] = cnw;
+  }
+  __syncthreads();
+  float cmax = wmax[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) cmax = fmaxf(cmax, wmax[w]);
+
+#pragma unroll 1
+  for (int tile = first; tile < ntile; tile += wph) {
+  const int64_t n = (int64_t)tile * TT + wave * 32 + t;
+  const bool live = n < p.n_tokens;
+  // this lane's half row
   uint4 xv[8];
   {
     const uint16_t* src = reinterpret_cast<const uint16_t*>(p.x) + (live ? n : 0) * p.x_stride +
@@ -531,46 +605,6 @@ __global__ __launch_bounds__(256, 2) void encode_centroid_kernel(EncodeParams p)
     for (int i = 0; i < 8; ++i)
       xv[i] = live ? *reinterpret_cast<const uint4*>(src + 8 * i) : make_uint4(0u, 0u, 0u, 0u);
   }
-  {
-    // all sixteen 16-byte pieces of this thread in flight at once
-    uint4 v[16];
-#pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const int j = 16 * it + (tid >> 4), c = tid & 15;
-      v[it] = make_uint4(0u, 0u, 0u, 0u);
-      if (j < C) v[it] = *reinterpret_cast<const uint4*>(cen + (int64_t)j * D + 8 * c);
-    }
-#pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const int j = 16 * it + (tid >> 4), c = tid & 15;
-      if (j < 32 * nb) *reinterpret_cast<uint4*>(&tab[j * ROW + 8 * c]) = v[it];
-    }
-  }
-  __syncthreads();
-  {
-    const int j = tid;
-    float s2 = 0.0f;
-    if (j < C) {
-#pragma unroll
-      for (int i = 0; i < D; i += 8) {
-        const uint4 v = *reinterpret_cast<const uint4*>(&tab[j * ROW + i]);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          s2 = __builtin_fmaf(lo_bf16(w[k]), lo_bf16(w[k]), s2);
-          s2 = __builtin_fmaf(hi_bf16(w[k]), hi_bf16(w[k]), s2);
-        }
-      }
-    }
-    hn[j] = j < C ? -0.5f * s2 : -1e30f;
-    float cn = sqrtf(s2) * (1.0f + 0x1p-10f);
-    cnu[j] = cn;
-#pragma unroll
-    for (int o = 32; o; o >>= 1) cn = fmaxf(cn, __shfl_xor(cn, o));
-    if (lane == 0) wmax[wave] = cn;
-  }
-  __syncthreads();
-  const float cmax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
 
   // 2. v_j for the 128 centroids of this half; top three with packed positions
   float m1 = -3.0e38f, m2 = -3.0e38f, m3 = -3.0e38f;
@@ -595,16 +629,16 @@ __global__ __launch_bounds__(256, 2) void encode_centroid_kernel(EncodeParams p)
     block_values(cb, acc);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float pv = __uint_as_float((__float_as_uint(acc[r]) & 0xFFFFFF00u) | (uint32_t)(16 * cb + r));
+      const float pv = __uint_as_float((__float_as_uint(acc[r]) & ~TAGM) | (uint32_t)(16 * cb + r));
       m3 = __builtin_amdgcn_fmed3f(m2, m3, pv);
       m2 = __builtin_amdgcn_fmed3f(m1, m2, pv);
       m1 = fmaxf(m1, pv);
     }
   }
-  // tag the half in bit 7, merge the two halves' top three
-  m1 = __uint_as_float(__float_as_uint(m1) | ((uint32_t)hf << 7));
-  m2 = __uint_as_float(__float_as_uint(m2) | ((uint32_t)hf << 7));
-  m3 = __uint_as_float(__float_as_uint(m3) | ((uint32_t)hf << 7));
+  // tag the half above the position bits, merge the two halves' top three
+  m1 = __uint_as_float(__float_as_uint(m1) | ((uint32_t)hf << LOCB));
+  m2 = __uint_as_float(__float_as_uint(m2) | ((uint32_t)hf << LOCB));
+  m3 = __uint_as_float(__float_as_uint(m3) | ((uint32_t)hf << LOCB));
   auto swf = [&](float v) { return __uint_as_float(swap_halves(__float_as_uint(v), hf)); };
   const float b1 = swf(m1), b2 = swf(m2), b3 = swf(m3);
   const float t1 = fmaxf(m1, b1);
@@ -633,13 +667,13 @@ __global__ __launch_bounds__(256, 2) void encode_centroid_kernel(EncodeParams p)
   // a (packed best) beats every centroid whose value is at most c, given the sum of
   // the two values' error bounds
   auto separated = [&](float a, float c, float esum) {
-    const float va = a - 0x1p-15f * fabsf(a), vc = c + 0x1p-15f * fabsf(c);
+    const float va = a - TSLACK * fabsf(a), vc = c + TSLACK * fabsf(c);
     const float rhs = esum + go * (xxu - va - vc) + 0x1p-20f * (fabsf(va) + fabsf(vc) + xxu);
     return va - vc > rhs;
   };
   auto cidx = [](float v) {
-    const uint32_t tg = __float_as_uint(v) & 0xFFu;
-    const int hw = (int)(tg >> 7), loc = (int)(tg & 0x7Fu), cb = loc >> 4, r = loc & 15;
+    const uint32_t tg = __float_as_uint(v) & TAGM;
+    const int hw = (int)(tg >> LOCB), loc = (int)(tg & (TAGM >> 1)), cb = loc >> 4, r = loc & 15;
     return 32 * cb + 8 * (r >> 2) + 4 * hw + (r & 3);
   };
   int best = cidx(t1);
@@ -659,13 +693,15 @@ __global__ __launch_bounds__(256, 2) void encode_centroid_kernel(EncodeParams p)
     uint32_t* q = &tq[wave][0];
     float* qd = &tqd[wave][0];
     int single = pair ? cidx(hf ? t2 : t1) : -1;   // one candidate per lane of a pair token
-    uint32_t mask[4] = {0u, 0u, 0u, 0u};            // bit 16 cb + r: candidate value of this lane
+    uint32_t mask[NBM / 2];                         // bit 16 cb + r: candidate value of this lane
+#pragma unroll
+    for (int w = 0; w < NBM / 2; ++w) mask[w] = 0u;
     const bool full = !uniq && !pair;
     if (__any(full)) {
       // every value below tau is separated from the best one (the right-hand side of
       // the test grows far slower than the gap), so the values >= tau are a superset of
       // the centroids that can still be nearest; all of them are rescored
-      const float va = t1 - 0x1p-15f * fabsf(t1);
+      const float va = t1 - TSLACK * fabsf(t1);
       const float tau = va - 2.0f * (2.0f * E + go * (xxu + 2.0f * fabsf(va)) +
                                      0x1p-20f * (2.0f * fabsf(va) + xxu) + 0x1p-14f * fabsf(va));
       for (int cb = 0; cb < nb; ++cb) {
@@ -681,34 +717,40 @@ __global__ __launch_bounds__(256, 2) void encode_centroid_kernel(EncodeParams p)
     const int64_t nw0 = n - t;   // first token of this wave
     float bd = __builtin_inff();
     int bj = 0x7FFFFFFF;
-    bool pending = single >= 0 || (mask[0] | mask[1] | mask[2] | mask[3]) != 0u;
+    auto any_mask = [&]() {
+      uint32_t o = 0u;
+#pragma unroll
+      for (int w = 0; w < NBM / 2; ++w) o |= mask[w];
+      return o != 0u;
+    };
+    bool pending = single >= 0 || any_mask();
     while (__any(pending)) {
       if (lane == 0) tqn[wave] = 0;
       __builtin_amdgcn_wave_barrier();
       if (pending) {
         if (single >= 0) {
           const uint32_t slot = atomicAdd(&tqn[wave], 1u);
-          if (slot < 64u) { q[slot] = ((uint32_t)lane << 8) | (uint32_t)single; single = -1; }
+          if (slot < 64u) { q[slot] = ((uint32_t)lane << 10) | (uint32_t)single; single = -1; }
         }
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < NBM / 2; ++w) {
           while (mask[w]) {
             const int bit = __builtin_ctz(mask[w]);
             const uint32_t slot = atomicAdd(&tqn[wave], 1u);
             if (slot >= 64u) break;
             const int cb = 2 * w + (bit >> 4), r = bit & 15;
             const int j = 32 * cb + 8 * (r >> 2) + 4 * hf + (r & 3);
-            q[slot] = ((uint32_t)lane << 8) | (uint32_t)j;
+            q[slot] = ((uint32_t)lane << 10) | (uint32_t)j;
             mask[w] &= mask[w] - 1u;
           }
         }
-        pending = single >= 0 || (mask[0] | mask[1] | mask[2] | mask[3]) != 0u;
+        pending = single >= 0 || any_mask();
       }
       __builtin_amdgcn_wave_barrier();
       const int ntask = min((int)tqn[wave], 64);
       if (lane < ntask) {
         const uint32_t tk = q[lane];
-        const int j = (int)(tk & 0xFFu);
-        const int64_t nt = nw0 + (int)((tk >> 8) & 31u);
+        const int j = (int)(tk & 0x3FFu);
+        const int64_t nt = nw0 + (int)((tk >> 10) & 31u);
         const uint16_t* xr = reinterpret_cast<const uint16_t*>(p.x) + nt * p.x_stride + (int64_t)h * D;
         const uint16_t* crow = &tab[j * ROW];
         float acc = 0.0f;
@@ -732,9 +774,9 @@ __global__ __launch_bounds__(256, 2) void encode_centroid_kernel(EncodeParams p)
       __builtin_amdgcn_wave_barrier();
       for (int i = 0; i < ntask; ++i) {
         const uint32_t tk = q[i];
-        if ((int)(tk >> 8) == lane) {
+        if ((int)(tk >> 10) == lane) {
           const float d = qd[i];
-          const int j = (int)(tk & 0xFFu);
+          const int j = (int)(tk & 0x3FFu);
           if (d < bd || (d == bd && j < bj)) { bd = d; bj = j; }
         }
       }
@@ -746,6 +788,58 @@ __global__ __launch_bounds__(256, 2) void encode_centroid_kernel(EncodeParams p)
   }
 
   // 4. residual, group scale/zero, codes
+  auto store_index = [&](int64_t row) {
+    if (p.index_bytes == 2) reinterpret_cast<uint16_t*>(p.index)[row] = (uint16_t)best;
+    else reinterpret_cast<uint8_t*>(p.index)[row] = (uint8_t)best;
+  };
+  if constexpr (COEFF) {
+    // 4'. coefficients of the residual row; the partner's half of x by a lane swap
+    uint4 xo[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      xo[i] = make_uint4(swap_halves(xv[i].x, hf), swap_halves(xv[i].y, hf),
+                         swap_halves(xv[i].z, hf), swap_halves(xv[i].w, hf));
+    const uint16_t* crow = &tab[best * ROW];
+    float cf[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) cf[j] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {   // channels 8 k .. 8 k + 7, ascending
+      const uint4 xw = ((k >> 3) == hf) ? xv[k & 7] : xo[k & 7];
+      const uint4 cv = *reinterpret_cast<const uint4*>(crow + 8 * k);
+      const uint32_t xa[4] = {xw.x, xw.y, xw.z, xw.w}, ca[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float xe = (e & 1) ? hi_bf16(xa[e >> 1]) : lo_bf16(xa[e >> 1]);
+        const float ce = (e & 1) ? hi_bf16(ca[e >> 1]) : lo_bf16(ca[e >> 1]);
+        const float r = xe - ce;
+        const float4 b0 = *reinterpret_cast<const float4*>(&bt[(8 * k + e) * 16 + 8 * hf]);
+        const float4 b1 = *reinterpret_cast<const float4*>(&bt[(8 * k + e) * 16 + 8 * hf + 4]);
+        const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float prod = r * bb[j];
+          cf[j] = cf[j] + prod;
+        }
+      }
+    }
+    // one group of 16 across the two lanes
+    float mn = cf[0], mx = cf[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) { mn = fminf(mn, cf[j]); mx = fmaxf(mx, cf[j]); }
+    mn = fminf(mn, swf(mn));
+    mx = fmaxf(mx, swf(mx));
+    uint32_t cw[8 * BITS / 32];
+    const GroupQ gq = quantize_with<BITS, 8>(cf, mn, mx, cw);
+    if (live) {
+      const int64_t row = (int64_t)h * p.capacity + p.token_offset + n;
+      p.codes[row * 2 + hf] = cw[0];   // 16 INT4 codes: two words, one per lane
+      if (hf == 0) {
+        p.sz[row] = gq.word;
+        store_index(row);
+      }
+    }
+  } else {
   const uint16_t* crow = &tab[best * ROW + 64 * hf];
   uint32_t words[WPL], szw[NG];
 #pragma unroll
@@ -810,8 +904,26 @@ __global__ __launch_bounds__(256, 2) void encode_centroid_kernel(EncodeParams p)
     if constexpr (NG == 4) *reinterpret_cast<uint4*>(sd) = make_uint4(szw[0], szw[1], szw[2], szw[3]);
     else if constexpr (NG == 2) *reinterpret_cast<uint2*>(sd) = make_uint2(szw[0], szw[1]);
     else sd[0] = szw[0];
-    if (hf == 0) reinterpret_cast<uint8_t*>(p.index)[row] = (uint8_t)best;
+    if (hf == 0) store_index(row);
   }
+  }   // !COEFF
+  }   // tiles
+}
+
+// Persistent grid: workgroups per head = how many are resident at once (LDS and
+// registers decide) divided over the heads, at most one per tile.
+template <int BITS, int G, int CM, bool COEFF>
+hipError_t launch_centroid_t(const EncodeParams& p, hipStream_t s) {
+  auto k = encode_centroid_kernel<BITS, G, CM, COEFF>;
+  constexpr int NT = 64 * cen_waves(CM, COEFF), TT = NT / 2;
+  int occ = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(k), NT, 0);
+  if (e != hipSuccess) return e;
+  const int64_t ntile = (p.n_tokens + TT - 1) / TT;
+  const int64_t resident = (int64_t)std::max(1, occ) * cu_count();
+  const int wph = (int)std::max<int64_t>(1, std::min<int64_t>(ntile, resident / p.H));
+  hipLaunchKernelGGL(k, dim3((unsigned)(wph * p.H)), dim3(NT), 0, s, p);
+  return hipGetLastError();
 }
 
 template <typename XT, int D>
@@ -879,17 +991,19 @@ hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   const bool bf16 = a.c.x_dtype == KVC_BF16;
-  // centroid base, bf16 d = 128, <= 256 centroids: register-resident MFMA assignment
-  if (bf16 && a.c.D == 128 && p.mode == MODE_CENTROID && a.c.C <= 256 && p.x_stride % 8 == 0 &&
-      (a.c.group == 16 || a.c.group == 32 || a.c.group == 64)) {
-    const dim3 grid((unsigned)(((p.n_tokens + 127) / 128) * a.c.H));
-#define KVC_ENC_CEN(B, G) \
-    if (a.c.bits == B && a.c.group == G) { \
-      hipLaunchKernelGGL((encode_centroid_kernel<B, G>), grid, dim3(256), 0, s, p); \
-      return hipGetLastError(); \
-    }
-    KVC_ENC_CEN(2, 16) KVC_ENC_CEN(2, 32) KVC_ENC_CEN(2, 64)
-    KVC_ENC_CEN(4, 16) KVC_ENC_CEN(4, 32) KVC_ENC_CEN(4, 64)
+  // centroid and coefficient (m = 16, INT4) bases, bf16 d = 128, <= 512 centroids:
+  // register-resident MFMA assignment, persistent workgroups per head
+  const bool cen_ok = p.mode == MODE_CENTROID && (a.c.group == 16 || a.c.group == 32 || a.c.group == 64);
+  const bool coeff_ok = p.mode == MODE_COEFF && a.c.m == 16 && a.c.group == 16 && a.c.bits == 4;
+  if (bf16 && a.c.D == 128 && (cen_ok || coeff_ok) && a.c.C <= 512 && p.x_stride % 8 == 0) {
+#define KVC_ENC_CEN(B, G, CM, CF)                                                        \
+    if (a.c.bits == B && a.c.group == G && (a.c.C <= 256) == (CM == 256) && coeff_ok == CF) \
+      return launch_centroid_t<B, G, CM, CF>(p, s);
+    KVC_ENC_CEN(2, 16, 256, false) KVC_ENC_CEN(2, 32, 256, false) KVC_ENC_CEN(2, 64, 256, false)
+    KVC_ENC_CEN(4, 16, 256, false) KVC_ENC_CEN(4, 32, 256, false) KVC_ENC_CEN(4, 64, 256, false)
+    KVC_ENC_CEN(2, 16, 512, false) KVC_ENC_CEN(2, 32, 512, false) KVC_ENC_CEN(2, 64, 512, false)
+    KVC_ENC_CEN(4, 16, 512, false) KVC_ENC_CEN(4, 32, 512, false) KVC_ENC_CEN(4, 64, 512, false)
+    KVC_ENC_CEN(4, 16, 256, true) KVC_ENC_CEN(4, 16, 512, true)
 #undef KVC_ENC_CEN
   }
   // centroid and coefficient bases on bf16 d = 128 data: MFMA shortlist + exact rescoring

@@ -87,6 +87,8 @@ hipError_t launch_attend_mixed(const AttendLaunch& a, hipStream_t s);
 // stores the launch status in *err.  launch_predict_fused writes the prediction only
 // (the decoder's base), with the same kernels and arithmetic as the encoder.
 bool launch_encode_fused(const EncodeLaunch& a, hipStream_t s, hipError_t* err);
+// compute units of the current device (256 if the query fails)
+int cu_count();
 bool launch_predict_fused(const EncodeLaunch& a, float* out, hipStream_t s, hipError_t* err);
 
 // Whether the matrix-product predictor bases (DPLR, temporal values) are built.

@@ -474,14 +474,6 @@ __global__ __launch_bounds__(512) void pred_kernel(PredParams p) {
   }
 }
 
-int cu_count() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-    return 256;
-  return n;
-}
-
 // Persistent grid: as many workgroups as are resident at once (the kernel's register and
 // LDS use decide how many per CU), matrix modes split evenly over the heads.
 template <int BITS, int G, int PM, int NIN>
@@ -610,6 +602,14 @@ bool fused_codec(const EncodeLaunch& a) {
 }
 
 }  // namespace
+
+int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
 
 bool launch_encode_fused(const EncodeLaunch& a, hipStream_t s, hipError_t* err) {
   const int mode = fused_mode(a);

@@ -154,3 +154,27 @@ def test_cfg1_chunk_encode_full_size_sampled():
         assert not np.any(np.all(got["codes"][:, lo:hi] == 0xFFFFFFFF, axis=-1)
                           & np.all(got["scale_zero"][:, lo:hi] == 0xFFFFFFFF, axis=-1))
         assert np.all(got["codes"][:, :lo] == 0xFFFFFFFF)
+
+
+def test_centroid_encode_whole_history_several_tiles_per_workgroup():
+    """All 32760 history tokens of the 12-head, 256-centroid layer in one call: the
+    encoder's workgroups then walk several 128-token tiles of their head each (the
+    grid holds as many workgroups as are resident at once).  Sampled rows, including
+    the ragged last tile, are checked against the oracle; every row is written."""
+    dev = device()
+    d = synth.cfg1()
+    n = d["K"].shape[0]
+    rng = np.random.default_rng(1)
+    sample = np.unique(np.concatenate([rng.choice(n, size=384, replace=False),
+                                       np.arange(n - 8, n)]))
+    codec = kvc.Codec(12, 128, 2, 32, kvc.BASE_CENTROID, 256)
+    st = kvc.Store.allocate(codec, n, dev)
+    fill_sentinel(st)
+    base = kvc.BaseParams(centroids=to_dev(d["Ck"], dev))
+    kvc.kvc_encode(codec, to_dev(d["K"], dev), st, 0, base)
+    got = store_np(st)
+    sub = dict(codes=got["codes"][:, sample], scale_zero=got["scale_zero"][:, sample],
+               index=got["index"][:, sample])
+    check_centroid_store(sub, nm.bf16_to_f32(d["K"][sample]), nm.bf16_to_f32(d["Ck"]), 2, 32)
+    assert not np.any(np.all(got["codes"] == 0xFFFFFFFF, axis=-1)
+                      & np.all(got["scale_zero"] == 0xFFFFFFFF, axis=-1))
