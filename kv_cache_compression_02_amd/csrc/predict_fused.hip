@@ -34,26 +34,32 @@ struct RankParams {
   int n, r, hd, nin;
 };
 
-template <int RB>        // r <= 32 RB
+
+
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+// t = v_lr [in0 ; in1] for 64 tokens per workgroup on v_mfma_f32_16x16x32_bf16: RB
+// blocks of 16 rank rows x 4 blocks of 16 tokens per wave, the contraction split over
+// the four waves and the partial sums added in a fixed order.  Every load instruction
+// reads 64 contiguous bytes of 16 rows (lane (row, q) takes elements 32 ks + 8 q ..).
+template <int RB>        // r <= 16 RB
 __global__ __launch_bounds__(256) void rank_kernel(RankParams p) {
-  __shared__ float red[3][2 * RB][16][64];
+  __shared__ float red[4][4 * RB * 4][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 31, hf = lane >> 5;
+  const int col = lane & 15, q = lane >> 4;
   const int n0 = blockIdx.x * 64;
   const int K = p.nin * p.hd;
   const int slice = K / 4;
-  f32x16_t acc[2][RB];
+  f32x4_t acc[4][RB];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < RB; ++b)
+    for (int b = 0; b < RB; ++b) acc[a][b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  int64_t trow[4];
+  bool tok[4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
-  int64_t trow[2];
-  bool tok[2];
-#pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
-    const int n = n0 + 32 * tb + col;
+  for (int tb = 0; tb < 4; ++tb) {
+    const int n = n0 + 16 * tb + col;
     tok[tb] = n < p.n;
     trow[tb] = (int64_t)(tok[tb] ? n : 0) * p.ps;
   }
@@ -61,61 +67,51 @@ __global__ __launch_bounds__(256) void rank_kernel(RankParams p) {
   bool rok[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const int rr = 32 * rb + col;
+    const int rr = 16 * rb + col;
     rok[rb] = rr < p.r;
     arow[rb] = p.vlr + (int64_t)(rok[rb] ? rr : 0) * K;
   }
   const bf16x8_t zero = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll 4
-  for (int k = wave * slice; k < (wave + 1) * slice; k += 16) {
-    const int kk = k + 8 * hf;
-    const int j = kk >= p.hd ? 1 : 0;
+  for (int k = wave * slice; k < (wave + 1) * slice; k += 32) {
+    const int kk = k + 8 * q;
+    const int j = kk >= p.hd ? 1 : 0;   // a 32-wide step never straddles the two inputs
     const uint16_t* src = (j ? p.in1 : p.in0) + (kk - j * p.hd);
-    bf16x8_t bx[2];
+    bf16x8_t bx[4];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+    for (int tb = 0; tb < 4; ++tb)
       bx[tb] = tok[tb] ? *reinterpret_cast<const bf16x8_t*>(src + trow[tb]) : zero;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const bf16x8_t a = rok[rb] ? *reinterpret_cast<const bf16x8_t*>(arow[rb] + kk) : zero;
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-        acc[tb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bx[tb], acc[tb][rb], 0, 0, 0);
+      for (int tb = 0; tb < 4; ++tb)
+        acc[tb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bx[tb], acc[tb][rb], 0, 0, 0);
     }
   }
-  if (wave > 0) {
+  // every wave's partial sums to LDS; thread (token, part) then adds the four waves'
+  // values in wave order for its 16 rank rows and stores them as 64 contiguous bytes
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) red[wave - 1][tb * RB + rb][i][lane] = acc[tb][rb][i];
-  }
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int w = 0; w < 3; ++w)
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[tb][rb][i] = acc[tb][rb][i] + red[w][tb * RB + rb][i][lane];
-  // acc[tb][rb][4q + s] = t[n][32 rb + 8 q + 4 hf + s], n = n0 + 32 tb + col
-#pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
-    if (!tok[tb]) continue;
-    float* trow_out = p.t + (int64_t)(n0 + 32 * tb + col) * p.r;
+  for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = 32 * rb + 8 * q + 4 * hf;
-        if (c < p.r)
-          *reinterpret_cast<float4*>(trow_out + c) =
-              make_float4(acc[tb][rb][4 * q], acc[tb][rb][4 * q + 1], acc[tb][rb][4 * q + 2],
-                          acc[tb][rb][4 * q + 3]);
-      }
+      for (int i = 0; i < 4; ++i) red[wave][(tb * RB + rb) * 4 + i][lane] = acc[tb][rb][i];
+  __syncthreads();
+  const int tt = tid >> 2, pp = tid & 3;    // token n0 + tt, rank rows 16 pp .. 16 pp + 15
+  const int n = n0 + tt;
+  if (pp >= RB || 16 * pp >= p.r || n >= p.n) return;
+  const int tb = tt >> 4, cl = tt & 15;
+  float* trow_out = p.t + (int64_t)n * p.r + 16 * pp;
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) {
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = (tb * RB + pp) * 4 + i, l = (qq << 4) | cl;
+      v[i] = ((red[0][e][l] + red[1][e][l]) + red[2][e][l]) + red[3][e][l];
+    }
+    *reinterpret_cast<float4*>(trow_out + 4 * qq) = make_float4(v[0], v[1], v[2], v[3]);
   }
 }
 
@@ -145,8 +141,6 @@ struct PredParams {
 // Output channel held by MFMA row i of output block ob (16 x 16 blocks): row 4 q + s
 // of block ob is channel 32 q + 4 ob + s, so lane (t, q) receives channels 32 q + 4 ob + s.
 __device__ __forceinline__ int out_channel(int ob, int i) { return 32 * (i >> 2) + 4 * ob + (i & 3); }
-
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 
 // LDS geometry: permuted weight rows, U with permuted columns (always 64 + 8 wide,
 // zero past r), then one 16-token staging tile per wave.
@@ -514,8 +508,8 @@ hipError_t launch_rank(const EncodeLaunch& a, float* t, hipStream_t s) {
   r.hd = a.c.H * D;
   r.nin = a.c.n_inputs;
   const dim3 grid((unsigned)((a.n_tokens + 63) / 64));
-  if (r.r <= 32) hipLaunchKernelGGL(rank_kernel<1>, grid, dim3(256), 0, s, r);
-  else hipLaunchKernelGGL(rank_kernel<2>, grid, dim3(256), 0, s, r);
+  if (r.r <= 32) hipLaunchKernelGGL(rank_kernel<2>, grid, dim3(256), 0, s, r);
+  else hipLaunchKernelGGL(rank_kernel<4>, grid, dim3(256), 0, s, r);
   return hipGetLastError();
 }
 
