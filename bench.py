@@ -198,19 +198,38 @@ def bench_dplr(args, torch, kvc, synth, dev):
     log("timing")
     t_step, ev = _timed(torch, step, args.steps, args.warmup)
     t_ev = sum(a.elapsed_time(b) for a, b in ev) / len(ev) * 1e-3
-    x_bytes = layers * 2 * n * H * D * 2
-    code_bytes = 2 * n * H * (D * 4 // 8 + 4 * D // 32) + 2 * (layers - 1) * n * H * (D * 2 // 8 + 4 * D // 32)
-    param_bytes = (layers - 1) * sum(int(np.prod(prm[k].shape)) * 2 for k in ("WK", "UK", "VK", "WV", "UV", "VV"))
-    alg = x_bytes + code_bytes + param_bytes
+    # algorithmic bytes: every tensor the closed-loop chain must move, once - the layer's
+    # K and V read, the previous reconstructions read as predictor inputs (values also
+    # read this layer's reconstructed keys), codes + scale/zero and the reconstructions
+    # written, the predictor parameters read
+    row = n * H * D * 2
+    cz2 = n * H * (D * 2 // 8 + 4 * D // 32)
+    cz4 = n * H * (D * 4 // 8 + 4 * D // 32)
+    par_k = sum(int(np.prod(prm[k].shape)) * 2 for k in ("WK", "UK", "VK"))
+    par_v = sum(int(np.prod(prm[k].shape)) * 2 for k in ("WV", "UV", "VV"))
+    per_k, per_v = 2 * row + cz2 + row + par_k, 3 * row + cz2 + row + par_v
+    alg = 2 * (row + cz4 + row) + (layers - 1) * (per_k + per_v)
     flops = (layers - 1) * n * 2 * (H * D * r + H * D * D + H * D * r          # keys
                                     + 2 * H * D * r + 2 * H * D * D + H * D * r)  # values
     gbs = alg / t_ev / 1e9
+    # the dominant call: one layer's value encode (rank-r product + fused predictor and
+    # quantizer), timed alone
+    l = layers // 2
+    k_in, v_in = rec[l & 1][0], rec[(l + 1) & 1][1]
+    vcall = lambda _: kvc.kvc_encode(vcod, xs[l][1], stores[l][1], 0,
+                                     kvc.BaseParams(prev0=k_in, prev1=v_in, w_block=WV, u=UV, v_lr=VVt),
+                                     recon_out=rec[l & 1][1], workspace=ws)
+    _, ev_v = _timed(torch, vcall, max(1, min(args.steps, 10)), 1)
+    t_v = sum(a.elapsed_time(b) for a, b in ev_v) / len(ev_v) * 1e-3
+    v_gbs = per_v / t_v / 1e9
     return _line("cross-layer block-DPLR chain encode GB/s (30 layers K+V)", gbs, "GB/s", args,
                  t_step, "bf16", {"workload": "block-DPLR cross-layer chain, 30 layers x 12 heads "
                                   "x 128, 32760 tokens, rank 64, INT2 g32 (INT4 g32 layer 0)",
                                   "layers": layers, "tokens": n, "heads": H, "rank": r},
-                 {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                  "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "chain", "ms": t_ev * 1e3},
+                 {"bound": "hbm", "achieved": v_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": v_gbs / HBM_PEAK_GBS, "traffic": None,
+                  "kernel": "value encode call (rank_kernel + pred_kernel)", "ms": t_v * 1e3},
+                 chain_ms=t_ev * 1e3, chain_frac_hbm=gbs / HBM_PEAK_GBS,
                  predictor_tflops=flops / t_ev / 1e12, algorithmic_bytes=alg, flops=flops)
 
 
@@ -273,8 +292,16 @@ def bench_temporal(args, torch, kvc, synth, dev):
     t_att = sum(a.elapsed_time(b) for a, b in ev_att) / len(ev_att) * 1e-3
     flops = attention_flops(nq, nk, D, H)
     achieved = flops / t_att / 1e12
-    enc_bytes = 2 * nk * H * D * 2 + 2 * T * H * (D * 4 // 8 + 4 * D // 64) \
-        + 2 * (F - 1) * T * H * (D * 2 // 8 + 4 * D // 64)
+    # encode bytes the closed-loop chain must move once: each frame's K and V read, the
+    # reconstructions it predicts from read (keys: frames t-1 and t-2, the same frame at
+    # t = 1; values: this frame's keys and the previous values), codes + scale/zero and
+    # reconstructions written, the value map M and beta read per frame
+    row = T * H * D * 2
+    cz2, cz4 = T * H * (D * 2 // 8 + 4 * D // 64), T * H * (D * 4 // 8 + 4 * D // 64)
+    par = H * D * D * 2 + H * D * 4
+    enc_bytes = 2 * (row + cz4 + row) + sum(
+        (row + (2 if t >= 2 else 1) * row + cz2 + row) + (3 * row + cz2 + row + par)
+        for t in range(1, F))
     t_enc = t_ev - t_att
     return _line("temporal chain: attention query-tok/s (16-frame K+V encode + attention)",
                  nq / t_ev, "query-tok/s", args, t_step, "bf16",
@@ -283,7 +310,10 @@ def bench_temporal(args, torch, kvc, synth, dev):
                               "4680 q x 24960 keys", "heads": H, "frames": F, "tokens": nk,
                   "queries": nq},
                  {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                  "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None, "kernel": "attend_bf16_kernel",
+                  "frac": achieved / BF16_PEAK_TFLOPS,
+                  "traffic": recorded_traffic("attend_bf16_kernel_dense_temporal_40x128_4680q_24960k.md",
+                                              "kv_cache_compression_02_amd/csrc/attend.hip"),
+                  "kernel": "attend_bf16_kernel",
                   "ms": t_att * 1e3},
                  encode={"ms": t_enc * 1e3, "bytes": enc_bytes, "GB/s": enc_bytes / t_enc / 1e9,
                          "frac_hbm": enc_bytes / t_enc / 1e9 / HBM_PEAK_GBS})
@@ -341,7 +371,9 @@ def bench_mixed(args, torch, kvc, synth, dev):
                                       "coefficients, INT2 g32 values, 4680 queries",
                           "heads": H, "keys": nk, "queries": nq, "centroids": C, "coeff_dim": m},
                  {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                  "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                  "frac": achieved / BF16_PEAK_TFLOPS,
+                  "traffic": recorded_traffic("attend_bf16_kernel_mixed_12x128_4680q_65520k.md",
+                                              "kv_cache_compression_02_amd/csrc/attend.hip"),
                   "kernel": "attend_bf16_kernel (mixed)", "ms": t_ev * 1e3},
                  full_attention_equivalent_tflops=attention_flops(nq, nk, D, H) / t_ev / 1e12,
                  encode={"keys_ms": t_k * 1e3, "values_ms": t_v * 1e3, "bytes": enc_k + enc_v,
