@@ -38,80 +38,95 @@ struct RankParams {
 
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 
-// t = v_lr [in0 ; in1] for 64 tokens per workgroup on v_mfma_f32_16x16x32_bf16: RB
-// blocks of 16 rank rows x 4 blocks of 16 tokens per wave, the contraction split over
-// the four waves and the partial sums added in a fixed order.  Every load instruction
-// reads 64 contiguous bytes of 16 rows (lane (row, q) takes elements 32 ks + 8 q ..).
+// t = v_lr [in0 ; in1] on v_mfma_f32_16x16x32_bf16.  A workgroup of eight waves takes
+// 128 tokens, each wave 16 of them over the whole contraction, so every t element is one
+// MFMA accumulation chain in ascending k and the same on every call.  v_lr is staged
+// through LDS in chunks of 128 columns shared by the eight waves (double-buffered: the
+// next chunk and the waves' next input fragments are in flight while the current chunk's
+// MFMAs run); every global load reads 64 contiguous bytes of 16 rows.
+constexpr int RK_KC = 128;              // contraction chunk
+constexpr int RK_ROW = RK_KC + 8;       // padded LDS row (bf16)
+constexpr int RK_TOK = 128;             // tokens per workgroup
 template <int RB>        // r <= 16 RB
-__global__ __launch_bounds__(256) void rank_kernel(RankParams p) {
-  __shared__ float red[4][4 * RB * 4][64];
+__global__ __launch_bounds__(512) void rank_kernel(RankParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t vl[2][16 * RB * RK_ROW];
+  constexpr int PIECES = 16 * RB * (RK_KC / 8);        // 16-byte pieces of a chunk
+  constexpr int PPT = (PIECES + 511) / 512;            // per thread
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, q = lane >> 4;
-  const int n0 = blockIdx.x * 64;
-  const int K = p.nin * p.hd;
-  const int slice = K / 4;
-  f32x4_t acc[4][RB];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < RB; ++b) acc[a][b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  int64_t trow[4];
-  bool tok[4];
-#pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
-    const int n = n0 + 16 * tb + col;
-    tok[tb] = n < p.n;
-    trow[tb] = (int64_t)(tok[tb] ? n : 0) * p.ps;
-  }
-  const uint16_t* arow[RB];
-  bool rok[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int rr = 16 * rb + col;
-    rok[rb] = rr < p.r;
-    arow[rb] = p.vlr + (int64_t)(rok[rb] ? rr : 0) * K;
-  }
+  const int n = blockIdx.x * RK_TOK + wave * 16 + col;   // token of B-operand column col
+  const bool tok = n < p.n;
+  const int64_t trow = (int64_t)(tok ? n : 0) * p.ps;
+  const int K = p.nin * p.hd, nch = K / RK_KC;           // hd is a multiple of 128
   const bf16x8_t zero = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll 4
-  for (int k = wave * slice; k < (wave + 1) * slice; k += 32) {
-    const int kk = k + 8 * q;
-    const int j = kk >= p.hd ? 1 : 0;   // a 32-wide step never straddles the two inputs
-    const uint16_t* src = (j ? p.in1 : p.in0) + (kk - j * p.hd);
-    bf16x8_t bx[4];
+  auto load_stage = [&](int c, uint4 (&v)[PPT]) {
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-      bx[tb] = tok[tb] ? *reinterpret_cast<const bf16x8_t*>(src + trow[tb]) : zero;
+    for (int i = 0; i < PPT; ++i) {
+      const int e = tid + 512 * i, row = e >> 4, pc = e & 15;
+      v[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (e < PIECES && row < p.r)
+        v[i] = *reinterpret_cast<const uint4*>(p.vlr + (int64_t)row * K + c * RK_KC + 8 * pc);
+    }
+  };
+  auto store_stage = [&](int b, const uint4 (&v)[PPT]) {
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int e = tid + 512 * i, row = e >> 4, pc = e & 15;
+      if (e < PIECES) *reinterpret_cast<uint4*>(&vl[b][row * RK_ROW + 8 * pc]) = v[i];
+    }
+  };
+  auto load_b = [&](int c, bf16x8_t (&bx)[4]) {
+    const int k0 = c * RK_KC;
+    const int j = k0 >= p.hd ? 1 : 0;   // a chunk never straddles the two inputs
+    const uint16_t* src = (j ? p.in1 : p.in0) + (k0 - j * p.hd) + trow + 8 * q;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      bx[ks] = tok ? *reinterpret_cast<const bf16x8_t*>(src + 32 * ks) : zero;
+  };
+  f32x4_t acc[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  bf16x8_t bcur[4];
+  {
+    uint4 v[PPT];
+    load_stage(0, v);
+    load_b(0, bcur);
+    store_stage(0, v);
+  }
+  __syncthreads();
+#pragma unroll 1
+  for (int c = 0; c < nch; ++c) {
+    const int b = c & 1;
+    uint4 v[PPT];
+    bf16x8_t bnxt[4];
+    const bool more = c + 1 < nch;
+    if (more) {
+      load_stage(c + 1, v);
+      load_b(c + 1, bnxt);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&vl[b][(16 * rb + col) * RK_ROW + 32 * ks + 8 * q]);
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bcur[ks], acc[rb], 0, 0, 0);
+      }
+    if (more) store_stage(b ^ 1, v);
+    __syncthreads();
+    if (more) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) bcur[ks] = bnxt[ks];
+    }
+  }
+  // lane (col, q) holds t[n][16 rb + 4 q + i]: 64 contiguous bytes per token and block
+  if (tok) {
+    float* trow_out = p.t + (int64_t)n * p.r;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const bf16x8_t a = rok[rb] ? *reinterpret_cast<const bf16x8_t*>(arow[rb] + kk) : zero;
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-        acc[tb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bx[tb], acc[tb][rb], 0, 0, 0);
+      const int c0 = 16 * rb + 4 * q;
+      if (c0 < p.r)
+        *reinterpret_cast<float4*>(trow_out + c0) = make_float4(acc[rb][0], acc[rb][1], acc[rb][2], acc[rb][3]);
     }
-  }
-  // every wave's partial sums to LDS; thread (token, part) then adds the four waves'
-  // values in wave order for its 16 rank rows and stores them as 64 contiguous bytes
-#pragma unroll
-  for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave][(tb * RB + rb) * 4 + i][lane] = acc[tb][rb][i];
-  __syncthreads();
-  const int tt = tid >> 2, pp = tid & 3;    // token n0 + tt, rank rows 16 pp .. 16 pp + 15
-  const int n = n0 + tt;
-  if (pp >= RB || 16 * pp >= p.r || n >= p.n) return;
-  const int tb = tt >> 4, cl = tt & 15;
-  float* trow_out = p.t + (int64_t)n * p.r + 16 * pp;
-#pragma unroll
-  for (int qq = 0; qq < 4; ++qq) {
-    float v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = (tb * RB + pp) * 4 + i, l = (qq << 4) | cl;
-      v[i] = ((red[0][e][l] + red[1][e][l]) + red[2][e][l]) + red[3][e][l];
-    }
-    *reinterpret_cast<float4*>(trow_out + 4 * qq) = make_float4(v[0], v[1], v[2], v[3]);
   }
 }
 
@@ -507,9 +522,9 @@ hipError_t launch_rank(const EncodeLaunch& a, float* t, hipStream_t s) {
   r.r = a.c.rank;
   r.hd = a.c.H * D;
   r.nin = a.c.n_inputs;
-  const dim3 grid((unsigned)((a.n_tokens + 63) / 64));
-  if (r.r <= 32) hipLaunchKernelGGL(rank_kernel<2>, grid, dim3(256), 0, s, r);
-  else hipLaunchKernelGGL(rank_kernel<4>, grid, dim3(256), 0, s, r);
+  const dim3 grid((unsigned)((a.n_tokens + RK_TOK - 1) / RK_TOK));
+  if (r.r <= 32) hipLaunchKernelGGL(rank_kernel<2>, grid, dim3(512), 0, s, r);
+  else hipLaunchKernelGGL(rank_kernel<4>, grid, dim3(512), 0, s, r);
   return hipGetLastError();
 }
 
