@@ -483,6 +483,21 @@ def main() -> int:
         "encode": {"ms": t_enc * 1e3, "bytes": enc_b, "GB/s": enc_b / t_enc / 1e9,
                    "frac_hbm": enc_b / t_enc / 1e9 / HBM_PEAK_GBS},
     }
+    # decode of the whole compressed history (K and V) to bf16, timed apart from the step
+    kdec = torch.empty((nk, H, D), dtype=torch.bfloat16, device=dev)
+    vdec = torch.empty_like(kdec)
+
+    def dec(_):
+        kvc.kvc_decode(codec, ks, 0, nk, kb, out=kdec, out_dtype=kvc.BF16)
+        kvc.kvc_decode(codec, vs, 0, nk, vb, out=vdec, out_dtype=kvc.BF16)
+
+    _, ev_d = _timed(torch, dec, max(1, min(args.steps, 10)), 1)
+    t_dec = sum(a.elapsed_time(b) for a, b in ev_d) / len(ev_d) * 1e-3
+    # per tensor: codes + scale/zero + index read, bf16 rows written, the table once
+    dec_b = 2 * (nk * H * (D * bits // 8 + 4 * D // group + 1) + nk * H * D * 2 + H * C * D * 2)
+    line["decode"] = {"ms": t_dec * 1e3, "bytes": dec_b, "GB/s": dec_b / t_dec / 1e9,
+                      "frac_hbm": dec_b / t_dec / 1e9 / HBM_PEAK_GBS,
+                      "what": "decode of the 32760-token history, K and V, to bf16"}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(d)
     print(json.dumps(line))

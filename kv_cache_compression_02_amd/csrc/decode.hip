@@ -62,8 +62,20 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
                                : reinterpret_cast<const uint16_t*>(p.index)[row];
     a = min(a, p.C - 1);   // out-of-contract indices must not read past the table
     const XT* crow = reinterpret_cast<const XT*>(p.centroids) + ((int64_t)h * p.C + a) * p.D + i0;
+    if constexpr (sizeof(XT) == 2) {   // one 16-byte read of 8 bf16 values
+      const uint4 w = *reinterpret_cast<const uint4*>(crow);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-    for (int k = 0; k < 8; ++k) base[k] = load_x<XT>(crow + k);
+      for (int k = 0; k < 4; ++k) {
+        base[2 * k] = bf16_bits_to_f32(ww[k] & 0xFFFFu);
+        base[2 * k + 1] = bf16_bits_to_f32(ww[k] >> 16);
+      }
+    } else {                           // two 16-byte reads of 8 fp32 values
+      const float4 u0 = *reinterpret_cast<const float4*>(crow);
+      const float4 u1 = *reinterpret_cast<const float4*>(crow + 4);
+      base[0] = u0.x; base[1] = u0.y; base[2] = u0.z; base[3] = u0.w;
+      base[4] = u1.x; base[5] = u1.y; base[6] = u1.z; base[7] = u1.w;
+    }
   } else if (p.mode == DM_TEMPORAL_K) {
     const XT* p0 = reinterpret_cast<const XT*>(p.prev0) + n * p.prev_stride + (int64_t)h * p.D + i0;
     const XT* p1 = reinterpret_cast<const XT*>(p.prev1) + n * p.prev_stride + (int64_t)h * p.D + i0;
@@ -84,11 +96,20 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
 
   const int64_t orow = (n * p.H + h) * (int64_t)p.D + i0;
   OT* out = reinterpret_cast<OT*>(p.out) + orow;
+  float v[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    uint32_t code = (bits8 >> (p.bits * k)) & mask;
-    float v = base[k] + dequant_one(code, s, z);
-    store_x<OT>(out + k, v);
+    const uint32_t code = (bits8 >> (p.bits * k)) & mask;
+    v[k] = base[k] + dequant_one(code, s, z);
+  }
+  if constexpr (sizeof(OT) == 2) {     // 8 bf16 (round to nearest even): one 16-byte store
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = f32_to_bf16_bits(v[2 * k]) | (f32_to_bf16_bits(v[2 * k + 1]) << 16);
+    *reinterpret_cast<uint4*>(out) = make_uint4(o[0], o[1], o[2], o[3]);
+  } else {
+    *reinterpret_cast<float4*>(out) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(out + 4) = make_float4(v[4], v[5], v[6], v[7]);
   }
   if (p.pred && p.mode != DM_BUFFER) {
 #pragma unroll

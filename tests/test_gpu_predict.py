@@ -138,9 +138,11 @@ def _dplr_bound(xs, W, Uf, Vt, r):
     return 2 * (nin * D + 4) * U * blk + low
 
 
-def test_dplr_chain_teacher_forced_and_free_running():
+@pytest.mark.parametrize("r", [16, 48])
+def test_dplr_chain_teacher_forced_and_free_running(r):
+    """r = 48 leaves the last 16-row block of the rank matrix and of U partly empty."""
     dev = device()
-    H, D, r, L, n = 3, 128, 16, 4, 100
+    H, D, L, n = 3, 128, 4, 100
     prm = synth.cfg2_params(heads=H, dim=D, rank=r)
     layers = [(nm.bf16_to_f32(k), nm.bf16_to_f32(v))
               for k, v in synth.cfg2_layers(params=prm, n_tokens=n, n_layers=L, chunk=50)]
