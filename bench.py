@@ -177,23 +177,42 @@ def bench_dplr(args, torch, kvc, synth, dev):
                kvc.Store.allocate(anchor if l == 0 else vcod, n, dev)) for l in range(layers)]
     rec = [[torch.empty((n, H, D), dtype=torch.bfloat16, device=dev) for _ in range(2)]
            for _ in range(2)]
-    ws = kvc.kvc.workspace_for(kvc.kvc.OP_ENCODE, vcod, n, dev)
+    ws = kvc.kvc.workspace_for(kvc.kvc.OP_ENCODE, vcod, n, dev)      # keys (current stream)
+    ws_v = kvc.kvc.workspace_for(kvc.kvc.OP_ENCODE, vcod, n, dev)    # values (second stream)
+    s_v = torch.cuda.Stream(device=dev)   # default priority
 
     def step(_):
+        # keys on the current stream, values on s_v: layer l's values and layer l+1's keys
+        # both need only K^_l, so they run concurrently.  Events order the rest: values
+        # wait for their layer's keys; keys of layer l overwrite the buffer that the values
+        # of layer l-2 read, so they wait for those.
+        main = torch.cuda.current_stream()
+        k_done, v_done = [], []
         for l in range(layers):
             k, v = xs[l]
             rk, rv = rec[l & 1]
             pk, pv = rec[(l + 1) & 1]
+            if l >= 2:
+                main.wait_event(v_done[l - 2])
             if l == 0:
                 kvc.kvc_encode(anchor, k, stores[l][0], 0, None, recon_out=rk)
-                kvc.kvc_encode(anchor, v, stores[l][1], 0, None, recon_out=rv)
             else:
                 kvc.kvc_encode(kcod, k, stores[l][0], 0,
                                kvc.BaseParams(prev0=pk, w_block=WK, u=UK, v_lr=VKt),
                                recon_out=rk, workspace=ws)
-                kvc.kvc_encode(vcod, v, stores[l][1], 0,
-                               kvc.BaseParams(prev0=rk, prev1=pv, w_block=WV, u=UV, v_lr=VVt),
-                               recon_out=rv, workspace=ws)
+            k_done.append(torch.cuda.Event())
+            k_done[l].record(main)
+            with torch.cuda.stream(s_v):
+                s_v.wait_event(k_done[l])
+                if l == 0:
+                    kvc.kvc_encode(anchor, v, stores[l][1], 0, None, recon_out=rv)
+                else:
+                    kvc.kvc_encode(vcod, v, stores[l][1], 0,
+                                   kvc.BaseParams(prev0=rk, prev1=pv, w_block=WV, u=UV, v_lr=VVt),
+                                   recon_out=rv, workspace=ws_v)
+                v_done.append(torch.cuda.Event())
+                v_done[l].record(s_v)
+        main.wait_event(v_done[-1])
 
     log("timing")
     t_step, ev = _timed(torch, step, args.steps, args.warmup)
@@ -264,19 +283,33 @@ def bench_temporal(args, torch, kvc, synth, dev):
     def fr(x, t):
         return x[t * T:(t + 1) * T]
 
+    s_v = torch.cuda.Stream(device=dev)   # default priority
+
     def step(i):
+        # keys on the current stream, values on s_v: frame t's values and frame t+1's keys
+        # both need only K^_t, so they run concurrently; values wait for their frame's keys
+        main = torch.cuda.current_stream()
         for t in range(F):
             if t == 0:
                 kvc.kvc_encode(anchor, fr(K, 0), ks[0], 0, None, recon_out=fr(khat, 0))
-                kvc.kvc_encode(anchor, fr(V, 0), vs[0], 0, None, recon_out=fr(vhat, 0))
-                continue
-            p2 = fr(khat, t - 2) if t > 1 else fr(khat, t - 1)
-            kvc.kvc_encode(kcod, fr(K, t), ks[t], 0,
-                           kvc.BaseParams(prev0=fr(khat, t - 1), prev1=p2, coef_a=a_d, coef_b=b_d),
-                           recon_out=fr(khat, t))
-            kvc.kvc_encode(kcod, fr(V, t), vs[t], 0,
-                           kvc.BaseParams(aux=fr(khat, t), prev0=fr(vhat, t - 1), w_block=M,
-                                          coef_a=be_d), recon_out=fr(vhat, t), workspace=ws)
+            else:
+                p2 = fr(khat, t - 2) if t > 1 else fr(khat, t - 1)
+                kvc.kvc_encode(kcod, fr(K, t), ks[t], 0,
+                               kvc.BaseParams(prev0=fr(khat, t - 1), prev1=p2, coef_a=a_d, coef_b=b_d),
+                               recon_out=fr(khat, t))
+            k_done = torch.cuda.Event()
+            k_done.record(main)
+            with torch.cuda.stream(s_v):
+                s_v.wait_event(k_done)
+                if t == 0:
+                    kvc.kvc_encode(anchor, fr(V, 0), vs[0], 0, None, recon_out=fr(vhat, 0))
+                else:
+                    kvc.kvc_encode(kcod, fr(V, t), vs[t], 0,
+                                   kvc.BaseParams(aux=fr(khat, t), prev0=fr(vhat, t - 1), w_block=M,
+                                                  coef_a=be_d), recon_out=fr(vhat, t), workspace=ws)
+        v_end = torch.cuda.Event()
+        v_end.record(s_v)
+        main.wait_event(v_end)
         if i is not None:
             e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             e[0].record()

@@ -191,3 +191,66 @@ def test_dplr_chain_teacher_forced_and_free_running(r):
         st, nv_, pv = _enc(vcod, vb, dev, base)
         _quant_bound_ok(vx, nv_.float().cpu().numpy(), st, 2, 32, pv.cpu().numpy())
         gk, gv = nk_, nv_
+
+
+def test_dplr_chain_on_two_streams_matches_one_stream():
+    """The library keeps no state between calls, so a chain whose value encodes run on a
+    second stream (overlapping the next layer's key encode, ordered by events, each
+    stream with its own workspace) stores exactly what the one-stream chain stores."""
+    dev = device()
+    H, D, r, L, n = 4, 128, 32, 6, 700
+    prm = synth.cfg2_params(heads=H, dim=D, rank=r)
+    layers = [(to_dev(k, dev), to_dev(v, dev))
+              for k, v in synth.cfg2_layers(params=prm, n_tokens=n, n_layers=L, chunk=350)]
+    dv = {k: to_dev(prm[k], dev) for k in ("WK", "UK", "WV", "UV")}
+    vk_t = to_dev(np.ascontiguousarray(prm["VK"].T), dev)
+    vv_t = to_dev(np.ascontiguousarray(prm["VV"].T), dev)
+    anchor = kvc.Codec(H, D, 4, 32, kvc.BASE_NONE)
+    kcod = kvc.Codec(H, D, 2, 32, kvc.BASE_DPLR, rank=r, n_inputs=1)
+    vcod = kvc.Codec(H, D, 2, 32, kvc.BASE_DPLR, rank=r, n_inputs=2)
+
+    def run(two_streams):
+        stores = [(kvc.Store.allocate(anchor if l == 0 else kcod, n, dev),
+                   kvc.Store.allocate(anchor if l == 0 else vcod, n, dev)) for l in range(L)]
+        rec = [[torch.empty((n, H, D), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+               for _ in range(2)]
+        ws_k = kvc.kvc.workspace_for(kvc.kvc.OP_ENCODE, vcod, n, dev)
+        ws_v = kvc.kvc.workspace_for(kvc.kvc.OP_ENCODE, vcod, n, dev) if two_streams else ws_k
+        main = torch.cuda.current_stream()
+        s_v = torch.cuda.Stream(device=dev) if two_streams else main
+        recons = []
+        v_done = []
+        for l in range(L):
+            (k, v), (rk, rv), (pk, pv) = layers[l], rec[l & 1], rec[(l + 1) & 1]
+            if l >= 2:
+                main.wait_event(v_done[l - 2])
+            if l == 0:
+                kvc.kvc_encode(anchor, k, stores[l][0], 0, None, recon_out=rk)
+            else:
+                kvc.kvc_encode(kcod, k, stores[l][0], 0,
+                               kvc.BaseParams(prev0=pk, w_block=dv["WK"], u=dv["UK"], v_lr=vk_t),
+                               recon_out=rk, workspace=ws_k)
+            k_done = torch.cuda.Event()
+            k_done.record(main)
+            with torch.cuda.stream(s_v):
+                s_v.wait_event(k_done)
+                if l == 0:
+                    kvc.kvc_encode(anchor, v, stores[l][1], 0, None, recon_out=rv)
+                else:
+                    kvc.kvc_encode(vcod, v, stores[l][1], 0,
+                                   kvc.BaseParams(prev0=rk, prev1=pv, w_block=dv["WV"], u=dv["UV"],
+                                                  v_lr=vv_t), recon_out=rv, workspace=ws_v)
+                v_done.append(torch.cuda.Event())
+                v_done[l].record(s_v)
+                recons.append(rv.clone())
+        main.wait_event(v_done[-1])
+        torch.cuda.synchronize()
+        return [(store_np(a), store_np(b)) for a, b in stores], [x.cpu() for x in recons]
+
+    one_st, one_rec = run(False)
+    two_st, two_rec = run(True)
+    for (a1, b1), (a2, b2) in zip(one_st, two_st):
+        for key in ("codes", "scale_zero"):
+            assert np.array_equal(a1[key], a2[key]) and np.array_equal(b1[key], b2[key])
+    for x, y in zip(one_rec, two_rec):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
