@@ -157,11 +157,14 @@ struct PredParams {
 // of block ob is channel 32 q + 4 ob + s, so lane (t, q) receives channels 32 q + 4 ob + s.
 __device__ __forceinline__ int out_channel(int ob, int i) { return 32 * (i >> 2) + 4 * ob + (i & 3); }
 
-// LDS geometry: permuted weight rows, U with permuted columns (always 64 + 8 wide,
-// zero past r), then one 16-token staging tile per wave.
-constexpr int URW = 64 + 8;
+// LDS geometry: permuted weight rows, U with permuted columns (64 wide, zero past r),
+// then one 16-token staging tile per wave.  Rows are padded by 16 elements (U rows 40
+// dwords, weight rows 72 or 136) so that the 32 lanes served together by a 16-byte LDS
+// read (rows t = 0..15, column blocks q and q + 1) fall on distinct 4-bank slots.
+constexpr int URW = 64 + 16;
 constexpr int STG = 16 * D;                  // staging tile (bf16 elements)
-__host__ __device__ constexpr int w_elems(int nin) { return 128 * (nin * D + 8); }
+__host__ __device__ constexpr int w_row(int nin) { return nin * D + 16; }
+__host__ __device__ constexpr int w_elems(int nin) { return 128 * w_row(nin); }
 
 // 16-byte loads that give zeros when `ok` is false (a branch, not a select of addresses)
 __device__ __forceinline__ uint4 ld_u4(const void* p, bool ok) {
@@ -184,7 +187,7 @@ __global__ __launch_bounds__(512) void pred_kernel(PredParams p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   constexpr bool MAT = PM == PM_DPLR || PM == PM_TEMPORAL_V;
   constexpr bool LR = PM == PM_DPLR;
-  constexpr int WROW = NIN * D + 8;          // padded weight row (bf16)
+  constexpr int WROW = w_row(NIN);           // padded weight row (bf16)
   constexpr int PER = 32 / BITS;             // codes per word
   constexpr int LW = 32 / PER;               // code words of a lane (32 values)
   constexpr int GL = G < 32 ? G : 32;        // values of one group in a lane
