@@ -482,9 +482,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void encode_shortlist_kernel(EncodePar
 // (accumulator seeded with -|c_j|^2 / 2; the contraction index is permuted so that
 // every lane feeds its own half row), one lane per (token, half) holding 128 of the
 // CM values.  A lane keeps the top three of its values with the centroid's
-// position packed into the low 8 (CM = 256) or 9 (CM = 512) mantissa bits, and merges
-// them with its partner
-// half.  With E >= |v_j - V_j| (the MFMA error, counted at two units in the last
+// position packed into the low 8 (CM = 256) or 9 (CM = 512) mantissa bits (the
+// position within the half replaces the low byte, the half bit goes above it), and
+// merges them with its partner half.  With E >= |v_j - V_j| (the MFMA error, counted at two units in the last
 // place per addition), g = (d + 3) 2^-24 the relative error of the exact fp32
 // distance, and V the true values, d_j > d_w for the exact fp32 distances whenever
 //     (v_w - v_j) - g (|x|^2 - v_w - v_j) > 2 E,
@@ -502,6 +502,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void encode_shortlist_kernel(EncodePar
 // rint(r * rcp(s) - z * rcp(s)); the two agree unless the product lies within
 // (|z / s| + L + 2) 2^-19 of a half-integer, and a group with such an element is
 // redone with the IEEE division.
+// |lo|^2 + |hi|^2 + acc for a packed bf16 pair (v_dot2_f32_bf16; the products are
+// exact in fp32).  Used only for norm bounds, which carry a relative slack of 2^-10.
+__device__ __forceinline__ float sq2_bf16(uint32_t w, float acc) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  const bf2 v = __builtin_bit_cast(bf2, w);
+  return __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
+}
+
 // waves per workgroup of the centroid codec: eight when the LDS allows one workgroup
 // per CU (two waves per SIMD either way)
 __host__ __device__ constexpr int cen_waves(int cm, bool coeff) { return (cm == 512 || coeff) ? 8 : 4; }
@@ -573,8 +581,7 @@ __global__ __launch_bounds__(64 * cen_waves(CM, COEFF), 2 * 4 / cen_waves(CM, CO
           const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            s2 = __builtin_fmaf(lo_bf16(w[k]), lo_bf16(w[k]), s2);
-            s2 = __builtin_fmaf(hi_bf16(w[k]), hi_bf16(w[k]), s2);
+            s2 = sq2_bf16(w[k], s2);
           }
         }
       }
@@ -629,16 +636,23 @@ __global__ __launch_bounds__(64 * cen_waves(CM, COEFF), 2 * 4 / cen_waves(CM, CO
     block_values(cb, acc);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float pv = __uint_as_float((__float_as_uint(acc[r]) & ~TAGM) | (uint32_t)(16 * cb + r));
+      // the position 16 cb + r (< 2^LOCB <= 256) replaces the low byte: one v_perm_b32
+      const float pv = __uint_as_float(
+          __builtin_amdgcn_perm(__float_as_uint(acc[r]), (uint32_t)(16 * cb + r), 0x07060500u));
       m3 = __builtin_amdgcn_fmed3f(m2, m3, pv);
       m2 = __builtin_amdgcn_fmed3f(m1, m2, pv);
-      m1 = fmaxf(m1, pv);
+      // max(m1, pv) for finite values, written as a median so that no canonicalizing
+      // instruction is added for the tag-modified operand
+      m1 = __builtin_amdgcn_fmed3f(m1, pv, 3.40282347e38f);
     }
   }
   // tag the half above the position bits, merge the two halves' top three
-  m1 = __uint_as_float(__float_as_uint(m1) | ((uint32_t)hf << LOCB));
-  m2 = __uint_as_float(__float_as_uint(m2) | ((uint32_t)hf << LOCB));
-  m3 = __uint_as_float(__float_as_uint(m3) | ((uint32_t)hf << LOCB));
+  auto half_tag = [&](float v) {   // bit LOCB := hf (for CM = 256 it is a tag bit, 0)
+    return __uint_as_float((__float_as_uint(v) & ~(1u << LOCB)) | ((uint32_t)hf << LOCB));
+  };
+  m1 = half_tag(m1);
+  m2 = half_tag(m2);
+  m3 = half_tag(m3);
   auto swf = [&](float v) { return __uint_as_float(swap_halves(__float_as_uint(v), hf)); };
   const float b1 = swf(m1), b2 = swf(m2), b3 = swf(m3);
   const float t1 = fmaxf(m1, b1);
@@ -652,8 +666,7 @@ __global__ __launch_bounds__(64 * cen_waves(CM, COEFF), 2 * 4 / cen_waves(CM, CO
     const uint32_t w[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      xs = __builtin_fmaf(lo_bf16(w[k]), lo_bf16(w[k]), xs);
-      xs = __builtin_fmaf(hi_bf16(w[k]), hi_bf16(w[k]), xs);
+      xs = sq2_bf16(w[k], xs);
     }
   }
   const float xxu = (xs + swf(xs)) * (1.0f + 0x1p-10f);
