@@ -546,6 +546,21 @@ __global__ __launch_bounds__(64 * cen_waves(CM, COEFF), 2 * 4 / cen_waves(CM, CO
   const int nb = (C + 31) >> 5;
   const uint16_t* cen = reinterpret_cast<const uint16_t*>(p.centroids) + (int64_t)h * C * D;
 
+  // this lane's half row of a tile's token (zeros past the last token); the first
+  // tile's rows are requested before the table is staged, each next tile's while the
+  // current one is encoded
+  auto load_half_row = [&](int tl, uint4 (&dst)[8]) {
+    const int64_t nn = (int64_t)tl * TT + wave * 32 + t;
+    const bool lv = tl < ntile && nn < p.n_tokens;
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(p.x) + (lv ? nn : 0) * p.x_stride +
+                          (int64_t)h * D + 64 * hf;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      dst[i] = lv ? *reinterpret_cast<const uint4*>(src + 8 * i) : make_uint4(0u, 0u, 0u, 0u);
+  };
+  uint4 xv[8];
+  load_half_row(first, xv);
+
   // 1. the head's centroid table (rows C .. 32 nb - 1 zero), row norms, the basis
 #pragma unroll
   for (int half16 = 0; half16 < (CM + NT - 1) / NT; ++half16) {   // rounds of 16 pieces a thread
@@ -603,15 +618,8 @@ __global__ __launch_bounds__(64 * cen_waves(CM, COEFF), 2 * 4 / cen_waves(CM, CO
   for (int tile = first; tile < ntile; tile += wph) {
   const int64_t n = (int64_t)tile * TT + wave * 32 + t;
   const bool live = n < p.n_tokens;
-  // this lane's half row
-  uint4 xv[8];
-  {
-    const uint16_t* src = reinterpret_cast<const uint16_t*>(p.x) + (live ? n : 0) * p.x_stride +
-                          (int64_t)h * D + 64 * hf;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      xv[i] = live ? *reinterpret_cast<const uint4*>(src + 8 * i) : make_uint4(0u, 0u, 0u, 0u);
-  }
+  uint4 xnext[8];
+  load_half_row(tile + wph, xnext);
 
   // 2. v_j for the 128 centroids of this half; top three with packed positions
   float m1 = -3.0e38f, m2 = -3.0e38f, m3 = -3.0e38f;
@@ -920,6 +928,8 @@ __global__ __launch_bounds__(64 * cen_waves(CM, COEFF), 2 * 4 / cen_waves(CM, CO
     if (hf == 0) store_index(row);
   }
   }   // !COEFF
+#pragma unroll
+  for (int i = 0; i < 8; ++i) xv[i] = xnext[i];
   }   // tiles
 }
 
