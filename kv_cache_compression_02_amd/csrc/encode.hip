@@ -639,9 +639,7 @@ __global__ __launch_bounds__(64 * cen_waves(CM, COEFF), 2 * 4 / cen_waves(CM, CO
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bx, acc, 0, 0, 0);
     }
   };
-  for (int cb = 0; cb < nb; ++cb) {
-    f32x16_t acc;
-    block_values(cb, acc);
+  auto top3 = [&](const f32x16_t& acc, int cb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       // the position 16 cb + r (< 2^LOCB <= 256) replaces the low byte: one v_perm_b32
@@ -652,6 +650,26 @@ __global__ __launch_bounds__(64 * cen_waves(CM, COEFF), 2 * 4 / cen_waves(CM, CO
       // max(m1, pv) for finite values, written as a median so that no canonicalizing
       // instruction is added for the tag-modified operand
       m1 = __builtin_amdgcn_fmed3f(m1, pv, 3.40282347e38f);
+    }
+  };
+  // software-pipelined over the blocks: the MFMAs of block cb+1 are issued among the
+  // top-three updates of block cb (two accumulators, the loop body one basic block)
+  {
+    f32x16_t acc0, acc1;
+    block_values(0, acc0);
+    int cb = 0;
+    for (; cb + 2 < nb; cb += 2) {
+      block_values(cb + 1, acc1);
+      top3(acc0, cb);
+      block_values(cb + 2, acc0);
+      top3(acc1, cb + 1);
+    }
+    if (cb + 1 < nb) {
+      block_values(cb + 1, acc1);
+      top3(acc0, cb);
+      top3(acc1, cb + 1);
+    } else {
+      top3(acc0, cb);
     }
   }
   // tag the half above the position bits, merge the two halves' top three
