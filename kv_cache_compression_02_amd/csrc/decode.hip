@@ -4,9 +4,9 @@
 // compressed state holds (Coral-KV arXiv 2610.12514 Table 9 caption); adding the
 // dequantized residual to the base gives the reconstruction (Coral-KV Fig. 3).
 //
-// One thread per (token, head, 8 consecutive channels): loads its code bits, the
-// group's scale/zero word and 16 bytes of the base row, writes 8 outputs with one
-// vector store.  HBM-bound streaming kernel.
+// One thread per (token, head, 16 consecutive channels): loads its code words, the
+// group's scale/zero word and 32 bytes of the base row, writes 16 outputs with 16-byte
+// vector stores.  HBM-bound streaming kernel.
 #include "kvc_device.h"
 #include "kvc_internal.h"
 
@@ -17,6 +17,8 @@ namespace {
 struct DecodeParams {
   int64_t n_tokens, token_offset, capacity;
   int H, D, C, bits, group, groups, code_words, index_bytes, mode;
+  uint32_t total;      // threads of this launch: n_tokens * H * (D / 16) < 2^31
+  int cshift, gshift;  // log2(D / 16), log2(group)
   const uint32_t* codes;
   const uint32_t* sz;
   const void* index;
@@ -33,99 +35,131 @@ struct DecodeParams {
 
 enum { DM_NONE = 0, DM_CENTROID = 1, DM_TEMPORAL_K = 3, DM_BUFFER = 4 };
 
+// 16 consecutive values of a row in dtype XT (16-byte aligned) as fp32.
+template <typename XT>
+__device__ __forceinline__ void load16(const XT* src, float (&v)[16]) {
+  if constexpr (sizeof(XT) == 2) {
+    const uint4 a = *reinterpret_cast<const uint4*>(src);
+    const uint4 b = *reinterpret_cast<const uint4*>(src + 8);
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      v[2 * k] = bf16_bits_to_f32(w[k] & 0xFFFFu);
+      v[2 * k + 1] = bf16_bits_to_f32(w[k] >> 16);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float4 u = *reinterpret_cast<const float4*>(src + 4 * k);
+      v[4 * k] = u.x; v[4 * k + 1] = u.y; v[4 * k + 2] = u.z; v[4 * k + 3] = u.w;
+    }
+  }
+}
+
+// One thread per (token, head, 16 consecutive channels): the 16 codes are one (INT2)
+// or two (INT4) aligned words, the channels share one scale/zero word (groups are >= 16
+// wide), and the outputs go out as 16-byte stores, consecutive threads writing
+// consecutive pieces of the token-major output rows.
 template <typename XT, typename OT>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
-  const int64_t chunks_per_vec = p.D / 8;
-  const int64_t total = p.n_tokens * p.H * chunks_per_vec;
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= total) return;
-  const int c8 = (int)(e % chunks_per_vec);
-  const int64_t nh = e / chunks_per_vec;
-  const int h = (int)(nh % p.H);
-  const int64_t n = nh / p.H;
-  const int i0 = c8 * 8;
+  const uint32_t e = blockIdx.x * 256u + threadIdx.x;
+  if (e >= p.total) return;
+  const uint32_t c16 = e & ((1u << p.cshift) - 1u);
+  const uint32_t nh = e >> p.cshift;
+  const uint32_t n = nh / (uint32_t)p.H;
+  const uint32_t h = nh - n * (uint32_t)p.H;
+  const int i0 = (int)c16 * 16;
   const int64_t row = (int64_t)h * p.capacity + p.token_offset + n;
 
-  // scale / zero of the group holding channels i0..i0+7 (groups are >= 16 wide)
-  const uint32_t szw = p.sz[row * p.groups + i0 / p.group];
+  const uint32_t szw = p.sz[row * p.groups + (i0 >> p.gshift)];
   const float s = f16_bits_to_f32(szw & 0xFFFFu);
   const float z = f16_bits_to_f32(szw >> 16);
-  // 8 codes = 8*bits consecutive bits starting at bit i0*bits
-  const int bitpos = i0 * p.bits;
-  const uint32_t word = p.codes[row * p.code_words + bitpos / 32];
-  const uint32_t bits8 = word >> (bitpos % 32);
-  const uint32_t mask = (1u << p.bits) - 1u;
+  const uint32_t* cw = p.codes + row * p.code_words + (int64_t)c16 * (p.bits >> 1);
+  const uint32_t w0 = cw[0];
+  const uint32_t w1 = p.bits == 4 ? cw[1] : 0u;
 
-  float base[8];
+  float base[16];
   if (p.mode == DM_CENTROID) {
     int a = p.index_bytes == 1 ? reinterpret_cast<const uint8_t*>(p.index)[row]
                                : reinterpret_cast<const uint16_t*>(p.index)[row];
     a = min(a, p.C - 1);   // out-of-contract indices must not read past the table
-    const XT* crow = reinterpret_cast<const XT*>(p.centroids) + ((int64_t)h * p.C + a) * p.D + i0;
-    if constexpr (sizeof(XT) == 2) {   // one 16-byte read of 8 bf16 values
-      const uint4 w = *reinterpret_cast<const uint4*>(crow);
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        base[2 * k] = bf16_bits_to_f32(ww[k] & 0xFFFFu);
-        base[2 * k + 1] = bf16_bits_to_f32(ww[k] >> 16);
-      }
-    } else {                           // two 16-byte reads of 8 fp32 values
-      const float4 u0 = *reinterpret_cast<const float4*>(crow);
-      const float4 u1 = *reinterpret_cast<const float4*>(crow + 4);
-      base[0] = u0.x; base[1] = u0.y; base[2] = u0.z; base[3] = u0.w;
-      base[4] = u1.x; base[5] = u1.y; base[6] = u1.z; base[7] = u1.w;
-    }
+    load16<XT>(reinterpret_cast<const XT*>(p.centroids) + ((int64_t)h * p.C + a) * p.D + i0, base);
   } else if (p.mode == DM_TEMPORAL_K) {
-    const XT* p0 = reinterpret_cast<const XT*>(p.prev0) + n * p.prev_stride + (int64_t)h * p.D + i0;
-    const XT* p1 = reinterpret_cast<const XT*>(p.prev1) + n * p.prev_stride + (int64_t)h * p.D + i0;
+    float x0[16], x1[16];
+    load16<XT>(reinterpret_cast<const XT*>(p.prev0) + (int64_t)n * p.prev_stride + (int64_t)h * p.D + i0, x0);
+    load16<XT>(reinterpret_cast<const XT*>(p.prev1) + (int64_t)n * p.prev_stride + (int64_t)h * p.D + i0, x1);
+    float ca[16], cb[16];
+    load16<float>(p.coef_a + h * p.D + i0, ca);
+    load16<float>(p.coef_b + h * p.D + i0, cb);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      float a = p.coef_a[h * p.D + i0 + k] * load_x<XT>(p0 + k);
-      float b = p.coef_b[h * p.D + i0 + k] * load_x<XT>(p1 + k);
+    for (int k = 0; k < 16; ++k) {
+      const float a = ca[k] * x0[k];
+      const float b = cb[k] * x1[k];
       base[k] = a + b;
     }
   } else if (p.mode == DM_BUFFER) {
-    const float* bb = p.base_buf + (n * p.H + h) * (int64_t)p.D + i0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) base[k] = bb[k];
+    load16<float>(p.base_buf + ((int64_t)n * p.H + h) * p.D + i0, base);
   } else {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) base[k] = 0.0f;
+    for (int k = 0; k < 16; ++k) base[k] = 0.0f;
   }
 
-  const int64_t orow = (n * p.H + h) * (int64_t)p.D + i0;
-  OT* out = reinterpret_cast<OT*>(p.out) + orow;
-  float v[8];
+  const int64_t orow = ((int64_t)n * p.H + h) * p.D + i0;
+  float v[16];
+  const uint32_t mask = (1u << p.bits) - 1u;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const uint32_t code = (bits8 >> (p.bits * k)) & mask;
+  for (int k = 0; k < 16; ++k) {
+    const int bit = p.bits * k;   // 0..60
+    const uint32_t code = ((bit < 32 ? (w0 >> bit) : (w1 >> (bit - 32)))) & mask;
     v[k] = base[k] + dequant_one(code, s, z);
   }
-  if constexpr (sizeof(OT) == 2) {     // 8 bf16 (round to nearest even): one 16-byte store
-    uint32_t o[4];
+  OT* out = reinterpret_cast<OT*>(p.out) + orow;
+  if constexpr (sizeof(OT) == 2) {     // 16 bf16 (round to nearest even): two 16-byte stores
+    uint32_t o[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = f32_to_bf16_bits(v[2 * k]) | (f32_to_bf16_bits(v[2 * k + 1]) << 16);
+    for (int k = 0; k < 8; ++k) o[k] = f32_to_bf16_bits(v[2 * k]) | (f32_to_bf16_bits(v[2 * k + 1]) << 16);
     *reinterpret_cast<uint4*>(out) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(out + 8) = make_uint4(o[4], o[5], o[6], o[7]);
   } else {
-    *reinterpret_cast<float4*>(out) = make_float4(v[0], v[1], v[2], v[3]);
-    *reinterpret_cast<float4*>(out + 4) = make_float4(v[4], v[5], v[6], v[7]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      *reinterpret_cast<float4*>(out + 4 * k) = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
   }
   if (p.pred && p.mode != DM_BUFFER) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) p.pred[orow + k] = base[k];
+    for (int k = 0; k < 4; ++k)
+      *reinterpret_cast<float4*>(p.pred + orow + 4 * k) =
+          make_float4(base[4 * k], base[4 * k + 1], base[4 * k + 2], base[4 * k + 3]);
   }
 }
 
+// Launches in token ranges whose thread count stays below 2^31 (32-bit indexing in
+// the kernel); every pointer that is indexed by the token moves with the range.
 template <typename XT>
-hipError_t launch_decode_x(const DecodeParams& p, int out_dtype, hipStream_t s) {
-  const int64_t total = p.n_tokens * p.H * (p.D / 8);
-  dim3 grid((unsigned)((total + 255) / 256));
-  if (out_dtype == KVC_BF16)
-    hipLaunchKernelGGL((decode_kernel<XT, uint16_t>), grid, dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((decode_kernel<XT, float>), grid, dim3(256), 0, s, p);
-  return hipGetLastError();
+hipError_t launch_decode_x(const DecodeParams& p0, int out_dtype, hipStream_t s) {
+  const int64_t per_token = (int64_t)p0.H * (p0.D / 16);
+  const int64_t step = std::max<int64_t>(1, ((int64_t)1 << 31) / per_token - 256);
+  const int osz = out_dtype == KVC_BF16 ? 2 : 4;
+  for (int64_t t0 = 0; t0 < p0.n_tokens; t0 += step) {
+    DecodeParams p = p0;
+    p.n_tokens = std::min(step, p0.n_tokens - t0);
+    p.token_offset = p0.token_offset + t0;
+    p.total = (uint32_t)(p.n_tokens * per_token);
+    const int64_t elems = t0 * p0.H * p0.D;
+    p.out = reinterpret_cast<char*>(p0.out) + elems * osz;
+    if (p0.pred) p.pred = p0.pred + elems;
+    if (p0.base_buf) p.base_buf = p0.base_buf + elems;
+    if (p0.prev0) p.prev0 = reinterpret_cast<const XT*>(p0.prev0) + t0 * p0.prev_stride;
+    if (p0.prev1) p.prev1 = reinterpret_cast<const XT*>(p0.prev1) + t0 * p0.prev_stride;
+    const dim3 grid((p.total + 255u) / 256u);
+    if (out_dtype == KVC_BF16)
+      hipLaunchKernelGGL((decode_kernel<XT, uint16_t>), grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((decode_kernel<XT, float>), grid, dim3(256), 0, s, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -157,6 +191,10 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t s) {
   p.coef_b = a.b.coef_b;
   p.out = a.out;
   p.pred = a.pred;
+  p.cshift = __builtin_ctz((unsigned)(a.c.D / 16));
+  p.gshift = __builtin_ctz((unsigned)a.c.group);
+  if (a.c.D % 16 != 0 || (a.c.group & (a.c.group - 1)) != 0 || a.c.group < 16 || (a.c.bits != 2 && a.c.bits != 4))
+    return hipErrorInvalidValue;
   switch (a.c.base) {
     case KVC_BASE_NONE: p.mode = DM_NONE; break;
     case KVC_BASE_CENTROID: p.mode = DM_CENTROID; break;
