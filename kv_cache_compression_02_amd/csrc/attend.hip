@@ -116,6 +116,15 @@ constexpr int VROW = BK + 16;    // V^T tile row (fp16 elements), padded to 40 d
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ float byte_f(uint32_t x, int k) { return (float)((x >> (8 * k)) & 0xFFu); }
+// A code held in a 16-bit half of w, read as the f16 denormal q * 2^-24.  v_fma_mix_f32
+// widens it exactly, so fma(code_lo(w), s * 2^24, z) == fma(q, s, z) bit for bit (s an
+// fp16 value, s * 2^24 exact in fp32): one instruction per code, no integer conversion.
+__device__ __forceinline__ float code_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float code_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
   typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
   bf2 v = {(__bf16)a, (__bf16)b};   // v_cvt_pk_bf16_f32: round to nearest even
@@ -228,6 +237,8 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
   const int vword = (8 * c8 * VBITS) >> 5;
   const int vgrp = (8 * c8) / p.v.group;
   const int vsh = (8 * c8 * VBITS) & 31;          // bit offset of the 8 codes in their word
+  // INT2 V: byte selector that puts the two keys' 16 code bits side by side
+  const uint32_t vsel = vsh ? 0x07060302u : 0x05040100u;
   // index entries are read as the aligned dword holding them (k0 is a multiple of 64, so
   // the shift within the dword depends on the thread only)
   const uint32_t kimask = p.k.idxb == 1 ? 0xFFu : 0xFFFFu, vimask = p.v.idxb == 1 ? 0xFFu : 0xFFFFu;
@@ -346,34 +357,31 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
       }
     } else {
     // ---- K: 16 consecutive channels of key kk -> row-major bf16
-      const float sc = f16_bits_to_f32(kpr.sz & 0xFFFFu), ze = f16_bits_to_f32(kpr.sz >> 16);
-      float q[16];
+      const float s24 = f16_bits_to_f32(kpr.sz & 0xFFFFu) * 0x1p24f, ze = f16_bits_to_f32(kpr.sz >> 16);
+      float dq[16];   // code * s + z per channel
       if constexpr (BITS == 2) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          uint32_t b = (kpr.code[0] >> (2 * r)) & 0x03030303u;   // codes r, r+4, r+8, r+12
-          // keep b opaque so each code converts with one v_cvt_f32_ubyteN (rather than
-          // a bit-field extract per code followed by a conversion)
-          asm volatile("" : "+v"(b));
-#pragma unroll
-          for (int k = 0; k < 4; ++k) q[r + 4 * k] = byte_f(b, k);
+        for (int r = 0; r < 8; ++r) {
+          const uint32_t b = (kpr.code[0] >> (2 * r)) & 0x00030003u;   // codes r, r+8
+          dq[r] = __builtin_fmaf(code_lo(b), s24, ze);
+          dq[r + 8] = __builtin_fmaf(code_hi(b), s24, ze);
         }
       } else {
 #pragma unroll
         for (int wd = 0; wd < 2; ++wd)
 #pragma unroll
-          for (int r = 0; r < 2; ++r) {
-            const uint32_t b = (kpr.code[wd] >> (4 * r)) & 0x0F0F0F0Fu;  // codes r, r+2, r+4, r+6
-#pragma unroll
-            for (int k = 0; k < 4; ++k) q[8 * wd + r + 2 * k] = byte_f(b, k);
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t b = (kpr.code[wd] >> (4 * r)) & 0x000F000Fu;   // codes r, r+4 of word wd
+            dq[8 * wd + r] = __builtin_fmaf(code_lo(b), s24, ze);
+            dq[8 * wd + r + 4] = __builtin_fmaf(code_hi(b), s24, ze);
           }
       }
       const uint32_t cw[8] = {kpr.c0.x, kpr.c0.y, kpr.c0.z, kpr.c0.w, kpr.c1.x, kpr.c1.y, kpr.c1.z, kpr.c1.w};
       uint32_t o[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float x0 = lo_bf16(cw[i]) + __builtin_fmaf(q[2 * i], sc, ze);
-        const float x1 = hi_bf16(cw[i]) + __builtin_fmaf(q[2 * i + 1], sc, ze);
+        const float x0 = lo_bf16(cw[i]) + dq[2 * i];
+        const float x1 = hi_bf16(cw[i]) + dq[2 * i + 1];
         o[i] = pk_bf16(x0, x1);
       }
       uint4* dst = reinterpret_cast<uint4*>(&k_lds[buf][kk * KR + 16 * kw]);
@@ -383,32 +391,39 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
     // ---- V: channels 8c8..8c8+7 of keys 2kp, 2kp+1 -> transposed fp16 (swizzled)
     {
       float x[2][8];   // [key j][channel c]
+      float dq[2][8];  // code * s + z
+      float s24[2], ze[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const float sc = f16_bits_to_f32(vp.sz[j] & 0xFFFFu), ze = f16_bits_to_f32(vp.sz[j] >> 16);
-        float q[8];
-        if constexpr (VBITS == 2) {
-          const uint32_t w = vp.code[j] >> vsh;               // 8 codes in bits 0..15
+        s24[j] = f16_bits_to_f32(vp.sz[j] & 0xFFFFu) * 0x1p24f;
+        ze[j] = f16_bits_to_f32(vp.sz[j] >> 16);
+      }
+      if constexpr (VBITS == 2) {
+        // the two keys' 8 codes side by side (key 0 low half, key 1 high half)
+        const uint32_t w = __builtin_amdgcn_perm(vp.code[1], vp.code[0], vsel);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const uint32_t b = (w >> (2 * r)) & 0x00030003u;     // channel r of both keys
+          dq[0][r] = __builtin_fmaf(code_lo(b), s24[0], ze[0]);
+          dq[1][r] = __builtin_fmaf(code_hi(b), s24[1], ze[1]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const uint32_t b = (w >> (2 * r)) & 0x0303u;       // codes r, r+4
-            q[r] = byte_f(b, 0);
-            q[r + 4] = byte_f(b, 1);
+            const uint32_t b = (vp.code[j] >> (4 * r)) & 0x000F000Fu;   // channels r, r+4
+            dq[j][r] = __builtin_fmaf(code_lo(b), s24[j], ze[j]);
+            dq[j][r + 4] = __builtin_fmaf(code_hi(b), s24[j], ze[j]);
           }
-        } else {
-          const uint32_t w = vp.code[j];                       // 8 codes in bits 0..31
+      }
 #pragma unroll
-          for (int r = 0; r < 2; ++r) {
-            const uint32_t b = (w >> (4 * r)) & 0x0F0F0F0Fu;   // codes r, r+2, r+4, r+6
-#pragma unroll
-            for (int k = 0; k < 4; ++k) q[r + 2 * k] = byte_f(b, k);
-          }
-        }
+      for (int j = 0; j < 2; ++j) {
         const uint32_t cw[4] = {vp.c[j].x, vp.c[j].y, vp.c[j].z, vp.c[j].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          x[j][2 * i] = lo_bf16(cw[i]) + __builtin_fmaf(q[2 * i], sc, ze);
-          x[j][2 * i + 1] = hi_bf16(cw[i]) + __builtin_fmaf(q[2 * i + 1], sc, ze);
+          x[j][2 * i] = lo_bf16(cw[i]) + dq[j][2 * i];
+          x[j][2 * i + 1] = hi_bf16(cw[i]) + dq[j][2 * i + 1];
         }
       }
 #pragma unroll
