@@ -538,15 +538,18 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
     // (one 16-byte read each: row 32 d + col, block (2 kh + half) ^ (2 d + col / 16) =
     // 2 (kh ^ d) + (half ^ col / 16)); (kb, hf) = kh covers keys 32*kb + 16*hf +
     // {4*half+0..3, 8+4*half+0..3}
+    // (the mixed-dimensional kernel, which holds B^T q as well, reads the last two
+    // channel blocks during the PV MFMAs instead, to stay within 256 registers)
+    constexpr int VE = MIXED ? 2 : 4;   // channel blocks read before the softmax
     f16x8_t vf[4][4];
-    {
-      const uint16_t* vbase = &v_lds[buf][col * VROW + 8 * (half ^ (col >> 4))];
+    const uint16_t* vbase = &v_lds[buf][col * VROW + 8 * (half ^ (col >> 4))];
+    auto read_vf = [&](int d) {
 #pragma unroll
-      for (int d = 0; d < 4; ++d)
+      for (int kh = 0; kh < 4; ++kh)
+        vf[d][kh] = *reinterpret_cast<const f16x8_t*>(vbase + 32 * d * VROW + 16 * (kh ^ d));
+    };
 #pragma unroll
-        for (int kh = 0; kh < 4; ++kh)
-          vf[d][kh] = *reinterpret_cast<const f16x8_t*>(vbase + 32 * d * VROW + 16 * (kh ^ d));
-    }
+    for (int d = 0; d < VE; ++d) read_vf(d);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (MIXED) {   // + (B^T q) . c: hi*hi + hi*lo + lo*hi
 #pragma unroll
@@ -615,6 +618,7 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
     // O^T += V^T P^T
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
+      if (d + VE < 4) read_vf(d + VE);
 #pragma unroll
       for (int kh = 0; kh < 4; ++kh)
         oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[d][kh], pb[kh >> 1][kh & 1], oacc[d], 0, 0, 0);
