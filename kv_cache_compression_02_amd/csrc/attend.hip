@@ -318,7 +318,66 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
       }
     }
   };
-  auto dequant = [&](const KPre<BITS>& kpr, const VPre& vp, int buf) {
+  // Pieces of load_idx / load_data for the centroid/plain kernels, whose K decode runs
+  // among the score MFMAs: the K and V prefetches (and their index words) are issued at
+  // different points of a tile, each one tile ahead of its use.
+  auto load_kidx = [&](int t, int& ki) {
+    if constexpr (KCEN)
+      ki = (int)__builtin_amdgcn_raw_buffer_load_b32(rk_idx, (((uint32_t)(t * BK) + kk) * p.k.idxb) & ~3u, 0, 0);
+    else
+      ki = 0;
+  };
+  auto load_vidx = [&](int t, int (&vi)[2]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if constexpr (VCEN)
+        vi[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(
+            rv_idx, (((uint32_t)(t * BK) + 2 * kp + j) * p.v.idxb) & ~3u, 0, 0);
+      else
+        vi[j] = 0;
+    }
+  };
+  auto load_k = [&](int t, int ki, KPre<BITS>& kpr) {
+    const uint32_t n = (uint32_t)(t * BK) + kk;
+    if constexpr (BITS == 2) {
+      kpr.code[0] = __builtin_amdgcn_raw_buffer_load_b32(rk_code, n * kwb + kword * 4, 0, 0);
+    } else {
+      typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+      const u2 c = __builtin_amdgcn_raw_buffer_load_b64(rk_code, n * kwb + kword * 4, 0, 0);
+      kpr.code[0] = c.x;
+      kpr.code[1] = c.y;
+    }
+    kpr.sz = __builtin_amdgcn_raw_buffer_load_b32(rk_sz, n * kgb + kgrp * 4, 0, 0);
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    if constexpr (KCEN) {
+      const uint32_t off = idx_of((uint32_t)ki, kish, kimask, p.k.C) * (DM * 2) + 32 * kw;
+      const u4 a0 = __builtin_amdgcn_raw_buffer_load_b128(rk_cen, off, 0, 0);
+      const u4 a1 = __builtin_amdgcn_raw_buffer_load_b128(rk_cen, off + 16, 0, 0);
+      kpr.c0 = uint4{a0.x, a0.y, a0.z, a0.w};
+      kpr.c1 = uint4{a1.x, a1.y, a1.z, a1.w};
+    } else {
+      kpr.c0 = uint4{0u, 0u, 0u, 0u};
+      kpr.c1 = kpr.c0;
+    }
+  };
+  auto load_v = [&](int t, const int (&vi)[2], VPre& vp) {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t m = (uint32_t)(t * BK) + 2 * kp + j;
+      vp.code[j] = __builtin_amdgcn_raw_buffer_load_b32(rv_code, m * vwb + vword * 4, 0, 0);
+      vp.sz[j] = __builtin_amdgcn_raw_buffer_load_b32(rv_sz, m * vgb + vgrp * 4, 0, 0);
+      if constexpr (VCEN) {
+        const uint32_t off =
+            idx_of((uint32_t)vi[j], j ? vish1 : vish0, vimask, p.v.C) * (DM * 2) + 16 * c8;
+        const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rv_cen, off, 0, 0);
+        vp.c[j] = uint4{a.x, a.y, a.z, a.w};
+      } else {
+        vp.c[j] = uint4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto dequant = [&](const KPre<BITS>& kpr, const VPre& vp, int buf, bool do_k = true) {
     if constexpr (DENSE) {
       uint4* dst = reinterpret_cast<uint4*>(&k_lds[buf][kk * KR + 16 * kw]);
       dst[0] = kpr.c0;
@@ -357,6 +416,7 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
       }
     } else {
     // ---- K: 16 consecutive channels of key kk -> row-major bf16
+     if (do_k) {
       const float s24 = f16_bits_to_f32(kpr.sz & 0xFFFFu) * 0x1p24f, ze = f16_bits_to_f32(kpr.sz >> 16);
       float dq[16];   // code * s + z per channel
       if constexpr (BITS == 2) {
@@ -387,6 +447,7 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
       uint4* dst = reinterpret_cast<uint4*>(&k_lds[buf][kk * KR + 16 * kw]);
       dst[0] = uint4{o[0], o[1], o[2], o[3]};
       dst[1] = uint4{o[4], o[5], o[6], o[7]};
+     }
     }
     // ---- V: channels 8c8..8c8+7 of keys 2kp, 2kp+1 -> transposed fp16 (swizzled)
     {
@@ -497,9 +558,54 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
   float l_run = 0.0f;
   const float c2 = p.scale_log2;
 
+  // prefetch state: the next tile's compressed rows, the index words of the one after
+  KPre<BITS> kpre;
+  VPre vpre;
+  int kidx, vidx[2];
+
+  // The K decode of the next tile cut into 16 steps, one per score MFMA: steps 0..7
+  // dequantize two channels each (codes as f16 denormals through v_fma_mix), steps
+  // 8..15 add the centroid and round one channel pair, step 15 stores the row.
+  struct KDec {
+    float s24, ze, dq[16];
+    uint32_t o[8];
+  };
+  auto kstep = [&](int j, KDec& st, const KPre<BITS>& kpr, int dbuf) {
+    if (j == 0) {
+      st.s24 = f16_bits_to_f32(kpr.sz & 0xFFFFu) * 0x1p24f;
+      st.ze = f16_bits_to_f32(kpr.sz >> 16);
+    }
+    if (j < 8) {
+      if constexpr (BITS == 2) {
+        const uint32_t b = (kpr.code[0] >> (2 * j)) & 0x00030003u;   // codes j, j+8
+        st.dq[j] = __builtin_fmaf(code_lo(b), st.s24, st.ze);
+        st.dq[j + 8] = __builtin_fmaf(code_hi(b), st.s24, st.ze);
+      } else {
+        const int wd = j >> 2, r = j & 3;
+        const uint32_t b = (kpr.code[wd] >> (4 * r)) & 0x000F000Fu;   // codes r, r+4 of word wd
+        st.dq[8 * wd + r] = __builtin_fmaf(code_lo(b), st.s24, st.ze);
+        st.dq[8 * wd + r + 4] = __builtin_fmaf(code_hi(b), st.s24, st.ze);
+      }
+    } else {
+      const int i = j - 8;
+      const uint32_t cwi = (i < 4) ? (i == 0 ? kpr.c0.x : i == 1 ? kpr.c0.y : i == 2 ? kpr.c0.z : kpr.c0.w)
+                                   : (i == 4 ? kpr.c1.x : i == 5 ? kpr.c1.y : i == 6 ? kpr.c1.z : kpr.c1.w);
+      st.o[i] = pk_bf16(lo_bf16(cwi) + st.dq[2 * i], hi_bf16(cwi) + st.dq[2 * i + 1]);
+      if (j == 15) {
+        uint4* dst = reinterpret_cast<uint4*>(&k_lds[dbuf][kk * KR + 16 * kw]);
+        dst[0] = uint4{st.o[0], st.o[1], st.o[2], st.o[3]};
+        dst[1] = uint4{st.o[4], st.o[5], st.o[6], st.o[7]};
+      }
+    }
+  };
+
   // MASK: the tile runs past the last key (only the final tile of a ragged history)
-  auto compute = [&](int t, int buf, auto mask_tag) {
+  // KDEC: the next tile's K rows are decoded among the score MFMAs (hard scheduling
+  // fences keep one decode step after each MFMA, so the wave's VALU work issues while
+  // its MFMAs run), then tile t+2's K rows and tile t+3's K index words are requested.
+  auto compute = [&](int t, int buf, auto mask_tag, auto kdec_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool KDEC = decltype(kdec_tag)::value;
     const int k0 = t * BK;
     // S^T = K Q^T (raw scores)
     // K fragments stream through two groups of 4 registers: the reads of group g+1
@@ -513,6 +619,29 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
     bf16x8_t kf[2][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) kf[0][i] = *reinterpret_cast<const bf16x8_t*>(krow + 16 * i);
+    if constexpr (KDEC) {
+      KDec st;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {   // g: (kb, ks half) = (g >> 1, g & 1)
+        if (g + 1 < 4) {
+          const int kb1 = (g + 1) >> 1, k1 = 4 * ((g + 1) & 1);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            kf[(g + 1) & 1][i] =
+                *reinterpret_cast<const bf16x8_t*>(krow + kb1 * 32 * KR + 16 * (k1 + i));
+        }
+        const int kb = g >> 1, k0s = 4 * (g & 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[g & 1][i], qreg[k0s + i], sacc[kb], 0, 0, 0);
+          kstep(4 * g + i, st, kpre, buf ^ 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (t + 2 < te) load_k(t + 2, kidx, kpre);
+      if (t + 3 < te) load_kidx(t + 3, kidx);
+    } else {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {   // g: (kb, ks half) = (g >> 1, g & 1)
       if (g + 1 < 4) {
@@ -534,6 +663,7 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
       if (g < 2) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
     // all V^T fragments of the tile are read now, so they arrive during the softmax
     // (one 16-byte read each: row 32 d + col, block (2 kh + half) ^ (2 d + col / 16) =
     // 2 (kh ^ d) + (half ^ col / 16)); (kb, hf) = kh covers keys 32*kb + 16*hf +
@@ -627,9 +757,6 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
 
   // ---- prologue: first tile decoded into buffer 0, the next prefetched, indices of
   //      the one after
-  KPre<BITS> kpre;
-  VPre vpre;
-  int kidx, vidx[2];
   load_idx(tb, kidx, vidx);
   load_data(tb, kidx, vidx, kpre, vpre);
   if (tb + 1 < te) load_idx(tb + 1, kidx, vidx);
@@ -643,17 +770,34 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
   // the final tile of a ragged history (the only one that masks keys) runs after the
   // loop, so the loop body has one variant
   const int tfull = (te * BK > nk) ? te - 1 : te;
-  for (int t = tb; t < tfull; ++t) {
-    const int buf = (t - tb) & 1;
-    if (t + 1 < te) {
-      dequant(kpre, vpre, buf ^ 1);
-      if (t + 2 < te) load_data(t + 2, kidx, vidx, kpre, vpre);
-      if (t + 3 < te) load_idx(t + 3, kidx, vidx);
+  if constexpr (!DENSE && !MIXED) {
+    // V decode first, K decode among the score MFMAs (see compute)
+    int t = tb;
+    for (; t < min(tfull, te - 1); ++t) {
+      const int buf = (t - tb) & 1;
+      dequant(kpre, vpre, buf ^ 1, false);
+      if (t + 2 < te) load_v(t + 2, vidx, vpre);
+      if (t + 3 < te) load_vidx(t + 3, vidx);
+      compute(t, buf, std::false_type{}, std::true_type{});
+      __syncthreads();
     }
-    compute(t, buf, std::false_type{});
-    __syncthreads();
+    if (t < tfull) {   // the last tile, complete: nothing left to decode
+      compute(t, (t - tb) & 1, std::false_type{}, std::false_type{});
+      __syncthreads();
+    }
+  } else {
+    for (int t = tb; t < tfull; ++t) {
+      const int buf = (t - tb) & 1;
+      if (t + 1 < te) {
+        dequant(kpre, vpre, buf ^ 1);
+        if (t + 2 < te) load_data(t + 2, kidx, vidx, kpre, vpre);
+        if (t + 3 < te) load_idx(t + 3, kidx, vidx);
+      }
+      compute(t, buf, std::false_type{}, std::false_type{});
+      __syncthreads();
+    }
   }
-  if (tfull < te) compute(tfull, (tfull - tb) & 1, std::true_type{});
+  if (tfull < te) compute(tfull, (tfull - tb) & 1, std::true_type{}, std::false_type{});
 
   // ---- epilogue: O[q][h][c] = O^T[c][q] / l (a split's partial output when splitting)
   float* const outp = p.splits > 1 ? p.part_o + (int64_t)split * p.nq * p.H * DM : p.out;
