@@ -193,7 +193,9 @@ kvc_status kvc_decode(const kvc_codec* codec, const kvc_store* src, int64_t toke
  *     same softmax, summed in another order); NULL, or a smaller workspace, runs one
  *     pass over the keys.  The contents are overwritten.
  * Errors: KVC_E_NULL, KVC_E_SHAPE (n_keys > capacity, n_keys < 1, mismatched
- * heads/d), KVC_E_UNSUPPORTED, KVC_E_ALIGN, KVC_E_DEVICE. */
+ * heads/d; bf16 path: a store whose per-head code or scale/zero rows span 2 GiB or
+ * more, or a dense cache of 2 GiB or more - the kernels address them with 32-bit byte
+ * offsets), KVC_E_UNSUPPORTED, KVC_E_ALIGN, KVC_E_DEVICE. */
 kvc_status kvc_attend_compressed(const kvc_codec* kc, const kvc_store* k,
                                  const kvc_base_params* kp, const kvc_codec* vc,
                                  const kvc_store* v, const kvc_base_params* vp, int64_t n_keys,

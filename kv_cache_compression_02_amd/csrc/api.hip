@@ -260,6 +260,15 @@ kvc_status kvc_decode(const kvc_codec* codec, const kvc_store* src, int64_t toke
   return from_hip(launch_decode(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
+// The bf16 attention kernels address each head's code and scale/zero rows (and a dense
+// cache as a whole) through buffer resources with 32-bit byte ranges.
+static bool attend_ranges_fit(const CodecArgs& c, const StoreArgs& s) {
+  const int64_t lim = (int64_t)1 << 31;
+  if (c.bits == 16) return (int64_t)s.capacity * c.H * c.D * 2 < lim;
+  return (int64_t)s.capacity * c.code_words * 4 < lim && (int64_t)s.capacity * c.groups * 4 < lim &&
+         (int64_t)s.capacity * c.index_bytes < lim;
+}
+
 static kvc_status check_attend(const kvc_codec* kc, const kvc_store* k, const kvc_base_params* kp,
                                const kvc_codec* vc, const kvc_store* v, const kvc_base_params* vp,
                                int64_t n_keys, const void* q, int64_t n_queries, float* out,
@@ -305,8 +314,9 @@ kvc_status kvc_attend_compressed(const kvc_codec* kc, const kvc_store* k,
     if (c->base != KVC_BASE_NONE && c->base != KVC_BASE_CENTROID) return KVC_E_UNSUPPORTED;
   if (a.kc.x_dtype == KVC_BF16 && a.kc.D != 128) return KVC_E_UNSUPPORTED;
   if ((a.kc.bits == 16) != (a.vc.bits == 16)) return KVC_E_UNSUPPORTED;   // both dense or neither
-  if (a.kc.bits == 16 && (int64_t)a.ks.capacity * a.kc.H * a.kc.D * 2 >= (int64_t)1 << 31)
-    return KVC_E_SHAPE;   // one 32-bit buffer range per dense cache
+  if (a.kc.x_dtype == KVC_BF16 &&
+      (!attend_ranges_fit(a.kc, a.ks) || !attend_ranges_fit(a.vc, a.vs)))
+    return KVC_E_SHAPE;
   a.scale = softmax_scale;
   return from_hip(launch_attend(a, reinterpret_cast<hipStream_t>(stream)));
 }
@@ -327,6 +337,7 @@ kvc_status kvc_attend_mixed_dim(const kvc_codec* kc, const kvc_store* k,
   if (a.kc.x_dtype != KVC_BF16 || a.kc.D != 128 || a.kc.m != 16 || a.kc.groups != 1)
     return KVC_E_UNSUPPORTED;
   if (!a.kb.basis) return KVC_E_NULL;
+  if (!attend_ranges_fit(a.kc, a.ks) || !attend_ranges_fit(a.vc, a.vs)) return KVC_E_SHAPE;
   a.scale = softmax_scale;
   return from_hip(launch_attend_mixed(a, reinterpret_cast<hipStream_t>(stream)));
 }

@@ -99,6 +99,15 @@ def test_attend_validation_errors():
     bf64 = kvc.Codec(2, 64, 4, 32, kvc.BASE_NONE, x_dtype=kvc.BF16)
     assert att(bf64, bf64) == kvc.KVC_E_UNSUPPORTED        # bf16 MFMA path is d = 128
     assert att(kc, kc, fn=L.kvc_attend_mixed_dim) == kvc.KVC_E_UNSUPPORTED
+    # a store whose per-head code rows exceed the kernels' 32-bit buffer ranges
+    # (2^25 tokens x 64 B of INT4 codes = 2 GiB) is refused before any launch
+    big = kvc._Store(FAKE, FAKE, None, 1 << 25)
+    k4 = kvc.Codec(2, 128, 4, 32, kvc.BASE_NONE, x_dtype=kvc.BF16)
+    r = L.kvc_attend_compressed(ctypes.byref(k4.c()), ctypes.byref(big), ctypes.byref(b),
+                                ctypes.byref(k4.c()), ctypes.byref(big), ctypes.byref(b), 8,
+                                ctypes.c_void_p(FAKE), 4, ctypes.c_float(0.1),
+                                ctypes.c_void_p(FAKE), None, None, 0, None)
+    assert r == kvc.KVC_E_SHAPE
 
 
 def test_python_binding_raises_on_status():
