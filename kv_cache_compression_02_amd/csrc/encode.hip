@@ -532,8 +532,8 @@ __global__ __launch_bounds__(64 * cen_waves(CM, COEFF), 2 * 4 / cen_waves(CM, CO
   __shared__ float cnu[CM];   // |c_j| (upper bound), 0 beyond C
   __shared__ float wmax[NW];
   __shared__ uint32_t tq[NW][64];   // rescoring tasks of each wave: lane << 10 | centroid
-  __shared__ float tqd[NW][64];
-  __shared__ uint32_t tqn[NW];
+  // per lane, the least (distance bits << 32 | centroid) of its tasks in a round
+  __shared__ unsigned long long tres[NW][64];
   __shared__ __attribute__((aligned(16))) float bt[COEFF ? D * 16 : 4];   // basis [i][j], fp32
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -730,7 +730,7 @@ __global__ __launch_bounds__(64 * cen_waves(CM, COEFF), 2 * 4 / cen_waves(CM, CO
   //    queue; lane i computes task i in the exact fp32 order from the token's row
   if (__any(!uniq)) {
     uint32_t* q = &tq[wave][0];
-    float* qd = &tqd[wave][0];
+    unsigned long long* rs = &tres[wave][0];
     int single = pair ? cidx(hf ? t2 : t1) : -1;   // one candidate per lane of a pair token
     uint32_t mask[NBM / 2];                         // bit 16 cb + r: candidate value of this lane
 #pragma unroll
@@ -756,36 +756,47 @@ __global__ __launch_bounds__(64 * cen_waves(CM, COEFF), 2 * 4 / cen_waves(CM, CO
     const int64_t nw0 = n - t;   // first token of this wave
     float bd = __builtin_inff();
     int bj = 0x7FFFFFFF;
-    auto any_mask = [&]() {
-      uint32_t o = 0u;
+    // Task list without atomics: lane l's tasks (its `single` candidate, then its mask
+    // bits in ascending order) take the consecutive slots from the exclusive prefix sum
+    // of the lanes' task counts, 64 slots per round.  Each task lane folds its exact
+    // distance into its owner lane's slot with a 64-bit LDS minimum on
+    // (distance bits << 32 | centroid): distances are non-negative, so the bit order is
+    // the numeric order, and equal distances go to the lower index.
+    int cnt = single >= 0 ? 1 : 0;
 #pragma unroll
-      for (int w = 0; w < NBM / 2; ++w) o |= mask[w];
-      return o != 0u;
-    };
-    bool pending = single >= 0 || any_mask();
-    while (__any(pending)) {
-      if (lane == 0) tqn[wave] = 0;
-      __builtin_amdgcn_wave_barrier();
-      if (pending) {
+    for (int w = 0; w < NBM / 2; ++w) cnt += __builtin_popcount(mask[w]);
+    int off = cnt;   // inclusive prefix sum over the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(off, d);
+      if (lane >= d) off += o;
+    }
+    const int total = __shfl(off, 63);
+    off -= cnt;
+    for (int r0 = 0; r0 < total; r0 += 64) {
+      rs[lane] = ~0ull;
+      {
+        int g = off;
         if (single >= 0) {
-          const uint32_t slot = atomicAdd(&tqn[wave], 1u);
-          if (slot < 64u) { q[slot] = ((uint32_t)lane << 10) | (uint32_t)single; single = -1; }
+          if (g >= r0 && g < r0 + 64) q[g - r0] = ((uint32_t)lane << 10) | (uint32_t)single;
+          ++g;
         }
         for (int w = 0; w < NBM / 2; ++w) {
-          while (mask[w]) {
-            const int bit = __builtin_ctz(mask[w]);
-            const uint32_t slot = atomicAdd(&tqn[wave], 1u);
-            if (slot >= 64u) break;
-            const int cb = 2 * w + (bit >> 4), r = bit & 15;
-            const int j = 32 * cb + 8 * (r >> 2) + 4 * hf + (r & 3);
-            q[slot] = ((uint32_t)lane << 10) | (uint32_t)j;
-            mask[w] &= mask[w] - 1u;
+          uint32_t m = mask[w];
+          while (m) {
+            const int bit = __builtin_ctz(m);
+            m &= m - 1u;
+            if (g >= r0 && g < r0 + 64) {
+              const int cb = 2 * w + (bit >> 4), r = bit & 15;
+              const int j = 32 * cb + 8 * (r >> 2) + 4 * hf + (r & 3);
+              q[g - r0] = ((uint32_t)lane << 10) | (uint32_t)j;
+            }
+            ++g;
           }
         }
-        pending = single >= 0 || any_mask();
       }
       __builtin_amdgcn_wave_barrier();
-      const int ntask = min((int)tqn[wave], 64);
+      const int ntask = min(total - r0, 64);
       if (lane < ntask) {
         const uint32_t tk = q[lane];
         const int j = (int)(tk & 0x3FFu);
@@ -808,16 +819,14 @@ __global__ __launch_bounds__(64 * cen_waves(CM, COEFF), 2 * 4 / cen_waves(CM, CO
             acc = acc + q1;
           }
         }
-        qd[lane] = acc;
+        atomicMin(&rs[tk >> 10], ((unsigned long long)__float_as_uint(acc) << 32) | (uint32_t)j);
       }
       __builtin_amdgcn_wave_barrier();
-      for (int i = 0; i < ntask; ++i) {
-        const uint32_t tk = q[i];
-        if ((int)(tk >> 10) == lane) {
-          const float d = qd[i];
-          const int j = (int)(tk & 0x3FFu);
-          if (d < bd || (d == bd && j < bj)) { bd = d; bj = j; }
-        }
+      const unsigned long long mine = rs[lane];
+      if (mine != ~0ull) {
+        const float d = __uint_as_float((uint32_t)(mine >> 32));
+        const int j = (int)(uint32_t)mine;
+        if (d < bd || (d == bd && j < bj)) { bd = d; bj = j; }
       }
       __builtin_amdgcn_wave_barrier();
     }
