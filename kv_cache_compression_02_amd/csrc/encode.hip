@@ -960,6 +960,411 @@ __global__ __launch_bounds__(64 * cen_waves(CM, COEFF), 2 * 4 / cen_waves(CM, CO
   }   // tiles
 }
 
+// ---------------------------------------------------------------------------
+// Centroid codec with 16-token waves (bf16 d = 128, at most CM = 256 or 512 centroids,
+// no reconstruction output).  The same computation as encode_centroid_kernel, laid out
+// for more waves per SIMD: on v_mfma_f32_16x16x32_bf16 a wave scores 16 tokens, and
+// lane (t, q) = (lane & 15, lane >> 4) holds channels 32 ks + 8 q .. 32 ks + 8 q + 7
+// (ks = 0..3) of token t, i.e. a quarter of its row.  Per 16-centroid block the lane
+// gets the values of centroids 16 cb + 4 q + r (r = 0..3) for its token; it keeps their
+// top three with the position 4 cb + r in the low byte and q above it (8 tag bits for
+// CM = 256, 9 for 512), and the four lanes of a token merge their top threes.  The
+// separation test, the exact rescoring (tasks from a wave-wide prefix sum, results by
+// 64-bit LDS minimum, token rows re-read from memory in the oracle's fp32 order) and
+// the quantizer are those of encode_centroid_kernel; a quantization group spans two
+// (g = 16) or four (g = 32, 64) lanes, whose min and max are joined by lane exchanges.
+// With at most 128 registers per lane, four waves share a SIMD (two workgroups of
+// eight waves per CU with 256 centroids, one of sixteen with 512), which hides the
+// latency of small launches that one tile per workgroup cannot.
+__host__ __device__ constexpr int c16_waves(int cm) { return cm == 512 ? 16 : 8; }
+
+template <int BITS, int G, int CM>
+__global__ __launch_bounds__(64 * c16_waves(CM), 4) void encode_c16_kernel(EncodeParams p) {
+  constexpr int D = 128, ROW = D + 8;
+  constexpr int NW = c16_waves(CM), NT = 64 * NW, TT = 16 * NW;   // waves, threads, tokens
+  constexpr int NBM = CM / 16;                 // centroid blocks at most
+  constexpr int LOCB = CM == 256 ? 6 : 7;      // bits of a value's position in a lane
+  constexpr uint32_t TAGM = (4u << LOCB) - 1u; // position + quarter
+  constexpr float TSLACK = CM == 256 ? 0x1p-15f : 0x1p-14f;   // relative change by the tag
+  constexpr int MW = (4 * NBM + 31) / 32;      // mask words of a lane
+  constexpr int L = (1 << BITS) - 1;
+  __shared__ __attribute__((aligned(16))) uint16_t tab[CM * ROW];
+  __shared__ __attribute__((aligned(16))) float hn[CM];
+  __shared__ float cnu[CM];   // |c_j| (upper bound), 0 beyond C
+  __shared__ float wmax[NW];
+  __shared__ uint32_t tq[NW][64];                 // rescoring tasks: lane << 10 | centroid
+  __shared__ unsigned long long tres[NW][64];     // per lane: least (distance bits, centroid)
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = lane & 15, q = lane >> 4;
+  const int ntile = (int)((p.n_tokens + TT - 1) / TT);
+  const int wph = (int)gridDim.x / p.H;   // workgroups per head
+  const int b = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = b / wph, first = b % wph;
+  const int C = p.C;
+  const int nb = (C + 15) >> 4;
+  const uint16_t* cen = reinterpret_cast<const uint16_t*>(p.centroids) + (int64_t)h * C * D;
+
+  // this lane's quarter row of a tile's token (zeros past the last token)
+  auto load_quarter = [&](int tl, uint4 (&dst)[4]) {
+    const int64_t nn = (int64_t)tl * TT + wave * 16 + t;
+    const bool lv = tl < ntile && nn < p.n_tokens;
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(p.x) + (lv ? nn : 0) * p.x_stride +
+                          (int64_t)h * D + 8 * q;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      dst[ks] = lv ? *reinterpret_cast<const uint4*>(src + 32 * ks) : make_uint4(0u, 0u, 0u, 0u);
+  };
+  uint4 xv[4];
+  load_quarter(first, xv);
+
+  // 1. the head's centroid table (rows C .. 16 nb - 1 zero) and row norms
+#pragma unroll
+  for (int rnd = 0; rnd < (CM + NT / 16 * 8 - 1) / (NT / 16 * 8); ++rnd) {
+    uint4 v[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int j = (NT / 16) * (8 * rnd + it) + (tid >> 4), c = tid & 15;
+      v[it] = make_uint4(0u, 0u, 0u, 0u);
+      if (j < C) v[it] = *reinterpret_cast<const uint4*>(cen + (int64_t)j * D + 8 * c);
+    }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int j = (NT / 16) * (8 * rnd + it) + (tid >> 4), c = tid & 15;
+      if (j < 16 * nb && j < CM) *reinterpret_cast<uint4*>(&tab[j * ROW + 8 * c]) = v[it];
+    }
+  }
+  __syncthreads();
+  {
+    float cnw = 0.0f;
+    for (int j = tid; j < CM; j += NT) {
+      float s2 = 0.0f;
+      if (j < C) {
+#pragma unroll
+        for (int i = 0; i < D; i += 8) {
+          const uint4 v = *reinterpret_cast<const uint4*>(&tab[j * ROW + i]);
+          s2 = sq2_bf16(v.x, s2);
+          s2 = sq2_bf16(v.y, s2);
+          s2 = sq2_bf16(v.z, s2);
+          s2 = sq2_bf16(v.w, s2);
+        }
+      }
+      hn[j] = j < C ? -0.5f * s2 : -1e30f;
+      const float cn = sqrtf(s2) * (1.0f + 0x1p-10f);
+      cnu[j] = cn;
+      cnw = fmaxf(cnw, cn);
+    }
+#pragma unroll
+    for (int o = 32; o; o >>= 1) cnw = fmaxf(cnw, __shfl_xor(cnw, o));
+    if (lane == 0) wmax[wave] = cnw;
+  }
+  __syncthreads();
+  float cmax = wmax[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) cmax = fmaxf(cmax, wmax[w]);
+
+  auto xq = [&](float v, int m) { return __shfl_xor(v, m); };
+  auto xqi = [&](uint32_t v, int m) { return (uint32_t)__shfl_xor((int)v, m); };
+
+#pragma unroll 1
+  for (int tile = first; tile < ntile; tile += wph) {
+  const int64_t n = (int64_t)tile * TT + wave * 16 + t;
+  const bool live = n < p.n_tokens;
+  uint4 xnext[4];
+  load_quarter(tile + wph, xnext);
+
+  // 2. v_j = x.c_j - |c_j|^2 / 2 for the lane's 4 centroids of each block; top three
+  float m1 = -3.0e38f, m2 = -3.0e38f, m3 = -3.0e38f;
+  auto block_values = [&](int cb, f32x4_t& acc) {
+    const float4 hv = *reinterpret_cast<const float4*>(&hn[16 * cb + 4 * q]);
+    acc[0] = hv.x; acc[1] = hv.y; acc[2] = hv.z; acc[3] = hv.w;
+    const uint16_t* arow = &tab[(16 * cb + t) * ROW + 8 * q];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(arow + 32 * ks);
+      bf16x8_t bx;
+      __builtin_memcpy(&bx, &xv[ks], 16);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bx, acc, 0, 0, 0);
+    }
+  };
+  auto top3 = [&](const f32x4_t& acc, int cb) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      // the position 4 cb + r (< 2^LOCB) replaces the low byte: one v_perm_b32
+      const float pv = __uint_as_float(
+          __builtin_amdgcn_perm(__float_as_uint(acc[r]), (uint32_t)(4 * cb + r), 0x07060500u));
+      m3 = __builtin_amdgcn_fmed3f(m2, m3, pv);
+      m2 = __builtin_amdgcn_fmed3f(m1, m2, pv);
+      m1 = __builtin_amdgcn_fmed3f(m1, pv, 3.40282347e38f);   // max, as a median
+    }
+  };
+  {
+    f32x4_t acc0, acc1;
+    block_values(0, acc0);
+    int cb = 0;
+    for (; cb + 2 < nb; cb += 2) {
+      block_values(cb + 1, acc1);
+      top3(acc0, cb);
+      block_values(cb + 2, acc0);
+      top3(acc1, cb + 1);
+    }
+    if (cb + 1 < nb) {
+      block_values(cb + 1, acc1);
+      top3(acc0, cb);
+      top3(acc1, cb + 1);
+    } else {
+      top3(acc0, cb);
+    }
+  }
+  // the quarter above the position bits; merge the four lanes' top threes
+  auto q_tag = [&](float v) {
+    return __uint_as_float((__float_as_uint(v) & ~(3u << LOCB)) | ((uint32_t)q << LOCB));
+  };
+  m1 = q_tag(m1);
+  m2 = q_tag(m2);
+  m3 = q_tag(m3);
+#pragma unroll
+  for (int mk = 16; mk <= 32; mk <<= 1) {
+    const float b1 = xq(m1, mk), b2 = xq(m2, mk), b3 = xq(m3, mk);
+    const float n1 = fmaxf(m1, b1);
+    const float n2 = fmaxf(fmaxf(m2, b2), fminf(m1, b1));
+    const float n3 = fmaxf(fmaxf(m3, b3), fmaxf(fminf(m2, b1), fminf(m1, b2)));
+    m1 = n1; m2 = n2; m3 = n3;
+  }
+  const float t1 = m1, t2 = m2, t3 = m3;
+
+  // |x|^2 (upper bound) and the separation test
+  float xs = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    xs = sq2_bf16(xv[ks].x, xs);
+    xs = sq2_bf16(xv[ks].y, xs);
+    xs = sq2_bf16(xv[ks].z, xs);
+    xs = sq2_bf16(xv[ks].w, xs);
+  }
+  xs = xs + xq(xs, 16);
+  xs = xs + xq(xs, 32);
+  const float xxu = xs * (1.0f + 0x1p-10f);
+  const float xn = sqrtf(xxu) * (1.0f + 0x1p-10f);
+  auto erow = [&](float cj) {
+    return (2.0f * (D + 2) * 0x1p-24f) * cj * (cj + xn) * (1.0f + 0x1p-10f) + 1e-30f;
+  };
+  const float E = erow(cmax);
+  const float go = (D + 3) * 0x1p-24f * (1.0f + 0x1p-10f);
+  auto separated = [&](float a, float c, float esum) {
+    const float va = a - TSLACK * fabsf(a), vc = c + TSLACK * fabsf(c);
+    const float rhs = esum + go * (xxu - va - vc) + 0x1p-20f * (fabsf(va) + fabsf(vc) + xxu);
+    return va - vc > rhs;
+  };
+  auto cidx = [](float v) {
+    const uint32_t tg = __float_as_uint(v) & TAGM;
+    const int qq = (int)(tg >> LOCB), pos = (int)(tg & ((1u << LOCB) - 1u));
+    return 16 * (pos >> 2) + 4 * qq + (pos & 3);
+  };
+  int best = cidx(t1);
+  bool uniq = !live || separated(t1, t2, 2.0f * E), pair = false;
+  if (!uniq) {
+    const float e1 = erow(cnu[best]), e2 = erow(cnu[cidx(t2)]);
+    const bool beats_rest = separated(t1, t3, e1 + E);
+    uniq = beats_rest && separated(t1, t2, e1 + e2);
+    pair = beats_rest && !uniq;
+  }
+
+  // 3. exact rescoring of the tokens the test leaves open
+  if (__any(!uniq)) {
+    uint32_t* qt = &tq[wave][0];
+    unsigned long long* rs = &tres[wave][0];
+    // a pair token's two candidates go to its lanes q = 0 and 1
+    const int single = (pair && q < 2) ? cidx(q ? t2 : t1) : -1;
+    uint32_t mask[MW];   // bit 4 cb + r: candidate value of this lane
+#pragma unroll
+    for (int w = 0; w < MW; ++w) mask[w] = 0u;
+    const bool full = !uniq && !pair;
+    if (__any(full)) {
+      const float va = t1 - TSLACK * fabsf(t1);
+      const float tau = va - 2.0f * (2.0f * E + go * (xxu + 2.0f * fabsf(va)) +
+                                     0x1p-20f * (2.0f * fabsf(va) + xxu) + 0x1p-14f * fabsf(va));
+      for (int cb = 0; cb < nb; ++cb) {
+        f32x4_t acc;
+        block_values(cb, acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * cb + 4 * q + r, pos = 4 * cb + r;
+          if (full && j < C && acc[r] >= tau) mask[pos >> 5] |= 1u << (pos & 31);
+        }
+      }
+    }
+    const int64_t nw0 = n - t;   // first token of this wave
+    float bd = __builtin_inff();
+    int bj = 0x7FFFFFFF;
+    int cnt = single >= 0 ? 1 : 0;
+#pragma unroll
+    for (int w = 0; w < MW; ++w) cnt += __builtin_popcount(mask[w]);
+    int off = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(off, d);
+      if (lane >= d) off += o;
+    }
+    const int total = __shfl(off, 63);
+    off -= cnt;
+    for (int r0 = 0; r0 < total; r0 += 64) {
+      rs[lane] = ~0ull;
+      {
+        int g = off;
+        if (single >= 0) {
+          if (g >= r0 && g < r0 + 64) qt[g - r0] = ((uint32_t)lane << 10) | (uint32_t)single;
+          ++g;
+        }
+        for (int w = 0; w < MW; ++w) {
+          uint32_t m = mask[w];
+          while (m) {
+            const int pos = 32 * w + __builtin_ctz(m);
+            m &= m - 1u;
+            if (g >= r0 && g < r0 + 64)
+              qt[g - r0] = ((uint32_t)lane << 10) | (uint32_t)(16 * (pos >> 2) + 4 * q + (pos & 3));
+            ++g;
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      const int ntask = min(total - r0, 64);
+      if (lane < ntask) {
+        const uint32_t tk = qt[lane];
+        const int j = (int)(tk & 0x3FFu);
+        const int64_t nt = nw0 + (int)((tk >> 10) & 15u);
+        const uint16_t* xr = reinterpret_cast<const uint16_t*>(p.x) + nt * p.x_stride + (int64_t)h * D;
+        const uint16_t* crow = &tab[j * ROW];
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {   // channels in ascending order
+          const uint4 xw = *reinterpret_cast<const uint4*>(xr + 8 * i);
+          const uint4 cw = *reinterpret_cast<const uint4*>(crow + 8 * i);
+          const uint32_t xa[4] = {xw.x, xw.y, xw.z, xw.w}, ca[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float d0 = lo_bf16(xa[k]) - lo_bf16(ca[k]);
+            const float q0 = d0 * d0;
+            acc = acc + q0;
+            const float d1 = hi_bf16(xa[k]) - hi_bf16(ca[k]);
+            const float q1 = d1 * d1;
+            acc = acc + q1;
+          }
+        }
+        atomicMin(&rs[tk >> 10], ((unsigned long long)__float_as_uint(acc) << 32) | (uint32_t)j);
+      }
+      __builtin_amdgcn_wave_barrier();
+      const unsigned long long mine = rs[lane];
+      if (mine != ~0ull) {
+        const float d = __uint_as_float((uint32_t)(mine >> 32));
+        const int j = (int)(uint32_t)mine;
+        if (d < bd || (d == bd && j < bj)) { bd = d; bj = j; }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    // the token's four lanes agree on the least (distance, index)
+#pragma unroll
+    for (int mk = 16; mk <= 32; mk <<= 1) {
+      const float od = xq(bd, mk);
+      const int oj = (int)xqi((uint32_t)bj, mk);
+      if (od < bd || (od == bd && oj < bj)) { bd = od; bj = oj; }
+    }
+    if (!uniq) best = bj;
+  }
+
+  // 4. residual, group scale/zero, codes of the lane's quarter row
+  const uint16_t* crow = &tab[best * ROW + 8 * q];
+  const int64_t row = (int64_t)h * p.capacity + p.token_offset + n;
+  constexpr int KG = G == 64 ? 2 : 1;   // k-steps of one group
+#pragma unroll
+  for (int kg = 0; kg < 4; kg += KG) {
+    float r[8 * KG];
+#pragma unroll
+    for (int u = 0; u < KG; ++u) {
+      const uint4 cv = *reinterpret_cast<const uint4*>(crow + 32 * (kg + u));
+      const uint4 xw = xv[kg + u];
+      const uint32_t xa[4] = {xw.x, xw.y, xw.z, xw.w}, ca[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        r[8 * u + 2 * k] = lo_bf16(xa[k]) - lo_bf16(ca[k]);
+        r[8 * u + 2 * k + 1] = hi_bf16(xa[k]) - hi_bf16(ca[k]);
+      }
+    }
+    float mn = r[0], mx = r[0];
+#pragma unroll
+    for (int i = 1; i < 8 * KG; ++i) { mn = fminf(mn, r[i]); mx = fmaxf(mx, r[i]); }
+    // the group's other lanes: q ^ 1 (g = 16), all four (g = 32, 64)
+    mn = fminf(mn, xq(mn, 16));
+    mx = fmaxf(mx, xq(mx, 16));
+    if constexpr (G >= 32) {
+      mn = fminf(mn, xq(mn, 32));
+      mx = fmaxf(mx, xq(mx, 32));
+    }
+    const GroupQ gq = group_scale_zero(mn, mx, L);
+    // codes, 8 per k-step: the reciprocal quotient, redone with the IEEE division
+    // when an element lies within the bound of a rounding boundary (see quantize_with)
+    uint32_t cw[KG];
+#pragma unroll
+    for (int u = 0; u < KG; ++u) cw[u] = 0u;
+    if (gq.s != 0.0f) {
+      const float rinv = __builtin_amdgcn_rcpf(gq.s);
+      const float nzr = -(gq.z * rinv);
+      const float thr = 0.5f - (fabsf(nzr) + (float)(L + 2)) * 0x1p-19f;
+      bool bad = false;
+#pragma unroll
+      for (int i = 0; i < 8 * KG; ++i) {
+        const float y = __builtin_fmaf(r[i], rinv, nzr);
+        const float k = __builtin_rintf(y);
+        bad |= fabsf(y - k) > thr;
+        const uint32_t code = (uint32_t)__builtin_amdgcn_fmed3f(k, 0.0f, (float)L);
+        cw[i >> 3] |= code << (BITS * (i & 7));
+      }
+      if (bad) {
+#pragma unroll
+        for (int u = 0; u < KG; ++u) cw[u] = 0u;
+#pragma unroll
+        for (int i = 0; i < 8 * KG; ++i) cw[i >> 3] |= quantize_one(r[i], gq, L) << (BITS * (i & 7));
+      }
+    }
+    // stores: channel piece (ks, q) holds bits 8 BITS (4 ks + q) .. of the token's row
+#pragma unroll
+    for (int u = 0; u < KG; ++u) {
+      const int ks = kg + u;
+      if constexpr (BITS == 4) {
+        if (live) p.codes[row * 16 + 4 * ks + q] = cw[u];
+      } else {
+        const uint32_t pw = xqi(cw[u], 16);   // the partner quarter's 16 bits
+        if (live && (q & 1) == 0) p.codes[row * 8 + 2 * ks + (q >> 1)] = cw[u] | (pw << 16);
+      }
+    }
+    // scale/zero word of the group (one lane per group)
+    const int gi = G == 16 ? 2 * kg + (q >> 1) : (G == 32 ? kg : kg >> 1);
+    const bool owner = G == 16 ? (q & 1) == 0 : q == 0;
+    if (live && owner) p.sz[row * (D / G) + gi] = gq.word;
+  }
+  if (live && q == 0) {
+    if (p.index_bytes == 2) reinterpret_cast<uint16_t*>(p.index)[row] = (uint16_t)best;
+    else reinterpret_cast<uint8_t*>(p.index)[row] = (uint8_t)best;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xv[i] = xnext[i];
+  }   // tiles
+}
+
+template <int BITS, int G, int CM>
+hipError_t launch_c16_t(const EncodeParams& p, hipStream_t s) {
+  auto k = encode_c16_kernel<BITS, G, CM>;
+  constexpr int NT = 64 * c16_waves(CM), TT = NT / 4;
+  int occ = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(k), NT, 0);
+  if (e != hipSuccess) return e;
+  const int64_t ntile = (p.n_tokens + TT - 1) / TT;
+  const int64_t resident = (int64_t)std::max(1, occ) * cu_count();
+  const int wph = (int)std::max<int64_t>(1, std::min<int64_t>(ntile, resident / p.H));
+  hipLaunchKernelGGL(k, dim3((unsigned)(wph * p.H)), dim3(NT), 0, s, p);
+  return hipGetLastError();
+}
+
 // Persistent grid: workgroups per head = how many are resident at once (LDS and
 // registers decide) divided over the heads, at most one per tile.
 template <int BITS, int G, int CM, bool COEFF>
@@ -1045,6 +1450,15 @@ hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s) {
   // register-resident MFMA assignment, persistent workgroups per head
   const bool cen_ok = p.mode == MODE_CENTROID && (a.c.group == 16 || a.c.group == 32 || a.c.group == 64);
   const bool coeff_ok = p.mode == MODE_COEFF && a.c.m == 16 && a.c.group == 16 && a.c.bits == 4;
+  if (bf16 && a.c.D == 128 && cen_ok && !p.recon && !p.pred && a.c.C <= 512 && p.x_stride % 8 == 0) {
+#define KVC_ENC_C16(B, G, CM)                                                            \
+    if (a.c.bits == B && a.c.group == G && (a.c.C <= 256) == (CM == 256)) return launch_c16_t<B, G, CM>(p, s);
+    KVC_ENC_C16(2, 16, 256) KVC_ENC_C16(2, 32, 256) KVC_ENC_C16(2, 64, 256)
+    KVC_ENC_C16(4, 16, 256) KVC_ENC_C16(4, 32, 256) KVC_ENC_C16(4, 64, 256)
+    KVC_ENC_C16(2, 16, 512) KVC_ENC_C16(2, 32, 512) KVC_ENC_C16(2, 64, 512)
+    KVC_ENC_C16(4, 16, 512) KVC_ENC_C16(4, 32, 512) KVC_ENC_C16(4, 64, 512)
+#undef KVC_ENC_C16
+  }
   if (bf16 && a.c.D == 128 && (cen_ok || coeff_ok) && a.c.C <= 512 && p.x_stride % 8 == 0) {
 #define KVC_ENC_CEN(B, G, CM, CF)                                                        \
     if (a.c.bits == B && a.c.group == G && (a.c.C <= 256) == (CM == 256) && coeff_ok == CF) \
