@@ -73,6 +73,24 @@ def test_bf16_centroid_encode_bit_exact_ragged(bits, group):
     assert np.array_equal(bf16_to_f32_np(rec), nm.round_bf16(xhat))
 
 
+@pytest.mark.parametrize("bits,group,n_centroids",
+                         [(2, 16, 40), (4, 16, 40), (2, 64, 40), (4, 64, 300), (4, 32, 300),
+                          (2, 16, 300)])
+def test_bf16_centroid_encode_without_reconstruction_ragged(bits, group, n_centroids):
+    """Encodes with no reconstruction output take the 16-token-wave kernel: every
+    (bits, group) it instantiates, both table sizes (40 -> 256-row, 300 -> 512-row),
+    300 tokens (a ragged last tile) written at row offset 5."""
+    dev = device()
+    d = _small_video(seed=17, n_centroids=n_centroids)
+    x, C = nm.bf16_to_f32(d["K"]), nm.bf16_to_f32(d["Ck"])
+    codec = kvc.Codec(3, 128, bits, group, kvc.BASE_CENTROID, n_centroids)
+    st, _, _, _ = _encode(codec, d["K"], d["Ck"], dev, cap=310, off=5)
+    got = store_np(st)
+    check_centroid_store(got, x, C, bits, group, rows=slice(5, 305))
+    assert np.all(got["codes"][:, :5] == 0xFFFFFFFF) and np.all(got["codes"][:, 305:] == 0xFFFFFFFF)
+    assert np.all(got["scale_zero"][:, :5] == 0xFFFFFFFF) and np.all(got["scale_zero"][:, 305:] == 0xFFFFFFFF)
+
+
 def test_plain_group_quantization_and_zero_residual():
     dev = device()
     d = _small_video(seed=8)
