@@ -203,6 +203,29 @@ kvc_status kvc_attend_compressed(const kvc_codec* kc, const kvc_store* k,
                                  float* out, float* lse, void* workspace, size_t workspace_bytes,
                                  void* stream);
 
+/* kvc_attend_compressed_chunk - attention over the compressed history plus an
+ * uncompressed current chunk: O = softmax(Q [K_hist ; K_chunk]^T * softmax_scale)
+ * [V_hist ; V_chunk] per head, no mask, where the first n_keys keys and values are
+ * decoded from stores k and v exactly as in kvc_attend_compressed and the last n_chunk
+ * are read as they are.  (The TempoKV page keeps the most recent frames uncompressed,
+ * and quantized keys take attention mass from the unquantized current chunk; this is
+ * that layout.)  The two parts are attended separately and merged by their
+ * log-sum-exp, the same softmax summed in another order.
+ *   kc, vc, k, v, kp, vp, n_keys, q, out, lse: as kvc_attend_compressed (bf16 path only:
+ *     d = 128, compressed K and V with centroid or no base).
+ *   chunk_k, chunk_v: [n_chunk][H][d] bf16, token stride H*d, n_chunk >= 1.
+ *   workspace: required, kvc_workspace_bytes(KVC_OP_ATTEND_CHUNK, kc, n_keys,
+ *     n_queries) bytes; the contents are overwritten.
+ * Errors: as kvc_attend_compressed; KVC_E_SHAPE also for a chunk of 2 GiB or more,
+ *   KVC_E_WORKSPACE for a missing or smaller workspace. */
+kvc_status kvc_attend_compressed_chunk(const kvc_codec* kc, const kvc_store* k,
+                                       const kvc_base_params* kp, const kvc_codec* vc,
+                                       const kvc_store* v, const kvc_base_params* vp,
+                                       int64_t n_keys, const void* chunk_k, const void* chunk_v,
+                                       int64_t n_chunk, const void* q, int64_t n_queries,
+                                       float softmax_scale, float* out, float* lse,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* kvc_attend_mixed_dim - NanoKV-Fast style attention from the stored representation
  * without rebuilding keys (NanoKV page, '03 / Measured results'): the score of key n
  * is (q . C_k[a_n] + (B^T q) . c_n) * softmax_scale, c_n = dequantized coefficients;
@@ -219,10 +242,12 @@ kvc_status kvc_attend_mixed_dim(const kvc_codec* kc, const kvc_store* k,
                                 void* stream);
 
 /* Workspace bytes of an entry point (op: KVC_OP_*) for n_tokens tokens (the keys for
- * the attention ops) and n_queries queries.  Encode / decode: required by the DPLR
- * and temporal-value bases, 0 otherwise.  Attention: the optional workspace that
- * enables key splitting (0 when a single pass is used anyway). */
-enum { KVC_OP_ENCODE = 0, KVC_OP_DECODE = 1, KVC_OP_ATTEND = 2, KVC_OP_ATTEND_MIXED = 3 };
+ * the attention ops; the history keys for KVC_OP_ATTEND_CHUNK) and n_queries queries.
+ * Encode / decode: required by the DPLR and temporal-value bases, 0 otherwise.
+ * Attention: the optional workspace that enables key splitting (0 when a single pass is
+ * used anyway); with a current chunk: the required partial results. */
+enum { KVC_OP_ENCODE = 0, KVC_OP_DECODE = 1, KVC_OP_ATTEND = 2, KVC_OP_ATTEND_MIXED = 3,
+       KVC_OP_ATTEND_CHUNK = 4 };
 size_t kvc_workspace_bytes(int32_t op, const kvc_codec* codec, int64_t n_tokens,
                            int64_t n_queries);
 

@@ -197,6 +197,7 @@ size_t kvc_workspace_bytes(int32_t op, const kvc_codec* codec, int64_t n_tokens,
   if (resolve_codec(codec, &c) != KVC_OK || n_tokens < 0) return 0;
   if (op == KVC_OP_ENCODE || op == KVC_OP_DECODE) return encode_workspace_bytes(c, n_tokens);
   if (op == KVC_OP_ATTEND || op == KVC_OP_ATTEND_MIXED) return attend_workspace_bytes(c, n_tokens, n_queries);
+  if (op == KVC_OP_ATTEND_CHUNK) return attend_chunk_workspace_bytes(c, n_tokens, n_queries);
   return 0;
 }
 
@@ -319,6 +320,36 @@ kvc_status kvc_attend_compressed(const kvc_codec* kc, const kvc_store* k,
     return KVC_E_SHAPE;
   a.scale = softmax_scale;
   return from_hip(launch_attend(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+kvc_status kvc_attend_compressed_chunk(const kvc_codec* kc, const kvc_store* k,
+                                       const kvc_base_params* kp, const kvc_codec* vc,
+                                       const kvc_store* v, const kvc_base_params* vp,
+                                       int64_t n_keys, const void* chunk_k, const void* chunk_v,
+                                       int64_t n_chunk, const void* q, int64_t n_queries,
+                                       float softmax_scale, float* out, float* lse,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  AttendLaunch a;
+  kvc_status st = check_attend(kc, k, kp, vc, v, vp, n_keys, q, n_queries, out, lse, &a);
+  if (st != KVC_OK) return st;
+  for (const CodecArgs* c : {&a.kc, &a.vc})
+    if (c->base != KVC_BASE_NONE && c->base != KVC_BASE_CENTROID) return KVC_E_UNSUPPORTED;
+  if (a.kc.x_dtype != KVC_BF16 || a.kc.D != 128 || a.kc.bits == 16 || a.vc.bits == 16)
+    return KVC_E_UNSUPPORTED;
+  if (n_chunk < 1) return KVC_E_SHAPE;
+  if (!chunk_k || !chunk_v) return KVC_E_NULL;
+  if (!aligned16(chunk_k) || !aligned16(chunk_v) || (workspace && !aligned16(workspace)))
+    return KVC_E_ALIGN;
+  if (!attend_ranges_fit(a.kc, a.ks) || !attend_ranges_fit(a.vc, a.vs) ||
+      n_chunk * a.kc.H * a.kc.D * 2 >= ((int64_t)1 << 31))
+    return KVC_E_SHAPE;
+  if (n_queries > 0 &&
+      (!workspace || workspace_bytes < attend_chunk_workspace_bytes(a.kc, n_keys, n_queries)))
+    return KVC_E_WORKSPACE;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
+  a.scale = softmax_scale;
+  return from_hip(launch_attend_chunk(a, chunk_k, chunk_v, n_chunk, reinterpret_cast<hipStream_t>(stream)));
 }
 
 kvc_status kvc_attend_mixed_dim(const kvc_codec* kc, const kvc_store* k,

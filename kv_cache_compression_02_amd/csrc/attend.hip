@@ -821,6 +821,8 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
   }
 }
 
+constexpr int MAX_PARTS = 9;   // partial results one merge takes (8 key splits + a chunk)
+
 // Merge of the key splits: O = sum_s w_s O_s, w_s = exp(lse_s - lse) with
 // lse = log sum_s exp(lse_s); one thread per (query, head, 4 channels).
 __global__ __launch_bounds__(256) void attend_combine_kernel(AttnParams p) {
@@ -831,7 +833,7 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttnParams p) {
   const int c4 = (int)(i % (DM / 4));
   const int64_t q = qh / p.H;
   const int h = (int)(qh % p.H);
-  float ls[8];
+  float ls[MAX_PARTS];
   float m = -__builtin_inff();
   for (int s = 0; s < p.splits; ++s) {
     ls[s] = p.part_lse[((int64_t)s * p.H + h) * p.nq + q];
@@ -975,6 +977,37 @@ hipError_t launch_combine(const AttnParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The bf16 kernel over compressed K and V of the given bit widths and bases: every
+// (K bits, V bits, K base, V base) combination is its own kernel so the prefetch loads
+// stay branch-free.
+hipError_t launch_compressed_bf16(const AttnParams& p, int kbits, int vbits, dim3 grid, hipStream_t s) {
+  const bool kc = p.k.mode == SRC_CENTROID, vc = p.v.mode == SRC_CENTROID;
+  const dim3 block(NT);
+#define KVC_ATT(KB_, VB_, KC_, VC_)                                                       \
+  if (kbits == KB_ && vbits == VB_ && kc == KC_ && vc == VC_) {                         \
+    hipLaunchKernelGGL((attend_bf16_kernel<KB_, VB_, KC_, VC_, false>), grid, block, 0, s, p); \
+    return hipGetLastError();                                                            \
+  }
+#define KVC_ATT_BITS(KC_, VC_) \
+  KVC_ATT(2, 2, KC_, VC_) KVC_ATT(2, 4, KC_, VC_) KVC_ATT(4, 2, KC_, VC_) KVC_ATT(4, 4, KC_, VC_)
+  KVC_ATT_BITS(true, true)
+  KVC_ATT_BITS(true, false)
+  KVC_ATT_BITS(false, true)
+  KVC_ATT_BITS(false, false)
+#undef KVC_ATT_BITS
+#undef KVC_ATT
+  return hipErrorInvalidValue;
+}
+
+// Key splits of the history when a current chunk is attended as well: one part more
+// than the splits must fit the merge.
+int chunk_history_splits(int H, int64_t nq, int64_t nk) {
+  const int ntiles = (int)((nk + BK - 1) / BK);
+  const int sp = std::min(choose_splits(H, nq, nk), MAX_PARTS - 1);
+  const int tps = (ntiles + sp - 1) / sp;
+  return (ntiles + tps - 1) / tps;
+}
+
 }  // namespace
 
 size_t attend_workspace_bytes(const CodecArgs& kc, int64_t n_keys, int64_t n_queries) {
@@ -1005,23 +1038,9 @@ hipError_t launch_attend(const AttendLaunch& a, hipStream_t s) {
       hipLaunchKernelGGL((attend_bf16_kernel<2, 2, false, false, false, true>), grid, block, 0, s, p);
       return launch_combine(p, s);
     }
-    const bool kc = p.k.mode == SRC_CENTROID, vc = p.v.mode == SRC_CENTROID;
-    // every (K bits, V bits, K base, V base) combination is its own kernel so the
-    // prefetch loads stay branch-free
-#define KVC_ATT(KB_, VB_, KC_, VC_)                                                       \
-  if (a.kc.bits == KB_ && a.vc.bits == VB_ && kc == KC_ && vc == VC_) {                 \
-    hipLaunchKernelGGL((attend_bf16_kernel<KB_, VB_, KC_, VC_, false>), grid, block, 0, s, p); \
-    return launch_combine(p, s);                                                         \
-  }
-#define KVC_ATT_BITS(KC_, VC_) \
-  KVC_ATT(2, 2, KC_, VC_) KVC_ATT(2, 4, KC_, VC_) KVC_ATT(4, 2, KC_, VC_) KVC_ATT(4, 4, KC_, VC_)
-    KVC_ATT_BITS(true, true)
-    KVC_ATT_BITS(true, false)
-    KVC_ATT_BITS(false, true)
-    KVC_ATT_BITS(false, false)
-#undef KVC_ATT_BITS
-#undef KVC_ATT
-    return hipErrorInvalidValue;
+    const hipError_t e = launch_compressed_bf16(p, a.kc.bits, a.vc.bits, grid, s);
+    if (e != hipSuccess) return e;
+    return launch_combine(p, s);
   } else {
     p.splits = 1;
     const int nqb = (int)((a.n_queries + 63) / 64);
@@ -1031,6 +1050,65 @@ hipError_t launch_attend(const AttendLaunch& a, hipStream_t s) {
       hipLaunchKernelGGL(attend_f32_kernel<64>, dim3(nqb * a.kc.H), dim3(64), 0, s, p);
   }
   return hipGetLastError();
+}
+
+size_t attend_chunk_workspace_bytes(const CodecArgs& kc, int64_t n_keys, int64_t n_queries) {
+  if (kc.x_dtype != KVC_BF16 || kc.D != DM || n_queries <= 0 || n_keys <= 0) return 0;
+  const int sp = chunk_history_splits(kc.H, n_queries, n_keys);
+  return (size_t)(sp + 1) * n_queries * kc.H * (DM + 1) * sizeof(float);
+}
+
+// Compressed history (key splits 0 .. S-1) and the uncompressed current chunk (part S)
+// attended as separate parts of one softmax; attend_combine_kernel merges the S + 1
+// normalized partial outputs by their log-sum-exp.
+hipError_t launch_attend_chunk(const AttendLaunch& a, const void* chunk_k, const void* chunk_v,
+                               int64_t n_chunk, hipStream_t s) {
+  if (a.n_queries == 0) return hipSuccess;
+  const int H = a.kc.H;
+  const int64_t nq = a.n_queries;
+  AttnParams p{};
+  p.q = a.q;
+  p.nq = nq;
+  p.nk = a.n_keys;
+  p.H = H;
+  p.scale = a.scale;
+  p.scale_log2 = a.scale * 1.4426950408889634f;
+  p.k = make_src(a.kc, a.ks, a.kb);
+  p.v = make_src(a.vc, a.vs, a.vb);
+  const int ntiles = (int)((a.n_keys + BK - 1) / BK);
+  const int sp = chunk_history_splits(H, nq, a.n_keys);
+  p.splits = sp;
+  p.tps = (ntiles + sp - 1) / sp;
+  p.part_o = reinterpret_cast<float*>(a.workspace);
+  p.part_lse = p.part_o + (int64_t)(sp + 1) * nq * H * DM;
+  if (sp == 1) {   // a single history part writes its normalized result as part 0
+    p.out = p.part_o;
+    p.lse = p.part_lse;
+  }
+  const int nqb = (int)((nq + BQ - 1) / BQ);
+  hipError_t e = launch_compressed_bf16(p, a.kc.bits, a.vc.bits, dim3(nqb * H * sp), s);
+  if (e != hipSuccess) return e;
+  // the chunk: a dense bf16 cache [n_chunk][H][d], part sp
+  AttnParams pc = p;
+  pc.nk = n_chunk;
+  pc.splits = 1;
+  pc.tps = (int)((n_chunk + BK - 1) / BK);
+  pc.k = Src{};
+  pc.v = Src{};
+  pc.k.codes = reinterpret_cast<const uint32_t*>(chunk_k);
+  pc.v.codes = reinterpret_cast<const uint32_t*>(chunk_v);
+  pc.k.cap = pc.v.cap = n_chunk;
+  pc.k.bits = pc.v.bits = 16;
+  pc.out = p.part_o + (int64_t)sp * nq * H * DM;
+  pc.lse = p.part_lse + (int64_t)sp * H * nq;
+  hipLaunchKernelGGL((attend_bf16_kernel<2, 2, false, false, false, true>), dim3(nqb * H), dim3(NT), 0, s, pc);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  AttnParams pm = p;
+  pm.splits = sp + 1;
+  pm.out = a.out;
+  pm.lse = a.lse;
+  return launch_combine(pm, s);
 }
 
 hipError_t launch_attend_mixed(const AttendLaunch& a, hipStream_t s) {

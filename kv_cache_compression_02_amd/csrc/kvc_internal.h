@@ -81,6 +81,8 @@ hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t s);
 hipError_t launch_attend(const AttendLaunch& a, hipStream_t s);
 hipError_t launch_attend_mixed(const AttendLaunch& a, hipStream_t s);
+hipError_t launch_attend_chunk(const AttendLaunch& a, const void* chunk_k, const void* chunk_v,
+                               int64_t n_chunk, hipStream_t s);
 
 // Fused predictor + quantizer for bf16 d = 128 (anchors, temporal keys and values,
 // block-DPLR): returns false when a call is outside its shapes, else launches and
@@ -97,6 +99,7 @@ bool predict_available();
 // Workspace bytes that let attention split the keys across workgroups (0 when one
 // pass is used anyway).
 size_t attend_workspace_bytes(const CodecArgs& kc, int64_t n_keys, int64_t n_queries);
+size_t attend_chunk_workspace_bytes(const CodecArgs& kc, int64_t n_keys, int64_t n_queries);
 
 // Workspace bytes of the predictor paths (0 otherwise).
 size_t encode_workspace_bytes(const CodecArgs& c, int64_t n_tokens);

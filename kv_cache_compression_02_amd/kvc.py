@@ -23,10 +23,11 @@ F32, BF16 = 0, 1
 # kvc_base_kind
 BASE_NONE, BASE_CENTROID, BASE_DPLR, BASE_TEMPORAL, BASE_COEFF = range(5)
 # workspace ops
-OP_ENCODE, OP_DECODE, OP_ATTEND, OP_ATTEND_MIXED = range(4)
+OP_ENCODE, OP_DECODE, OP_ATTEND, OP_ATTEND_MIXED, OP_ATTEND_CHUNK = range(5)
 
 EXPORTED = ("kvc_store_bytes", "kvc_encode", "kvc_decode", "kvc_attend_compressed",
-            "kvc_attend_mixed_dim", "kvc_workspace_bytes", "kvc_status_str", "kvc_abi_version")
+            "kvc_attend_compressed_chunk", "kvc_attend_mixed_dim", "kvc_workspace_bytes",
+            "kvc_status_str", "kvc_abi_version")
 
 
 class KvcError(RuntimeError):
@@ -78,6 +79,10 @@ def lib():
     L.kvc_attend_compressed.restype = I32
     L.kvc_attend_mixed_dim.argtypes = att
     L.kvc_attend_mixed_dim.restype = I32
+    L.kvc_attend_compressed_chunk.argtypes = [P(_Codec), P(_Store), P(_Base), P(_Codec), P(_Store),
+                                              P(_Base), I64, VP, VP, I64, VP, I64, ctypes.c_float,
+                                              VP, VP, VP, SZ, VP]
+    L.kvc_attend_compressed_chunk.restype = I32
     L.kvc_workspace_bytes.argtypes = [I32, P(_Codec), I64, I64]
     L.kvc_workspace_bytes.restype = SZ
     L.kvc_status_str.argtypes = [I32]
@@ -287,6 +292,32 @@ def kvc_attend_compressed(kc: Codec, kstore: Store, kbase: Optional[BaseParams],
     """O = softmax(Q K^T * scale) V over the first n_keys compressed keys/values."""
     return _attend(lib().kvc_attend_compressed, "kvc_attend_compressed", kc, kstore, kbase, vc,
                    vstore, vbase, n_keys, q, softmax_scale, out, lse, want_lse, workspace)
+
+
+def kvc_attend_compressed_chunk(kc: Codec, kstore: Store, kbase: Optional[BaseParams], vc: Codec,
+                                vstore: Store, vbase: Optional[BaseParams], n_keys: int,
+                                chunk_k: torch.Tensor, chunk_v: torch.Tensor, q: torch.Tensor,
+                                softmax_scale: float, workspace: torch.Tensor, out=None, lse=None,
+                                want_lse: bool = False):
+    """Attention over the first n_keys compressed keys/values plus an uncompressed
+    current chunk (chunk_k, chunk_v: bf16 [n_chunk][H][d]), one softmax over both."""
+    nq = q.shape[0]
+    if chunk_k.shape != chunk_v.shape or chunk_k.dtype != torch.bfloat16:
+        raise ValueError("chunk_k and chunk_v must be bf16 tensors of one shape")
+    if out is None:
+        out = torch.empty((nq, kc.heads, kc.head_dim), dtype=torch.float32, device=q.device)
+    if want_lse and lse is None:
+        lse = torch.empty((kc.heads, nq), dtype=torch.float32, device=q.device)
+    kb = (kbase or BaseParams()).c()
+    vb = (vbase or BaseParams()).c()
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().kvc_attend_compressed_chunk(
+        ctypes.byref(kc.c()), ctypes.byref(kstore.c()), ctypes.byref(kb), ctypes.byref(vc.c()),
+        ctypes.byref(vstore.c()), ctypes.byref(vb), n_keys, _p(chunk_k, "chunk_k"),
+        _p(chunk_v, "chunk_v"), chunk_k.shape[0], _p(q, "q"), nq, ctypes.c_float(softmax_scale),
+        _p(out, "out"), _p(lse, "lse"), _p(workspace, "workspace"), ws_bytes, _stream()),
+        "kvc_attend_compressed_chunk")
+    return (out, lse) if want_lse else out
 
 
 def kvc_attend_mixed_dim(kc: Codec, kstore: Store, kbase: Optional[BaseParams], vc: Codec,

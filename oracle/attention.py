@@ -13,9 +13,14 @@ results').  Readings taken here:
 * mixed-dimensional scores for a key with centroid a and coefficients c:
   s = (q . C[a] + (B^T q) . c) * scale, which equals q . (C[a] + B c) * scale.
 
+* with an uncompressed current chunk (the TempoKV page keeps the most recent frames
+  uncompressed; quantized keys take attention mass from the unquantized current
+  chunk): one softmax over the history keys followed by the chunk keys.
+
 Pins (tests/test_oracle_attention.py): torch's fp64 scaled_dot_product_attention
-on CPU, one key -> O = v, zero query -> mean of V, and the mixed-dimensional
-identity against scores computed from explicitly reconstructed keys.
+on CPU, one key -> O = v, zero query -> mean of V, the mixed-dimensional identity
+against scores computed from explicitly reconstructed keys, and for the chunk form
+the log-sum-exp merge of the two parts' separate attentions.
 """
 from __future__ import annotations
 
@@ -45,6 +50,15 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, return_
         out[:, h] = (p @ v64[:, h]) / den
         lse[h] = (m + np.log(den))[:, 0]
     return (out, lse) if return_lse else out
+
+
+def attention_with_chunk(q: np.ndarray, k_hist: np.ndarray, v_hist: np.ndarray,
+                         k_chunk: np.ndarray, v_chunk: np.ndarray, scale: float,
+                         return_lse: bool = False):
+    """Attention over the history keys/values followed by the current chunk's, fp64:
+    the definition, one softmax over the concatenated keys."""
+    return attention(q, np.concatenate([k_hist, k_chunk]), np.concatenate([v_hist, v_chunk]),
+                     scale, return_lse)
 
 
 def mixed_scores(q: np.ndarray, Ck: np.ndarray, idx: np.ndarray, B: np.ndarray,

@@ -108,6 +108,23 @@ def test_attend_validation_errors():
                                 ctypes.c_void_p(FAKE), 4, ctypes.c_float(0.1),
                                 ctypes.c_void_p(FAKE), None, None, 0, None)
     assert r == kvc.KVC_E_SHAPE
+    # current chunk: a workspace is required, and the chunk must be given
+    ok = kvc.Codec(2, 128, 2, 32, kvc.BASE_NONE, x_dtype=kvc.BF16)
+    st2 = kvc._Store(FAKE, FAKE, None, 16)
+
+    def chunk(ck=FAKE, ws=FAKE, ws_bytes=1 << 20, nch=5):
+        return L.kvc_attend_compressed_chunk(
+            ctypes.byref(ok.c()), ctypes.byref(st2), ctypes.byref(b), ctypes.byref(ok.c()),
+            ctypes.byref(st2), ctypes.byref(b), 8, ctypes.c_void_p(ck) if ck else None,
+            ctypes.c_void_p(FAKE), nch, ctypes.c_void_p(FAKE), 4, ctypes.c_float(0.1),
+            ctypes.c_void_p(FAKE), None, ctypes.c_void_p(ws) if ws else None, ws_bytes, None)
+    assert chunk(ws=0, ws_bytes=0) == kvc.KVC_E_WORKSPACE
+    assert chunk(ws_bytes=16) == kvc.KVC_E_WORKSPACE
+    assert chunk(ck=0) == kvc.KVC_E_NULL
+    assert chunk(nch=0) == kvc.KVC_E_SHAPE
+    assert chunk(ck=FAKE + 8) == kvc.KVC_E_ALIGN
+    need = L.kvc_workspace_bytes(kvc.OP_ATTEND_CHUNK, ctypes.byref(ok.c()), 8, 4)
+    assert need >= 2 * 4 * 2 * 129 * 4   # two parts (history, chunk) of 4 queries x 2 heads
 
 
 def test_python_binding_raises_on_status():

@@ -141,3 +141,55 @@ def test_cfg1_full_size_attention_sampled():
     ref = oatt.attention(nm.bf16_to_f32(d["Q"][sample]), kh, vh, d["scale"])
     err = np.abs(o[sample] - ref).max()
     assert err <= 2e-2, err
+
+
+@pytest.mark.parametrize("n_keys,n_chunk", [(300, 77), (64, 1), (129, 200)])
+def test_bf16_attention_with_current_chunk_small(n_keys, n_chunk):
+    """Compressed history plus an uncompressed bf16 chunk, one softmax over both: the
+    history part may split its keys, the chunk is a further part, all merged by
+    log-sum-exp; against the fp64 oracle over [decoded history ; chunk]."""
+    dev = device()
+    d = synth.cfg1(seed=14, hist_frames=3, query_frames=1, tokens=100, heads=3, dim=128,
+                   n_centroids=40)
+    (kc, ks, kb), (vc, vs, vb) = _compress(d, 3, 128, 2, 32, 40, kvc.BF16, dev)
+    rng = np.random.default_rng(n_chunk)
+    ck = synth.bf16_bits(rng.standard_normal((n_chunk, 3, 128)) * 2.0)
+    cv = synth.bf16_bits(rng.standard_normal((n_chunk, 3, 128)))
+    q = to_dev(d["Q"], dev)
+    ws = kvc.kvc.workspace_for(kvc.kvc.OP_ATTEND_CHUNK, kc, n_keys, dev, n_queries=q.shape[0])
+    assert ws is not None
+    out, lse = kvc.kvc_attend_compressed_chunk(kc, ks, kb, vc, vs, vb, n_keys, to_dev(ck, dev),
+                                               to_dev(cv, dev), q, d["scale"], ws, want_lse=True)
+    torch.cuda.synchronize()
+    kh, vh = _oracle_cache(d, 2, 32, "bf16")
+    ref, rlse = oatt.attention_with_chunk(nm.bf16_to_f32(d["Q"]), kh[:n_keys], vh[:n_keys],
+                                          nm.bf16_to_f32(ck), nm.bf16_to_f32(cv), d["scale"],
+                                          return_lse=True)
+    assert np.abs(out.cpu().numpy() - ref).max() <= 2e-2
+    assert np.abs(lse.cpu().numpy() - rlse).max() <= 2e-2
+
+
+def test_cfg1_full_size_attention_with_current_chunk_sampled():
+    """cfg1 with the last 3 frames (4680 tokens) kept uncompressed: 28080 compressed
+    history keys + the 4680-token chunk, 4680 queries; a seeded sample of 48 queries
+    against the oracle."""
+    dev = device()
+    d, kh, vh = _cfg1_full()
+    lo, hi = d["chunk"]
+    (kc, ks, kb), (vc, vs, vb) = _compress(d, 12, 128, 2, 32, 256, kvc.BF16, dev, n=lo)
+    q = to_dev(d["Q"], dev)
+    ws = kvc.kvc.workspace_for(kvc.kvc.OP_ATTEND_CHUNK, kc, lo, dev, n_queries=q.shape[0])
+    out = kvc.kvc_attend_compressed_chunk(kc, ks, kb, vc, vs, vb, lo,
+                                          to_dev(np.ascontiguousarray(d["K"][lo:hi]), dev),
+                                          to_dev(np.ascontiguousarray(d["V"][lo:hi]), dev),
+                                          q, d["scale"], ws)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(np.isfinite(o))
+    rng = np.random.default_rng(2)
+    sample = np.sort(rng.choice(q.shape[0], size=48, replace=False))
+    ref = oatt.attention_with_chunk(nm.bf16_to_f32(d["Q"][sample]), kh[:lo], vh[:lo],
+                                    nm.bf16_to_f32(d["K"][lo:hi]), nm.bf16_to_f32(d["V"][lo:hi]),
+                                    d["scale"])
+    err = np.abs(o[sample] - ref).max()
+    assert err <= 2e-2, err

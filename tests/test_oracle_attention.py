@@ -84,3 +84,26 @@ def test_mixed_with_identity_basis_equals_centroid_codec_attention():
     v = rng.standard_normal((nk, h, d))
     assert np.allclose(attention.mixed_attention(q, Ck, e["idx"], B, e["chat"], v, 0.3),
                        attention.attention(q, khat, v, 0.3), atol=1e-12)
+
+
+def test_chunk_attention_is_the_lse_merge_of_its_parts():
+    """One softmax over [history; chunk] equals the two parts' attentions weighted by
+    exp(lse_part - lse) (flash-attention's split merge), and the merged lse is the
+    log of the summed exponentials; brute force on a tiny case checks one output."""
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((7, 2, 16))
+    kh, vh = rng.standard_normal((11, 2, 16)), rng.standard_normal((11, 2, 16))
+    kc, vc = rng.standard_normal((3, 2, 16)) * 2.0, rng.standard_normal((3, 2, 16))
+    out, lse = attention.attention_with_chunk(q, kh, vh, kc, vc, 0.3, return_lse=True)
+    o1, l1 = attention.attention(q, kh, vh, 0.3, return_lse=True)
+    o2, l2 = attention.attention(q, kc, vc, 0.3, return_lse=True)
+    w1 = np.exp(l1 - lse).T[..., None]   # [nq, H, 1]
+    w2 = np.exp(l2 - lse).T[..., None]
+    assert np.allclose(w1 + w2, 1.0, atol=1e-12)
+    assert np.allclose(out, w1 * o1 + w2 * o2, atol=1e-12)
+    assert np.allclose(lse, np.logaddexp(l1, l2), atol=1e-12)
+    # brute force: query 4, head 1
+    s = [float(q[4, 1] @ k) * 0.3 for k in np.concatenate([kh, kc])[:, 1]]
+    p = np.exp(np.array(s) - max(s))
+    ref = (p[:, None] * np.concatenate([vh, vc])[:, 1]).sum(0) / p.sum()
+    assert np.allclose(out[4, 1], ref, atol=1e-12)
