@@ -13,9 +13,10 @@ inputs are resident in HBM when the timed region starts.  The metric is query
 tokens per second (each query token covers all 12 heads).
 
 Prints ONE JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
-`--workload dplr|temporal|mixed` measures the other paths instead (the 30-layer
-cross-layer chain, the temporal chain + attention over its reconstruction, and
-mixed-dimensional attention); the default line is the one above.
+`--workload dplr|temporal|mixed|chunk` measures the other paths instead (the 30-layer
+cross-layer chain, the temporal chain + attention over its reconstruction,
+mixed-dimensional attention, and attention over a compressed history plus an
+uncompressed current chunk); the default line is the one above.
 """
 from __future__ import annotations
 
@@ -352,6 +353,51 @@ def bench_temporal(args, torch, kvc, synth, dev):
                          "frac_hbm": enc_bytes / t_enc / 1e9 / HBM_PEAK_GBS})
 
 
+def bench_chunk(args, torch, kvc, synth, dev):
+    """cfg1 with the most recent 3 frames kept uncompressed: 4680 queries attend to the
+    28080 compressed history tokens (centroid + INT2 g32, 256 centroids/head) and the
+    4680-token current chunk in bf16, one softmax over both (history key splits and the
+    chunk as separate parts, merged by log-sum-exp).  One step = that attention."""
+    d = synth.cfg1()
+    H, D, C = d["heads"], d["dim"], d["centroids"]
+    lo, hi = d["chunk"]
+    nq = d["Q"].shape[0]
+
+    def b16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view("int16")).view(torch.bfloat16).to(dev)
+
+    codec = kvc.Codec(H, D, d["bits"], d["group"], kvc.BASE_CENTROID, C)
+    ks, vs = kvc.Store.allocate(codec, lo, dev), kvc.Store.allocate(codec, lo, dev)
+    kb = kvc.BaseParams(centroids=b16(d["Ck"]))
+    vb = kvc.BaseParams(centroids=b16(d["Cv"]))
+    kvc.kvc_encode(codec, b16(d["K"][:lo]), ks, 0, kb)
+    kvc.kvc_encode(codec, b16(d["V"][:lo]), vs, 0, vb)
+    Kc, Vc, Q = b16(d["K"][lo:hi]), b16(d["V"][lo:hi]), b16(d["Q"])
+    out = torch.empty((nq, H, D), dtype=torch.float32, device=dev)
+    ws = kvc.kvc.workspace_for(kvc.kvc.OP_ATTEND_CHUNK, codec, lo, dev, n_queries=nq)
+
+    def step(_):
+        kvc.kvc_attend_compressed_chunk(codec, ks, kb, codec, vs, vb, lo, Kc, Vc, Q, d["scale"],
+                                        ws, out=out)
+
+    log("timing")
+    t_step, ev = _timed(torch, step, args.steps, args.warmup)
+    t_ev = sum(a.elapsed_time(b) for a, b in ev) / len(ev) * 1e-3
+    achieved = attention_flops(nq, hi, D, H) / t_ev / 1e12
+    return _line("compressed-history + current-chunk attention query-tok/s", nq / t_ev,
+                 "query-tok/s", args, t_step, "bf16",
+                 {"workload": "centroid+INT2 g32 history of 28080 tokens + uncompressed 4680-token "
+                              "current chunk, 12 heads x 128, 256 centroids/head, 4680 queries",
+                  "heads": H, "head_dim": D, "history_tokens": lo, "chunk_tokens": hi - lo,
+                  "queries": nq},
+                 {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
+                  "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
+                  "traffic": recorded_traffic("attend_bf16_kernel_chunk_12x128_4680q_28080k_4680c.md",
+                                              "kv_cache_compression_02_amd/csrc/attend.hip"),
+                  "kernel": "attend_bf16_kernel (history parts + chunk part + merge)",
+                  "ms": t_ev * 1e3})
+
+
 def bench_mixed(args, torch, kvc, synth, dev):
     """NanoKV-Fast style attention: 12 heads x 128, 65520 keys with 512 centroids per
     head, INT4 key coefficients on a 16-dim basis, INT2 g32 values; 4680 queries scored as
@@ -423,9 +469,10 @@ def main() -> int:
     ap.add_argument("--copy-ref", action="store_true",
                     help="run one plain 256 MiB device copy first (calibrates HBM counters)")
     ap.add_argument("--workload", default="centroid",
-                    choices=("centroid", "dplr", "temporal", "mixed"),
+                    choices=("centroid", "dplr", "temporal", "mixed", "chunk"),
                     help="centroid: the default line; the others measure the cross-layer "
-                         "chain, the temporal chain + attention, mixed-dimensional attention")
+                         "chain, the temporal chain + attention, mixed-dimensional attention, "
+                         "attention over the compressed history plus an uncompressed chunk")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -441,7 +488,8 @@ def main() -> int:
     if args.copy_ref:
         copy_reference(torch, dev)
     if args.workload != "centroid":
-        line = {"dplr": bench_dplr, "temporal": bench_temporal, "mixed": bench_mixed}[args.workload](
+        line = {"dplr": bench_dplr, "temporal": bench_temporal, "mixed": bench_mixed,
+                "chunk": bench_chunk}[args.workload](
             args, torch, kvc, synth, dev)
         print(json.dumps(line))
         return 0
