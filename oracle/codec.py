@@ -32,6 +32,7 @@ from __future__ import annotations
 import numpy as np
 
 from .numerics import f16
+from .rotation import rotate
 
 
 # ------------------------------- assignment -------------------------------
@@ -175,21 +176,27 @@ def to_store(q, s16, z16, bits: int, idx=None, n_centroids: int | None = None) -
     return out
 
 
-def encode_residual(x: np.ndarray, base: np.ndarray, bits: int, group: int) -> dict:
-    """r = x - base (fp32), quantize.  x, base: [N, H, d] float32."""
+def encode_residual(x: np.ndarray, base: np.ndarray, bits: int, group: int,
+                    rotation: int = 0) -> dict:
+    """r = x - base (fp32), optionally rotated by H_n / sqrt(n) per group of n
+    channels (n = ``rotation``, see rotation.py), quantize.  x, base: [N, H, d] float32."""
     r = np.asarray(x, dtype=np.float32) - np.asarray(base, dtype=np.float32)
+    if rotation:
+        r = rotate(r, rotation)
     q, s16, z16 = quantize(r, bits, group)
     return dict(q=q, s16=s16, z16=z16, base=np.asarray(base, dtype=np.float32))
 
 
-def encode_centroid(x: np.ndarray, C: np.ndarray, bits: int, group: int) -> dict:
-    """Centroid base: a = argmin ||x - C_a||^2, base = C[a].  Returns natural-layout
-    outputs plus the packed head-major ``store``."""
+def encode_centroid(x: np.ndarray, C: np.ndarray, bits: int, group: int,
+                    rotation: int = 0) -> dict:
+    """Centroid base: a = argmin ||x - C_a||^2, base = C[a] (the assignment is made on
+    the unrotated vectors).  Returns natural-layout outputs plus the packed head-major
+    ``store``."""
     x = np.asarray(x, dtype=np.float32)
     C = np.asarray(C, dtype=np.float32)
     idx, dist = assign(x, C)
     base = C[np.arange(C.shape[0])[None, :], idx]
-    out = encode_residual(x, base, bits, group)
+    out = encode_residual(x, base, bits, group, rotation)
     out.update(idx=idx, dist=dist)
     out["store"] = to_store(out["q"], out["s16"], out["z16"], bits, idx, C.shape[1])
     return out
@@ -204,13 +211,17 @@ def encode_none(x: np.ndarray, bits: int, group: int) -> dict:
 
 
 def decode_store(store: dict, bits: int, group: int, d: int, base: np.ndarray | None = None,
-                 C: np.ndarray | None = None) -> np.ndarray:
-    """Reconstruction base + ((q * s) + z) from a head-major store, as [N][H][d] float32.
+                 C: np.ndarray | None = None, rotation: int = 0) -> np.ndarray:
+    """Reconstruction base + ((q * s) + z) from a head-major store, as [N][H][d] float32;
+    with ``rotation`` = n the dequantized vector is rotated back by H_n / sqrt(n) (its
+    own inverse) before the base is added.
 
     The base is given explicitly, or gathered from centroids C [H][K][d] via the index."""
     q = np.transpose(unpack_codes(store["codes"], bits, d), (1, 0, 2))
     s16, z16 = unpack_scale_zero(np.transpose(store["scale_zero"], (1, 0, 2)))
     deq = dequantize(q, s16, z16, group)
+    if rotation:
+        deq = rotate(deq, rotation)
     if base is None:
         if C is None:
             base = np.zeros_like(deq)
