@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 1
+#define KVC_ABI_VERSION 2
 
 typedef enum {
   KVC_OK = 0,
@@ -99,6 +99,18 @@ typedef struct {
                           [K_l ; V_{l-1}])                                       */
   int32_t coeff_dim;   /* COEFF: m = 16                                          */
   int32_t x_dtype;     /* kvc_dtype of x, centroids, queries, reconstructions    */
+  int32_t rotation;    /* Hn residual transform (Coral-KV Fig. 5, Fig. 9b-c):
+                          0 = none; n = 16 or 64 = the residual of every group of
+                          n consecutive channels is multiplied by H_n / sqrt(n)
+                          (H_n the Sylvester Hadamard matrix) before it is
+                          quantized, and the dequantized vector is multiplied by
+                          the same matrix (its own inverse) before the base is
+                          added.  Needs KVC_BASE_CENTROID, bf16, d = 128, at most
+                          512 centroids and a group that n divides, with group
+                          <= 64.  The rounded transform is the Sylvester
+                          recursion H_2m [a; b] = [H_m a + H_m b; H_m a - H_m b]
+                          in fp32 (pairs at distance 1 combined first, then 2,
+                          4, ..., n/2), then the exact 1/sqrt(n) scaling.        */
 } kvc_codec;
 
 /* A compressed store (device buffers owned by the caller). */
@@ -158,6 +170,9 @@ kvc_status kvc_store_bytes(const kvc_codec* codec, int64_t capacity, size_t* cod
  *   workspace: device scratch of kvc_workspace_bytes(KVC_OP_ENCODE, ...) bytes for
  *              the matrix-product bases (DPLR; temporal values without pred_out); the
  *              contents on return are unspecified.  NULL, 0 otherwise.
+ * A rotated codec (codec->rotation != 0) quantizes the rotated residual; it takes no
+ * recon_out or pred_out (decode the store instead) and needs x_token_stride to be a
+ * multiple of 8.
  * Errors: KVC_E_NULL, KVC_E_SHAPE (token_offset + n_tokens > capacity, bad
  * codec), KVC_E_UNSUPPORTED, KVC_E_ALIGN, KVC_E_WORKSPACE, KVC_E_DEVICE. */
 kvc_status kvc_encode(const kvc_codec* codec, const void* x, int64_t n_tokens,
@@ -192,6 +207,10 @@ kvc_status kvc_decode(const kvc_codec* codec, const kvc_store* src, int64_t toke
  *     across workgroups and merges the partial results by their log-sum-exp (the
  *     same softmax, summed in another order); NULL, or a smaller workspace, runs one
  *     pass over the keys.  The contents are overwritten.
+ *   Rotated codecs (kc->rotation or vc->rotation nonzero; Coral-KV Fig. 5): each
+ *     decoded tile rotates its dequantized residuals back before the centroid is added,
+ *     with the decoder's arithmetic, so the tiles hold exactly what kvc_decode returns
+ *     (rounded to bf16).  K and V must then both use KVC_BASE_CENTROID.
  * Errors: KVC_E_NULL, KVC_E_SHAPE (n_keys > capacity, n_keys < 1, mismatched
  * heads/d; bf16 path: a store whose per-head code or scale/zero rows span 2 GiB or
  * more, or a dense cache of 2 GiB or more - the kernels address them with 32-bit byte
@@ -231,7 +250,7 @@ kvc_status kvc_attend_compressed_chunk(const kvc_codec* kc, const kvc_store* k,
  * is (q . C_k[a_n] + (B^T q) . c_n) * softmax_scale, c_n = dequantized coefficients;
  * softmax over all n_keys keys; values decoded from their centroid store.
  *   kc: KVC_BASE_COEFF (bf16, d = 128, m = 16); kp: centroids + basis.
- *   vc: KVC_BASE_CENTROID (bf16, d = 128); vp: centroids.
+ *   vc: KVC_BASE_CENTROID (bf16, d = 128, not rotated); vp: centroids.
  *   q, out, lse, workspace: as kvc_attend_compressed.
  * Errors: as kvc_attend_compressed. */
 kvc_status kvc_attend_mixed_dim(const kvc_codec* kc, const kvc_store* k,

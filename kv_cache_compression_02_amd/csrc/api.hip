@@ -29,10 +29,11 @@ kvc_status resolve_codec(const kvc_codec* c, CodecArgs* out) {
   a.n_inputs = c->n_inputs;
   a.m = c->coeff_dim;
   a.x_dtype = c->x_dtype;
+  a.rot = c->rotation;
   if (a.H < 1 || a.H > 4096) return KVC_E_SHAPE;
   if (a.D != 64 && a.D != 128) return KVC_E_UNSUPPORTED;
   if (a.bits == 16) {   // uncompressed bf16 cache, token-major (attention inputs only)
-    if (a.base != KVC_BASE_NONE || a.x_dtype != KVC_BF16) return KVC_E_UNSUPPORTED;
+    if (a.base != KVC_BASE_NONE || a.x_dtype != KVC_BF16 || a.rot != 0) return KVC_E_UNSUPPORTED;
     a.vec_len = a.D;
     a.group = a.D;
     a.code_words = a.D / 2;
@@ -71,6 +72,12 @@ kvc_status resolve_codec(const kvc_codec* c, CodecArgs* out) {
     if (a.base == KVC_BASE_DPLR) return KVC_E_UNSUPPORTED;
   }
   if (a.vec_len % a.group) return KVC_E_SHAPE;
+  if (a.rot != 0) {   // Hn residual transform: the centroid codec's 16-token-wave encoder
+    if (a.rot != 16 && a.rot != 64) return KVC_E_UNSUPPORTED;
+    if (a.base != KVC_BASE_CENTROID || a.x_dtype != KVC_BF16 || a.D != 128 || a.C > 512 ||
+        a.group > 64 || a.group % a.rot != 0)
+      return KVC_E_UNSUPPORTED;
+  }
   a.code_words = a.vec_len * a.bits / 32;
   a.groups = a.vec_len / a.group;
   a.index_bytes = (a.base == KVC_BASE_CENTROID || a.base == KVC_BASE_COEFF) ? (a.C <= 256 ? 1 : 2) : 0;
@@ -222,6 +229,7 @@ kvc_status kvc_encode(const kvc_codec* codec, const void* x, int64_t n_tokens,
   st = resolve_base(base, a.c, &a.b, true);
   if (st != KVC_OK) return st;
   if (a.c.base == KVC_BASE_COEFF && recon_out) return KVC_E_UNSUPPORTED;
+  if (a.c.rot != 0 && (recon_out || pred_out || stride % 8 != 0)) return KVC_E_UNSUPPORTED;
   st = check_predict_workspace(a.c, a.b, n_tokens, pred_out, workspace, workspace_bytes);
   if (st != KVC_OK) return st;
   a.x = x;
@@ -318,6 +326,9 @@ kvc_status kvc_attend_compressed(const kvc_codec* kc, const kvc_store* k,
   if (a.kc.x_dtype == KVC_BF16 &&
       (!attend_ranges_fit(a.kc, a.ks) || !attend_ranges_fit(a.vc, a.vs)))
     return KVC_E_SHAPE;
+  // rotated residuals are undone in the tile decode of the centroid-K-and-V kernels
+  if ((a.kc.rot || a.vc.rot) && (a.kc.base != KVC_BASE_CENTROID || a.vc.base != KVC_BASE_CENTROID))
+    return KVC_E_UNSUPPORTED;
   a.scale = softmax_scale;
   return from_hip(launch_attend(a, reinterpret_cast<hipStream_t>(stream)));
 }
@@ -335,6 +346,8 @@ kvc_status kvc_attend_compressed_chunk(const kvc_codec* kc, const kvc_store* k,
   for (const CodecArgs* c : {&a.kc, &a.vc})
     if (c->base != KVC_BASE_NONE && c->base != KVC_BASE_CENTROID) return KVC_E_UNSUPPORTED;
   if (a.kc.x_dtype != KVC_BF16 || a.kc.D != 128 || a.kc.bits == 16 || a.vc.bits == 16)
+    return KVC_E_UNSUPPORTED;
+  if ((a.kc.rot || a.vc.rot) && (a.kc.base != KVC_BASE_CENTROID || a.vc.base != KVC_BASE_CENTROID))
     return KVC_E_UNSUPPORTED;
   if (n_chunk < 1) return KVC_E_SHAPE;
   if (!chunk_k || !chunk_v) return KVC_E_NULL;
@@ -365,6 +378,7 @@ kvc_status kvc_attend_mixed_dim(const kvc_codec* kc, const kvc_store* k,
   a.workspace = workspace;
   a.workspace_bytes = workspace ? workspace_bytes : 0;
   if (a.kc.base != KVC_BASE_COEFF || a.vc.base != KVC_BASE_CENTROID) return KVC_E_UNSUPPORTED;
+  if (a.vc.rot != 0) return KVC_E_UNSUPPORTED;
   if (a.kc.x_dtype != KVC_BF16 || a.kc.D != 128 || a.kc.m != 16 || a.kc.groups != 1)
     return KVC_E_UNSUPPORTED;
   if (!a.kb.basis) return KVC_E_NULL;

@@ -40,6 +40,7 @@ struct Src {
   const void* cen;     // [H][C][D] cache dtype
   int64_t cap;
   int bits, group, groups, words, idxb, C, mode;
+  int rot;             // Hn residual transform width: 0, 16 or 64
 };
 
 struct AttnParams {
@@ -178,7 +179,37 @@ __device__ __forceinline__ int vpos(int row, int key) {
 // into bf16 high and low parts (16 + 16); the queries carry B^T q split the same way,
 // and three extra MFMA steps add (B^T q) . c to q . C[a] with about 2^-16 relative
 // error - the score is formed without reconstructing the key.
-template <int BITS, int VBITS, bool KCEN, bool VCEN, bool MIXED, bool DENSE = false>
+// Hn transform back (Coral-KV Fig. 5: residuals were rotated per group of n channels
+// before quantization) on a lane's W consecutive channels of one vector, pieces of the
+// vector on consecutive lanes (piece = lane's index within the vector): butterflies at
+// channel distance 1 .. W/2 in the lane, then W, 2W, .. n/2 with the lanes 1, 2, ..
+// apart - the order of the Sylvester recursion, so the result is the codec decoder's
+// to the bit.  The values come in already scaled by 1/sqrt(n) (exact).
+template <int W>
+__device__ __forceinline__ void hn_back(float (&v)[W], int piece, int n) {
+#pragma unroll
+  for (int h = 1; h < W; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      if (i & h) continue;
+      const float a = v[i], b = v[i + h];
+      v[i] = a + b;
+      v[i + h] = a - b;
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 8; m <<= 1) {
+    if (m * W >= n) break;
+    const bool up = (piece & m) != 0;
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      const float o = __shfl_xor(v[i], m);
+      v[i] = up ? o - v[i] : v[i] + o;
+    }
+  }
+}
+
+template <int BITS, int VBITS, bool KCEN, bool VCEN, bool MIXED, bool DENSE = false, bool ROT = false>
 __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
   constexpr int KR = MIXED ? DM + 32 + 8 : KROW;   // K tile row (bf16 elements)
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BK * KR];     // bf16
@@ -239,28 +270,24 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
   const int vsh = (8 * c8 * VBITS) & 31;          // bit offset of the 8 codes in their word
   // INT2 V: byte selector that puts the two keys' 16 code bits side by side
   const uint32_t vsel = vsh ? 0x07060302u : 0x05040100u;
-  // index entries are read as the aligned dword holding them (k0 is a multiple of 64, so
-  // the shift within the dword depends on the thread only)
-  const uint32_t kimask = p.k.idxb == 1 ? 0xFFu : 0xFFFFu, vimask = p.v.idxb == 1 ? 0xFFu : 0xFFFFu;
-  const uint32_t kish = 8u * ((uint32_t)(kk * p.k.idxb) & 3u);
-  const uint32_t vish0 = 8u * ((uint32_t)(2 * kp * p.v.idxb) & 3u);
-  const uint32_t vish1 = 8u * ((uint32_t)((2 * kp + 1) * p.v.idxb) & 3u);
-
-  auto idx_of = [](uint32_t word, uint32_t sh, uint32_t mask, int C) -> uint32_t {
-    return min((word >> sh) & mask, (uint32_t)(C - 1));
+  // index entries are read one at a time (byte or short buffer loads), so the range
+  // check of the buffer resource covers exactly the stored entries
+  auto load_index = [](__amdgpu_buffer_rsrc_t r, uint32_t key, int idxb) -> int {
+    return idxb == 1 ? (int)__builtin_amdgcn_raw_buffer_load_b8(r, key, 0, 0)
+                     : (int)__builtin_amdgcn_raw_buffer_load_b16(r, 2u * key, 0, 0);
   };
-  // the raw index words are kept in registers; shift, mask and clamp happen at use
+  auto idx_of = [](int v, int C) -> uint32_t { return min((uint32_t)v, (uint32_t)(C - 1)); };
+  // the index entries are kept in registers; the clamp happens at use
   auto load_idx = [&](int t, int& ki, int (&vi)[2]) {
     const uint32_t k0 = (uint32_t)(t * BK);
     if constexpr (KCEN)
-      ki = (int)__builtin_amdgcn_raw_buffer_load_b32(rk_idx, ((k0 + kk) * p.k.idxb) & ~3u, 0, 0);
+      ki = load_index(rk_idx, k0 + kk, p.k.idxb);
     else
       ki = 0;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       if constexpr (VCEN)
-        vi[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(
-            rv_idx, ((k0 + 2 * kp + j) * p.v.idxb) & ~3u, 0, 0);
+        vi[j] = load_index(rv_idx, k0 + 2 * kp + j, p.v.idxb);
       else
         vi[j] = 0;
     }
@@ -294,7 +321,7 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
     kpr.sz = __builtin_amdgcn_raw_buffer_load_b32(rk_sz, n * kgb + kgrp * 4, 0, 0);
     typedef uint32_t u4 __attribute__((ext_vector_type(4)));
     if constexpr (KCEN) {
-      const uint32_t off = idx_of((uint32_t)ki, kish, kimask, p.k.C) * (DM * 2) + 32 * kw;
+      const uint32_t off = idx_of(ki, p.k.C) * (DM * 2) + 32 * kw;
       const u4 a0 = __builtin_amdgcn_raw_buffer_load_b128(rk_cen, off, 0, 0);
       const u4 a1 = __builtin_amdgcn_raw_buffer_load_b128(rk_cen, off + 16, 0, 0);
       kpr.c0 = uint4{a0.x, a0.y, a0.z, a0.w};
@@ -310,7 +337,7 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
       vp.sz[j] = __builtin_amdgcn_raw_buffer_load_b32(rv_sz, m * vgb + vgrp * 4, 0, 0);
       if constexpr (VCEN) {
         const uint32_t off =
-            idx_of((uint32_t)vi[j], j ? vish1 : vish0, vimask, p.v.C) * (DM * 2) + 16 * c8;
+            idx_of(vi[j], p.v.C) * (DM * 2) + 16 * c8;
         const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rv_cen, off, 0, 0);
         vp.c[j] = uint4{a.x, a.y, a.z, a.w};
       } else {
@@ -323,7 +350,7 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
   // different points of a tile, each one tile ahead of its use.
   auto load_kidx = [&](int t, int& ki) {
     if constexpr (KCEN)
-      ki = (int)__builtin_amdgcn_raw_buffer_load_b32(rk_idx, (((uint32_t)(t * BK) + kk) * p.k.idxb) & ~3u, 0, 0);
+      ki = load_index(rk_idx, (uint32_t)(t * BK) + kk, p.k.idxb);
     else
       ki = 0;
   };
@@ -331,8 +358,7 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       if constexpr (VCEN)
-        vi[j] = (int)__builtin_amdgcn_raw_buffer_load_b32(
-            rv_idx, (((uint32_t)(t * BK) + 2 * kp + j) * p.v.idxb) & ~3u, 0, 0);
+        vi[j] = load_index(rv_idx, (uint32_t)(t * BK) + 2 * kp + j, p.v.idxb);
       else
         vi[j] = 0;
     }
@@ -350,7 +376,7 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
     kpr.sz = __builtin_amdgcn_raw_buffer_load_b32(rk_sz, n * kgb + kgrp * 4, 0, 0);
     typedef uint32_t u4 __attribute__((ext_vector_type(4)));
     if constexpr (KCEN) {
-      const uint32_t off = idx_of((uint32_t)ki, kish, kimask, p.k.C) * (DM * 2) + 32 * kw;
+      const uint32_t off = idx_of(ki, p.k.C) * (DM * 2) + 32 * kw;
       const u4 a0 = __builtin_amdgcn_raw_buffer_load_b128(rk_cen, off, 0, 0);
       const u4 a1 = __builtin_amdgcn_raw_buffer_load_b128(rk_cen, off + 16, 0, 0);
       kpr.c0 = uint4{a0.x, a0.y, a0.z, a0.w};
@@ -369,7 +395,7 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
       vp.sz[j] = __builtin_amdgcn_raw_buffer_load_b32(rv_sz, m * vgb + vgrp * 4, 0, 0);
       if constexpr (VCEN) {
         const uint32_t off =
-            idx_of((uint32_t)vi[j], j ? vish1 : vish0, vimask, p.v.C) * (DM * 2) + 16 * c8;
+            idx_of(vi[j], p.v.C) * (DM * 2) + 16 * c8;
         const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rv_cen, off, 0, 0);
         vp.c[j] = uint4{a.x, a.y, a.z, a.w};
       } else {
@@ -417,7 +443,12 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
     } else {
     // ---- K: 16 consecutive channels of key kk -> row-major bf16
      if (do_k) {
-      const float s24 = f16_bits_to_f32(kpr.sz & 0xFFFFu) * 0x1p24f, ze = f16_bits_to_f32(kpr.sz >> 16);
+      float s24 = f16_bits_to_f32(kpr.sz & 0xFFFFu) * 0x1p24f, ze = f16_bits_to_f32(kpr.sz >> 16);
+      if constexpr (ROT) {   // the 1/sqrt(n) of the transform, folded in exactly
+        const float sc = p.k.rot == 64 ? 0.125f : (p.k.rot == 16 ? 0.25f : 1.0f);
+        s24 *= sc;
+        ze *= sc;
+      }
       float dq[16];   // code * s + z per channel
       if constexpr (BITS == 2) {
 #pragma unroll
@@ -435,6 +466,9 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
             dq[8 * wd + r] = __builtin_fmaf(code_lo(b), s24, ze);
             dq[8 * wd + r + 4] = __builtin_fmaf(code_hi(b), s24, ze);
           }
+      }
+      if constexpr (ROT) {
+        if (p.k.rot) hn_back<16>(dq, kw, p.k.rot);   // 8 lanes per key row, 16 channels each
       }
       const uint32_t cw[8] = {kpr.c0.x, kpr.c0.y, kpr.c0.z, kpr.c0.w, kpr.c1.x, kpr.c1.y, kpr.c1.z, kpr.c1.w};
       uint32_t o[8];
@@ -458,6 +492,11 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
       for (int j = 0; j < 2; ++j) {
         s24[j] = f16_bits_to_f32(vp.sz[j] & 0xFFFFu) * 0x1p24f;
         ze[j] = f16_bits_to_f32(vp.sz[j] >> 16);
+        if constexpr (ROT) {   // the 1/sqrt(n) of the transform, folded in exactly
+          const float sc = p.v.rot == 64 ? 0.125f : (p.v.rot == 16 ? 0.25f : 1.0f);
+          s24[j] *= sc;
+          ze[j] *= sc;
+        }
       }
       if constexpr (VBITS == 2) {
         // the two keys' 8 codes side by side (key 0 low half, key 1 high half)
@@ -477,6 +516,12 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
             dq[j][r] = __builtin_fmaf(code_lo(b), s24[j], ze[j]);
             dq[j][r + 4] = __builtin_fmaf(code_hi(b), s24[j], ze[j]);
           }
+      }
+      if constexpr (ROT) {
+        if (p.v.rot) {   // 16 lanes per value row, 8 channels each
+          hn_back<8>(dq[0], c8, p.v.rot);
+          hn_back<8>(dq[1], c8, p.v.rot);
+        }
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -770,7 +815,7 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
   // the final tile of a ragged history (the only one that masks keys) runs after the
   // loop, so the loop body has one variant
   const int tfull = (te * BK > nk) ? te - 1 : te;
-  if constexpr (!DENSE && !MIXED) {
+  if constexpr (!DENSE && !MIXED && !ROT) {
     // V decode first, K decode among the score MFMAs (see compute)
     int t = tb;
     for (; t < min(tfull, te - 1); ++t) {
@@ -941,6 +986,7 @@ Src make_src(const CodecArgs& c, const StoreArgs& st, const BaseArgs& b) {
   s.idxb = c.index_bytes;
   s.C = c.C;
   s.mode = (c.base == KVC_BASE_CENTROID || c.base == KVC_BASE_COEFF) ? SRC_CENTROID : SRC_NONE;
+  s.rot = c.rot;
   return s;
 }
 
@@ -983,6 +1029,17 @@ hipError_t launch_combine(const AttnParams& p, hipStream_t s) {
 hipError_t launch_compressed_bf16(const AttnParams& p, int kbits, int vbits, dim3 grid, hipStream_t s) {
   const bool kc = p.k.mode == SRC_CENTROID, vc = p.v.mode == SRC_CENTROID;
   const dim3 block(NT);
+  if (p.k.rot || p.v.rot) {   // rotated residuals: centroid K and V (validated by the caller)
+    if (!kc || !vc) return hipErrorInvalidValue;
+#define KVC_ATT_ROT(KB_, VB_)                                                                    \
+    if (kbits == KB_ && vbits == VB_) {                                                          \
+      hipLaunchKernelGGL((attend_bf16_kernel<KB_, VB_, true, true, false, false, true>), grid, block, 0, s, p); \
+      return hipGetLastError();                                                                  \
+    }
+    KVC_ATT_ROT(2, 2) KVC_ATT_ROT(2, 4) KVC_ATT_ROT(4, 2) KVC_ATT_ROT(4, 4)
+#undef KVC_ATT_ROT
+    return hipErrorInvalidValue;
+  }
 #define KVC_ATT(KB_, VB_, KC_, VC_)                                                       \
   if (kbits == KB_ && vbits == VB_ && kc == KC_ && vc == VC_) {                         \
     hipLaunchKernelGGL((attend_bf16_kernel<KB_, VB_, KC_, VC_, false>), grid, block, 0, s, p); \

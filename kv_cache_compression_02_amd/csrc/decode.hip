@@ -17,6 +17,7 @@ namespace {
 struct DecodeParams {
   int64_t n_tokens, token_offset, capacity;
   int H, D, C, bits, group, groups, code_words, index_bytes, mode;
+  int rot;             // Hn residual transform width (0, 16 or 64)
   uint32_t total;      // threads of this launch: n_tokens * H * (D / 16) < 2^31
   int cshift, gshift;  // log2(D / 16), log2(group)
   const uint32_t* codes;
@@ -111,8 +112,42 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   for (int k = 0; k < 16; ++k) {
     const int bit = p.bits * k;   // 0..60
     const uint32_t code = ((bit < 32 ? (w0 >> bit) : (w1 >> (bit - 32)))) & mask;
-    v[k] = base[k] + dequant_one(code, s, z);
+    v[k] = dequant_one(code, s, z);
   }
+  if (p.rot != 0) {
+    // Hn transform back (H_n / sqrt(n) is its own inverse) with the rounding of the
+    // Sylvester recursion: butterflies at channel distance 1, 2, 4, 8 inside the
+    // thread, then for n = 64 at 16 and 32 with the threads 1 and 2 lanes apart (the
+    // neighbouring 16-channel pieces of the row; rows start at multiples of 8 lanes
+    // and a launch covers whole rows, so the partner is live).  Lower channel of a
+    // pair: a + b, upper: a - b; the 1/sqrt(n) scale is exact.
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (k & h) continue;
+        const float a = v[k], b = v[k + h];
+        v[k] = a + b;
+        v[k + h] = a - b;
+      }
+    }
+    if (p.rot == 64) {
+#pragma unroll
+      for (int m = 1; m <= 2; m <<= 1) {
+        const bool up = (c16 & (uint32_t)m) != 0;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const float o = __shfl_xor(v[k], m);
+          v[k] = up ? o - v[k] : v[k] + o;
+        }
+      }
+    }
+    const float sc = p.rot == 64 ? 0.125f : 0.25f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] *= sc;
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) v[k] = base[k] + v[k];
   OT* out = reinterpret_cast<OT*>(p.out) + orow;
   if constexpr (sizeof(OT) == 2) {     // 16 bf16 (round to nearest even): two 16-byte stores
     uint32_t o[8];
@@ -191,6 +226,7 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t s) {
   p.coef_b = a.b.coef_b;
   p.out = a.out;
   p.pred = a.pred;
+  p.rot = a.c.rot;
   p.cshift = __builtin_ctz((unsigned)(a.c.D / 16));
   p.gshift = __builtin_ctz((unsigned)a.c.group);
   if (a.c.D % 16 != 0 || (a.c.group & (a.c.group - 1)) != 0 || a.c.group < 16 || (a.c.bits != 2 && a.c.bits != 4))

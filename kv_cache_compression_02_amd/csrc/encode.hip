@@ -978,7 +978,56 @@ __global__ __launch_bounds__(64 * cen_waves(CM, COEFF), 2 * 4 / cen_waves(CM, CO
 // latency of small launches that one tile per workgroup cannot.
 __host__ __device__ constexpr int c16_waves(int cm) { return cm == 512 ? 16 : 8; }
 
-template <int BITS, int G, int CM>
+// Hn residual transform (Coral-KV Fig. 5: each group of N residual channels is
+// rotated independently) of one quantization step's residuals in the lane layout of
+// encode_c16_kernel: value 8 u + e of lane quarter q is channel 32 (kg + u) + 8 q + e.
+// The rounding is that of the Sylvester recursion H_2m [a; b] = [H_m a + H_m b;
+// H_m a - H_m b]: butterflies at channel distance 1, 2, 4 inside the lane, 8 with the
+// lane 16 apart (quarter q ^ 1), for N = 64 then 16 with the lane 32 apart (q ^ 2) and
+// 32 between the lane's two k-steps; the lower channel of a pair takes a + b, the
+// upper a - b.  The 1/sqrt(N) scale (1/4, 1/8) is exact.
+template <int N, int KG>
+__device__ __forceinline__ void hn_rotate_c16(float (&r)[8 * KG], int q) {
+  static_assert(N == 16 || (N == 64 && KG == 2), "rotation width and quantization step");
+#pragma unroll
+  for (int u = 0; u < KG; ++u) {
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i & h) continue;
+        const float a = r[8 * u + i], b = r[8 * u + i + h];
+        r[8 * u + i] = a + b;
+        r[8 * u + i + h] = a - b;
+      }
+    }
+  }
+  const bool up8 = (q & 1) != 0;
+#pragma unroll
+  for (int i = 0; i < 8 * KG; ++i) {
+    const float o = __shfl_xor(r[i], 16);
+    r[i] = up8 ? o - r[i] : r[i] + o;
+  }
+  if constexpr (N == 64) {
+    const bool up16 = (q & 2) != 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float o = __shfl_xor(r[i], 32);
+      r[i] = up16 ? o - r[i] : r[i] + o;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float a = r[i], b = r[8 + i];
+      r[i] = a + b;
+      r[8 + i] = a - b;
+    }
+  }
+  constexpr float sc = N == 64 ? 0.125f : 0.25f;
+#pragma unroll
+  for (int i = 0; i < 8 * KG; ++i) r[i] *= sc;
+}
+
+template <int BITS, int G, int CM, int ROT>
 __global__ __launch_bounds__(64 * c16_waves(CM), 4) void encode_c16_kernel(EncodeParams p) {
   constexpr int D = 128, ROW = D + 8;
   constexpr int NW = c16_waves(CM), NT = 64 * NW, TT = 16 * NW;   // waves, threads, tokens
@@ -1290,6 +1339,7 @@ __global__ __launch_bounds__(64 * c16_waves(CM), 4) void encode_c16_kernel(Encod
         r[8 * u + 2 * k + 1] = hi_bf16(xa[k]) - hi_bf16(ca[k]);
       }
     }
+    if constexpr (ROT != 0) hn_rotate_c16<ROT, KG>(r, q);
     float mn = r[0], mx = r[0];
 #pragma unroll
     for (int i = 1; i < 8 * KG; ++i) { mn = fminf(mn, r[i]); mx = fmaxf(mx, r[i]); }
@@ -1351,9 +1401,9 @@ __global__ __launch_bounds__(64 * c16_waves(CM), 4) void encode_c16_kernel(Encod
   }   // tiles
 }
 
-template <int BITS, int G, int CM>
+template <int BITS, int G, int CM, int ROT>
 hipError_t launch_c16_t(const EncodeParams& p, hipStream_t s) {
-  auto k = encode_c16_kernel<BITS, G, CM>;
+  auto k = encode_c16_kernel<BITS, G, CM, ROT>;
   constexpr int NT = 64 * c16_waves(CM), TT = NT / 4;
   int occ = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(k), NT, 0);
@@ -1446,19 +1496,29 @@ hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   const bool bf16 = a.c.x_dtype == KVC_BF16;
+  const bool c16_ok = bf16 && a.c.D == 128 && p.mode == MODE_CENTROID && !p.recon && !p.pred &&
+                      a.c.C <= 512 && p.x_stride % 8 == 0;
+  if (a.c.rot != 0 && !c16_ok) return hipErrorInvalidValue;   // rotation: 16-token-wave kernel only
   // centroid and coefficient (m = 16, INT4) bases, bf16 d = 128, <= 512 centroids:
   // register-resident MFMA assignment, persistent workgroups per head
   const bool cen_ok = p.mode == MODE_CENTROID && (a.c.group == 16 || a.c.group == 32 || a.c.group == 64);
   const bool coeff_ok = p.mode == MODE_COEFF && a.c.m == 16 && a.c.group == 16 && a.c.bits == 4;
   if (bf16 && a.c.D == 128 && cen_ok && !p.recon && !p.pred && a.c.C <= 512 && p.x_stride % 8 == 0) {
-#define KVC_ENC_C16(B, G, CM)                                                            \
-    if (a.c.bits == B && a.c.group == G && (a.c.C <= 256) == (CM == 256)) return launch_c16_t<B, G, CM>(p, s);
-    KVC_ENC_C16(2, 16, 256) KVC_ENC_C16(2, 32, 256) KVC_ENC_C16(2, 64, 256)
-    KVC_ENC_C16(4, 16, 256) KVC_ENC_C16(4, 32, 256) KVC_ENC_C16(4, 64, 256)
-    KVC_ENC_C16(2, 16, 512) KVC_ENC_C16(2, 32, 512) KVC_ENC_C16(2, 64, 512)
-    KVC_ENC_C16(4, 16, 512) KVC_ENC_C16(4, 32, 512) KVC_ENC_C16(4, 64, 512)
+#define KVC_ENC_C16(B, G, CM, R)                                                         \
+    if (a.c.bits == B && a.c.group == G && (a.c.C <= 256) == (CM == 256) && a.c.rot == R) \
+      return launch_c16_t<B, G, CM, R>(p, s);
+#define KVC_ENC_C16_CM(CM)                                                                \
+    KVC_ENC_C16(2, 16, CM, 0) KVC_ENC_C16(2, 32, CM, 0) KVC_ENC_C16(2, 64, CM, 0)          \
+    KVC_ENC_C16(4, 16, CM, 0) KVC_ENC_C16(4, 32, CM, 0) KVC_ENC_C16(4, 64, CM, 0)          \
+    KVC_ENC_C16(2, 16, CM, 16) KVC_ENC_C16(2, 32, CM, 16) KVC_ENC_C16(2, 64, CM, 16)       \
+    KVC_ENC_C16(4, 16, CM, 16) KVC_ENC_C16(4, 32, CM, 16) KVC_ENC_C16(4, 64, CM, 16)       \
+    KVC_ENC_C16(2, 64, CM, 64) KVC_ENC_C16(4, 64, CM, 64)
+    KVC_ENC_C16_CM(256)
+    KVC_ENC_C16_CM(512)
+#undef KVC_ENC_C16_CM
 #undef KVC_ENC_C16
   }
+  if (a.c.rot != 0) return hipErrorInvalidValue;   // a width / group pair without a kernel
   if (bf16 && a.c.D == 128 && (cen_ok || coeff_ok) && a.c.C <= 512 && p.x_stride % 8 == 0) {
 #define KVC_ENC_CEN(B, G, CM, CF)                                                        \
     if (a.c.bits == B && a.c.group == G && (a.c.C <= 256) == (CM == 256) && coeff_ok == CF) \

@@ -14,6 +14,7 @@ namespace kvc {
 struct CodecArgs {
   int H = 0, D = 0, bits = 0, group = 0, base = 0, C = 0, rank = 0, n_inputs = 0, m = 0;
   int x_dtype = 0;
+  int rot = 0;         // Hn residual transform width: 0, 16 or 64
   int vec_len = 0;     // values quantized per token-head (D, or m for COEFF)
   int code_words = 0;  // uint32 words per token-head
   int groups = 0;      // scale/zero words per token-head

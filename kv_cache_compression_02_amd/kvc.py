@@ -39,7 +39,7 @@ class KvcError(RuntimeError):
 class _Codec(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("heads", "head_dim", "bits", "group", "base",
                                               "n_centroids", "rank", "n_inputs", "coeff_dim",
-                                              "x_dtype")]
+                                              "x_dtype", "rotation")]
 
 
 class _Store(ctypes.Structure):
@@ -137,10 +137,12 @@ class Codec:
     n_inputs: int = 0
     coeff_dim: int = 0
     x_dtype: int = BF16
+    rotation: int = 0
 
     def c(self) -> _Codec:
         return _Codec(self.heads, self.head_dim, self.bits, self.group, self.base,
-                      self.n_centroids, self.rank, self.n_inputs, self.coeff_dim, self.x_dtype)
+                      self.n_centroids, self.rank, self.n_inputs, self.coeff_dim, self.x_dtype,
+                      self.rotation)
 
 
 @dataclass

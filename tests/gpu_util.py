@@ -43,12 +43,12 @@ def bf16_to_f32_np(t: torch.Tensor) -> np.ndarray:
 
 
 def check_centroid_store(got: dict, x: np.ndarray, C: np.ndarray, bits: int, group: int,
-                         rows=slice(None), window: float = 1e-5):
+                         rows=slice(None), window: float = 1e-5, rotation: int = 0):
     """Bit-exact comparison of a centroid-codec store against the oracle on token rows
     `rows` (head-major store).  Assignments may differ only inside the near-tie window
     (relative top-2 gap < `window`); for such tokens the GPU's index must itself lie in
     the window and the codes must equal the oracle quantizer run with the GPU's index."""
-    want = ocodec.encode_centroid(x, C, bits, group)
+    want = ocodec.encode_centroid(x, C, bits, group, rotation=rotation)
     gi = got["index"][:, rows].T.astype(np.int64)           # [N, H]
     wi = want["idx"]
     diff = gi != wi
@@ -61,7 +61,7 @@ def check_centroid_store(got: dict, x: np.ndarray, C: np.ndarray, bits: int, gro
         dg = np.take_along_axis(dist, gi[..., None], -1)[..., 0]
         assert np.all((dg - d1)[diff] <= window * d1[diff])
         base = C[np.arange(C.shape[0])[None, :], gi]
-        re = ocodec.encode_residual(x, base, bits, group)
+        re = ocodec.encode_residual(x, base, bits, group, rotation)
         want_store = ocodec.to_store(re["q"], re["s16"], re["z16"], bits, gi, C.shape[1])
     else:
         want_store = want["store"]

@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
     assert declared == set(kvc.EXPORTED)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.kvc_abi_version() == 1
+    assert L.kvc_abi_version() == 2
 
 
 def test_status_strings():
@@ -125,6 +125,47 @@ def test_attend_validation_errors():
     assert chunk(ck=FAKE + 8) == kvc.KVC_E_ALIGN
     need = L.kvc_workspace_bytes(kvc.OP_ATTEND_CHUNK, ctypes.byref(ok.c()), 8, 4)
     assert need >= 2 * 4 * 2 * 129 * 4   # two parts (history, chunk) of 4 queries x 2 heads
+
+
+def test_rotation_validation_errors():
+    L = _lib()
+    rc = kvc.Codec(2, 128, 2, 64, kvc.BASE_CENTROID, 256, rotation=64)
+    b = kvc._Base()
+    b.centroids = FAKE
+    # widths other than 16 / 64, groups the width does not divide, groups above 64
+    for bad in (kvc.Codec(2, 128, 2, 64, kvc.BASE_CENTROID, 256, rotation=32),
+                kvc.Codec(2, 128, 2, 32, kvc.BASE_CENTROID, 256, rotation=64),
+                kvc.Codec(2, 128, 2, 128, kvc.BASE_CENTROID, 256, rotation=64),
+                kvc.Codec(2, 128, 2, 64, kvc.BASE_NONE, rotation=64),
+                kvc.Codec(2, 128, 2, 64, kvc.BASE_CENTROID, 600, rotation=64),
+                kvc.Codec(2, 64, 2, 64, kvc.BASE_CENTROID, 256, rotation=64),
+                kvc.Codec(2, 128, 2, 64, kvc.BASE_CENTROID, 256, x_dtype=kvc.F32, rotation=16)):
+        assert _enc(bad, base=b) == kvc.KVC_E_UNSUPPORTED, bad
+    # no reconstruction / prediction output from the rotated encoder, strides of 8
+    st = kvc._Store(FAKE, FAKE, FAKE, 16)
+    r = L.kvc_encode(ctypes.byref(rc.c()), ctypes.c_void_p(FAKE), 4, 0, ctypes.byref(b),
+                     ctypes.byref(st), 0, ctypes.c_void_p(FAKE), None, None, 0, None)
+    assert r == kvc.KVC_E_UNSUPPORTED
+    assert _enc(rc, base=b, stride=2 * 128 + 4) == kvc.KVC_E_UNSUPPORTED
+    # attention: rotated residuals need centroid K and V; the mixed-dimensional form
+    # takes no rotated values
+    st2 = kvc._Store(FAKE, FAKE, FAKE, 16)
+
+    def att(kc, vc, fn=L.kvc_attend_compressed):
+        return fn(ctypes.byref(kc.c()), ctypes.byref(st2), ctypes.byref(b), ctypes.byref(vc.c()),
+                  ctypes.byref(st2), ctypes.byref(b), 8, ctypes.c_void_p(FAKE), 4,
+                  ctypes.c_float(0.1), ctypes.c_void_p(FAKE), None, None, 0, None)
+    plain_none = kvc.Codec(2, 128, 2, 64, kvc.BASE_NONE)
+    assert att(rc, plain_none) == kvc.KVC_E_UNSUPPORTED
+    assert att(plain_none, rc) == kvc.KVC_E_UNSUPPORTED
+    coeff = kvc.Codec(2, 128, 4, 16, kvc.BASE_COEFF, 256, coeff_dim=16)
+    b.basis = FAKE
+    assert att(coeff, rc, fn=L.kvc_attend_mixed_dim) == kvc.KVC_E_UNSUPPORTED
+    # the workspace does not depend on the rotation
+    plain = kvc.Codec(2, 128, 2, 64, kvc.BASE_CENTROID, 256)
+    for op in (kvc.OP_ATTEND, kvc.OP_ATTEND_CHUNK):
+        assert (L.kvc_workspace_bytes(op, ctypes.byref(rc.c()), 5000, 300)
+                == L.kvc_workspace_bytes(op, ctypes.byref(plain.c()), 5000, 300))
 
 
 def test_python_binding_raises_on_status():

@@ -75,6 +75,40 @@ def test_bf16_attention_small_ragged(n_keys):
         assert np.allclose(out.cpu().numpy(), np.broadcast_to(vh[:1], out.shape), atol=1e-6)
 
 
+@pytest.mark.parametrize("bits,group", [(2, 64), (4, 16), (2, 16), (4, 64)])
+def test_bf16_attention_other_groups(bits, group):
+    """Scale/zero groups of 16 and 64 channels (one and four per K decode lane)."""
+    dev = device()
+    d = synth.cfg1(seed=13, hist_frames=3, query_frames=1, tokens=100, heads=3, dim=128,
+                   n_centroids=40)
+    (kc, ks, kb), (vc, vs, vb) = _compress(d, 3, 128, bits, group, 40, kvc.BF16, dev)
+    q = to_dev(d["Q"], dev)
+    out = kvc.kvc_attend_compressed(kc, ks, kb, vc, vs, vb, 300, q, d["scale"])
+    torch.cuda.synchronize()
+    kh, vh = _oracle_cache(d, bits, group, "bf16")
+    ref = oatt.attention(nm.bf16_to_f32(d["Q"]), kh, vh, d["scale"])
+    err = np.abs(out.cpu().numpy() - ref).max()
+    assert err <= 2e-2, err
+
+
+@pytest.mark.parametrize("n_keys,n_centroids", [(129, 40), (1, 40), (130, 40), (129, 300), (3, 300)])
+def test_bf16_attention_store_capacity_equals_keys(n_keys, n_centroids):
+    """Stores exactly n_keys rows long: the last keys' index entries (1 byte with at most
+    256 centroids, else 2) end the buffer at any byte, not at a 4-byte boundary."""
+    dev = device()
+    d = synth.cfg1(seed=15, hist_frames=3, query_frames=1, tokens=100, heads=3, dim=128,
+                   n_centroids=n_centroids)
+    (kc, ks, kb), (vc, vs, vb) = _compress(d, 3, 128, 2, 32, n_centroids, kvc.BF16, dev, n=n_keys)
+    assert ks.index.shape[-1] == n_keys
+    q = to_dev(d["Q"], dev)
+    out = kvc.kvc_attend_compressed(kc, ks, kb, vc, vs, vb, n_keys, q, d["scale"])
+    torch.cuda.synchronize()
+    kh, vh = _oracle_cache(d, 2, 32, "bf16", n=n_keys)
+    ref = oatt.attention(nm.bf16_to_f32(d["Q"]), kh, vh, d["scale"])
+    err = np.abs(out.cpu().numpy() - ref).max()
+    assert err <= 2e-2, err
+
+
 @pytest.mark.parametrize("n_keys", [2000, 1100])
 def test_bf16_attention_key_splits(n_keys):
     """With a workspace the keys are split across workgroups (here 4 or 2 splits, the
