@@ -13,10 +13,11 @@ inputs are resident in HBM when the timed region starts.  The metric is query
 tokens per second (each query token covers all 12 heads).
 
 Prints ONE JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
-`--workload dplr|temporal|mixed|chunk` measures the other paths instead (the 30-layer
+`--workload dplr|temporal|mixed|chunk|rotated` measures the other paths instead (the 30-layer
 cross-layer chain, the temporal chain + attention over its reconstruction,
-mixed-dimensional attention, and attention over a compressed history plus an
-uncompressed current chunk); the default line is the one above.
+mixed-dimensional attention, attention over a compressed history plus an
+uncompressed current chunk, and the default workload with H64-rotated residuals); the
+default line is the one above.
 """
 from __future__ import annotations
 
@@ -460,6 +461,73 @@ def bench_mixed(args, torch, kvc, synth, dev):
                          "frac_hbm": (enc_k + enc_v) / (t_k + t_v) / 1e9 / HBM_PEAK_GBS})
 
 
+def bench_rotated(args, torch, kvc, synth, dev):
+    """The default workload's shapes with the Hn residual transform: K and V residuals
+    rotated by H64 / 8 per 64-channel group before INT2 g64 quantization (256
+    centroids/head).  One step = encode of the 4680-token chunk (K, V) + attention of
+    4680 queries over the 32760-token history, whose tile decode rotates back."""
+    d = synth.cfg1()
+    H, D, C = d["heads"], d["dim"], d["centroids"]
+    bits, group, rot = 2, 64, 64
+    lo, hi = d["chunk"]
+    nk, nq = d["K"].shape[0], d["Q"].shape[0]
+
+    def b16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view("int16")).view(torch.bfloat16).to(dev)
+
+    K, V, Q = b16(d["K"]), b16(d["V"]), b16(d["Q"])
+    codec = kvc.Codec(H, D, bits, group, kvc.BASE_CENTROID, C, rotation=rot)
+    ks, vs = kvc.Store.allocate(codec, nk, dev), kvc.Store.allocate(codec, nk, dev)
+    kb = kvc.BaseParams(centroids=b16(d["Ck"]))
+    vb = kvc.BaseParams(centroids=b16(d["Cv"]))
+    kvc.kvc_encode(codec, K[:lo], ks, 0, kb)
+    kvc.kvc_encode(codec, V[:lo], vs, 0, vb)
+    Kc, Vc = K[lo:hi].contiguous(), V[lo:hi].contiguous()
+    out = torch.empty((nq, H, D), dtype=torch.float32, device=dev)
+    ws = kvc.kvc.workspace_for(kvc.kvc.OP_ATTEND, codec, nk, dev, n_queries=nq)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e: e[0].record()
+        kvc.kvc_encode(codec, Kc, ks, lo, kb)
+        kvc.kvc_encode(codec, Vc, vs, lo, vb)
+        if e: e[1].record()
+        kvc.kvc_attend_compressed(codec, ks, kb, codec, vs, vb, nk, Q, d["scale"], out=out,
+                                  workspace=ws)
+        if e: e[2].record()
+
+    log("timing")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    t_enc = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps * 1e-3
+    t_att = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps * 1e-3
+    achieved = attention_flops(nq, nk, D, H) / t_att / 1e12
+    enc_b = 2 * encode_bytes(hi - lo, H, D, bits, group, C)
+    line = _line("compressed-KV attention query-tok/s, H64-rotated residuals (encode 3-frame "
+                 "chunk + attention over history)", nq * args.steps / elapsed, "query-tok/s",
+                 args, elapsed / args.steps, "bf16",
+                 {"workload": "centroid+H64-rotated INT2 g64 codec, 12 heads x 128, 256 "
+                              "centroids/head; encode 4680-token chunk (K,V) + attention 4680 q "
+                              "x 32760 keys",
+                  "heads": H, "head_dim": D, "history_tokens": nk, "queries": nq,
+                  "chunk_tokens": hi - lo, "bits": bits, "group": group, "rotation": rot,
+                  "centroids": C},
+                 {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
+                  "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
+                  "traffic": recorded_traffic("attend_bf16_kernel_rotated_h64_12x128_4680q_32760k.md",
+                                              "kv_cache_compression_02_amd/csrc/attend.hip"),
+                  "kernel": "attend_bf16_kernel (rotated)", "ms": t_att * 1e3})
+    line["encode"] = {"ms": t_enc * 1e3, "bytes": enc_b, "GB/s": enc_b / t_enc / 1e9,
+                      "frac_hbm": enc_b / t_enc / 1e9 / HBM_PEAK_GBS}
+    return line
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -469,10 +537,11 @@ def main() -> int:
     ap.add_argument("--copy-ref", action="store_true",
                     help="run one plain 256 MiB device copy first (calibrates HBM counters)")
     ap.add_argument("--workload", default="centroid",
-                    choices=("centroid", "dplr", "temporal", "mixed", "chunk"),
+                    choices=("centroid", "dplr", "temporal", "mixed", "chunk", "rotated"),
                     help="centroid: the default line; the others measure the cross-layer "
                          "chain, the temporal chain + attention, mixed-dimensional attention, "
-                         "attention over the compressed history plus an uncompressed chunk")
+                         "attention over the compressed history plus an uncompressed chunk, "
+                         "the default workload with H64-rotated residuals")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -489,7 +558,7 @@ def main() -> int:
         copy_reference(torch, dev)
     if args.workload != "centroid":
         line = {"dplr": bench_dplr, "temporal": bench_temporal, "mixed": bench_mixed,
-                "chunk": bench_chunk}[args.workload](
+                "chunk": bench_chunk, "rotated": bench_rotated}[args.workload](
             args, torch, kvc, synth, dev)
         print(json.dumps(line))
         return 0

@@ -179,12 +179,41 @@ __device__ __forceinline__ int vpos(int row, int key) {
 // into bf16 high and low parts (16 + 16); the queries carry B^T q split the same way,
 // and three extra MFMA steps add (B^T q) . c to q . C[a] with about 2^-16 relative
 // error - the score is formed without reconstructing the key.
+// The value of the lane M = 1, 2 or 4 apart within aligned groups of 8 lanes, by DPP
+// (quad_perm [1,0,3,2] / [2,3,0,1]; for 4, lanes 0-3 of each group read 4-7 by
+// row_shl:4 and lanes 4-7 read 0-3 by row_shr:4, selected by bank masks).
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  int r;
+  if constexpr (M == 1) {
+    r = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);
+  } else if constexpr (M == 2) {
+    r = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);
+  } else {
+    static_assert(M == 4, "lane distance");
+    r = __builtin_amdgcn_update_dpp(x, x, 0x104, 0xF, 0x5, false);
+    r = __builtin_amdgcn_update_dpp(r, x, 0x114, 0xF, 0xA, false);
+  }
+  return __builtin_bit_cast(float, r);
+}
+
+// One butterfly stage between lanes M apart: the lower piece takes a + b, the upper
+// a - b, both as fma(own, +-1, partner) - one rounding of the exact sum or difference.
+template <int M, int W>
+__device__ __forceinline__ void hn_lane_stage(float (&v)[W], int piece) {
+  const float sg = (piece & M) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < W; ++i) v[i] = __builtin_fmaf(v[i], sg, lane_xor<M>(v[i]));
+}
+
 // Hn transform back (Coral-KV Fig. 5: residuals were rotated per group of n channels
 // before quantization) on a lane's W consecutive channels of one vector, pieces of the
-// vector on consecutive lanes (piece = lane's index within the vector): butterflies at
-// channel distance 1 .. W/2 in the lane, then W, 2W, .. n/2 with the lanes 1, 2, ..
-// apart - the order of the Sylvester recursion, so the result is the codec decoder's
-// to the bit.  The values come in already scaled by 1/sqrt(n) (exact).
+// vector on consecutive lanes (piece = lane's index within the vector, groups of 8
+// lanes aligned): butterflies at channel distance 1 .. W/2 in the lane, then W, 2W, ..
+// n/2 with the lanes 1, 2, 4 apart - the order of the Sylvester recursion, so the
+// result is the codec decoder's to the bit.  The values come in already scaled by
+// 1/sqrt(n) (exact).
 template <int W>
 __device__ __forceinline__ void hn_back(float (&v)[W], int piece, int n) {
 #pragma unroll
@@ -197,15 +226,10 @@ __device__ __forceinline__ void hn_back(float (&v)[W], int piece, int n) {
       v[i + h] = a - b;
     }
   }
-#pragma unroll
-  for (int m = 1; m < 8; m <<= 1) {
-    if (m * W >= n) break;
-    const bool up = (piece & m) != 0;
-#pragma unroll
-    for (int i = 0; i < W; ++i) {
-      const float o = __shfl_xor(v[i], m);
-      v[i] = up ? o - v[i] : v[i] + o;
-    }
+  if (n > W) hn_lane_stage<1>(v, piece);
+  if (n > 2 * W) hn_lane_stage<2>(v, piece);
+  if constexpr (W < 16) {
+    if (n > 4 * W) hn_lane_stage<4>(v, piece);
   }
 }
 
@@ -610,7 +634,8 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
 
   // The K decode of the next tile cut into 16 steps, one per score MFMA: steps 0..7
   // dequantize two channels each (codes as f16 denormals through v_fma_mix), steps
-  // 8..15 add the centroid and round one channel pair, step 15 stores the row.
+  // 8..15 add the centroid and round one channel pair, step 15 stores the row (with
+  // rotated residuals step 8 first rotates the 16 dequantized channels back).
   struct KDec {
     float s24, ze, dq[16];
     uint32_t o[8];
@@ -619,6 +644,11 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
     if (j == 0) {
       st.s24 = f16_bits_to_f32(kpr.sz & 0xFFFFu) * 0x1p24f;
       st.ze = f16_bits_to_f32(kpr.sz >> 16);
+      if constexpr (ROT) {   // the 1/sqrt(n) of the transform, folded in exactly
+        const float sc = p.k.rot == 64 ? 0.125f : (p.k.rot == 16 ? 0.25f : 1.0f);
+        st.s24 *= sc;
+        st.ze *= sc;
+      }
     }
     if (j < 8) {
       if constexpr (BITS == 2) {
@@ -632,6 +662,9 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
         st.dq[8 * wd + r + 4] = __builtin_fmaf(code_hi(b), st.s24, st.ze);
       }
     } else {
+      if constexpr (ROT) {   // all 16 channels dequantized: rotate back before the centroid
+        if (j == 8 && p.k.rot) hn_back<16>(st.dq, kw, p.k.rot);
+      }
       const int i = j - 8;
       const uint32_t cwi = (i < 4) ? (i == 0 ? kpr.c0.x : i == 1 ? kpr.c0.y : i == 2 ? kpr.c0.z : kpr.c0.w)
                                    : (i == 4 ? kpr.c1.x : i == 5 ? kpr.c1.y : i == 6 ? kpr.c1.z : kpr.c1.w);
@@ -815,7 +848,7 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
   // the final tile of a ragged history (the only one that masks keys) runs after the
   // loop, so the loop body has one variant
   const int tfull = (te * BK > nk) ? te - 1 : te;
-  if constexpr (!DENSE && !MIXED && !ROT) {
+  if constexpr (!DENSE && !MIXED) {
     // V decode first, K decode among the score MFMAs (see compute)
     int t = tb;
     for (; t < min(tfull, te - 1); ++t) {
