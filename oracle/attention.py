@@ -17,10 +17,25 @@ results').  Readings taken here:
   uncompressed; quantized keys take attention mass from the unquantized current
   chunk): one softmax over the history keys followed by the chunk keys.
 
+* Jensen-bias correction (the INT2 Jensen-bias abstract on the Coral-KV listing page:
+  quantization noise in the cached keys inflates their softmax weight through the
+  convexity of exp; a per-score correction from the keys' quantization step sizes and
+  the query, by a second-order Taylor expansion): a key quantized with step s_c on
+  channel c carries noise e_c uniform on [-s_c/2, s_c/2] (variance s_c^2 / 12), so
+  log E[exp(scale q . (k + e))] = scale q . k + (scale^2 / 2) sum_c q_c^2 s_c^2 / 12 to
+  second order, and the corrected logit of a compressed key is
+  scale q . k_hat - (scale^2 / 24) sum_g s_g^2 ||q_g||^2 over its scale groups g (one
+  step per group).  Uncompressed current-chunk keys get no correction.  With the Hn
+  rotation the noise is uniform in rotated coordinates; each rotation block lies inside
+  one scale group and keeps the group's query norm, so the formula is unchanged.
+
 Pins (tests/test_oracle_attention.py): torch's fp64 scaled_dot_product_attention
 on CPU, one key -> O = v, zero query -> mean of V, the mixed-dimensional identity
-against scores computed from explicitly reconstructed keys, and for the chunk form
-the log-sum-exp merge of the two parts' separate attentions.
+against scores computed from explicitly reconstructed keys, for the chunk form
+the log-sum-exp merge of the two parts' separate attentions, and for the Jensen
+correction the exact log E[exp(a e)] = log(sinh(a s / 2) / (a s / 2)) of uniform
+noise (agreement to fourth order), a Monte Carlo check that the corrected weights
+are unbiased where the plain ones are not, and zero steps giving plain attention.
 """
 from __future__ import annotations
 
@@ -97,3 +112,36 @@ def softmax_pv(scores: np.ndarray, v: np.ndarray, return_lse: bool = False):
 
 def mixed_attention(q, Ck, idx, B, chat, v, scale, return_lse: bool = False):
     return softmax_pv(mixed_scores(q, Ck, idx, B, chat, scale), v, return_lse)
+
+
+def jensen_correction(q: np.ndarray, step: np.ndarray, group: int, scale: float) -> np.ndarray:
+    """(scale^2 / 24) sum_g s_g^2 ||q_g||^2 for every (head, query, key), fp64.
+
+    q [Nq,H,d]; step [Nk,H,d/group] (the keys' group step sizes) -> [H,Nq,Nk]."""
+    q64 = np.asarray(q, dtype=np.float64)
+    s64 = np.asarray(step, dtype=np.float64)
+    nq, heads, d = q64.shape
+    qn = (q64.reshape(nq, heads, d // group, group) ** 2).sum(-1)      # [Nq,H,G] ||q_g||^2
+    out = np.empty((heads, nq, s64.shape[0]), dtype=np.float64)
+    for h in range(heads):
+        out[h] = (scale * scale / 24.0) * (qn[:, h] @ (s64[:, h] ** 2).T)
+    return out
+
+
+def attention_jensen(q: np.ndarray, k: np.ndarray, v: np.ndarray, step: np.ndarray, group: int,
+                     scale: float, k_chunk=None, v_chunk=None, return_lse: bool = False):
+    """Softmax attention with the Jensen-bias correction subtracted from the logits of
+    the compressed keys k (step sizes `step`), followed by the optional uncompressed
+    chunk keys (no correction); fp64."""
+    q64 = np.asarray(q, dtype=np.float64)
+    k64 = np.asarray(k, dtype=np.float64)
+    heads = q64.shape[1]
+    corr = jensen_correction(q64, step, group, scale)
+    scores = np.stack([(q64[:, h] @ k64[:, h].T) * scale for h in range(heads)]) - corr
+    vals = np.asarray(v, dtype=np.float64)
+    if k_chunk is not None:
+        kc = np.asarray(k_chunk, dtype=np.float64)
+        sc = np.stack([(q64[:, h] @ kc[:, h].T) * scale for h in range(heads)])
+        scores = np.concatenate([scores, sc], axis=2)
+        vals = np.concatenate([vals, np.asarray(v_chunk, dtype=np.float64)])
+    return softmax_pv(scores, vals, return_lse)

@@ -107,3 +107,68 @@ def test_chunk_attention_is_the_lse_merge_of_its_parts():
     p = np.exp(np.array(s) - max(s))
     ref = (p[:, None] * np.concatenate([vh, vc])[:, 1]).sum(0) / p.sum()
     assert np.allclose(out[4, 1], ref, atol=1e-12)
+
+
+# ------------------------------ Jensen-bias correction ------------------------------
+
+def test_jensen_correction_is_the_second_order_term_of_uniform_noise():
+    # for e uniform on [-s/2, s/2]: log E[exp(a e)] = log(sinh(x) / x), x = a s / 2,
+    # = x^2 / 6 - x^4 / 180 + ...; the correction must be the x^2 / 6 term summed over
+    # channels, so it agrees with the exact value to within the x^4 term
+    rng = np.random.default_rng(5)
+    nq, nk, H, d, g = 7, 9, 2, 64, 16
+    q = rng.standard_normal((nq, H, d))
+    step = rng.uniform(0.01, 0.3, size=(nk, H, d // g))
+    scale = 0.125
+    corr = attention.jensen_correction(q, step, g, scale)
+    s_ch = np.repeat(step, g, axis=-1)                                   # [nk,H,d]
+    for h in range(H):
+        x = scale * q[:, h, None, :] * s_ch[None, :, h, :] / 2           # [nq,nk,d]
+        exact = np.where(x == 0, 0.0, np.log(np.sinh(x) / np.where(x == 0, 1, x))).sum(-1)
+        fourth = (x ** 4).sum(-1) / 180
+        assert np.all(np.abs(corr[h] - exact) <= 1.01 * fourth + 1e-15)
+        assert np.all(np.abs(corr[h] - exact) <= 0.05 * corr[h] + 1e-15)
+
+
+def test_jensen_corrected_weights_are_unbiased_by_monte_carlo():
+    # noisy keys k + e, e uniform with the per-group steps: the mean of exp(logit - corr)
+    # recovers exp(logit of k) within Monte Carlo error, the plain mean does not
+    rng = np.random.default_rng(6)
+    d, g, scale = 32, 16, 0.25
+    q = rng.standard_normal((1, 1, d))
+    k = rng.standard_normal((1, 1, d))
+    step = np.array([[[0.8, 1.2]]])
+    corr = attention.jensen_correction(q, step, g, scale)[0, 0, 0]
+    s_ch = np.repeat(step[0, 0], g)
+    e = (rng.random((400000, d)) - 0.5) * s_ch
+    logits = scale * ((k[0, 0] + e) @ q[0, 0])
+    true = scale * float(k[0, 0] @ q[0, 0])
+    w = np.exp(logits - true)
+    sem = w.std() / np.sqrt(w.size)
+    assert abs(np.exp(-corr) * w.mean() - 1.0) < 4 * sem + 2e-4
+    assert w.mean() - 1.0 > 20 * sem                   # the bias the correction removes
+
+
+def test_jensen_attention_reduces_to_plain_and_chunk_forms():
+    rng = np.random.default_rng(7)
+    nq, nk, nc, H, d, g = 5, 11, 4, 2, 32, 16
+    q, k, v = (rng.standard_normal((n, H, d)) for n in (nq, nk, nk))
+    kc, vc = rng.standard_normal((nc, H, d)), rng.standard_normal((nc, H, d))
+    zero = np.zeros((nk, H, d // g))
+    np.testing.assert_allclose(attention.attention_jensen(q, k, v, zero, g, 0.3),
+                               attention.attention(q, k, v, 0.3), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(
+        attention.attention_jensen(q, k, v, zero, g, 0.3, k_chunk=kc, v_chunk=vc),
+        attention.attention_with_chunk(q, k, v, kc, vc, 0.3), rtol=0, atol=1e-12)
+    # a uniform step on every key shifts all history logits of a query by the same
+    # amount: with no chunk the softmax is unchanged, with a chunk the history's total
+    # weight drops by exactly exp(-corr)
+    step = np.full((nk, H, d // g), 0.5)
+    np.testing.assert_allclose(attention.attention_jensen(q, k, v, step, g, 0.3),
+                               attention.attention(q, k, v, 0.3), rtol=0, atol=1e-12)
+    corr = attention.jensen_correction(q, step, g, 0.3)[:, :, 0]          # [H, nq]
+    _, lse_h = attention.attention(q, k, v, 0.3, return_lse=True)
+    _, lse_c = attention.attention(q, kc, vc, 0.3, return_lse=True)
+    _, lse = attention.attention_jensen(q, k, v, step, g, 0.3, k_chunk=kc, v_chunk=vc,
+                                        return_lse=True)
+    np.testing.assert_allclose(lse, np.logaddexp(lse_h - corr, lse_c), rtol=0, atol=1e-12)
