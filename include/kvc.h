@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 2
+#define KVC_ABI_VERSION 3
 
 typedef enum {
   KVC_OK = 0,
@@ -191,6 +191,20 @@ kvc_status kvc_decode(const kvc_codec* codec, const kvc_store* src, int64_t toke
                       int64_t n_tokens, const kvc_base_params* base, void* out, int32_t out_dtype,
                       float* pred_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Attention flags.
+ * KVC_ATTEND_JENSEN: Jensen-bias correction (the INT2 Jensen-bias abstract on the
+ *   Coral-KV listing page: rounding noise in quantized keys inflates their softmax
+ *   weight through the convexity of exp, which a per-score correction from the step
+ *   sizes and the query removes in expectation, by a second-order Taylor expansion).
+ *   The logit of a compressed key becomes softmax_scale * q . k_hat -
+ *   (softmax_scale^2 / 24) * sum_g s_g^2 * |q_g|^2 over its scale groups g (s_g = the
+ *   group's stored fp16 scale, the quantization step; q_g = the query's channels of
+ *   group g): the second-order term of log E[exp] for noise uniform on
+ *   [-s_g/2, s_g/2].  Keys of an uncompressed current chunk are not corrected.  The
+ *   correction enters the scores through one more bf16 MFMA per key block (s_g^2 and the
+ *   query term rounded to bf16).  Needs the bf16 path with centroid K and V. */
+enum { KVC_ATTEND_JENSEN = 1 };
+
 /* kvc_attend_compressed - O = softmax(Q K^T * softmax_scale) V per head, no mask,
  * over n_keys keys held compressed in stores k and v (rows 0..n_keys-1); K and V
  * tiles are decoded on the fly (NanoKV abstract: repeated attention over the
@@ -200,6 +214,7 @@ kvc_status kvc_decode(const kvc_codec* codec, const kvc_store* src, int64_t toke
  * bits = 16 on both K and V attends over uncompressed bf16 caches (for example the
  * reconstructions a predictor chain decodes; each cache below 2 GiB).
  *   q:   [n_queries][H][d] x_dtype, token stride H*d.
+ *   flags: 0 or KVC_ATTEND_JENSEN (other bits: KVC_E_UNSUPPORTED).
  *   out: [n_queries][H][d] fp32.
  *   lse: optional [H][n_queries] fp32 natural-log sum-exp of the scaled scores.
  *   workspace: optional device scratch.  With kvc_workspace_bytes(KVC_OP_ATTEND, kc,
@@ -219,8 +234,8 @@ kvc_status kvc_attend_compressed(const kvc_codec* kc, const kvc_store* k,
                                  const kvc_base_params* kp, const kvc_codec* vc,
                                  const kvc_store* v, const kvc_base_params* vp, int64_t n_keys,
                                  const void* q, int64_t n_queries, float softmax_scale,
-                                 float* out, float* lse, void* workspace, size_t workspace_bytes,
-                                 void* stream);
+                                 uint32_t flags, float* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /* kvc_attend_compressed_chunk - attention over the compressed history plus an
  * uncompressed current chunk: O = softmax(Q [K_hist ; K_chunk]^T * softmax_scale)
@@ -230,8 +245,9 @@ kvc_status kvc_attend_compressed(const kvc_codec* kc, const kvc_store* k,
  * and quantized keys take attention mass from the unquantized current chunk; this is
  * that layout.)  The two parts are attended separately and merged by their
  * log-sum-exp, the same softmax summed in another order.
- *   kc, vc, k, v, kp, vp, n_keys, q, out, lse: as kvc_attend_compressed (bf16 path only:
- *     d = 128, compressed K and V with centroid or no base).
+ *   kc, vc, k, v, kp, vp, n_keys, q, flags, out, lse: as kvc_attend_compressed (bf16
+ *     path only: d = 128, compressed K and V with centroid or no base); with
+ *     KVC_ATTEND_JENSEN only the history keys' logits are corrected.
  *   chunk_k, chunk_v: [n_chunk][H][d] bf16, token stride H*d, n_chunk >= 1.
  *   workspace: required, kvc_workspace_bytes(KVC_OP_ATTEND_CHUNK, kc, n_keys,
  *     n_queries) bytes; the contents are overwritten.
@@ -242,7 +258,7 @@ kvc_status kvc_attend_compressed_chunk(const kvc_codec* kc, const kvc_store* k,
                                        const kvc_store* v, const kvc_base_params* vp,
                                        int64_t n_keys, const void* chunk_k, const void* chunk_v,
                                        int64_t n_chunk, const void* q, int64_t n_queries,
-                                       float softmax_scale, float* out, float* lse,
+                                       float softmax_scale, uint32_t flags, float* out, float* lse,
                                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* kvc_attend_mixed_dim - NanoKV-Fast style attention from the stored representation

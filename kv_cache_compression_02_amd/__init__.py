@@ -5,7 +5,8 @@ include/kvc.h); ``kvc`` is a thin ctypes binding that marshals torch tensors
 (device memory and the current stream) into it.
 """
 from .kvc import (  # noqa: F401
-    BASE_CENTROID, BASE_COEFF, BASE_DPLR, BASE_NONE, BASE_TEMPORAL, BF16, F32, BaseParams,
+    ATTEND_JENSEN, BASE_CENTROID, BASE_COEFF, BASE_DPLR, BASE_NONE, BASE_TEMPORAL, BF16, F32,
+    BaseParams,
     Codec, KvcError, Store, kvc_attend_compressed, kvc_attend_compressed_chunk,
     kvc_attend_mixed_dim, kvc_decode,
     kvc_encode, kvc_store_bytes, kvc_workspace_bytes, lib,

@@ -307,12 +307,22 @@ static kvc_status check_attend(const kvc_codec* kc, const kvc_store* k, const kv
   return KVC_OK;
 }
 
+// Attention flags: the Jensen correction needs the bf16 path with centroid K and V.
+static kvc_status check_attend_flags(uint32_t flags, const AttendLaunch& a) {
+  if (flags & ~(uint32_t)KVC_ATTEND_JENSEN) return KVC_E_UNSUPPORTED;
+  if ((flags & KVC_ATTEND_JENSEN) &&
+      (a.kc.x_dtype != KVC_BF16 || a.kc.bits == 16 || a.kc.base != KVC_BASE_CENTROID ||
+       a.vc.base != KVC_BASE_CENTROID))
+    return KVC_E_UNSUPPORTED;
+  return KVC_OK;
+}
+
 kvc_status kvc_attend_compressed(const kvc_codec* kc, const kvc_store* k,
                                  const kvc_base_params* kp, const kvc_codec* vc,
                                  const kvc_store* v, const kvc_base_params* vp, int64_t n_keys,
                                  const void* q, int64_t n_queries, float softmax_scale,
-                                 float* out, float* lse, void* workspace, size_t workspace_bytes,
-                                 void* stream) {
+                                 uint32_t flags, float* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
   AttendLaunch a;
   kvc_status st = check_attend(kc, k, kp, vc, v, vp, n_keys, q, n_queries, out, lse, &a);
   if (st != KVC_OK) return st;
@@ -329,6 +339,9 @@ kvc_status kvc_attend_compressed(const kvc_codec* kc, const kvc_store* k,
   // rotated residuals are undone in the tile decode of the centroid-K-and-V kernels
   if ((a.kc.rot || a.vc.rot) && (a.kc.base != KVC_BASE_CENTROID || a.vc.base != KVC_BASE_CENTROID))
     return KVC_E_UNSUPPORTED;
+  st = check_attend_flags(flags, a);
+  if (st != KVC_OK) return st;
+  a.jensen = (flags & KVC_ATTEND_JENSEN) != 0;
   a.scale = softmax_scale;
   return from_hip(launch_attend(a, reinterpret_cast<hipStream_t>(stream)));
 }
@@ -338,7 +351,7 @@ kvc_status kvc_attend_compressed_chunk(const kvc_codec* kc, const kvc_store* k,
                                        const kvc_store* v, const kvc_base_params* vp,
                                        int64_t n_keys, const void* chunk_k, const void* chunk_v,
                                        int64_t n_chunk, const void* q, int64_t n_queries,
-                                       float softmax_scale, float* out, float* lse,
+                                       float softmax_scale, uint32_t flags, float* out, float* lse,
                                        void* workspace, size_t workspace_bytes, void* stream) {
   AttendLaunch a;
   kvc_status st = check_attend(kc, k, kp, vc, v, vp, n_keys, q, n_queries, out, lse, &a);
@@ -349,6 +362,9 @@ kvc_status kvc_attend_compressed_chunk(const kvc_codec* kc, const kvc_store* k,
     return KVC_E_UNSUPPORTED;
   if ((a.kc.rot || a.vc.rot) && (a.kc.base != KVC_BASE_CENTROID || a.vc.base != KVC_BASE_CENTROID))
     return KVC_E_UNSUPPORTED;
+  st = check_attend_flags(flags, a);
+  if (st != KVC_OK) return st;
+  a.jensen = (flags & KVC_ATTEND_JENSEN) != 0;
   if (n_chunk < 1) return KVC_E_SHAPE;
   if (!chunk_k || !chunk_v) return KVC_E_NULL;
   if (!aligned16(chunk_k) || !aligned16(chunk_v) || (workspace && !aligned16(workspace)))

@@ -59,6 +59,7 @@ struct AttnParams {
   int splits, tps;
   float* part_o;
   float* part_lse;
+  int jensen;   // subtract the Jensen-bias correction from compressed keys' logits
 };
 
 // Decode channels ch0..ch0+7 of key `key` (head h) as fp32 (cache dtype XT rounding
@@ -233,9 +234,17 @@ __device__ __forceinline__ void hn_back(float (&v)[W], int piece, int n) {
   }
 }
 
-template <int BITS, int VBITS, bool KCEN, bool VCEN, bool MIXED, bool DENSE = false, bool ROT = false>
+// JB (Jensen-bias correction, the INT2 Jensen-bias abstract on the Coral-KV listing
+// page): a compressed key with step s_g on scale group g has rounding noise of variance
+// s_g^2 / 12 per channel, which raises E[exp(logit)] by (scale^2 / 24) sum_g s_g^2
+// ||q_g||^2 to second order; the kernel subtracts that from the logit.  The K decode
+// writes s_g^2 (bf16) next to each key row (columns DM + g, zero for g >= d/group) and
+// every lane holds -(scale / 24) ||q_g||^2 of its query as a B operand (k = g), so one
+// more v_mfma_f32_32x32x16_bf16 per 32-key block adds the correction to the raw scores.
+template <int BITS, int VBITS, bool KCEN, bool VCEN, bool MIXED, bool DENSE = false, bool ROT = false,
+          bool JB = false>
 __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
-  constexpr int KR = MIXED ? DM + 32 + 8 : KROW;   // K tile row (bf16 elements)
+  constexpr int KR = MIXED ? DM + 32 + 8 : (JB ? DM + 16 + 8 : KROW);   // K tile row (bf16 elements)
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BK * KR];     // bf16
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][DM * VROW];   // fp16 bits
 
@@ -427,6 +436,15 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
       }
     }
   };
+  // JB: s_g^2 of a key row's scale group at column DM + g, written by the group's first lane
+  auto store_step_sq = [&](int dbuf, uint32_t szw) {
+    if constexpr (JB) {
+      if (((16 * kw) & (p.k.group - 1)) == 0) {
+        const float stp = f16_bits_to_f32(szw & 0xFFFFu);
+        k_lds[dbuf][kk * KR + DM + kgrp] = (uint16_t)f32_to_bf16_bits(stp * stp);
+      }
+    }
+  };
   auto dequant = [&](const KPre<BITS>& kpr, const VPre& vp, int buf, bool do_k = true) {
     if constexpr (DENSE) {
       uint4* dst = reinterpret_cast<uint4*>(&k_lds[buf][kk * KR + 16 * kw]);
@@ -505,6 +523,7 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
       uint4* dst = reinterpret_cast<uint4*>(&k_lds[buf][kk * KR + 16 * kw]);
       dst[0] = uint4{o[0], o[1], o[2], o[3]};
       dst[1] = uint4{o[4], o[5], o[6], o[7]};
+      store_step_sq(buf, kpr.sz);
      }
     }
     // ---- V: channels 8c8..8c8+7 of keys 2kp, 2kp+1 -> transposed fp16 (swizzled)
@@ -574,6 +593,38 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
     for (int ks = 0; ks < 8; ++ks) {
       if (myq < p.nq) qreg[ks] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * ks);
       else qreg[ks] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+
+  // JB: -(scale / 24) ||q_g||^2 for groups g = 0..7 (lanes of half 0; k = 8..15 and
+  // groups beyond d/group stay zero), and zeros in the unused step columns of both
+  // K buffers
+  bf16x8_t jbq = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  if constexpr (JB) {
+    float full[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      float a = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float qv = bf16_bits_to_f32((uint16_t)qreg[ks][e]);
+        a = __builtin_fmaf(qv, qv, a);
+      }
+      full[ks] = a + other_half(a, half);   // channels 16 ks .. 16 ks + 15
+    }
+    const int ksh = __builtin_ctz((unsigned)p.k.group) - 4;   // 16-channel blocks per group: 2^ksh
+    const float cf = -p.scale * (1.0f / 24.0f);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      float n = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) n += ((ks >> ksh) == g) ? full[ks] : 0.0f;
+      jbq[g] = half ? (short)0 : (short)f32_to_bf16_bits(cf * n);
+    }
+    const int g0 = DM / p.k.group;
+    for (int e = tid; e < 2 * BK * 16; e += NT) {
+      const int b = e / (BK * 16), r = (e >> 4) % BK, g = e & 15;
+      if (g >= g0) k_lds[b][r * KR + DM + g] = 0;
     }
   }
 
@@ -673,6 +724,7 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
         uint4* dst = reinterpret_cast<uint4*>(&k_lds[dbuf][kk * KR + 16 * kw]);
         dst[0] = uint4{st.o[0], st.o[1], st.o[2], st.o[3]};
         dst[1] = uint4{st.o[4], st.o[5], st.o[6], st.o[7]};
+        store_step_sq(dbuf, kpr.sz);
       }
     }
   };
@@ -746,9 +798,10 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
     // (one 16-byte read each: row 32 d + col, block (2 kh + half) ^ (2 d + col / 16) =
     // 2 (kh ^ d) + (half ^ col / 16)); (kb, hf) = kh covers keys 32*kb + 16*hf +
     // {4*half+0..3, 8+4*half+0..3}
-    // (the mixed-dimensional kernel, which holds B^T q as well, reads the last two
-    // channel blocks during the PV MFMAs instead, to stay within 256 registers)
-    constexpr int VE = MIXED ? 2 : 4;   // channel blocks read before the softmax
+    // (the mixed-dimensional kernel, which holds B^T q as well, and the rotated kernel
+    // with the Jensen correction read the last two channel blocks during the PV MFMAs
+    // instead, to stay within 256 registers)
+    constexpr int VE = (MIXED || (ROT && JB)) ? 2 : 4;   // channel blocks read before the softmax
     f16x8_t vf[4][4];
     const uint16_t* vbase = &v_lds[buf][col * VROW + 8 * (half ^ (col >> 4))];
     auto read_vf = [&](int d) {
@@ -768,6 +821,13 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ch, phi, sacc[kb], 0, 0, 0);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ch, plo, sacc[kb], 0, 0, 0);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cl, phi, sacc[kb], 0, 0, 0);
+      }
+    }
+    if constexpr (JB) {   // - (scale / 24) sum_g s_g^2 ||q_g||^2 into the raw scores
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8_t sq = *reinterpret_cast<const bf16x8_t*>(&k_lds[buf][(kb * 32 + col) * KR + DM + 8 * half]);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sq, jbq, sacc[kb], 0, 0, 0);
       }
     }
     if constexpr (MASK) {   // last, partial tile: mask keys >= nk
@@ -1062,15 +1122,21 @@ hipError_t launch_combine(const AttnParams& p, hipStream_t s) {
 hipError_t launch_compressed_bf16(const AttnParams& p, int kbits, int vbits, dim3 grid, hipStream_t s) {
   const bool kc = p.k.mode == SRC_CENTROID, vc = p.v.mode == SRC_CENTROID;
   const dim3 block(NT);
-  if (p.k.rot || p.v.rot) {   // rotated residuals: centroid K and V (validated by the caller)
+  const bool rot = p.k.rot || p.v.rot, jb = p.jensen != 0;
+  if (rot || jb) {   // rotated residuals / Jensen correction: centroid K and V (validated by the caller)
     if (!kc || !vc) return hipErrorInvalidValue;
-#define KVC_ATT_ROT(KB_, VB_)                                                                    \
-    if (kbits == KB_ && vbits == VB_) {                                                          \
-      hipLaunchKernelGGL((attend_bf16_kernel<KB_, VB_, true, true, false, false, true>), grid, block, 0, s, p); \
+#define KVC_ATT_RJ(KB_, VB_, R_, J_)                                                             \
+    if (kbits == KB_ && vbits == VB_ && rot == R_ && jb == J_) {                                 \
+      hipLaunchKernelGGL((attend_bf16_kernel<KB_, VB_, true, true, false, false, R_, J_>), grid, block, 0, s, p); \
       return hipGetLastError();                                                                  \
     }
-    KVC_ATT_ROT(2, 2) KVC_ATT_ROT(2, 4) KVC_ATT_ROT(4, 2) KVC_ATT_ROT(4, 4)
-#undef KVC_ATT_ROT
+#define KVC_ATT_RJ_BITS(R_, J_) \
+    KVC_ATT_RJ(2, 2, R_, J_) KVC_ATT_RJ(2, 4, R_, J_) KVC_ATT_RJ(4, 2, R_, J_) KVC_ATT_RJ(4, 4, R_, J_)
+    KVC_ATT_RJ_BITS(true, false)
+    KVC_ATT_RJ_BITS(false, true)
+    KVC_ATT_RJ_BITS(true, true)
+#undef KVC_ATT_RJ_BITS
+#undef KVC_ATT_RJ
     return hipErrorInvalidValue;
   }
 #define KVC_ATT(KB_, VB_, KC_, VC_)                                                       \
@@ -1120,6 +1186,7 @@ hipError_t launch_attend(const AttendLaunch& a, hipStream_t s) {
   p.lse = a.lse;
   p.k = make_src(a.kc, a.ks, a.kb);
   p.v = make_src(a.vc, a.vs, a.vb);
+  p.jensen = a.jensen;
   if (a.kc.x_dtype == KVC_BF16) {
     plan_splits(a, p);
     const int nqb = (int)((a.n_queries + BQ - 1) / BQ);
@@ -1165,6 +1232,7 @@ hipError_t launch_attend_chunk(const AttendLaunch& a, const void* chunk_k, const
   p.scale_log2 = a.scale * 1.4426950408889634f;
   p.k = make_src(a.kc, a.ks, a.kb);
   p.v = make_src(a.vc, a.vs, a.vb);
+  p.jensen = a.jensen;
   const int ntiles = (int)((a.n_keys + BK - 1) / BK);
   const int sp = chunk_history_splits(H, nq, a.n_keys);
   p.splits = sp;
@@ -1215,6 +1283,7 @@ hipError_t launch_attend_mixed(const AttendLaunch& a, hipStream_t s) {
   p.lse = a.lse;
   p.k = make_src(a.kc, a.ks, a.kb);
   p.v = make_src(a.vc, a.vs, a.vb);
+  p.jensen = a.jensen;
   p.basis = reinterpret_cast<const uint16_t*>(a.kb.basis);
   plan_splits(a, p);
   const int nqb = (int)((a.n_queries + BQ - 1) / BQ);

@@ -75,6 +75,7 @@ struct AttendLaunch {
   float* lse = nullptr;
   void* workspace = nullptr;      // optional: enables splitting the keys across workgroups
   size_t workspace_bytes = 0;
+  int jensen = 0;                 // KVC_ATTEND_JENSEN: correct the compressed keys' logits
 };
 
 // Launchers (return hipSuccess or the launch error).

@@ -24,6 +24,7 @@ F32, BF16 = 0, 1
 BASE_NONE, BASE_CENTROID, BASE_DPLR, BASE_TEMPORAL, BASE_COEFF = range(5)
 # workspace ops
 OP_ENCODE, OP_DECODE, OP_ATTEND, OP_ATTEND_MIXED, OP_ATTEND_CHUNK = range(5)
+ATTEND_JENSEN = 1
 
 EXPORTED = ("kvc_store_bytes", "kvc_encode", "kvc_decode", "kvc_attend_compressed",
             "kvc_attend_compressed_chunk", "kvc_attend_mixed_dim", "kvc_workspace_bytes",
@@ -73,15 +74,16 @@ def lib():
     L.kvc_encode.restype = I32
     L.kvc_decode.argtypes = [P(_Codec), P(_Store), I64, I64, P(_Base), VP, I32, VP, VP, SZ, VP]
     L.kvc_decode.restype = I32
+    U32 = ctypes.c_uint32
     att = [P(_Codec), P(_Store), P(_Base), P(_Codec), P(_Store), P(_Base), I64, VP, I64,
            ctypes.c_float, VP, VP, VP, SZ, VP]
-    L.kvc_attend_compressed.argtypes = att
+    L.kvc_attend_compressed.argtypes = att[:10] + [U32] + att[10:]
     L.kvc_attend_compressed.restype = I32
     L.kvc_attend_mixed_dim.argtypes = att
     L.kvc_attend_mixed_dim.restype = I32
     L.kvc_attend_compressed_chunk.argtypes = [P(_Codec), P(_Store), P(_Base), P(_Codec), P(_Store),
                                               P(_Base), I64, VP, VP, I64, VP, I64, ctypes.c_float,
-                                              VP, VP, VP, SZ, VP]
+                                              U32, VP, VP, VP, SZ, VP]
     L.kvc_attend_compressed_chunk.restype = I32
     L.kvc_workspace_bytes.argtypes = [I32, P(_Codec), I64, I64]
     L.kvc_workspace_bytes.restype = SZ
@@ -270,7 +272,7 @@ def workspace_for(op: int, codec: Codec, n_tokens: int, device, n_queries: int =
 
 
 def _attend(fn, name, kc, kstore, kbase, vc, vstore, vbase, n_keys, q, softmax_scale, out, lse,
-            want_lse, workspace):
+            want_lse, workspace, flags=None):
     nq = q.shape[0]
     if out is None:
         out = torch.empty((nq, kc.heads, kc.head_dim), dtype=torch.float32, device=q.device)
@@ -279,10 +281,12 @@ def _attend(fn, name, kc, kstore, kbase, vc, vstore, vbase, n_keys, q, softmax_s
     kb = (kbase or BaseParams()).c()
     vb = (vbase or BaseParams()).c()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(fn(ctypes.byref(kc.c()), ctypes.byref(kstore.c()), ctypes.byref(kb),
-              ctypes.byref(vc.c()), ctypes.byref(vstore.c()), ctypes.byref(vb), n_keys, _p(q, "q"),
-              nq, ctypes.c_float(softmax_scale), _p(out, "out"), _p(lse, "lse"),
-              _p(workspace, "workspace"), ws_bytes,
+    head = [ctypes.byref(kc.c()), ctypes.byref(kstore.c()), ctypes.byref(kb),
+            ctypes.byref(vc.c()), ctypes.byref(vstore.c()), ctypes.byref(vb), n_keys, _p(q, "q"),
+            nq, ctypes.c_float(softmax_scale)]
+    if flags is not None:   # entry points that take attention flags
+        head.append(ctypes.c_uint32(flags))
+    _check(fn(*head, _p(out, "out"), _p(lse, "lse"), _p(workspace, "workspace"), ws_bytes,
               _stream()), name)
     return (out, lse) if want_lse else out
 
@@ -290,19 +294,21 @@ def _attend(fn, name, kc, kstore, kbase, vc, vstore, vbase, n_keys, q, softmax_s
 def kvc_attend_compressed(kc: Codec, kstore: Store, kbase: Optional[BaseParams], vc: Codec,
                           vstore: Store, vbase: Optional[BaseParams], n_keys: int,
                           q: torch.Tensor, softmax_scale: float, out=None, lse=None,
-                          want_lse: bool = False, workspace=None):
-    """O = softmax(Q K^T * scale) V over the first n_keys compressed keys/values."""
+                          want_lse: bool = False, workspace=None, flags: int = 0):
+    """O = softmax(Q K^T * scale) V over the first n_keys compressed keys/values
+    (flags: 0 or ATTEND_JENSEN)."""
     return _attend(lib().kvc_attend_compressed, "kvc_attend_compressed", kc, kstore, kbase, vc,
-                   vstore, vbase, n_keys, q, softmax_scale, out, lse, want_lse, workspace)
+                   vstore, vbase, n_keys, q, softmax_scale, out, lse, want_lse, workspace, flags)
 
 
 def kvc_attend_compressed_chunk(kc: Codec, kstore: Store, kbase: Optional[BaseParams], vc: Codec,
                                 vstore: Store, vbase: Optional[BaseParams], n_keys: int,
                                 chunk_k: torch.Tensor, chunk_v: torch.Tensor, q: torch.Tensor,
                                 softmax_scale: float, workspace: torch.Tensor, out=None, lse=None,
-                                want_lse: bool = False):
+                                want_lse: bool = False, flags: int = 0):
     """Attention over the first n_keys compressed keys/values plus an uncompressed
-    current chunk (chunk_k, chunk_v: bf16 [n_chunk][H][d]), one softmax over both."""
+    current chunk (chunk_k, chunk_v: bf16 [n_chunk][H][d]), one softmax over both
+    (flags: 0 or ATTEND_JENSEN, which corrects the history keys' logits)."""
     nq = q.shape[0]
     if chunk_k.shape != chunk_v.shape or chunk_k.dtype != torch.bfloat16:
         raise ValueError("chunk_k and chunk_v must be bf16 tensors of one shape")
@@ -317,7 +323,8 @@ def kvc_attend_compressed_chunk(kc: Codec, kstore: Store, kbase: Optional[BasePa
         ctypes.byref(kc.c()), ctypes.byref(kstore.c()), ctypes.byref(kb), ctypes.byref(vc.c()),
         ctypes.byref(vstore.c()), ctypes.byref(vb), n_keys, _p(chunk_k, "chunk_k"),
         _p(chunk_v, "chunk_v"), chunk_k.shape[0], _p(q, "q"), nq, ctypes.c_float(softmax_scale),
-        _p(out, "out"), _p(lse, "lse"), _p(workspace, "workspace"), ws_bytes, _stream()),
+        ctypes.c_uint32(flags), _p(out, "out"), _p(lse, "lse"), _p(workspace, "workspace"),
+        ws_bytes, _stream()),
         "kvc_attend_compressed_chunk")
     return (out, lse) if want_lse else out
 

@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
     assert declared == set(kvc.EXPORTED)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.kvc_abi_version() == 2
+    assert L.kvc_abi_version() == 3
 
 
 def test_status_strings():
@@ -86,10 +86,12 @@ def test_attend_validation_errors():
     st = kvc._Store(FAKE, FAKE, None, 16)
     b = kvc._Base()
 
-    def att(kc, vc, nk=8, q=FAKE, out=FAKE, fn=L.kvc_attend_compressed):
+    def att(kc, vc, nk=8, q=FAKE, out=FAKE, fn=L.kvc_attend_compressed, flags=0):
+        fl = [] if fn == L.kvc_attend_mixed_dim else [ctypes.c_uint32(flags)]
         return fn(ctypes.byref(kc.c()), ctypes.byref(st), ctypes.byref(b), ctypes.byref(vc.c()),
                   ctypes.byref(st), ctypes.byref(b), nk, ctypes.c_void_p(q) if q else None, 4,
-                  ctypes.c_float(0.1), ctypes.c_void_p(out) if out else None, None, None, 0, None)
+                  ctypes.c_float(0.1), *fl, ctypes.c_void_p(out) if out else None, None, None, 0,
+                  None)
 
     assert att(kc, vc) == kvc.KVC_E_SHAPE                  # head mismatch
     assert att(kc, kc, nk=0) == kvc.KVC_E_SHAPE
@@ -105,24 +107,28 @@ def test_attend_validation_errors():
     k4 = kvc.Codec(2, 128, 4, 32, kvc.BASE_NONE, x_dtype=kvc.BF16)
     r = L.kvc_attend_compressed(ctypes.byref(k4.c()), ctypes.byref(big), ctypes.byref(b),
                                 ctypes.byref(k4.c()), ctypes.byref(big), ctypes.byref(b), 8,
-                                ctypes.c_void_p(FAKE), 4, ctypes.c_float(0.1),
+                                ctypes.c_void_p(FAKE), 4, ctypes.c_float(0.1), 0,
                                 ctypes.c_void_p(FAKE), None, None, 0, None)
     assert r == kvc.KVC_E_SHAPE
     # current chunk: a workspace is required, and the chunk must be given
     ok = kvc.Codec(2, 128, 2, 32, kvc.BASE_NONE, x_dtype=kvc.BF16)
     st2 = kvc._Store(FAKE, FAKE, None, 16)
 
-    def chunk(ck=FAKE, ws=FAKE, ws_bytes=1 << 20, nch=5):
+    def chunk(ck=FAKE, ws=FAKE, ws_bytes=1 << 20, nch=5, flags=0):
         return L.kvc_attend_compressed_chunk(
             ctypes.byref(ok.c()), ctypes.byref(st2), ctypes.byref(b), ctypes.byref(ok.c()),
             ctypes.byref(st2), ctypes.byref(b), 8, ctypes.c_void_p(ck) if ck else None,
-            ctypes.c_void_p(FAKE), nch, ctypes.c_void_p(FAKE), 4, ctypes.c_float(0.1),
+            ctypes.c_void_p(FAKE), nch, ctypes.c_void_p(FAKE), 4, ctypes.c_float(0.1), flags,
             ctypes.c_void_p(FAKE), None, ctypes.c_void_p(ws) if ws else None, ws_bytes, None)
     assert chunk(ws=0, ws_bytes=0) == kvc.KVC_E_WORKSPACE
     assert chunk(ws_bytes=16) == kvc.KVC_E_WORKSPACE
     assert chunk(ck=0) == kvc.KVC_E_NULL
     assert chunk(nch=0) == kvc.KVC_E_SHAPE
     assert chunk(ck=FAKE + 8) == kvc.KVC_E_ALIGN
+    # Jensen correction: centroid K and V only; unknown flag bits are refused
+    assert chunk(flags=kvc.ATTEND_JENSEN) == kvc.KVC_E_UNSUPPORTED     # base NONE
+    assert chunk(flags=2) == kvc.KVC_E_UNSUPPORTED
+    assert att(kc, kc, flags=kvc.ATTEND_JENSEN) == kvc.KVC_E_UNSUPPORTED   # fp32 path
     need = L.kvc_workspace_bytes(kvc.OP_ATTEND_CHUNK, ctypes.byref(ok.c()), 8, 4)
     assert need >= 2 * 4 * 2 * 129 * 4   # two parts (history, chunk) of 4 queries x 2 heads
 
@@ -152,9 +158,10 @@ def test_rotation_validation_errors():
     st2 = kvc._Store(FAKE, FAKE, FAKE, 16)
 
     def att(kc, vc, fn=L.kvc_attend_compressed):
+        fl = [] if fn == L.kvc_attend_mixed_dim else [ctypes.c_uint32(0)]
         return fn(ctypes.byref(kc.c()), ctypes.byref(st2), ctypes.byref(b), ctypes.byref(vc.c()),
                   ctypes.byref(st2), ctypes.byref(b), 8, ctypes.c_void_p(FAKE), 4,
-                  ctypes.c_float(0.1), ctypes.c_void_p(FAKE), None, None, 0, None)
+                  ctypes.c_float(0.1), *fl, ctypes.c_void_p(FAKE), None, None, 0, None)
     plain_none = kvc.Codec(2, 128, 2, 64, kvc.BASE_NONE)
     assert att(rc, plain_none) == kvc.KVC_E_UNSUPPORTED
     assert att(plain_none, rc) == kvc.KVC_E_UNSUPPORTED
