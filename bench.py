@@ -13,11 +13,11 @@ inputs are resident in HBM when the timed region starts.  The metric is query
 tokens per second (each query token covers all 12 heads).
 
 Prints ONE JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
-`--workload dplr|temporal|mixed|chunk|rotated` measures the other paths instead (the 30-layer
+`--workload dplr|temporal|mixed|chunk|rotated|jensen` measures the other paths instead (the 30-layer
 cross-layer chain, the temporal chain + attention over its reconstruction,
 mixed-dimensional attention, attention over a compressed history plus an
-uncompressed current chunk, and the default workload with H64-rotated residuals); the
-default line is the one above.
+uncompressed current chunk, the default workload with H64-rotated residuals, and the
+current-chunk attention with the Jensen-bias correction); the default line is the one above.
 """
 from __future__ import annotations
 
@@ -354,11 +354,12 @@ def bench_temporal(args, torch, kvc, synth, dev):
                          "frac_hbm": enc_bytes / t_enc / 1e9 / HBM_PEAK_GBS})
 
 
-def bench_chunk(args, torch, kvc, synth, dev):
+def bench_chunk(args, torch, kvc, synth, dev, jensen: bool = False):
     """cfg1 with the most recent 3 frames kept uncompressed: 4680 queries attend to the
     28080 compressed history tokens (centroid + INT2 g32, 256 centroids/head) and the
     4680-token current chunk in bf16, one softmax over both (history key splits and the
-    chunk as separate parts, merged by log-sum-exp).  One step = that attention."""
+    chunk as separate parts, merged by log-sum-exp).  One step = that attention; with
+    `jensen` the history keys' logits carry the Jensen-bias correction."""
     d = synth.cfg1()
     H, D, C = d["heads"], d["dim"], d["centroids"]
     lo, hi = d["chunk"]
@@ -377,23 +378,28 @@ def bench_chunk(args, torch, kvc, synth, dev):
     out = torch.empty((nq, H, D), dtype=torch.float32, device=dev)
     ws = kvc.kvc.workspace_for(kvc.kvc.OP_ATTEND_CHUNK, codec, lo, dev, n_queries=nq)
 
+    flags = kvc.ATTEND_JENSEN if jensen else 0
+
     def step(_):
         kvc.kvc_attend_compressed_chunk(codec, ks, kb, codec, vs, vb, lo, Kc, Vc, Q, d["scale"],
-                                        ws, out=out)
+                                        ws, out=out, flags=flags)
 
     log("timing")
     t_step, ev = _timed(torch, step, args.steps, args.warmup)
     t_ev = sum(a.elapsed_time(b) for a, b in ev) / len(ev) * 1e-3
     achieved = attention_flops(nq, hi, D, H) / t_ev / 1e12
-    return _line("compressed-history + current-chunk attention query-tok/s", nq / t_ev,
+    jb = ", Jensen-corrected history logits" if jensen else ""
+    return _line("compressed-history + current-chunk attention query-tok/s" + jb, nq / t_ev,
                  "query-tok/s", args, t_step, "bf16",
                  {"workload": "centroid+INT2 g32 history of 28080 tokens + uncompressed 4680-token "
-                              "current chunk, 12 heads x 128, 256 centroids/head, 4680 queries",
+                              "current chunk, 12 heads x 128, 256 centroids/head, 4680 queries" + jb,
                   "heads": H, "head_dim": D, "history_tokens": lo, "chunk_tokens": hi - lo,
-                  "queries": nq},
+                  "queries": nq, "jensen": jensen},
                  {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
                   "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
-                  "traffic": recorded_traffic("attend_bf16_kernel_chunk_12x128_4680q_28080k_4680c.md",
+                  "traffic": recorded_traffic("attend_bf16_kernel_chunk_jensen_12x128_4680q_28080k_4680c.md"
+                                              if jensen else
+                                              "attend_bf16_kernel_chunk_12x128_4680q_28080k_4680c.md",
                                               "kv_cache_compression_02_amd/csrc/attend.hip"),
                   "kernel": "attend_bf16_kernel (history parts + chunk part + merge)",
                   "ms": t_ev * 1e3})
@@ -537,11 +543,12 @@ def main() -> int:
     ap.add_argument("--copy-ref", action="store_true",
                     help="run one plain 256 MiB device copy first (calibrates HBM counters)")
     ap.add_argument("--workload", default="centroid",
-                    choices=("centroid", "dplr", "temporal", "mixed", "chunk", "rotated"),
+                    choices=("centroid", "dplr", "temporal", "mixed", "chunk", "rotated", "jensen"),
                     help="centroid: the default line; the others measure the cross-layer "
                          "chain, the temporal chain + attention, mixed-dimensional attention, "
                          "attention over the compressed history plus an uncompressed chunk, "
-                         "the default workload with H64-rotated residuals")
+                         "the default workload with H64-rotated residuals, the current-chunk "
+                         "attention with the Jensen-bias correction")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -558,7 +565,8 @@ def main() -> int:
         copy_reference(torch, dev)
     if args.workload != "centroid":
         line = {"dplr": bench_dplr, "temporal": bench_temporal, "mixed": bench_mixed,
-                "chunk": bench_chunk, "rotated": bench_rotated}[args.workload](
+                "chunk": bench_chunk, "rotated": bench_rotated,
+                "jensen": lambda *a: bench_chunk(*a, jensen=True)}[args.workload](
             args, torch, kvc, synth, dev)
         print(json.dumps(line))
         return 0
