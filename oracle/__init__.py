@@ -14,6 +14,8 @@ arXiv 2610.12514; TempoKV arXiv 2610.15324):
 * ``rotation``  Hn residual transform: an orthonormal Sylvester-Hadamard rotation of
                 each group of n residual channels before the quantizer (Coral-KV
                 Fig. 5, Fig. 9b-c).
+* ``fit``       online centroid fitting at block fill: Lloyd iterations whose
+                assignment is the codec's nearest-centroid search (Coral-KV Fig. 2c).
 * ``predict``   block-diagonal-plus-low-rank cross-layer predictors (Coral-KV
                 Fig. 3) and temporal key / cross value predictors (TempoKV Fig. 2b).
 * ``coeff``     coefficients of the centroid residual on a low-dimensional basis
@@ -33,4 +35,4 @@ Parity status: every function is pinned by the ``-m "not gpu"`` tests (brute
 force, closed forms, special cases, library routines, the pages' printed
 compression ratios); see the per-module docstrings.
 """
-from . import numerics, rotation, codec, predict, coeff, attention, ratio  # noqa: F401
+from . import numerics, rotation, codec, fit, predict, coeff, attention, ratio  # noqa: F401
