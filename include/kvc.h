@@ -180,6 +180,27 @@ kvc_status kvc_encode(const kvc_codec* codec, const void* x, int64_t n_tokens,
                       int64_t token_offset, void* recon_out, float* pred_out, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* kvc_fit_centroids - online centroid fitting at block fill (Coral-KV Fig. 2c: QVG
+ * fits video-specific centroids when a cache block reaches its token limit): `iterations`
+ * Lloyd steps on the n_tokens vectors x [n][H][d], per head, updating the centroid table
+ * in place.  Each step assigns every vector to its nearest centroid exactly as
+ * kvc_encode does (fp32 squared distance, ascending channels, ties to the lowest
+ * index), then sets every centroid that received vectors to their mean - the fp32 sum
+ * in ascending token order divided by the count, rounded to bf16 (nearest even) - and
+ * leaves the others unchanged.
+ *   codec: KVC_BASE_CENTROID, bf16, d = 128 (bits, group and rotation only shape the
+ *          scratch encode; the fit does not depend on them).
+ *   x_token_stride: elements between tokens of x (0 = H*d; a multiple of 8).
+ *   centroids: [H][C][d] bf16, the initial table on entry, the fitted one on return.
+ *   workspace: kvc_workspace_bytes(KVC_OP_FIT, codec, n_tokens, 0) bytes (a scratch
+ *              store of n_tokens rows); the contents on return are unspecified.
+ * n_tokens == 0 or iterations == 0 returns KVC_OK without launching anything.
+ * Errors: KVC_E_NULL, KVC_E_SHAPE (negative sizes, bad stride), KVC_E_UNSUPPORTED,
+ * KVC_E_ALIGN, KVC_E_WORKSPACE, KVC_E_DEVICE. */
+kvc_status kvc_fit_centroids(const kvc_codec* codec, const void* x, int64_t n_tokens,
+                             int64_t x_token_stride, void* centroids, int32_t iterations,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* kvc_decode - reconstruct rows [token_offset, token_offset + n_tokens) of a store:
  * out = base + ((code * s) + z), written as out_dtype [n][H][d] (bf16 output is the
  * fp32 value rounded to nearest even).  Predictor bases read `base` exactly as
@@ -280,9 +301,10 @@ kvc_status kvc_attend_mixed_dim(const kvc_codec* kc, const kvc_store* k,
  * the attention ops; the history keys for KVC_OP_ATTEND_CHUNK) and n_queries queries.
  * Encode / decode: required by the DPLR and temporal-value bases, 0 otherwise.
  * Attention: the optional workspace that enables key splitting (0 when a single pass is
- * used anyway); with a current chunk: the required partial results. */
+ * used anyway); with a current chunk: the required partial results.  Centroid fitting:
+ * the scratch store of n_tokens rows. */
 enum { KVC_OP_ENCODE = 0, KVC_OP_DECODE = 1, KVC_OP_ATTEND = 2, KVC_OP_ATTEND_MIXED = 3,
-       KVC_OP_ATTEND_CHUNK = 4 };
+       KVC_OP_ATTEND_CHUNK = 4, KVC_OP_FIT = 5 };
 size_t kvc_workspace_bytes(int32_t op, const kvc_codec* codec, int64_t n_tokens,
                            int64_t n_queries);
 

@@ -205,6 +205,7 @@ size_t kvc_workspace_bytes(int32_t op, const kvc_codec* codec, int64_t n_tokens,
   if (op == KVC_OP_ENCODE || op == KVC_OP_DECODE) return encode_workspace_bytes(c, n_tokens);
   if (op == KVC_OP_ATTEND || op == KVC_OP_ATTEND_MIXED) return attend_workspace_bytes(c, n_tokens, n_queries);
   if (op == KVC_OP_ATTEND_CHUNK) return attend_chunk_workspace_bytes(c, n_tokens, n_queries);
+  if (op == KVC_OP_FIT) return fit_workspace_bytes(c, n_tokens);
   return 0;
 }
 
@@ -240,6 +241,31 @@ kvc_status kvc_encode(const kvc_codec* codec, const void* x, int64_t n_tokens,
   a.pred = pred_out;
   a.workspace = workspace;
   return from_hip(launch_encode(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+kvc_status kvc_fit_centroids(const kvc_codec* codec, const void* x, int64_t n_tokens,
+                             int64_t x_token_stride, void* centroids, int32_t iterations,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  EncodeLaunch a;
+  kvc_status st = resolve_codec(codec, &a.c);
+  if (st != KVC_OK) return st;
+  if (a.c.base != KVC_BASE_CENTROID || a.c.x_dtype != KVC_BF16 || a.c.D != 128 || a.c.bits == 16)
+    return KVC_E_UNSUPPORTED;
+  if (n_tokens < 0 || iterations < 0) return KVC_E_SHAPE;
+  const int64_t hd = (int64_t)a.c.H * a.c.D;
+  const int64_t stride = x_token_stride ? x_token_stride : hd;
+  if (stride < hd || stride % 8) return KVC_E_SHAPE;
+  if (n_tokens == 0 || iterations == 0) return KVC_OK;
+  if (!x || !centroids) return KVC_E_NULL;
+  if (!aligned16(x) || !aligned16(centroids) || (workspace && !aligned16(workspace))) return KVC_E_ALIGN;
+  if (!workspace || workspace_bytes < fit_workspace_bytes(a.c, n_tokens)) return KVC_E_WORKSPACE;
+  a.x = x;
+  a.n_tokens = n_tokens;
+  a.x_stride = stride;
+  a.b.centroids = centroids;
+  a.b.prev_stride = hd;
+  a.workspace = workspace;
+  return from_hip(launch_fit(a, iterations, reinterpret_cast<hipStream_t>(stream)));
 }
 
 kvc_status kvc_decode(const kvc_codec* codec, const kvc_store* src, int64_t token_offset,

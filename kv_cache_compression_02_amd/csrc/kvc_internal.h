@@ -102,6 +102,10 @@ bool predict_available();
 // pass is used anyway).
 size_t attend_workspace_bytes(const CodecArgs& kc, int64_t n_keys, int64_t n_queries);
 size_t attend_chunk_workspace_bytes(const CodecArgs& kc, int64_t n_keys, int64_t n_queries);
+// Online centroid fitting: `iterations` Lloyd steps on a.x (n_tokens rows) updating the
+// table a.b.centroids in place; a.workspace holds a scratch store of n_tokens rows.
+size_t fit_workspace_bytes(const CodecArgs& c, int64_t n_tokens);
+hipError_t launch_fit(const EncodeLaunch& a, int iterations, hipStream_t s);
 
 // Workspace bytes of the predictor paths (0 otherwise).
 size_t encode_workspace_bytes(const CodecArgs& c, int64_t n_tokens);

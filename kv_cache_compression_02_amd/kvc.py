@@ -23,10 +23,10 @@ F32, BF16 = 0, 1
 # kvc_base_kind
 BASE_NONE, BASE_CENTROID, BASE_DPLR, BASE_TEMPORAL, BASE_COEFF = range(5)
 # workspace ops
-OP_ENCODE, OP_DECODE, OP_ATTEND, OP_ATTEND_MIXED, OP_ATTEND_CHUNK = range(5)
+OP_ENCODE, OP_DECODE, OP_ATTEND, OP_ATTEND_MIXED, OP_ATTEND_CHUNK, OP_FIT = range(6)
 ATTEND_JENSEN = 1
 
-EXPORTED = ("kvc_store_bytes", "kvc_encode", "kvc_decode", "kvc_attend_compressed",
+EXPORTED = ("kvc_store_bytes", "kvc_encode", "kvc_decode", "kvc_fit_centroids", "kvc_attend_compressed",
             "kvc_attend_compressed_chunk", "kvc_attend_mixed_dim", "kvc_workspace_bytes",
             "kvc_status_str", "kvc_abi_version")
 
@@ -74,6 +74,8 @@ def lib():
     L.kvc_encode.restype = I32
     L.kvc_decode.argtypes = [P(_Codec), P(_Store), I64, I64, P(_Base), VP, I32, VP, VP, SZ, VP]
     L.kvc_decode.restype = I32
+    L.kvc_fit_centroids.argtypes = [P(_Codec), VP, I64, I64, VP, I32, VP, SZ, VP]
+    L.kvc_fit_centroids.restype = I32
     U32 = ctypes.c_uint32
     att = [P(_Codec), P(_Store), P(_Base), P(_Codec), P(_Store), P(_Base), I64, VP, I64,
            ctypes.c_float, VP, VP, VP, SZ, VP]
@@ -289,6 +291,21 @@ def _attend(fn, name, kc, kstore, kbase, vc, vstore, vbase, n_keys, q, softmax_s
     _check(fn(*head, _p(out, "out"), _p(lse, "lse"), _p(workspace, "workspace"), ws_bytes,
               _stream()), name)
     return (out, lse) if want_lse else out
+
+
+def kvc_fit_centroids(codec: Codec, x: torch.Tensor, centroids: torch.Tensor, iterations: int,
+                      workspace: Optional[torch.Tensor] = None, x_token_stride: int = 0) -> None:
+    """Lloyd iterations on x [n][H][d] bf16, updating centroids [H][C][d] bf16 in place."""
+    if not x_token_stride:
+        x_token_stride = _row_stride(x, "x")
+    if workspace is None:
+        workspace = workspace_for(OP_FIT, codec, x.shape[0], x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().kvc_fit_centroids(ctypes.byref(codec.c()), ctypes.c_void_p(x.data_ptr()),
+                                   x.shape[0], x_token_stride,
+                                   _p(centroids, "centroids"), iterations,
+                                   _p(workspace, "workspace"), ws_bytes, _stream()),
+           "kvc_fit_centroids")
 
 
 def kvc_attend_compressed(kc: Codec, kstore: Store, kbase: Optional[BaseParams], vc: Codec,

@@ -175,6 +175,30 @@ def test_rotation_validation_errors():
                 == L.kvc_workspace_bytes(op, ctypes.byref(plain.c()), 5000, 300))
 
 
+def test_fit_validation_errors():
+    L = _lib()
+    c = kvc.Codec(2, 128, 2, 32, kvc.BASE_CENTROID, 40)
+
+    def fit(codec=c, x=FAKE, n=10, stride=0, cen=FAKE, it=2, ws=FAKE, ws_bytes=1 << 24):
+        return L.kvc_fit_centroids(ctypes.byref(codec.c()), ctypes.c_void_p(x) if x else None, n,
+                                   stride, ctypes.c_void_p(cen) if cen else None, it,
+                                   ctypes.c_void_p(ws) if ws else None, ws_bytes, None)
+    assert fit(codec=kvc.Codec(2, 128, 2, 32, kvc.BASE_NONE)) == kvc.KVC_E_UNSUPPORTED
+    assert fit(codec=kvc.Codec(2, 128, 2, 32, kvc.BASE_CENTROID, 40, x_dtype=kvc.F32)) == kvc.KVC_E_UNSUPPORTED
+    assert fit(n=-1) == kvc.KVC_E_SHAPE
+    assert fit(it=-1) == kvc.KVC_E_SHAPE
+    assert fit(stride=2 * 128 + 4) == kvc.KVC_E_SHAPE
+    assert fit(stride=100) == kvc.KVC_E_SHAPE
+    assert fit(n=0, x=0, cen=0) == kvc.KVC_OK          # nothing to do: nothing launched
+    assert fit(it=0) == kvc.KVC_OK
+    assert fit(x=0) == kvc.KVC_E_NULL
+    assert fit(cen=FAKE + 4) == kvc.KVC_E_ALIGN
+    assert fit(ws=0, ws_bytes=0) == kvc.KVC_E_WORKSPACE
+    need = L.kvc_workspace_bytes(kvc.OP_FIT, ctypes.byref(c.c()), 10, 0)
+    assert need >= 2 * 10 * (8 * 4 + 4 * 4 + 1)        # codes, scale/zero, index rows
+    assert fit(ws_bytes=need - 1) == kvc.KVC_E_WORKSPACE
+
+
 def test_python_binding_raises_on_status():
     _lib()
     with pytest.raises(kvc.KvcError) as e:
