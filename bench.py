@@ -13,11 +13,12 @@ inputs are resident in HBM when the timed region starts.  The metric is query
 tokens per second (each query token covers all 12 heads).
 
 Prints ONE JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
-`--workload dplr|temporal|mixed|chunk|rotated|jensen` measures the other paths instead (the 30-layer
+`--workload dplr|temporal|mixed|chunk|rotated|jensen|fit` measures the other paths instead (the 30-layer
 cross-layer chain, the temporal chain + attention over its reconstruction,
 mixed-dimensional attention, attention over a compressed history plus an
 uncompressed current chunk, the default workload with H64-rotated residuals, and the
-current-chunk attention with the Jensen-bias correction); the default line is the one above.
+current-chunk attention with the Jensen-bias correction, and online centroid fitting at
+block fill); the default line is the one above.
 """
 from __future__ import annotations
 
@@ -534,6 +535,46 @@ def bench_rotated(args, torch, kvc, synth, dev):
     return line
 
 
+def bench_fit(args, torch, kvc, synth, dev):
+    """Online centroid fitting at block fill on the cfg1 chunk: 10 Lloyd iterations on
+    the 4680-token block of K and of V (12 heads x 128, 256 centroids/head, from every
+    18th token).  One step = both fits.  Algorithmic bytes per iteration and tensor: the
+    block read by the assignment and again by the update, the table read and written."""
+    d = synth.cfg1()
+    H, D, C = d["heads"], d["dim"], d["centroids"]
+    lo, hi = d["chunk"]
+    n = hi - lo
+    iters = 10
+
+    def b16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view("int16")).view(torch.bfloat16).to(dev)
+
+    codec = kvc.Codec(H, D, d["bits"], d["group"], kvc.BASE_CENTROID, C)
+    X = [b16(d["K"][lo:hi]), b16(d["V"][lo:hi])]
+    init = [b16(np.ascontiguousarray(a[lo:hi][::18][:C].transpose(1, 0, 2))) for a in (d["K"], d["V"])]
+    tabs = [t.clone() for t in init]
+    ws = kvc.kvc.workspace_for(kvc.kvc.OP_FIT, codec, n, dev)
+
+    def step(_):
+        for x, t, t0 in zip(X, tabs, init):
+            t.copy_(t0)
+            kvc.kvc_fit_centroids(codec, x, t, iters, workspace=ws)
+
+    log("timing")
+    t_step, ev = _timed(torch, step, args.steps, args.warmup)
+    t_ev = sum(a.elapsed_time(b) for a, b in ev) / len(ev) * 1e-3
+    per_iter = 2 * (2 * n * H * D * 2 + 2 * H * C * D * 2 + n * H)
+    gbs = per_iter * iters / t_ev / 1e9
+    return _line("online centroid fit, token-iterations/s (Lloyd, K and V)",
+                 2 * n * iters / t_ev, "token-iterations/s", args, t_step, "bf16",
+                 {"workload": "Lloyd fit of 256 centroids/head on one 4680-token block of K and "
+                              "of V, 12 heads x 128, 10 iterations from every 18th token",
+                  "heads": H, "head_dim": D, "tokens": n, "centroids": C, "iterations": iters},
+                 {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                  "kernel": "encode_c16_kernel (assignment) + fit_update_kernel", "ms": t_ev * 1e3})
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -543,12 +584,13 @@ def main() -> int:
     ap.add_argument("--copy-ref", action="store_true",
                     help="run one plain 256 MiB device copy first (calibrates HBM counters)")
     ap.add_argument("--workload", default="centroid",
-                    choices=("centroid", "dplr", "temporal", "mixed", "chunk", "rotated", "jensen"),
+                    choices=("centroid", "dplr", "temporal", "mixed", "chunk", "rotated", "jensen",
+                             "fit"),
                     help="centroid: the default line; the others measure the cross-layer "
                          "chain, the temporal chain + attention, mixed-dimensional attention, "
                          "attention over the compressed history plus an uncompressed chunk, "
                          "the default workload with H64-rotated residuals, the current-chunk "
-                         "attention with the Jensen-bias correction")
+                         "attention with the Jensen-bias correction, online centroid fitting")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -566,7 +608,8 @@ def main() -> int:
     if args.workload != "centroid":
         line = {"dplr": bench_dplr, "temporal": bench_temporal, "mixed": bench_mixed,
                 "chunk": bench_chunk, "rotated": bench_rotated,
-                "jensen": lambda *a: bench_chunk(*a, jensen=True)}[args.workload](
+                "jensen": lambda *a: bench_chunk(*a, jensen=True),
+                "fit": bench_fit}[args.workload](
             args, torch, kvc, synth, dev)
         print(json.dumps(line))
         return 0

@@ -9,10 +9,10 @@
 //   - update: every centroid that received tokens becomes the mean of its tokens,
 //     rounded to bf16 (nearest even); a centroid that received none keeps its value.
 //
-// fit_update_kernel: a wave owns 64 channels of one centroid and walks the head's
-// assignments 64 tokens at a time; a ballot marks the tokens of its centroid and only
-// those rows are read, so the sums run in ascending token order (deterministic, fp32)
-// and the reads are the assignments once per wave plus each token's row once per
+// fit_update_kernel: a wave owns 64 channels of one centroid; the workgroup stages a
+// chunk of the head's assignments in LDS, a ballot pass lists the chunk's tokens of the
+// wave's centroid, and only those rows are read (8 loads in flight), so the sums run in
+// ascending token order (deterministic, fp32) and each token's row is read once per
 // centroid half.  The mean is the fp32 sum divided by the count (IEEE division).
 #include "kvc_device.h"
 #include "kvc_internal.h"
@@ -39,33 +39,70 @@ FitLayout fit_layout(const CodecArgs& c, int64_t n) {
 }
 
 // grid: H * ceil(C / 4) workgroups of 8 waves; wave w of block b: centroid 4 b + (w >> 1),
-// channels 64 (w & 1) .. + 63
+// channels 64 (w & 1) .. + 63.  Per chunk of FCH tokens the workgroup stages the head's
+// assignments in LDS; each wave compacts the positions of its centroid's tokens into its
+// own LDS list (ballots, ascending) and then reads those rows 8 at a time, adding them in
+// list order.
+constexpr int FCH = 2048;
+
 __global__ __launch_bounds__(512) void fit_update_kernel(const uint16_t* x, int64_t x_stride,
                                                          const void* index, int idxb, int64_t n,
                                                          int H, int C, uint16_t* centroids) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ uint16_t sidx[FCH];
+  __shared__ uint16_t list[8][FCH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int blocks = (C + 3) / 4;
   const int h = blockIdx.x / blocks;
   const int j = 4 * (blockIdx.x % blocks) + (wave >> 1);
-  if (j >= C) return;   // no barriers below: a wave past the table just ends
+  const bool live = j < C;   // waves past the table still take part in the barriers
   const int c = 64 * (wave & 1) + lane;
   const uint8_t* idx8 = reinterpret_cast<const uint8_t*>(index) + (int64_t)h * n * idxb;
   const uint16_t* xh = x + (int64_t)h * FD + c;
   float acc = 0.0f;
   int64_t count = 0;
-  for (int64_t t0 = 0; t0 < n; t0 += 64) {
-    const int64_t t = t0 + lane;
-    int a = -1;
-    if (t < n) a = idxb == 1 ? (int)idx8[t] : (int)reinterpret_cast<const uint16_t*>(idx8)[t];
-    uint64_t m = __ballot(a == j);
-    count += __popcll(m);
-    while (m) {   // wave-uniform: the same tokens for every lane, ascending
-      const int b = __builtin_ctzll(m);
-      m &= m - 1;
-      acc += bf16_bits_to_f32(xh[(t0 + b) * x_stride]);
+  for (int64_t base = 0; base < n; base += FCH) {
+    const int len = (int)min<int64_t>(FCH, n - base);
+    for (int e = tid; e < len; e += 512)
+      sidx[e] = idxb == 1 ? (uint16_t)idx8[base + e]
+                          : reinterpret_cast<const uint16_t*>(idx8)[base + e];
+    __syncthreads();
+    if (live) {
+      int nm = 0;   // wave-uniform list length
+      const uint64_t below = (1ull << lane) - 1;
+      for (int t0 = 0; t0 < len; t0 += 256) {   // four ballots per pass, reads issued first
+        int a[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int t = t0 + 64 * u + lane;
+          a[u] = t < len ? (int)sidx[t] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bool hit = a[u] == j;
+          const uint64_t m = __ballot(hit);
+          if (hit) list[wave][nm + __popcll(m & below)] = (uint16_t)(t0 + 64 * u + lane);
+          nm += __popcll(m);
+        }
+      }
+      count += nm;
+      // the list is written and read by this wave only; its stores precede its loads
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      for (int k0 = 0; k0 < nm; k0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          v[k] = k0 + k < nm ? bf16_bits_to_f32(xh[(base + list[wave][k0 + k]) * x_stride]) : 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (k0 + k < nm) acc += v[k];   // ascending token order
+      }
     }
+    __syncthreads();   // sidx is rewritten by the next chunk
   }
-  if (count) centroids[((int64_t)h * C + j) * FD + c] = (uint16_t)f32_to_bf16_bits(acc / (float)count);
+  if (live && count)
+    centroids[((int64_t)h * C + j) * FD + c] = (uint16_t)f32_to_bf16_bits(acc / (float)count);
 }
 
 }  // namespace
