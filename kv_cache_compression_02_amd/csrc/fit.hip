@@ -9,11 +9,12 @@
 //   - update: every centroid that received tokens becomes the mean of its tokens,
 //     rounded to bf16 (nearest even); a centroid that received none keeps its value.
 //
-// fit_update_kernel: a wave owns 64 channels of one centroid; the workgroup stages a
-// chunk of the head's assignments in LDS, a ballot pass lists the chunk's tokens of the
-// wave's centroid, and only those rows are read (8 loads in flight), so the sums run in
-// ascending token order (deterministic, fp32) and each token's row is read once per
-// centroid half.  The mean is the fp32 sum divided by the count (IEEE division).
+// fit_update_kernel: a workgroup owns 4 centroids (a wave: 64 channels of one); it
+// stages a chunk of the head's assignments in LDS, its 8 waves split the chunk and list
+// each centroid's tokens in ascending order (ballots), and only those rows are read (8
+// loads in flight), so the sums run in ascending token order (deterministic, fp32) and
+// each token's row is read once per centroid half.  The mean is the fp32 sum divided by
+// the count (IEEE division).
 #include "kvc_device.h"
 #include "kvc_internal.h"
 
@@ -38,68 +39,95 @@ FitLayout fit_layout(const CodecArgs& c, int64_t n) {
   return l;
 }
 
-// grid: H * ceil(C / 4) workgroups of 8 waves; wave w of block b: centroid 4 b + (w >> 1),
-// channels 64 (w & 1) .. + 63.  Per chunk of FCH tokens the workgroup stages the head's
-// assignments in LDS; each wave compacts the positions of its centroid's tokens into its
-// own LDS list (ballots, ascending) and then reads those rows 8 at a time, adding them in
-// list order.
+// grid: H * ceil(C / 4) workgroups of 8 waves, each for 4 centroids 4 b .. 4 b + 3.
+// Per chunk of FCH tokens: the workgroup stages the head's assignments in LDS; wave w
+// scans tokens [w FCH/8, (w + 1) FCH/8) of the chunk for the 4 centroids (a count pass,
+// then a pass that writes each hit at its wave's offset, so every centroid's list is in
+// ascending token order); then waves 2 q and 2 q + 1 (channel halves) read the rows of
+// centroid 4 b + q's list, 8 loads in flight, and add them in list order.
 constexpr int FCH = 2048;
+constexpr int FSEG = FCH / 8;   // tokens a wave scans per chunk
 
 __global__ __launch_bounds__(512) void fit_update_kernel(const uint16_t* x, int64_t x_stride,
                                                          const void* index, int idxb, int64_t n,
                                                          int H, int C, uint16_t* centroids) {
   __shared__ uint16_t sidx[FCH];
-  __shared__ uint16_t list[8][FCH];
+  __shared__ uint16_t list[4][FCH];
+  __shared__ int cnt[8][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int blocks = (C + 3) / 4;
   const int h = blockIdx.x / blocks;
-  const int j = 4 * (blockIdx.x % blocks) + (wave >> 1);
+  const int j0 = 4 * (blockIdx.x % blocks);
+  const int q = wave >> 1, j = j0 + q;
   const bool live = j < C;   // waves past the table still take part in the barriers
   const int c = 64 * (wave & 1) + lane;
   const uint8_t* idx8 = reinterpret_cast<const uint8_t*>(index) + (int64_t)h * n * idxb;
   const uint16_t* xh = x + (int64_t)h * FD + c;
+  const uint64_t below = (1ull << lane) - 1;
   float acc = 0.0f;
   int64_t count = 0;
   for (int64_t base = 0; base < n; base += FCH) {
     const int len = (int)min<int64_t>(FCH, n - base);
-    for (int e = tid; e < len; e += 512)
-      sidx[e] = idxb == 1 ? (uint16_t)idx8[base + e]
-                          : reinterpret_cast<const uint16_t*>(idx8)[base + e];
+    uint16_t st[FCH / 512];   // all of the thread's loads in flight before the stores
+#pragma unroll
+    for (int u = 0; u < FCH / 512; ++u) {
+      const int e = tid + 512 * u;
+      st[u] = e >= len ? (uint16_t)0xFFFFu
+                       : (idxb == 1 ? (uint16_t)idx8[base + e]
+                                    : reinterpret_cast<const uint16_t*>(idx8)[base + e]);
+    }
+#pragma unroll
+    for (int u = 0; u < FCH / 512; ++u) sidx[tid + 512 * u] = st[u];   // 0xFFFF past len
+    __syncthreads();
+    // count pass over the wave's segment (tokens past len hold 0xFFFF: no centroid)
+    int a[FSEG / 64];
+#pragma unroll
+    for (int u = 0; u < FSEG / 64; ++u) a[u] = (int)sidx[FSEG * wave + 64 * u + lane] - j0;
+    int n4[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < FSEG / 64; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) n4[r] += __popcll(__ballot(a[u] == r));
+    if (lane < 4) cnt[wave][lane] = lane == 0 ? n4[0] : lane == 1 ? n4[1] : lane == 2 ? n4[2] : n4[3];
+    __syncthreads();
+    // write pass: each hit at (earlier waves' count) + (earlier hits of this wave)
+    int off[4], tot[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      off[r] = 0;
+      tot[r] = 0;
+      for (int w = 0; w < 8; ++w) {
+        const int v = cnt[w][r];
+        if (w < wave) off[r] += v;
+        tot[r] += v;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < FSEG / 64; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool hit = a[u] == r;
+        const uint64_t m = __ballot(hit);
+        if (hit) list[r][off[r] + __popcll(m & below)] = (uint16_t)(FSEG * wave + 64 * u + lane);
+        off[r] += __popcll(m);
+      }
     __syncthreads();
     if (live) {
-      int nm = 0;   // wave-uniform list length
-      const uint64_t below = (1ull << lane) - 1;
-      for (int t0 = 0; t0 < len; t0 += 256) {   // four ballots per pass, reads issued first
-        int a[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int t = t0 + 64 * u + lane;
-          a[u] = t < len ? (int)sidx[t] : -1;
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const bool hit = a[u] == j;
-          const uint64_t m = __ballot(hit);
-          if (hit) list[wave][nm + __popcll(m & below)] = (uint16_t)(t0 + 64 * u + lane);
-          nm += __popcll(m);
-        }
-      }
+      const int nm = q == 0 ? tot[0] : q == 1 ? tot[1] : q == 2 ? tot[2] : tot[3];
       count += nm;
-      // the list is written and read by this wave only; its stores precede its loads
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       for (int k0 = 0; k0 < nm; k0 += 8) {
         float v[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-          v[k] = k0 + k < nm ? bf16_bits_to_f32(xh[(base + list[wave][k0 + k]) * x_stride]) : 0.0f;
+        for (int k = 0; k < 8; ++k) {   // unconditional loads (the last entry repeated) stay in flight together
+          const int e = min(k0 + k, nm - 1);
+          v[k] = bf16_bits_to_f32(xh[(base + list[q][e]) * x_stride]);
+        }
 #pragma unroll
         for (int k = 0; k < 8; ++k)
           if (k0 + k < nm) acc += v[k];   // ascending token order
       }
     }
-    __syncthreads();   // sidx is rewritten by the next chunk
+    __syncthreads();   // sidx, cnt and the lists are rewritten by the next chunk
   }
   if (live && count)
     centroids[((int64_t)h * C + j) * FD + c] = (uint16_t)f32_to_bf16_bits(acc / (float)count);
