@@ -98,16 +98,21 @@ def cpu_baseline(d: dict, sample_heads=(0, 1), enc_frames: int = 1, q_sample: in
     }
 
 
-def recorded_traffic(profile: str, source: str):
+def recorded_traffic(profile: str, source):
     """HBM bytes per launch of a kernel, as measured by the FETCH_SIZE and WRITE_SIZE
     passes summarized in `profile` (scaled by the reference copy's readings), or None.
-    The summary records the sha256 of the kernel source it measured; once that source
-    has changed the numbers no longer describe the kernel and None is returned."""
+    The summary records the sha256 of the kernel source it measured (of the sources'
+    concatenation when `source` is a tuple); once that source has changed the numbers no
+    longer describe the kernel and None is returned."""
     import hashlib
     import re
+    srcs = (source,) if isinstance(source, str) else tuple(source)
     try:
         text = open(os.path.join(ROOT, "profiles", profile)).read()
-        sha = hashlib.sha256(open(os.path.join(ROOT, source), "rb").read()).hexdigest()
+        h = hashlib.sha256()
+        for src in srcs:
+            h.update(open(os.path.join(ROOT, src), "rb").read())
+        sha = h.hexdigest()
     except OSError:
         return None
     m = re.search(r"traffic_per_launch: read_bytes=(\d+) write_bytes=(\d+) source_sha256=([0-9a-f]+)", text)
@@ -571,7 +576,12 @@ def bench_fit(args, torch, kvc, synth, dev):
                               "of V, 12 heads x 128, 10 iterations from every 18th token",
                   "heads": H, "head_dim": D, "tokens": n, "centroids": C, "iterations": iters},
                  {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                  "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                  "frac": gbs / HBM_PEAK_GBS,
+                  # per timed step: both tensors' 10 iterations of the two kernels
+                  "traffic": (lambda b: None if b is None else b * 2 * iters)(recorded_traffic(
+                      "fit_update_kernel_cfg1_chunk_12x128_4680tok_256c.md",
+                      ("kv_cache_compression_02_amd/csrc/encode.hip",
+                       "kv_cache_compression_02_amd/csrc/fit.hip"))),
                   "kernel": "encode_c16_kernel (assignment) + fit_update_kernel", "ms": t_ev * 1e3})
 
 
