@@ -4,9 +4,9 @@
 // compressed state holds (Coral-KV arXiv 2610.12514 Table 9 caption); adding the
 // dequantized residual to the base gives the reconstruction (Coral-KV Fig. 3).
 //
-// One thread per (token, head, 16 consecutive channels): loads its code words, the
-// group's scale/zero word and 32 bytes of the base row, writes 16 outputs with 16-byte
-// vector stores.  HBM-bound streaming kernel.
+// One thread per (token, head, 16 consecutive channels), heads on the grid's y axis: loads
+// its code words, the group's scale/zero word and 32 bytes of the base row, writes 16
+// outputs with 16-byte vector stores.  HBM-bound streaming kernel.
 #include "kvc_device.h"
 #include "kvc_internal.h"
 
@@ -18,7 +18,7 @@ struct DecodeParams {
   int64_t n_tokens, token_offset, capacity;
   int H, D, C, bits, group, groups, code_words, index_bytes, mode;
   int rot;             // Hn residual transform width (0, 16 or 64)
-  uint32_t total;      // threads of this launch: n_tokens * H * (D / 16) < 2^31
+  uint32_t total;      // threads per head of this launch: n_tokens * (D / 16) < 2^31
   int cshift, gshift;  // log2(D / 16), log2(group)
   const uint32_t* codes;
   const uint32_t* sz;
@@ -63,12 +63,14 @@ __device__ __forceinline__ void load16(const XT* src, float (&v)[16]) {
 // consecutive pieces of the token-major output rows.
 template <typename XT, typename OT>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
+  // head-major walk (blockIdx.y = head): the store's rows are read in order and the
+  // concurrently used centroid rows are one head's, which stay in L2 while the output
+  // streams through it
   const uint32_t e = blockIdx.x * 256u + threadIdx.x;
   if (e >= p.total) return;
   const uint32_t c16 = e & ((1u << p.cshift) - 1u);
-  const uint32_t nh = e >> p.cshift;
-  const uint32_t n = nh / (uint32_t)p.H;
-  const uint32_t h = nh - n * (uint32_t)p.H;
+  const uint32_t n = e >> p.cshift;
+  const uint32_t h = blockIdx.y;
   const int i0 = (int)c16 * 16;
   const int64_t row = (int64_t)h * p.capacity + p.token_offset + n;
 
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
 // the kernel); every pointer that is indexed by the token moves with the range.
 template <typename XT>
 hipError_t launch_decode_x(const DecodeParams& p0, int out_dtype, hipStream_t s) {
-  const int64_t per_token = (int64_t)p0.H * (p0.D / 16);
+  const int64_t per_token = p0.D / 16;   // threads per token of one head
   const int64_t step = std::max<int64_t>(1, ((int64_t)1 << 31) / per_token - 256);
   const int osz = out_dtype == KVC_BF16 ? 2 : 4;
   for (int64_t t0 = 0; t0 < p0.n_tokens; t0 += step) {
@@ -186,7 +188,7 @@ hipError_t launch_decode_x(const DecodeParams& p0, int out_dtype, hipStream_t s)
     if (p0.base_buf) p.base_buf = p0.base_buf + elems;
     if (p0.prev0) p.prev0 = reinterpret_cast<const XT*>(p0.prev0) + t0 * p0.prev_stride;
     if (p0.prev1) p.prev1 = reinterpret_cast<const XT*>(p0.prev1) + t0 * p0.prev_stride;
-    const dim3 grid((p.total + 255u) / 256u);
+    const dim3 grid((p.total + 255u) / 256u, (unsigned)p0.H);
     if (out_dtype == KVC_BF16)
       hipLaunchKernelGGL((decode_kernel<XT, uint16_t>), grid, dim3(256), 0, s, p);
     else
