@@ -126,3 +126,18 @@ def test_fit_cfg1_chunk_full_size_one_step():
     torch.cuda.synchronize()
     counts = _check_step(xb, C0, _bits(C))
     assert counts.sum() == 12 * (hi - lo)
+
+
+def test_fit_does_not_depend_on_the_codec_rotation():
+    """The assignment is made on unrotated vectors, so a rotated codec fits the same
+    table bit for bit."""
+    dev = device()
+    d = synth.cfg1(seed=34, hist_frames=3, query_frames=1, tokens=100, heads=3, dim=128,
+                   n_centroids=40)
+    x = to_dev(d["K"], dev)
+    C0 = _init(d["K"], 40, 7)
+    Ca, Cb = to_dev(C0, dev), to_dev(C0, dev)
+    kvc.kvc_fit_centroids(kvc.Codec(3, 128, 2, 64, kvc.BASE_CENTROID, 40), x, Ca, 2)
+    kvc.kvc_fit_centroids(kvc.Codec(3, 128, 2, 64, kvc.BASE_CENTROID, 40, rotation=64), x, Cb, 2)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(Ca), _bits(Cb))

@@ -123,3 +123,30 @@ def test_cfg1_full_size_jensen_with_current_chunk_sampled():
                                 v_chunk=nm.bf16_to_f32(d["V"][lo:hi]))
     err = np.abs(o[sample] - ref).max()
     assert err <= 2e-2, err
+
+
+def test_cfg1_full_size_rotated_jensen_with_current_chunk_sampled():
+    """All three together at the timed shape: H64-rotated INT2 g64 history (28080 keys),
+    Jensen-corrected history logits, the 4680-token uncompressed chunk; 32 sampled queries."""
+    dev = device()
+    d = synth.cfg1()
+    lo, hi = d["chunk"]
+    (kc, ks, kb), (vc, vs, vb) = _compress(d, 12, 2, 64, 256, dev, lo, rot=64)
+    q = to_dev(d["Q"], dev)
+    ws = kvc.kvc.workspace_for(kvc.kvc.OP_ATTEND_CHUNK, kc, lo, dev, n_queries=q.shape[0])
+    print("rotated + jensen cfg1 chunk", flush=True)
+    out = kvc.kvc_attend_compressed_chunk(kc, ks, kb, vc, vs, vb, lo,
+                                          to_dev(np.ascontiguousarray(d["K"][lo:hi]), dev),
+                                          to_dev(np.ascontiguousarray(d["V"][lo:hi]), dev),
+                                          q, d["scale"], ws, flags=kvc.ATTEND_JENSEN)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(np.isfinite(o))
+    kh, vh, step = _oracle(d, 2, 64, lo, rot=64)
+    rng = np.random.default_rng(5)
+    sample = np.sort(rng.choice(q.shape[0], size=32, replace=False))
+    ref = oatt.attention_jensen(nm.bf16_to_f32(d["Q"][sample]), kh, vh, step, 64, d["scale"],
+                                k_chunk=nm.bf16_to_f32(d["K"][lo:hi]),
+                                v_chunk=nm.bf16_to_f32(d["V"][lo:hi]))
+    err = np.abs(o[sample] - ref).max()
+    assert err <= 2e-2, err
