@@ -234,7 +234,13 @@ enum { KVC_ATTEND_JENSEN = 1 };
  * a bf16 cache would hold them), or any d in {64, 128} with f32 x_dtype (fp32 path).
  * bits = 16 on both K and V attends over uncompressed bf16 caches (for example the
  * reconstructions a predictor chain decodes; each cache below 2 GiB).
+ *   Only rows 0..n_keys-1 are read: rows beyond (a store sized for a longer history,
+ *     not yet written) never reach the result.
  *   q:   [n_queries][H][d] x_dtype, token stride H*d.
+ *   softmax_scale: finite and > 0 (else KVC_E_SHAPE).
+ *   Range of the bf16 path: decoded values are held as fp16 for the P V product, so
+ *     every decoded value (and every value of an uncompressed cache or chunk) must lie
+ *     within fp16's range, |v| <= 65504; larger values are outside the contract.
  *   flags: 0 or KVC_ATTEND_JENSEN (other bits: KVC_E_UNSUPPORTED).
  *   out: [n_queries][H][d] fp32.
  *   lse: optional [H][n_queries] fp32 natural-log sum-exp of the scaled scores.
@@ -248,9 +254,10 @@ enum { KVC_ATTEND_JENSEN = 1 };
  *     with the decoder's arithmetic, so the tiles hold exactly what kvc_decode returns
  *     (rounded to bf16).  K and V must then both use KVC_BASE_CENTROID.
  * Errors: KVC_E_NULL, KVC_E_SHAPE (n_keys > capacity, n_keys < 1, mismatched
- * heads/d; bf16 path: a store whose per-head code or scale/zero rows span 2 GiB or
- * more, or a dense cache of 2 GiB or more - the kernels address them with 32-bit byte
- * offsets), KVC_E_UNSUPPORTED, KVC_E_ALIGN, KVC_E_DEVICE. */
+ * heads/d, softmax_scale not finite and positive; bf16 path: a store whose per-head
+ * code or scale/zero rows span 2 GiB or more, or a dense cache of 2 GiB or more - the
+ * kernels address them with 32-bit byte offsets), KVC_E_UNSUPPORTED, KVC_E_ALIGN,
+ * KVC_E_DEVICE. */
 kvc_status kvc_attend_compressed(const kvc_codec* kc, const kvc_store* k,
                                  const kvc_base_params* kp, const kvc_codec* vc,
                                  const kvc_store* v, const kvc_base_params* vp, int64_t n_keys,

@@ -306,8 +306,11 @@ static bool attend_ranges_fit(const CodecArgs& c, const StoreArgs& s) {
 
 static kvc_status check_attend(const kvc_codec* kc, const kvc_store* k, const kvc_base_params* kp,
                                const kvc_codec* vc, const kvc_store* v, const kvc_base_params* vp,
-                               int64_t n_keys, const void* q, int64_t n_queries, float* out,
-                               float* lse, AttendLaunch* a) {
+                               int64_t n_keys, const void* q, int64_t n_queries, float scale,
+                               float* out, float* lse, AttendLaunch* a) {
+  // the softmax scale must be finite and positive: the bf16 kernels' lazy running max
+  // assumes that larger raw scores give larger logits
+  if (!(scale > 0.0f) || !(scale < __builtin_inff())) return KVC_E_SHAPE;
   kvc_status st = resolve_codec(kc, &a->kc);
   if (st != KVC_OK) return st;
   st = resolve_codec(vc, &a->vc);
@@ -350,7 +353,7 @@ kvc_status kvc_attend_compressed(const kvc_codec* kc, const kvc_store* k,
                                  uint32_t flags, float* out, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream) {
   AttendLaunch a;
-  kvc_status st = check_attend(kc, k, kp, vc, v, vp, n_keys, q, n_queries, out, lse, &a);
+  kvc_status st = check_attend(kc, k, kp, vc, v, vp, n_keys, q, n_queries, softmax_scale, out, lse, &a);
   if (st != KVC_OK) return st;
   if (workspace && !aligned16(workspace)) return KVC_E_ALIGN;
   a.workspace = workspace;
@@ -380,7 +383,7 @@ kvc_status kvc_attend_compressed_chunk(const kvc_codec* kc, const kvc_store* k,
                                        float softmax_scale, uint32_t flags, float* out, float* lse,
                                        void* workspace, size_t workspace_bytes, void* stream) {
   AttendLaunch a;
-  kvc_status st = check_attend(kc, k, kp, vc, v, vp, n_keys, q, n_queries, out, lse, &a);
+  kvc_status st = check_attend(kc, k, kp, vc, v, vp, n_keys, q, n_queries, softmax_scale, out, lse, &a);
   if (st != KVC_OK) return st;
   for (const CodecArgs* c : {&a.kc, &a.vc})
     if (c->base != KVC_BASE_NONE && c->base != KVC_BASE_CENTROID) return KVC_E_UNSUPPORTED;
@@ -414,7 +417,7 @@ kvc_status kvc_attend_mixed_dim(const kvc_codec* kc, const kvc_store* k,
                                 float* out, float* lse, void* workspace, size_t workspace_bytes,
                                 void* stream) {
   AttendLaunch a;
-  kvc_status st = check_attend(kc, k, kp, vc, v, vp, n_keys, q, n_queries, out, lse, &a);
+  kvc_status st = check_attend(kc, k, kp, vc, v, vp, n_keys, q, n_queries, softmax_scale, out, lse, &a);
   if (st != KVC_OK) return st;
   if (workspace && !aligned16(workspace)) return KVC_E_ALIGN;
   a.workspace = workspace;

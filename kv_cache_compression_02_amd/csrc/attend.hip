@@ -263,8 +263,10 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
   const int tb = split * p.tps, te = min(ntiles, tb + p.tps);   // this split's key tiles
 
   // Per-head buffer resources (SGPRs): every prefetch is a buffer load with a 32-bit
-  // byte offset, and the descriptor's record count bounds it - a read past the head's
-  // rows (the tail of the last tile) returns zeros instead of touching other memory.
+  // byte offset, and the descriptor's record count bounds it.  The count covers the
+  // n_keys attended rows only (not the store's capacity), so the tail of the last tile
+  // reads zeros - codes 0, scale and zero 0, centroid 0: finite values whose weight is
+  // masked to 0 - never whatever unwritten rows past n_keys hold.
   auto rsrc = [](const void* base, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                              0x00020000);
@@ -272,14 +274,15 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
   const int kwb = p.k.words * 4, kgb = p.k.groups * 4;   // bytes per key row
   const int vwb = p.v.words * 4, vgb = p.v.groups * 4;
   const int64_t khrow = (int64_t)h * p.k.cap, vhrow = (int64_t)h * p.v.cap;
-  const auto rk_code = rsrc(p.k.codes + khrow * p.k.words, p.k.cap * kwb);
-  const auto rk_sz = rsrc(p.k.sz + khrow * p.k.groups, p.k.cap * kgb);
-  const auto rv_code = rsrc(p.v.codes + vhrow * p.v.words, p.v.cap * vwb);
-  const auto rv_sz = rsrc(p.v.sz + vhrow * p.v.groups, p.v.cap * vgb);
+  const int64_t nkr = p.nk;   // rows visible to the loads (n_keys <= capacity)
+  const auto rk_code = rsrc(p.k.codes + khrow * p.k.words, nkr * kwb);
+  const auto rk_sz = rsrc(p.k.sz + khrow * p.k.groups, nkr * kgb);
+  const auto rv_code = rsrc(p.v.codes + vhrow * p.v.words, nkr * vwb);
+  const auto rv_sz = rsrc(p.v.sz + vhrow * p.v.groups, nkr * vgb);
   const auto rk_idx = rsrc(reinterpret_cast<const uint8_t*>(p.k.index) + khrow * p.k.idxb,
-                           KCEN ? p.k.cap * p.k.idxb : 0);
+                           KCEN ? nkr * p.k.idxb : 0);
   const auto rv_idx = rsrc(reinterpret_cast<const uint8_t*>(p.v.index) + vhrow * p.v.idxb,
-                           VCEN ? p.v.cap * p.v.idxb : 0);
+                           VCEN ? nkr * p.v.idxb : 0);
   const auto rk_cen = rsrc(reinterpret_cast<const uint16_t*>(p.k.cen) + (int64_t)h * p.k.C * DM,
                            KCEN ? (int64_t)p.k.C * DM * 2 : 0);
   const auto rv_cen = rsrc(reinterpret_cast<const uint16_t*>(p.v.cen) + (int64_t)h * p.v.C * DM,
@@ -287,8 +290,8 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
 
   // DENSE: one resource over the whole token-major cache, rows H*d apart
   const int hdb = p.H * DM * 2;
-  const auto rk_dense = rsrc(p.k.codes, DENSE ? p.k.cap * hdb : 0);
-  const auto rv_dense = rsrc(p.v.codes, DENSE ? p.v.cap * hdb : 0);
+  const auto rk_dense = rsrc(p.k.codes, DENSE ? nkr * hdb : 0);
+  const auto rv_dense = rsrc(p.v.codes, DENSE ? nkr * hdb : 0);
 
   // decode roles: 8 lanes share a K row (16 channels each), 16 lanes share a V row (8
   // channels each), so every load instruction reads whole contiguous rows
@@ -579,6 +582,7 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
       for (int c = 0; c < 8; ++c) {
         const int row = 8 * c8 + c;
         // the decoded value is the codec's bf16 reconstruction; fp16 holds it exactly
+        // inside fp16's range (|v| <= 65504, a limit the API states for this path)
         const uint32_t w = bf16x2_to_f16x2(pk_bf16(x[0][c], x[1][c]));   // keys 2kp, 2kp+1
         *reinterpret_cast<uint32_t*>(&v_lds[buf][row * VROW + vpos(row, 2 * kp)]) = w;
       }

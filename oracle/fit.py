@@ -22,7 +22,9 @@ step from one seed per blob; a duplicate centroid stays empty and unchanged (tie
 the lower index); one centroid becomes the rounded global mean; every step's output
 satisfies its own definition (each non-empty centroid is the rounded mean of the tokens
 the codec search assigns to it); the k-means objective does not grow by more than the
-bf16 rounding of the centroids from one iteration to the next.
+bf16 rounding of the centroids from one iteration to the next; a worked example fixes
+the rounding of the mean (exact mean 1 + 2^-8 + 2^-30 becomes fp32 1 + 2^-8, a bf16
+tie, so 1 - not the 1 + 2^-7 that a single rounding gives).
 """
 from __future__ import annotations
 

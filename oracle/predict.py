@@ -26,8 +26,11 @@ Pins (tests/test_oracle_predict.py): W = I, U = 0 reduces the DPLR predictor to
 previous-layer DPCM; a = 1, b = 0 reduces the temporal key predictor to
 previous-frame DPCM; M = 0 reduces the value predictor to a scaled previous
 frame; the block-DPLR map equals the dense (H*d)x(n*H*d) matrix assembled from
-its blocks and factors; chains reproduce their inputs within the O(s/2)
-quantization bound.
+its blocks and factors and a per-element brute force; the temporal value map equals
+a per-element sum in exact rational arithmetic with a non-symmetric M_h (a transposed
+M_h fails); the temporal chain's first predicted frame reads the anchor's
+reconstruction for both key terms (b != 0, so K_{-1} = 0 fails); chains reproduce
+their inputs within the O(s/2) quantization bound.
 """
 from __future__ import annotations
 

@@ -86,12 +86,17 @@ def test_attend_validation_errors():
     st = kvc._Store(FAKE, FAKE, None, 16)
     b = kvc._Base()
 
-    def att(kc, vc, nk=8, q=FAKE, out=FAKE, fn=L.kvc_attend_compressed, flags=0):
+    def att(kc, vc, nk=8, q=FAKE, out=FAKE, fn=L.kvc_attend_compressed, flags=0, scale=0.1):
         fl = [] if fn == L.kvc_attend_mixed_dim else [ctypes.c_uint32(flags)]
         return fn(ctypes.byref(kc.c()), ctypes.byref(st), ctypes.byref(b), ctypes.byref(vc.c()),
                   ctypes.byref(st), ctypes.byref(b), nk, ctypes.c_void_p(q) if q else None, 4,
-                  ctypes.c_float(0.1), *fl, ctypes.c_void_p(out) if out else None, None, None, 0,
+                  ctypes.c_float(scale), *fl, ctypes.c_void_p(out) if out else None, None, None, 0,
                   None)
+
+    # the softmax scale must be finite and positive, on every attention entry point
+    for bad in (0.0, -0.125, float("nan"), float("inf"), float("-inf")):
+        assert att(kc, kc, scale=bad) == kvc.KVC_E_SHAPE, bad
+        assert att(kc, kc, scale=bad, fn=L.kvc_attend_mixed_dim) == kvc.KVC_E_SHAPE, bad
 
     assert att(kc, vc) == kvc.KVC_E_SHAPE                  # head mismatch
     assert att(kc, kc, nk=0) == kvc.KVC_E_SHAPE
@@ -120,6 +125,13 @@ def test_attend_validation_errors():
             ctypes.byref(st2), ctypes.byref(b), 8, ctypes.c_void_p(ck) if ck else None,
             ctypes.c_void_p(FAKE), nch, ctypes.c_void_p(FAKE), 4, ctypes.c_float(0.1), flags,
             ctypes.c_void_p(FAKE), None, ctypes.c_void_p(ws) if ws else None, ws_bytes, None)
+    for bad in (0.0, -1.0, float("nan")):
+        r = L.kvc_attend_compressed_chunk(
+            ctypes.byref(ok.c()), ctypes.byref(st2), ctypes.byref(b), ctypes.byref(ok.c()),
+            ctypes.byref(st2), ctypes.byref(b), 8, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), 5,
+            ctypes.c_void_p(FAKE), 4, ctypes.c_float(bad), 0, ctypes.c_void_p(FAKE), None,
+            ctypes.c_void_p(FAKE), 1 << 20, None)
+        assert r == kvc.KVC_E_SHAPE, bad
     assert chunk(ws=0, ws_bytes=0) == kvc.KVC_E_WORKSPACE
     assert chunk(ws_bytes=16) == kvc.KVC_E_WORKSPACE
     assert chunk(ck=0) == kvc.KVC_E_NULL

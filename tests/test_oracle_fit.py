@@ -68,3 +68,24 @@ def test_each_step_satisfies_its_definition_and_the_objective_does_not_grow():
                     for h in range(H) for j in range(K)) * 4
         assert cur <= prev + slack
         prev, C = cur, Cn
+
+
+def test_mean_rounds_to_fp32_then_to_bf16():
+    """Worked example of the rounding the update takes: the exact mean rounded to fp32,
+    then to bf16 (nearest even at each step).  Four tokens whose channel 0 holds 2, 2,
+    2^-6 and 2^-28 (all bf16 values) have the exact mean 1 + 2^-8 + 2^-30.  In fp32 the
+    2^-30 is lost (half an ulp at 1 is 2^-24), leaving 1 + 2^-8, the midpoint between the
+    bf16 neighbours 1 and 1 + 2^-7, which ties to even: 1.  Rounding the exact mean to
+    bf16 in one step would give 1 + 2^-7.  Channel 1 is the control against truncation:
+    its mean 1.75 + 3 * 2^-9 is exact in fp32 and above the midpoint 1.75 + 2^-8, so it
+    rounds up to 1.7578125."""
+    x = np.zeros((4, 1, 16), np.float32)
+    x[:, 0, 0] = [2.0, 2.0, 2.0 ** -6, 2.0 ** -28]
+    x[:, 0, 1] = [1.75, 1.75, 1.75, 1.75 + 3 * 2.0 ** -7]
+    assert np.array_equal(nm.round_bf16(x), x)                  # bf16 inputs
+    C0 = np.zeros((1, 1, 16), np.float32)                       # one centroid: all tokens
+    C1, idx, counts = fit.lloyd_step(x, C0)
+    assert counts[0, 0] == 4 and np.all(idx == 0)
+    assert C1[0, 0, 0] == 1.0                                   # fp32 tie -> even
+    assert C1[0, 0, 1] == 1.7578125                             # above the midpoint -> up
+    assert np.all(C1[0, 0, 2:] == 0.0)

@@ -73,6 +73,55 @@ def test_temporal_v_special_cases():
     assert np.array_equal(out, nm.round_bf16(k).astype(np.float64))
 
 
+def test_temporal_v_per_element_brute_force():
+    """Each predicted value, summed term by term in exact rational arithmetic: channel i of
+    head h is sum_j M[h, i, j] * bf16(K_t)[h, j] + beta[h, i] * bf16(V_{t-1})[h, i].  M_h
+    is non-symmetric, so a transposed M_h (or a mixed-up head) fails."""
+    from fractions import Fraction
+    rng = np.random.default_rng(31)
+    n, h, d = 5, 3, 8
+    k = rng.standard_normal((n, h, d)).astype(np.float32)
+    v = rng.standard_normal((n, h, d)).astype(np.float32)
+    M = rng.standard_normal((h, d, d)) / np.sqrt(d)
+    assert np.abs(M - M.transpose(0, 2, 1)).max() > 0.1
+    beta = rng.uniform(0.3, 0.7, (h, d)).astype(np.float32)
+    got = predict.temporal_predict_v(k, v, M, beta)
+    kb, vb = nm.round_bf16(k), nm.round_bf16(v)
+    for t in range(n):
+        for hh in range(h):
+            for i in range(d):
+                exact = sum(Fraction(float(M[hh, i, j])) * Fraction(float(kb[t, hh, j]))
+                            for j in range(d))
+                exact += Fraction(float(beta[hh, i])) * Fraction(float(vb[t, hh, i]))
+                assert abs(got[t, hh, i] - float(exact)) <= 1e-13 * (1 + abs(float(exact)))
+    # the transposed map gives a different prediction
+    assert np.abs(predict.temporal_predict_v(k, v, M.transpose(0, 2, 1), beta) - got).max() > 1e-3
+
+
+def test_temporal_chain_first_frame_uses_the_anchor_twice():
+    """At t = 1 there is no K_{-1}: the key predictor reads the anchor frame's reconstruction
+    for both terms, (a * K^_0) + (b * K^_0) in fp32; at t = 2 it reads K^_1 and K^_0.  With
+    b != 0 this differs from taking K_{-1} as zero."""
+    rng = np.random.default_rng(32)
+    T, h, d = 6, 2, 64
+    ks = [rng.standard_normal((T, h, d)).astype(np.float32) for _ in range(3)]
+    vs = [rng.standard_normal((T, h, d)).astype(np.float32) for _ in range(3)]
+    a = rng.uniform(1.0, 1.2, (h, d)).astype(np.float32)
+    b = rng.uniform(-0.35, -0.25, (h, d)).astype(np.float32)
+    M = rng.standard_normal((h, d, d)) / np.sqrt(d)
+    beta = rng.uniform(0.3, 0.7, (h, d)).astype(np.float32)
+    outs = list(predict.temporal_chain(ks, vs, a, b, M, beta, 2, 64, 4))
+    k0 = nm.round_bf16(outs[0]["k"]["xhat"])
+    k1 = nm.round_bf16(outs[1]["k"]["xhat"])
+    for t, (x1, x2) in ((1, (k0, k0)), (2, (k1, k0))):
+        base = outs[t]["k"]["base"]
+        for idx in [(0, 0, 0), (2, 1, 17), (5, 0, 63), (3, 1, 40)]:
+            want = np.float32(np.float32(a[idx[1:]] * x1[idx]) + np.float32(b[idx[1:]] * x2[idx]))
+            assert base[idx] == want, (t, idx)
+    zero_prev = (a * k0).astype(np.float32)
+    assert np.abs(outs[1]["k"]["base"] - zero_prev).max() > 0.1
+
+
 def _group_bound(x, xhat, st_q, s16, z16, bits, group):
     """Max |x - xhat| per group against the quantizer bound (see the codec tests)."""
     L = (1 << bits) - 1
