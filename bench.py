@@ -89,11 +89,13 @@ def cpu_baseline(d: dict, sample_heads=(0, 1), enc_frames: int = 1, q_sample: in
     except Exception:  # pragma: no cover
         blas_threads = 1
     return {
-        "value": nq / step, "unit": "query-tok/s", "cores": int(blas_threads), "kind": "oracle",
+        "value": nq / step, "unit": "query-tok/s", "cores": len(os.sched_getaffinity(0)),
+        "blas_threads": int(blas_threads), "kind": "oracle",
+        "single_threaded_parts": ["encode", "decode"],
         "sample": (f"oracle encode of {enc_frames} frame(s) x {H} heads (K and V, single-threaded "
-                   f"numpy), decode of the {d['K'].shape[0]}-token history and fp64 attention of "
-                   f"{q_sample} queries for {len(hs)} heads ({blas_threads} BLAS threads); "
-                   f"scaled to one full step"),
+                   f"numpy), decode of the {d['K'].shape[0]}-token history (single-threaded "
+                   f"numpy) and fp64 attention of {q_sample} queries for {len(hs)} heads "
+                   f"({blas_threads} BLAS threads); scaled to one full step"),
         "seconds": {"encode": t_enc, "decode": t_dec, "attention": t_att, "step_estimate": step},
     }
 
@@ -149,6 +151,13 @@ def _timed(torch, step, steps: int, warmup: int):
         ev[i][1].record()
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) / steps, ev
+
+
+def percentiles_ms(times_s) -> dict:
+    """p10 / p50 / p90 of per-step times (seconds in, milliseconds out)."""
+    a = np.asarray(times_s, dtype=np.float64) * 1e3
+    return {"p10": float(np.percentile(a, 10)), "p50": float(np.percentile(a, 50)),
+            "p90": float(np.percentile(a, 90))}
 
 
 def _line(metric, value, unit, args, t_step, dtype, config, roofline, **extra):
@@ -664,8 +673,10 @@ def main() -> int:
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    t_enc = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps * 1e-3
-    t_att = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps * 1e-3
+    enc_s = [e[0].elapsed_time(e[1]) * 1e-3 for e in ev]
+    att_s = [e[1].elapsed_time(e[2]) * 1e-3 for e in ev]
+    t_enc = sum(enc_s) / args.steps
+    t_att = sum(att_s) / args.steps
     flops = attention_flops(nq, nk, D, H)
     enc_b = 2 * encode_bytes(hi - lo, H, D, bits, group, C)
     achieved = flops / t_att / 1e12
@@ -690,9 +701,11 @@ def main() -> int:
                      "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
                      "traffic": recorded_traffic("attend_bf16_kernel_centroid_int2_12x128_4680q_32760k.md",
                                                  "kv_cache_compression_02_amd/csrc/attend.hip"),
-                     "kernel": "attend_bf16_kernel", "ms": t_att * 1e3},
+                     "kernel": "attend_bf16_kernel", "ms": t_att * 1e3,
+                     "ms_percentiles": percentiles_ms(att_s)},
         "encode": {"ms": t_enc * 1e3, "bytes": enc_b, "GB/s": enc_b / t_enc / 1e9,
-                   "frac_hbm": enc_b / t_enc / 1e9 / HBM_PEAK_GBS},
+                   "frac_hbm": enc_b / t_enc / 1e9 / HBM_PEAK_GBS,
+                   "ms_percentiles": percentiles_ms(enc_s)},
     }
     # decode of the whole compressed history (K and V) to bf16, timed apart from the step
     kdec = torch.empty((nk, H, D), dtype=torch.bfloat16, device=dev)
@@ -709,6 +722,27 @@ def main() -> int:
     line["decode"] = {"ms": t_dec * 1e3, "bytes": dec_b, "GB/s": dec_b / t_dec / 1e9,
                       "frac_hbm": dec_b / t_dec / 1e9 / HBM_PEAK_GBS,
                       "what": "decode of the 32760-token history, K and V, to bf16"}
+    # the unfused alternative at the same shape: decode the whole history to bf16, then
+    # dense attention over the decoded caches (the same kernel family without the tile
+    # decode), timed as one call sequence against the fused attention above
+    dense = kvc.Codec(H, D, 16, 128, kvc.BASE_NONE)
+    dense_ws = kvc.kvc.workspace_for(kvc.kvc.OP_ATTEND, dense, nk, dev, n_queries=nq)
+    out_u = torch.empty_like(out)
+
+    def unfused(_):
+        dec(None)
+        kvc.kvc_attend_compressed(dense, kvc.Store.dense(kdec), None, dense, kvc.Store.dense(vdec),
+                                  None, nk, Q, d["scale"], out=out_u, workspace=dense_ws)
+
+    _, ev_u = _timed(torch, unfused, max(1, min(args.steps, 10)), 1)
+    u_s = [a.elapsed_time(b) * 1e-3 for a, b in ev_u]
+    t_u = sum(u_s) / len(u_s)
+    line["unfused_reference"] = {
+        "what": "kvc_decode of K and V to bf16 + dense attention over the decoded caches",
+        "ms": t_u * 1e3, "frac": flops / t_u / 1e12 / BF16_PEAK_TFLOPS,
+        "ms_percentiles": percentiles_ms(u_s),
+        "fused_over_unfused_speedup": t_u / t_att,
+        "max_abs_diff_vs_fused": float((out_u - out).abs().max().item())}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(d)
     print(json.dumps(line))

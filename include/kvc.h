@@ -135,7 +135,7 @@ typedef struct {
  *             values: prediction = M_h aux + (coef_a * prev0), aux = aligned K_t,
  *                     prev0 = V_{t-1}; M = w_block [H][d][d] bf16; coef_b = NULL.
  *   prev_token_stride: elements between consecutive tokens of prev0/prev1/aux
- *   (0 = H*d; a multiple of 8 for the matrix-product bases).
+ *   (0 = H*d; a multiple of 8, else KVC_E_ALIGN: the inputs are read in 16-byte pieces).
  * Matrix-product bases (DPLR, temporal values) compute an fp32 prediction first: it
  * goes to pred_out when given, else to the workspace; DPLR always needs the workspace
  * (kvc_workspace_bytes) for its rank-r intermediate. */

@@ -127,6 +127,7 @@ kvc_status resolve_base(const kvc_base_params* b, const CodecArgs& c, BaseArgs* 
     case KVC_BASE_TEMPORAL:
       if (!need_prev) break;
       if (!a.prev0 || !a.coef_a) return KVC_E_NULL;
+      if (a.prev_stride % 8) return KVC_E_ALIGN;   // 16-byte row pieces of the inputs
       if (a.w_block) {   // values: M aux + beta prev0
         if (!predict_available()) return KVC_E_UNSUPPORTED;
         if (!a.aux) return KVC_E_NULL;
@@ -138,6 +139,7 @@ kvc_status resolve_base(const kvc_base_params* b, const CodecArgs& c, BaseArgs* 
     case KVC_BASE_DPLR:
       if (!need_prev) break;
       if (!a.prev0 || !a.w_block || !a.u || !a.v_lr) return KVC_E_NULL;
+      if (a.prev_stride % 8) return KVC_E_ALIGN;
       if (c.n_inputs == 2 && !a.prev1) return KVC_E_NULL;
       break;
     default: break;

@@ -77,6 +77,12 @@ def test_encode_validation_errors():
     b.centroids = FAKE + 8
     assert _enc(cen, base=b) == kvc.KVC_E_ALIGN
     assert _enc(ok_codec, store=kvc._Store(FAKE + 4, FAKE, None, 16)) == kvc.KVC_E_ALIGN
+    # predictor inputs are read in 16-byte pieces: their token stride must be a multiple of 8
+    tk = kvc.Codec(2, 128, 2, 64, kvc.BASE_TEMPORAL)
+    b = kvc._Base()
+    b.prev0 = b.prev1 = b.coef_a = b.coef_b = FAKE
+    b.prev_token_stride = 2 * 128 + 4
+    assert _enc(tk, base=b) == kvc.KVC_E_ALIGN
 
 
 def test_attend_validation_errors():

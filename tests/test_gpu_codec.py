@@ -196,3 +196,31 @@ def test_centroid_encode_whole_history_several_tiles_per_workgroup():
     check_centroid_store(sub, nm.bf16_to_f32(d["K"][sample]), nm.bf16_to_f32(d["Ck"]), 2, 32)
     assert not np.any(np.all(got["codes"] == 0xFFFFFFFF, axis=-1)
                       & np.all(got["scale_zero"] == 0xFFFFFFFF, axis=-1))
+
+
+def test_cfg1_history_decode_full_size_sampled():
+    """The decode that the benchmark times: the whole 32760-token history of K and of V
+    (12 heads x 128, 256 centroids, INT2 g32) to bf16 in one call each.  On a seeded
+    sample of tokens (and the last ones) the store is checked against the oracle encode
+    and the decoded rows against the oracle's decode of those store rows, rounded to
+    bf16 (nearest even)."""
+    dev = device()
+    d = synth.cfg1()
+    n = d["K"].shape[0]
+    rng = np.random.default_rng(4)
+    sample = np.unique(np.concatenate([rng.choice(n, size=384, replace=False),
+                                       np.arange(n - 5, n)]))
+    codec = kvc.Codec(12, 128, 2, 32, kvc.BASE_CENTROID, 256)
+    for name, cname in (("K", "Ck"), ("V", "Cv")):
+        st = kvc.Store.allocate(codec, n, dev)
+        base = kvc.BaseParams(centroids=to_dev(d[cname], dev))
+        kvc.kvc_encode(codec, to_dev(d[name], dev), st, 0, base)
+        out = kvc.kvc_decode(codec, st, 0, n, base, out_dtype=kvc.BF16)
+        got = store_np(st)
+        sub = dict(codes=got["codes"][:, sample], scale_zero=got["scale_zero"][:, sample],
+                   index=got["index"][:, sample])
+        C = nm.bf16_to_f32(d[cname])
+        check_centroid_store(sub, nm.bf16_to_f32(d[name][sample]), C, 2, 32)
+        xhat = ocodec.decode_store(sub, 2, 32, 128, C=C)
+        dec = out[torch.from_numpy(sample).to(dev)].float().cpu().numpy()
+        assert np.array_equal(dec, nm.round_bf16(xhat))
