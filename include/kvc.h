@@ -18,7 +18,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Ownership: every buffer is owned by the caller.  The library never
- *   allocates or frees device memory and keeps no mutable global state.
+ *   allocates or frees device memory and keeps no mutable global state, with one
+ *   exception: kvc_encode_noalloc's fixed scratch array (one per GPU, part of the
+ *   loaded library) and the cached device address of that array.
  * - Pointers: all tensor pointers are DEVICE pointers and must be 16-byte
  *   aligned; descriptors (kvc_codec, kvc_store, kvc_base_params) are HOST
  *   structs read during the call only.  A call with nothing to process
@@ -179,6 +181,35 @@ kvc_status kvc_encode(const kvc_codec* codec, const void* x, int64_t n_tokens,
                       int64_t x_token_stride, const kvc_base_params* base, const kvc_store* dst,
                       int64_t token_offset, void* recon_out, float* pred_out, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/* Bytes of the device scratch array that kvc_encode_noalloc uses: one copy per GPU the
+ * library runs on, held until the process ends. */
+#define KVC_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* kvc_encode_noalloc - kvc_encode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments without the workspace, the same results bit for bit, and no
+ * allocation of any kind.  Where kvc_encode needs a workspace, this call uses a fixed
+ * scratch array of KVC_NOALLOC_SCRATCH_BYTES inside the library instead:
+ *   - KVC_BASE_DPLR on the fused predictor + quantizer (bf16, d = 128, group <= 64,
+ *     rank <= 64, x and input strides multiples of 8): the rank-r intermediate, n_tokens *
+ *     rank * 4 bytes, which must fit the scratch (else KVC_E_WORKSPACE; 65536 tokens at
+ *     rank 64);
+ *   - other shapes of the matrix-product bases (DPLR, temporal values) route the
+ *     prediction through an fp32 buffer: pred_out must then be given (else
+ *     KVC_E_UNSUPPORTED); DPLR keeps its rank-r intermediate in the scratch as above;
+ *   - every other base needs no scratch.
+ * The scratch belongs to the current device (`stream` must be on it) and is shared by
+ * every call on that device, which leaves it holding the last call's contents: calls
+ * that overlap on one GPU (two streams, two host threads) race and must not be issued.
+ * Nothing in it has to start at zero - the rank kernel writes every value before it is
+ * read.  The first call on a device looks up the array's device address
+ * (hipGetSymbolAddress) and keeps it.
+ * Errors: as kvc_encode, and KVC_E_WORKSPACE / KVC_E_UNSUPPORTED as above. */
+kvc_status kvc_encode_noalloc(const kvc_codec* codec, const void* x, int64_t n_tokens,
+                              int64_t x_token_stride, const kvc_base_params* base,
+                              const kvc_store* dst, int64_t token_offset, void* recon_out,
+                              float* pred_out, void* stream);
 
 /* kvc_fit_centroids - online centroid fitting at block fill (Coral-KV Fig. 2c: QVG
  * fits video-specific centroids when a cache block reaches its token limit): `iterations`

@@ -5,6 +5,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "kvc.h"
 #include "kvc_internal.h"
@@ -211,11 +212,12 @@ size_t kvc_workspace_bytes(int32_t op, const kvc_codec* codec, int64_t n_tokens,
   return 0;
 }
 
-kvc_status kvc_encode(const kvc_codec* codec, const void* x, int64_t n_tokens,
-                      int64_t x_token_stride, const kvc_base_params* base, const kvc_store* dst,
-                      int64_t token_offset, void* recon_out, float* pred_out, void* workspace,
-                      size_t workspace_bytes, void* stream) {
-  EncodeLaunch a;
+// Validation shared by kvc_encode and kvc_encode_noalloc: everything but the workspace.
+static kvc_status prepare_encode(const kvc_codec* codec, const void* x, int64_t n_tokens,
+                                 int64_t x_token_stride, const kvc_base_params* base,
+                                 const kvc_store* dst, int64_t token_offset, void* recon_out,
+                                 float* pred_out, EncodeLaunch* out) {
+  EncodeLaunch& a = *out;
   kvc_status st = resolve_codec(codec, &a.c);
   if (st != KVC_OK) return st;
   if (a.c.bits == 16) return KVC_E_UNSUPPORTED;
@@ -233,15 +235,85 @@ kvc_status kvc_encode(const kvc_codec* codec, const void* x, int64_t n_tokens,
   if (st != KVC_OK) return st;
   if (a.c.base == KVC_BASE_COEFF && recon_out) return KVC_E_UNSUPPORTED;
   if (a.c.rot != 0 && (recon_out || pred_out || stride % 8 != 0)) return KVC_E_UNSUPPORTED;
-  st = check_predict_workspace(a.c, a.b, n_tokens, pred_out, workspace, workspace_bytes);
-  if (st != KVC_OK) return st;
   a.x = x;
   a.n_tokens = n_tokens;
   a.x_stride = stride;
   a.token_offset = token_offset;
   a.recon = recon_out;
   a.pred = pred_out;
+  return KVC_OK;
+}
+
+kvc_status kvc_encode(const kvc_codec* codec, const void* x, int64_t n_tokens,
+                      int64_t x_token_stride, const kvc_base_params* base, const kvc_store* dst,
+                      int64_t token_offset, void* recon_out, float* pred_out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  EncodeLaunch a;
+  kvc_status st = prepare_encode(codec, x, n_tokens, x_token_stride, base, dst, token_offset,
+                                 recon_out, pred_out, &a);
+  if (st != KVC_OK) return st;
+  st = check_predict_workspace(a.c, a.b, n_tokens, pred_out, workspace, workspace_bytes);
+  if (st != KVC_OK) return st;
   a.workspace = workspace;
+  return from_hip(launch_encode(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of kvc_encode_noalloc (the cross-layer predictor's rank-r intermediate), one
+// copy per GPU, held by the loaded library until the process ends.  In host code
+// `scratch` is only a handle: its device address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and that pointer is what kernels receive.
+static __device__ __align__(256) unsigned char scratch[KVC_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[MAX_DEVICES];
+
+hipError_t scratch_for_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    scratch_ptr[dev] = ptr;
+  }
+  *out = scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvc_status kvc_encode_noalloc(const kvc_codec* codec, const void* x, int64_t n_tokens,
+                              int64_t x_token_stride, const kvc_base_params* base,
+                              const kvc_store* dst, int64_t token_offset, void* recon_out,
+                              float* pred_out, void* stream) {
+  EncodeLaunch a;
+  kvc_status st = prepare_encode(codec, x, n_tokens, x_token_stride, base, dst, token_offset,
+                                 recon_out, pred_out, &a);
+  if (st != KVC_OK) return st;
+  const bool matrix = a.c.base == KVC_BASE_DPLR || (a.c.base == KVC_BASE_TEMPORAL && a.b.w_block);
+  if (matrix && n_tokens > 0) {
+    // outside the fused kernel's shapes the prediction goes through an fp32 buffer, which
+    // only pred_out can provide here
+    if (!encode_fused_shape(a) && !pred_out) return KVC_E_UNSUPPORTED;
+    if (a.c.base == KVC_BASE_DPLR) {
+      const size_t need = (size_t)n_tokens * a.c.rank * sizeof(float);
+      if (need > (size_t)KVC_NOALLOC_SCRATCH_BYTES) return KVC_E_WORKSPACE;
+      void* ptr = nullptr;
+      st = from_hip(scratch_for_current_device(&ptr));
+      if (st != KVC_OK) return st;
+      a.rank_buf = reinterpret_cast<float*>(ptr);   // fully written by the rank kernel first
+    }
+  }
   return from_hip(launch_encode(a, reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -51,6 +51,7 @@ struct EncodeLaunch {
   void* recon = nullptr;
   float* pred = nullptr;
   void* workspace = nullptr;
+  float* rank_buf = nullptr;   // DPLR rank-r intermediate [n][r] fp32; nullptr: in the workspace
 };
 
 struct DecodeLaunch {
@@ -109,5 +110,11 @@ hipError_t launch_fit(const EncodeLaunch& a, int iterations, hipStream_t s);
 
 // Workspace bytes of the predictor paths (0 otherwise).
 size_t encode_workspace_bytes(const CodecArgs& c, int64_t n_tokens);
+// Where the DPLR rank-r intermediate t [n][r] fp32 lives: a.rank_buf when set, else the
+// workspace after room for an fp32 prediction [n][H][d].
+float* rank_intermediate(const EncodeLaunch& a);
+// Whether an encode runs the fused predictor + quantizer kernel (the prediction then
+// stays in registers; otherwise matrix-product bases first write an fp32 prediction).
+bool encode_fused_shape(const EncodeLaunch& a);
 
 }  // namespace kvc

@@ -113,6 +113,12 @@ __global__ void add_scaled_kernel(float* base, const float* coef, const uint16_t
 
 bool predict_available() { return true; }
 
+float* rank_intermediate(const EncodeLaunch& a) {
+  if (a.rank_buf) return a.rank_buf;
+  return reinterpret_cast<float*>(reinterpret_cast<char*>(a.workspace) +
+                                  (size_t)a.n_tokens * a.c.H * a.c.D * sizeof(float));
+}
+
 size_t encode_workspace_bytes(const CodecArgs& c, int64_t n_tokens) {
   const size_t pred = (size_t)n_tokens * c.H * c.D * sizeof(float);
   if (c.base == KVC_BASE_DPLR) return pred + (size_t)n_tokens * c.rank * sizeof(float);
@@ -142,8 +148,7 @@ hipError_t launch_predict(const EncodeLaunch& a, float* base_out, hipStream_t s)
   }
   if (a.c.base != KVC_BASE_DPLR) return hipErrorInvalidValue;
   const int r = a.c.rank, nin = a.c.n_inputs;
-  float* t = reinterpret_cast<float*>(reinterpret_cast<char*>(a.workspace) +
-                                      (size_t)N * HD * sizeof(float));
+  float* t = rank_intermediate(a);
   const uint16_t* vlr = reinterpret_cast<const uint16_t*>(a.b.v_lr);     // [r][nin*H*D]
   const uint16_t* wb = reinterpret_cast<const uint16_t*>(a.b.w_block);   // [H][D][nin*D]
   const uint16_t* u = reinterpret_cast<const uint16_t*>(a.b.u);          // [H*D][r]

@@ -563,8 +563,7 @@ PredParams make_params(const EncodeLaunch& a, int mode, float* pred) {
     p.g0 = reinterpret_cast<const uint16_t*>(a.b.prev0);
     p.g1 = reinterpret_cast<const uint16_t*>(a.b.prev1);
     p.u = reinterpret_cast<const uint16_t*>(a.b.u);
-    p.t = reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.workspace) +
-                                         (size_t)a.n_tokens * a.c.H * D * sizeof(float));
+    p.t = rank_intermediate(a);
   } else if (mode == PM_TEMPORAL_V) {
     p.g0 = reinterpret_cast<const uint16_t*>(a.b.aux);
     p.e0 = reinterpret_cast<const uint16_t*>(a.b.prev0);
@@ -623,13 +622,16 @@ int cu_count() {
   return n;
 }
 
+bool encode_fused_shape(const EncodeLaunch& a) {
+  return fused_mode(a) >= 0 && fused_codec(a) && a.x_stride % 8 == 0;
+}
+
 bool launch_encode_fused(const EncodeLaunch& a, hipStream_t s, hipError_t* err) {
   const int mode = fused_mode(a);
-  if (mode < 0 || !fused_codec(a) || a.x_stride % 8 != 0) return false;
+  if (!encode_fused_shape(a)) return false;
   if (a.n_tokens == 0) { *err = hipSuccess; return true; }
   if (mode == PM_DPLR) {
-    float* t = reinterpret_cast<float*>(reinterpret_cast<char*>(a.workspace) +
-                                        (size_t)a.n_tokens * a.c.H * D * sizeof(float));
+    float* t = rank_intermediate(a);
     const hipError_t e = launch_rank(a, t, s);
     if (e != hipSuccess) { *err = e; return true; }
   }
@@ -642,8 +644,7 @@ bool launch_predict_fused(const EncodeLaunch& a, float* out, hipStream_t s, hipE
   if ((mode != PM_DPLR && mode != PM_TEMPORAL_V) || !fused_codec(a)) return false;
   if (a.n_tokens == 0) { *err = hipSuccess; return true; }
   if (mode == PM_DPLR) {
-    float* t = reinterpret_cast<float*>(reinterpret_cast<char*>(a.workspace) +
-                                        (size_t)a.n_tokens * a.c.H * D * sizeof(float));
+    float* t = rank_intermediate(a);
     const hipError_t e = launch_rank(a, t, s);
     if (e != hipSuccess) { *err = e; return true; }
   }

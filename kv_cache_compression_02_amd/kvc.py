@@ -25,8 +25,11 @@ BASE_NONE, BASE_CENTROID, BASE_DPLR, BASE_TEMPORAL, BASE_COEFF = range(5)
 # workspace ops
 OP_ENCODE, OP_DECODE, OP_ATTEND, OP_ATTEND_MIXED, OP_ATTEND_CHUNK, OP_FIT = range(6)
 ATTEND_JENSEN = 1
+# bytes of the fixed per-device scratch of kvc_encode_noalloc (KVC_NOALLOC_SCRATCH_BYTES)
+KVC_NOALLOC_SCRATCH_BYTES = 16 << 20
 
-EXPORTED = ("kvc_store_bytes", "kvc_encode", "kvc_decode", "kvc_fit_centroids", "kvc_attend_compressed",
+EXPORTED = ("kvc_store_bytes", "kvc_encode", "kvc_encode_noalloc", "kvc_decode", "kvc_fit_centroids",
+            "kvc_attend_compressed",
             "kvc_attend_compressed_chunk", "kvc_attend_mixed_dim", "kvc_workspace_bytes",
             "kvc_status_str", "kvc_abi_version")
 
@@ -72,6 +75,8 @@ def lib():
     L.kvc_store_bytes.restype = I32
     L.kvc_encode.argtypes = [P(_Codec), VP, I64, I64, P(_Base), P(_Store), I64, VP, VP, VP, SZ, VP]
     L.kvc_encode.restype = I32
+    L.kvc_encode_noalloc.argtypes = [P(_Codec), VP, I64, I64, P(_Base), P(_Store), I64, VP, VP, VP]
+    L.kvc_encode_noalloc.restype = I32
     L.kvc_decode.argtypes = [P(_Codec), P(_Store), I64, I64, P(_Base), VP, I32, VP, VP, SZ, VP]
     L.kvc_decode.restype = I32
     L.kvc_fit_centroids.argtypes = [P(_Codec), VP, I64, I64, VP, I32, VP, SZ, VP]
@@ -245,6 +250,20 @@ def kvc_encode(codec: Codec, x: torch.Tensor, store: Store, token_offset: int = 
                             x_token_stride, ctypes.byref(b), ctypes.byref(store.c()), token_offset,
                             _p(recon_out, "recon_out"), _p(pred_out, "pred_out"),
                             _p(workspace, "workspace"), ws_bytes, _stream()), "kvc_encode")
+
+
+def kvc_encode_noalloc(codec: Codec, x: torch.Tensor, store: Store, token_offset: int = 0,
+                       base: Optional[BaseParams] = None, recon_out: Optional[torch.Tensor] = None,
+                       pred_out: Optional[torch.Tensor] = None, x_token_stride: int = 0) -> None:
+    """kvc_encode without a workspace: the library's fixed per-device scratch instead."""
+    b = (base or BaseParams()).c()
+    if not x_token_stride:
+        x_token_stride = _row_stride(x, "x")
+    _check(lib().kvc_encode_noalloc(ctypes.byref(codec.c()), ctypes.c_void_p(x.data_ptr()),
+                                    x.shape[0], x_token_stride, ctypes.byref(b),
+                                    ctypes.byref(store.c()), token_offset,
+                                    _p(recon_out, "recon_out"), _p(pred_out, "pred_out"),
+                                    _stream()), "kvc_encode_noalloc")
 
 
 def kvc_decode(codec: Codec, store: Store, token_offset: int, n_tokens: int,

@@ -245,3 +245,24 @@ def test_python_binding_checks_tensor_layouts():
     with pytest.raises(ValueError):
         kvc.BaseParams(prev0=torch.zeros(4, 2, 8), prev1=torch.zeros(8, 2, 8)[::2]).c()
     assert kvc.BaseParams(prev0=every_other).c().prev_token_stride == 48
+
+
+def test_encode_noalloc_validation_errors():
+    """The no-allocation encode refuses, before any launch, a rank-r intermediate larger
+    than its fixed scratch and a fallback shape that would need an fp32 prediction
+    buffer without pred_out."""
+    L = _lib()
+    b = kvc._Base()
+    b.prev0 = b.w_block = b.u = b.v_lr = FAKE
+
+    def enc(codec, n, store_cap, pred=None):
+        st = kvc._Store(FAKE, FAKE, None, store_cap)
+        return L.kvc_encode_noalloc(ctypes.byref(codec.c()), ctypes.c_void_p(FAKE), n, 0,
+                                    ctypes.byref(b), ctypes.byref(st), 0, None,
+                                    ctypes.c_void_p(pred) if pred else None, None)
+    fused = kvc.Codec(2, 128, 2, 32, kvc.BASE_DPLR, rank=64, n_inputs=1)
+    too_many = kvc.KVC_NOALLOC_SCRATCH_BYTES // (64 * 4) + 1
+    assert enc(fused, too_many, too_many) == kvc.KVC_E_WORKSPACE
+    fallback = kvc.Codec(2, 128, 2, 128, kvc.BASE_DPLR, rank=64, n_inputs=1)   # group 128
+    assert enc(fallback, 10, 10) == kvc.KVC_E_UNSUPPORTED
+    assert enc(kvc.Codec(2, 128, 2, 32, kvc.BASE_DPLR, rank=64, n_inputs=1), 10, 5) == kvc.KVC_E_SHAPE
