@@ -1087,14 +1087,26 @@ Src make_src(const CodecArgs& c, const StoreArgs& st, const BaseArgs& b) {
   return s;
 }
 
-// Key splits of the bf16 path: about two workgroups per CU when the (head, query
-// block) grid alone is smaller, at least 8 key tiles per split, at most 8 splits, and
-// no empty split.
+// Key splits of the bf16 path.  One workgroup fills a CU (its registers), so a launch of
+// W workgroups takes ceil(W / CUs) rounds of equal length; splitting the keys s ways
+// shortens a workgroup's run s-fold but multiplies the workgroups by s and adds a partial
+// output per split.  The count kept minimizes rounds x key tiles per split, and splits
+// only when that is at least 5% shorter than one pass (so a (head, query block) grid
+// that fills the chip runs unsplit): at most 8 splits, at least 8 key tiles each, none
+// empty.
 int choose_splits(int H, int64_t nq, int64_t nk) {
   const int64_t base = (int64_t)H * ((nq + BQ - 1) / BQ);
   const int ntiles = (int)((nk + BK - 1) / BK);
-  int sp = (int)std::min<int64_t>(8, (512 + base - 1) / base);
-  sp = std::max(1, std::min(sp, ntiles / 8));
+  const int64_t cus = cu_count();
+  auto cost = [&](int s) {
+    const int64_t tps = (ntiles + s - 1) / s;
+    return ((base * s + cus - 1) / cus) * tps;
+  };
+  const int smax = std::max(1, std::min(8, ntiles / 8));
+  int sp = 1;
+  for (int s = 2; s <= smax; ++s)
+    if (cost(s) < cost(sp)) sp = s;
+  if (sp > 1 && cost(sp) * 20 > cost(1) * 19) sp = 1;
   const int tps = (ntiles + sp - 1) / sp;
   return (ntiles + tps - 1) / tps;
 }

@@ -163,8 +163,9 @@ def test_cfg1_full_size_attention_sampled():
     d, kh, vh = _cfg1_full()
     (kc, ks, kb), (vc, vs, vb) = _compress(d, 12, 128, 2, 32, 256, kvc.BF16, dev)
     q = to_dev(d["Q"], dev)
+    # the benchmark's configuration: whatever workspace the library asks for (none here:
+    # the 228 (head, query block) workgroups fill the chip, so the keys run unsplit)
     ws = kvc.kvc.workspace_for(kvc.kvc.OP_ATTEND, kc, d["K"].shape[0], dev, n_queries=q.shape[0])
-    assert ws is not None   # the benchmark's configuration splits the keys
     out = kvc.kvc_attend_compressed(kc, ks, kb, vc, vs, vb, d["K"].shape[0], q, d["scale"],
                                     workspace=ws)
     torch.cuda.synchronize()
