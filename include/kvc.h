@@ -107,9 +107,11 @@ typedef struct {
                           (H_n the Sylvester Hadamard matrix) before it is
                           quantized, and the dequantized vector is multiplied by
                           the same matrix (its own inverse) before the base is
-                          added.  Needs KVC_BASE_CENTROID, bf16, d = 128, at most
-                          512 centroids and a group that n divides, with group
-                          <= 64.  The rounded transform is the Sylvester
+                          added (Coral-KV rotates the prediction residuals).
+                          Needs bf16, d = 128 and a group that n divides, with
+                          group <= 64, and KVC_BASE_CENTROID (at most 512
+                          centroids), KVC_BASE_NONE, KVC_BASE_TEMPORAL or
+                          KVC_BASE_DPLR (rank <= 64).  The rounded transform is the Sylvester
                           recursion H_2m [a; b] = [H_m a + H_m b; H_m a - H_m b]
                           in fp32 (pairs at distance 1 combined first, then 2,
                           4, ..., n/2), then the exact 1/sqrt(n) scaling.        */
@@ -172,9 +174,10 @@ kvc_status kvc_store_bytes(const kvc_codec* codec, int64_t capacity, size_t* cod
  *   workspace: device scratch of kvc_workspace_bytes(KVC_OP_ENCODE, ...) bytes for
  *              the matrix-product bases (DPLR; temporal values without pred_out); the
  *              contents on return are unspecified.  NULL, 0 otherwise.
- * A rotated codec (codec->rotation != 0) quantizes the rotated residual; it takes no
- * recon_out or pred_out (decode the store instead) and needs x_token_stride to be a
- * multiple of 8.
+ * A rotated codec (codec->rotation != 0) quantizes the rotated residual and needs
+ * x_token_stride to be a multiple of 8; recon_out then holds base + the dequantized
+ * residual rotated back (what kvc_decode returns).  The rotated centroid codec takes no
+ * recon_out or pred_out (decode the store instead).
  * Errors: KVC_E_NULL, KVC_E_SHAPE (token_offset + n_tokens > capacity, bad
  * codec), KVC_E_UNSUPPORTED, KVC_E_ALIGN, KVC_E_WORKSPACE, KVC_E_DEVICE. */
 kvc_status kvc_encode(const kvc_codec* codec, const void* x, int64_t n_tokens,

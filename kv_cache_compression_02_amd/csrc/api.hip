@@ -73,11 +73,18 @@ kvc_status resolve_codec(const kvc_codec* c, CodecArgs* out) {
     if (a.base == KVC_BASE_DPLR) return KVC_E_UNSUPPORTED;
   }
   if (a.vec_len % a.group) return KVC_E_SHAPE;
-  if (a.rot != 0) {   // Hn residual transform: the centroid codec's 16-token-wave encoder
+  if (a.rot != 0) {   // Hn residual transform: the 16-token-wave centroid encoder and the
+                      // fused predictor + quantizer (anchors, temporal and block-DPLR bases)
     if (a.rot != 16 && a.rot != 64) return KVC_E_UNSUPPORTED;
-    if (a.base != KVC_BASE_CENTROID || a.x_dtype != KVC_BF16 || a.D != 128 || a.C > 512 ||
-        a.group > 64 || a.group % a.rot != 0)
+    if (a.x_dtype != KVC_BF16 || a.D != 128 || a.group > 64 || a.group % a.rot != 0)
       return KVC_E_UNSUPPORTED;
+    if (a.base == KVC_BASE_CENTROID) {
+      if (a.C > 512) return KVC_E_UNSUPPORTED;
+    } else if (a.base == KVC_BASE_DPLR) {
+      if (a.rank > 64) return KVC_E_UNSUPPORTED;
+    } else if (a.base != KVC_BASE_NONE && a.base != KVC_BASE_TEMPORAL) {
+      return KVC_E_UNSUPPORTED;
+    }
   }
   a.code_words = a.vec_len * a.bits / 32;
   a.groups = a.vec_len / a.group;
@@ -234,7 +241,9 @@ static kvc_status prepare_encode(const kvc_codec* codec, const void* x, int64_t 
   st = resolve_base(base, a.c, &a.b, true);
   if (st != KVC_OK) return st;
   if (a.c.base == KVC_BASE_COEFF && recon_out) return KVC_E_UNSUPPORTED;
-  if (a.c.rot != 0 && (recon_out || pred_out || stride % 8 != 0)) return KVC_E_UNSUPPORTED;
+  // rotated codecs: strides of 8 elements; the centroid encoder returns the store only
+  if (a.c.rot != 0 && (stride % 8 != 0 || (a.c.base == KVC_BASE_CENTROID && (recon_out || pred_out))))
+    return KVC_E_UNSUPPORTED;
   a.x = x;
   a.n_tokens = n_tokens;
   a.x_stride = stride;

@@ -1449,6 +1449,9 @@ hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s) {
     hipError_t e = hipSuccess;
     if (launch_encode_fused(a, s, &e)) return e;
   }
+  // rotated predictor and plain codecs are encoded by the fused predictor + quantizer
+  // only; refuse before any prediction kernel is launched
+  if (a.c.rot != 0 && a.c.base != KVC_BASE_CENTROID) return hipErrorInvalidValue;
   EncodeParams p{};
   p.x = a.x;
   p.n_tokens = a.n_tokens;

@@ -151,6 +151,7 @@ struct PredParams {
   uint32_t* sz;
   uint16_t* recon;         // [n][H][D] bf16 or null
   float* pred;             // [n][H][D] fp32 or null
+  int rot;                 // Hn residual transform width: 0, 16 or 64
 };
 
 // Output channel held by MFMA row i of output block ob (16 x 16 blocks): row 4 q + s
@@ -181,6 +182,43 @@ __device__ __forceinline__ float4 ld_f4(const float* p, bool ok) {
 // Staging tile slot (16-byte units) of chunk c (8 channels) of token tok: chunk index
 // XOR token spreads both access patterns below over all 16 bank groups.
 __device__ __forceinline__ int stg_slot(int tok, int c) { return tok * 16 + (c ^ tok); }
+
+// Hn transform (Coral-KV Fig. 5 and Fig. 9b-c: each group of n residual channels is
+// rotated by the n-point Walsh-Hadamard matrix) of a lane's GL contiguous channels in the
+// layout below (lane q of a token holds channels 32 q .. 32 q + 31), with the rounding of
+// the Sylvester recursion H_2m [a; b] = [H_m a + H_m b; H_m a - H_m b]: butterflies at
+// channel distance 1, 2, 4, 8 (and 16 for n = 64) inside the lane, for n = 64 then 32
+// with the lane 16 apart (quarter q ^ 1); the lower channel of a pair takes a + b, the
+// upper a - b; then the exact 1/sqrt(n) scale.  H_n / sqrt(n) is its own inverse, so
+// the same call rotates the residual before the quantizer and the dequantized vector
+// back.  n divides the group (validated), so every block lies in one lane or one pair.
+template <int GL>
+__device__ __forceinline__ void hn_rotate_lane(float (&r)[GL], int n, int q) {
+#pragma unroll
+  for (int h = 1; h < 32 && h < GL; h <<= 1) {
+    if (h >= 16 && n != 64) break;
+#pragma unroll
+    for (int i = 0; i < GL; ++i) {
+      if (i & h) continue;
+      const float a = r[i], b = r[i + h];
+      r[i] = a + b;
+      r[i + h] = a - b;
+    }
+  }
+  if constexpr (GL == 32) {
+    if (n == 64) {
+      const bool up = (q & 1) != 0;
+#pragma unroll
+      for (int i = 0; i < GL; ++i) {
+        const float o = __shfl_xor(r[i], 16);
+        r[i] = up ? o - r[i] : r[i] + o;
+      }
+    }
+  }
+  const float sc = n == 64 ? 0.125f : 0.25f;
+#pragma unroll
+  for (int i = 0; i < GL; ++i) r[i] *= sc;
+}
 
 template <int BITS, int G, int PM, int NIN>
 __global__ __launch_bounds__(512) void pred_kernel(PredParams p) {
@@ -426,6 +464,7 @@ __global__ __launch_bounds__(512) void pred_kernel(PredParams p) {
             r[8 * i + 2 * k + 1] = hi_bf16(xa[k]) - pred[c + 1];
           }
         }
+        if (p.rot) hn_rotate_lane<GL>(r, p.rot, q);   // the rotated residual is quantized
         uint32_t cw[GL * BITS / 32];
         GroupQ gq;
         if constexpr (G == 64) {
@@ -443,14 +482,18 @@ __global__ __launch_bounds__(512) void pred_kernel(PredParams p) {
 #pragma unroll
         for (int w = 0; w < GL * BITS / 32; ++w) words[gi * (GL * BITS / 32) + w] = cw[w];
         if (p.recon) {
+          float dq[GL];   // dequantized residual, rotated back when the codec rotates
+#pragma unroll
+          for (int i = 0; i < GL; ++i) dq[i] = dequant_one(group_code<BITS, GL>(cw, i), gq.s, gq.z);
+          if (p.rot) hn_rotate_lane<GL>(dq, p.rot, q);
 #pragma unroll
           for (int i = 0; i < GL; i += 8) {
             uint32_t o[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
               const int i0 = i + 2 * k;
-              const float v0 = pred[GL * gi + i0] + dequant_one(group_code<BITS, GL>(cw, i0), gq.s, gq.z);
-              const float v1 = pred[GL * gi + i0 + 1] + dequant_one(group_code<BITS, GL>(cw, i0 + 1), gq.s, gq.z);
+              const float v0 = pred[GL * gi + i0] + dq[i0];
+              const float v1 = pred[GL * gi + i0 + 1] + dq[i0 + 1];
               o[k] = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
             }
             rq[(GL * gi + i) / 8] = make_uint4(o[0], o[1], o[2], o[3]);
@@ -583,6 +626,7 @@ PredParams make_params(const EncodeLaunch& a, int mode, float* pred) {
   p.sz = a.st.sz;
   p.recon = reinterpret_cast<uint16_t*>(a.recon);
   p.pred = pred;
+  p.rot = a.c.rot;
   p.segs = 1;   // set at launch
   return p;
 }

@@ -30,7 +30,10 @@ its blocks and factors and a per-element brute force; the temporal value map equ
 a per-element sum in exact rational arithmetic with a non-symmetric M_h (a transposed
 M_h fails); the temporal chain's first predicted frame reads the anchor's
 reconstruction for both key terms (b != 0, so K_{-1} = 0 fails); chains reproduce
-their inputs within the O(s/2) quantization bound.
+their inputs within the O(s/2) quantization bound; with an Hn rotation of the
+prediction residuals, inputs whose rotated residual sits on the quantization grid are
+reconstructed exactly (and not without the rotation), and the reconstruction error
+keeps the rotated quantizer's bound.
 """
 from __future__ import annotations
 
@@ -38,6 +41,7 @@ import numpy as np
 
 from .numerics import round_bf16
 from .codec import quantize, dequantize, to_store
+from .rotation import rotate
 
 
 def dplr_predict(inputs, W: np.ndarray, U: np.ndarray, Vlr: np.ndarray) -> np.ndarray:
@@ -86,23 +90,34 @@ def temporal_predict_v(k_t: np.ndarray, v1: np.ndarray, M: np.ndarray, beta: np.
     return cross + np.asarray(beta, dtype=np.float64) * y
 
 
-def encode_with_prediction(x: np.ndarray, pred: np.ndarray, bits: int, group: int) -> dict:
-    """Base = fp32(prediction); residual, quantize, reconstruct (fp32)."""
+def encode_with_prediction(x: np.ndarray, pred: np.ndarray, bits: int, group: int,
+                           rotation: int = 0) -> dict:
+    """Base = fp32(prediction); residual, quantize, reconstruct (fp32).  With
+    `rotation` = n the prediction residual is rotated by H_n / sqrt(n) per group of n
+    channels before it is quantized, and the dequantized vector rotated back before the
+    base is added (Coral-KV Fig. 5 and Fig. 9b-c: Hn applied to the prediction
+    residuals)."""
     base = np.asarray(pred, dtype=np.float64).astype(np.float32)
     r = np.asarray(x, dtype=np.float32) - base
+    if rotation:
+        r = rotate(r, rotation)
     q, s16, z16 = quantize(r, bits, group)
-    xhat = base + dequantize(q, s16, z16, group)
+    deq = dequantize(q, s16, z16, group)
+    if rotation:
+        deq = rotate(deq, rotation)
+    xhat = base + deq
     return dict(base=base, q=q, s16=s16, z16=z16, xhat=xhat, store=to_store(q, s16, z16, bits))
 
 
 def dplr_chain(layers, params: dict, bits: int, group: int, anchor_bits: int,
-               anchor_group: int | None = None, teacher=None):
+               anchor_group: int | None = None, teacher=None, rotation: int = 0):
     """Cross-layer chain over `layers` = iterable of (K_l, V_l) float32 [N,H,d].
 
     Layer 0 is the anchor (base 0, `anchor_bits`).  Layer l >= 1 predicts K_l from
     K_hat_{l-1} and V_l from [K_hat_l, V_hat_{l-1}].  With `teacher` (an iterable of
     (K_hat_{l}, V_hat_{l}) reconstructions), predictions read the teacher's state
-    instead of the chain's own.  Yields one dict per layer."""
+    instead of the chain's own.  `rotation` (16 or 64) rotates the prediction residuals
+    of layers l >= 1 (the anchor is not rotated).  Yields one dict per layer."""
     anchor_group = anchor_group or group
     kprev = vprev = None
     tit = iter(teacher) if teacher is not None else None
@@ -113,9 +128,9 @@ def dplr_chain(layers, params: dict, bits: int, group: int, anchor_bits: int,
             ev = encode_with_prediction(v, zero, anchor_bits, anchor_group)
         else:
             kp = dplr_predict([kprev], params["WK"], params["UK"], params["VK"])
-            ek = encode_with_prediction(k, kp, bits, group)
+            ek = encode_with_prediction(k, kp, bits, group, rotation)
             vp = dplr_predict([ek["xhat"], vprev], params["WV"], params["UV"], params["VV"])
-            ev = encode_with_prediction(v, vp, bits, group)
+            ev = encode_with_prediction(v, vp, bits, group, rotation)
         yield dict(layer=layer, k=ek, v=ev)
         if tit is not None:
             kprev, vprev = next(tit)
@@ -124,9 +139,10 @@ def dplr_chain(layers, params: dict, bits: int, group: int, anchor_bits: int,
 
 
 def temporal_chain(k_frames, v_frames, a, b, M, beta, bits: int, group: int, anchor_bits: int,
-                   anchor_group: int | None = None):
+                   anchor_group: int | None = None, rotation: int = 0):
     """TempoKV-style chain over frames (lists of [T,H,d] float32).  Frame 0 is the anchor.
-    Yields per-frame dicts with the key and value encodings."""
+    `rotation` (16 or 64) rotates the prediction residuals of frames t >= 1.  Yields
+    per-frame dicts with the key and value encodings."""
     anchor_group = anchor_group or group
     k1 = k2 = v1 = None
     for t, (k, v) in enumerate(zip(k_frames, v_frames)):
@@ -136,8 +152,8 @@ def temporal_chain(k_frames, v_frames, a, b, M, beta, bits: int, group: int, anc
             ev = encode_with_prediction(v, zero, anchor_bits, anchor_group)
         else:
             kp = temporal_predict_k(k1, k2 if t > 1 else k1, a, b)
-            ek = encode_with_prediction(k, kp, bits, group)
+            ek = encode_with_prediction(k, kp, bits, group, rotation)
             vp = temporal_predict_v(ek["xhat"], v1, M, beta)
-            ev = encode_with_prediction(v, vp, bits, group)
+            ev = encode_with_prediction(v, vp, bits, group, rotation)
         yield dict(frame=t, k=ek, v=ev)
         k2, k1, v1 = k1, ek["xhat"], ev["xhat"]

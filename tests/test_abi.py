@@ -160,7 +160,8 @@ def test_rotation_validation_errors():
     for bad in (kvc.Codec(2, 128, 2, 64, kvc.BASE_CENTROID, 256, rotation=32),
                 kvc.Codec(2, 128, 2, 32, kvc.BASE_CENTROID, 256, rotation=64),
                 kvc.Codec(2, 128, 2, 128, kvc.BASE_CENTROID, 256, rotation=64),
-                kvc.Codec(2, 128, 2, 64, kvc.BASE_NONE, rotation=64),
+                kvc.Codec(2, 128, 4, 16, kvc.BASE_COEFF, 256, coeff_dim=16, rotation=16),
+                kvc.Codec(2, 128, 2, 64, kvc.BASE_DPLR, rank=128, n_inputs=1, rotation=64),
                 kvc.Codec(2, 128, 2, 64, kvc.BASE_CENTROID, 600, rotation=64),
                 kvc.Codec(2, 64, 2, 64, kvc.BASE_CENTROID, 256, rotation=64),
                 kvc.Codec(2, 128, 2, 64, kvc.BASE_CENTROID, 256, x_dtype=kvc.F32, rotation=16)):
@@ -171,6 +172,9 @@ def test_rotation_validation_errors():
                      ctypes.byref(st), 0, ctypes.c_void_p(FAKE), None, None, 0, None)
     assert r == kvc.KVC_E_UNSUPPORTED
     assert _enc(rc, base=b, stride=2 * 128 + 4) == kvc.KVC_E_UNSUPPORTED
+    # predictor and plain codecs rotate too (with recon / pred outputs), at strides of 8
+    plain_rot = kvc.Codec(2, 128, 2, 64, kvc.BASE_NONE, rotation=64)
+    assert _enc(plain_rot, stride=2 * 128 + 4) == kvc.KVC_E_UNSUPPORTED
     # attention: rotated residuals need centroid K and V; the mixed-dimensional form
     # takes no rotated values
     st2 = kvc._Store(FAKE, FAKE, FAKE, 16)

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 import scipy.linalg
 
-from oracle import attention, codec, rotation
+from oracle import attention, codec, predict, rotation
 
 
 def _popcount_matrix(n):
@@ -148,3 +148,39 @@ def test_attention_in_rotated_coordinates_matches_decoded_cache(nk, nv):
     vr = rot64(Cv, nv)[np.arange(H)[None, :], ev["idx"]] + deq(ev, bits)
     got = rot64(attention.attention(rot64(q, nk), kr, vr, 0.09), nv)
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-5)
+
+
+@pytest.mark.parametrize("n,bits,group", [(64, 2, 64), (16, 2, 32), (16, 4, 16), (64, 4, 64)])
+def test_prediction_residuals_rotated_grid_round_trip(n, bits, group):
+    """The predictor path rotates the prediction residual: an input equal to the
+    prediction plus H v, v on the quantizer's grid, is reconstructed exactly through
+    the rotated codec and not through the plain one."""
+    x, C, a, v = _grid_case(n, bits, group, seed=3 * n + bits + group)
+    pred = C[np.arange(C.shape[0])[None, :], a].astype(np.float64)   # any fp32-exact base
+    enc = predict.encode_with_prediction(x, pred, bits, group, rotation=n)
+    np.testing.assert_array_equal(enc["xhat"], x)
+    np.testing.assert_array_equal(
+        codec.dequantize(enc["q"], enc["s16"], enc["z16"], group), v)
+    plain = predict.encode_with_prediction(x, pred, bits, group)
+    assert np.abs(plain["xhat"] - x).max() > 1e-3
+
+
+@pytest.mark.parametrize("n,bits,group", [(64, 2, 64), (16, 2, 32)])
+def test_rotated_dplr_chain_error_bound(n, bits, group):
+    """Each predicted layer of a rotated cross-layer chain keeps the rotated
+    quantizer's error bound: |x - x_hat| <= sqrt(sum over groups of g (s/2)^2)."""
+    rng = np.random.default_rng(8)
+    h, d, r, N, L = 2, 128, 8, 30, 3
+    WK = np.broadcast_to(np.eye(d), (h, d, d)) + 0.05 * rng.standard_normal((h, d, d))
+    WV = np.concatenate([0.5 * np.eye(d)] * 2, 1)[None] + 0.05 * rng.standard_normal((h, d, 2 * d))
+    params = dict(WK=WK, UK=0.05 * rng.standard_normal((h * d, r)), VK=0.05 * rng.standard_normal((h * d, r)),
+                  WV=WV, UV=0.05 * rng.standard_normal((h * d, r)), VV=0.05 * rng.standard_normal((2 * h * d, r)))
+    layers = [(rng.standard_normal((N, h, d)).astype(np.float32),
+               rng.standard_normal((N, h, d)).astype(np.float32)) for _ in range(L)]
+    outs = list(predict.dplr_chain(layers, params, bits, group, 4, anchor_group=32, rotation=n))
+    for (k, v), o in zip(layers[1:], outs[1:]):
+        for x, e in ((k, o["k"]), (v, o["v"])):
+            s = e["s16"].astype(np.float64)
+            bound = np.sqrt((group * (s / 2) ** 2).sum(-1)) * (1 + 1e-5) + 1e-5
+            err = np.linalg.norm((e["xhat"] - x).astype(np.float64), axis=-1)
+            assert np.all(err <= bound)
