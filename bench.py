@@ -510,8 +510,7 @@ def bench_rotated(args, torch, kvc, synth, dev):
 
     def step(e=None):
         if e: e[0].record()
-        kvc.kvc_encode(codec, Kc, ks, lo, kb)
-        kvc.kvc_encode(codec, Vc, vs, lo, vb)
+        kvc.kvc_encode_kv(codec, Kc, Vc, ks, vs, lo, kb, vb)
         if e: e[1].record()
         kvc.kvc_attend_compressed(codec, ks, kb, codec, vs, vb, nk, Q, d["scale"], out=out,
                                   workspace=ws)
@@ -657,8 +656,7 @@ def main() -> int:
 
     def step(e=None):
         if e: e[0].record()
-        kvc.kvc_encode(codec, Kc, ks, lo, kb)
-        kvc.kvc_encode(codec, Vc, vs, lo, vb)
+        kvc.kvc_encode_kv(codec, Kc, Vc, ks, vs, lo, kb, vb)   # the chunk's K and V, one launch
         if e: e[1].record()
         kvc.kvc_attend_compressed(codec, ks, kb, codec, vs, vb, nk, Q, d["scale"], out=out,
                                   workspace=att_ws)

@@ -185,6 +185,21 @@ kvc_status kvc_encode(const kvc_codec* codec, const void* x, int64_t n_tokens,
                       int64_t token_offset, void* recon_out, float* pred_out, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* kvc_encode_kv - kvc_encode of the keys xk into kdst and of the values xv into vdst,
+ * the two tensors of one chunk (Coral-KV Fig. 2c: a cache block is encoded when it
+ * fills), with one codec, token count, stride and offset, and each its own base
+ * parameters.  The stores are exactly what two kvc_encode calls write; where the codec
+ * allows (KVC_BASE_CENTROID, bf16, d = 128, <= 512 centroids, group 16/32/64) both
+ * tensors are encoded by a single launch, otherwise one after the other.  No
+ * reconstruction, prediction or workspace: bases that need a workspace (block-DPLR,
+ * temporal values) return KVC_E_UNSUPPORTED.  kdst and vdst must not overlap
+ * (KVC_E_SHAPE when they share a buffer).
+ * Errors: as kvc_encode. */
+kvc_status kvc_encode_kv(const kvc_codec* codec, const void* xk, const void* xv, int64_t n_tokens,
+                         int64_t x_token_stride, const kvc_base_params* kbase,
+                         const kvc_base_params* vbase, const kvc_store* kdst, const kvc_store* vdst,
+                         int64_t token_offset, void* stream);
+
 /* Bytes of the device scratch array that kvc_encode_noalloc uses: one copy per GPU the
  * library runs on, held until the process ends. */
 #define KVC_NOALLOC_SCRATCH_BYTES (16u << 20)
@@ -329,7 +344,18 @@ kvc_status kvc_attend_compressed_chunk(const kvc_codec* kc, const kvc_store* k,
  * softmax over all n_keys keys; values decoded from their centroid store.
  *   kc: KVC_BASE_COEFF (bf16, d = 128, m = 16); kp: centroids + basis.
  *   vc: KVC_BASE_CENTROID (bf16, d = 128, not rotated); vp: centroids.
- *   q, out, lse, workspace: as kvc_attend_compressed.
+ *   q, out, lse: as kvc_attend_compressed.
+ *   workspace: optional.  With kvc_workspace_bytes(KVC_OP_ATTEND_MIXED, kc, n_keys,
+ *     n_queries) bytes (and kc->n_centroids <= 4096) the call first copies the history
+ *     into centroid-block order - keys whose centroids lie in one block of 32
+ *     consecutive centroids become contiguous, each head's blocks in ascending order,
+ *     token order kept inside a block, every value row moving with its key - and
+ *     forms q . C_k[a] once per block and query instead of once per key; the order
+ *     changes only the summation order of the softmax.  The size covers those copies
+ *     (value rows sized for the widest value codec), their tables and the key splits'
+ *     partial results; the contents on return are unspecified.  With less or none the
+ *     centroid rows are gathered per key (and the keys split only when the workspace
+ *     holds kvc_attend_compressed's split partials).
  * Errors: as kvc_attend_compressed. */
 kvc_status kvc_attend_mixed_dim(const kvc_codec* kc, const kvc_store* k,
                                 const kvc_base_params* kp, const kvc_codec* vc,
@@ -342,7 +368,9 @@ kvc_status kvc_attend_mixed_dim(const kvc_codec* kc, const kvc_store* k,
  * the attention ops; the history keys for KVC_OP_ATTEND_CHUNK) and n_queries queries.
  * Encode / decode: required by the DPLR and temporal-value bases, 0 otherwise.
  * Attention: the optional workspace that enables key splitting (0 when a single pass is
- * used anyway); with a current chunk: the required partial results.  Centroid fitting:
+ * used anyway); with a current chunk: the required partial results; mixed-dimensional
+ * (codec = the key codec): the cluster-ordered copies of the history, their tables and
+ * the split partials.  Centroid fitting:
  * the scratch store of n_tokens rows. */
 enum { KVC_OP_ENCODE = 0, KVC_OP_DECODE = 1, KVC_OP_ATTEND = 2, KVC_OP_ATTEND_MIXED = 3,
        KVC_OP_ATTEND_CHUNK = 4, KVC_OP_FIT = 5 };

@@ -9,5 +9,5 @@ from .kvc import (  # noqa: F401
     BaseParams,
     Codec, KvcError, Store, kvc_attend_compressed, kvc_attend_compressed_chunk,
     kvc_attend_mixed_dim, kvc_decode, kvc_fit_centroids,
-    kvc_encode, kvc_encode_noalloc, kvc_store_bytes, kvc_workspace_bytes, lib,
+    kvc_encode, kvc_encode_kv, kvc_encode_noalloc, kvc_store_bytes, kvc_workspace_bytes, lib,
 )

@@ -213,7 +213,8 @@ size_t kvc_workspace_bytes(int32_t op, const kvc_codec* codec, int64_t n_tokens,
   CodecArgs c;
   if (resolve_codec(codec, &c) != KVC_OK || n_tokens < 0) return 0;
   if (op == KVC_OP_ENCODE || op == KVC_OP_DECODE) return encode_workspace_bytes(c, n_tokens);
-  if (op == KVC_OP_ATTEND || op == KVC_OP_ATTEND_MIXED) return attend_workspace_bytes(c, n_tokens, n_queries);
+  if (op == KVC_OP_ATTEND) return attend_workspace_bytes(c, n_tokens, n_queries);
+  if (op == KVC_OP_ATTEND_MIXED) return attend_mixed_workspace_bytes(c, n_tokens, n_queries);
   if (op == KVC_OP_ATTEND_CHUNK) return attend_chunk_workspace_bytes(c, n_tokens, n_queries);
   if (op == KVC_OP_FIT) return fit_workspace_bytes(c, n_tokens);
   return 0;
@@ -265,6 +266,27 @@ kvc_status kvc_encode(const kvc_codec* codec, const void* x, int64_t n_tokens,
   if (st != KVC_OK) return st;
   a.workspace = workspace;
   return from_hip(launch_encode(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+kvc_status kvc_encode_kv(const kvc_codec* codec, const void* xk, const void* xv, int64_t n_tokens,
+                         int64_t x_token_stride, const kvc_base_params* kbase,
+                         const kvc_base_params* vbase, const kvc_store* kdst, const kvc_store* vdst,
+                         int64_t token_offset, void* stream) {
+  EncodeLaunch a, b;
+  kvc_status st = prepare_encode(codec, xk, n_tokens, x_token_stride, kbase, kdst, token_offset,
+                                 nullptr, nullptr, &a);
+  if (st != KVC_OK) return st;
+  st = prepare_encode(codec, xv, n_tokens, x_token_stride, vbase, vdst, token_offset, nullptr,
+                      nullptr, &b);
+  if (st != KVC_OK) return st;
+  // bases that need a workspace (block-DPLR, temporal values) are not taken here
+  if (check_predict_workspace(a.c, a.b, n_tokens, nullptr, nullptr, 0) != KVC_OK ||
+      check_predict_workspace(b.c, b.b, n_tokens, nullptr, nullptr, 0) != KVC_OK)
+    return KVC_E_UNSUPPORTED;
+  if (n_tokens > 0 && (kdst->codes == vdst->codes || kdst->scale_zero == vdst->scale_zero ||
+                       (a.c.index_bytes && kdst->index == vdst->index)))
+    return KVC_E_SHAPE;   // the two stores overlap
+  return from_hip(launch_encode_pair(a, b, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -254,13 +254,13 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
   const int half = lane >> 5;
   const int col = lane & 31;
   const int nqb = (int)((p.nq + BQ - 1) / BQ);
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int split = tile % p.splits, hq = tile / p.splits;
-  const int h = hq / nqb;
-  const int64_t myq = (int64_t)(hq % nqb) * BQ + wave * QW + col;
   const int nk = (int)p.nk;
   const int ntiles = (nk + BK - 1) / BK;
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = tile % p.splits, hq = tile / p.splits;
   const int tb = split * p.tps, te = min(ntiles, tb + p.tps);   // this split's key tiles
+  const int h = hq / nqb;
+  const int64_t myq = (int64_t)(hq % nqb) * BQ + wave * QW + col;
 
   // Per-head buffer resources (SGPRs): every prefetch is a buffer load with a 32-bit
   // byte offset, and the descriptor's record count bounds it.  The count covers the
@@ -998,6 +998,633 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttnParams p) {
 }
 
 // ----------------------------------------------------------------------------
+// Mixed-dimensional attention over cluster-ordered keys
+// ----------------------------------------------------------------------------
+// The NanoKV-Fast score of key n is q . C_k[a_n] + (B^T q) . c_n (NanoKV abstract and
+// project page: scores on the low-dimensional coefficients, without reconstructing
+// K).  Keys whose centroids fall in one block of CL_BLK consecutive centroids share
+// the 32 x CL_BLK table Q C_blk^T of a wave's queries, so the history is first put in
+// centroid-block order (attention does not depend on the order of its keys; the
+// values move with their keys), the table is formed once per block with 8 MFMAs, and
+// a key's first term enters the score MFMA as a one-hot product: the K tile row holds,
+// next to the key's coefficients, a one-hot row over the block's 32 centroids, and the
+// table (split into bf16 high and low parts, exact to about 2^-16) is the other
+// operand.  Per 64-key tile a wave runs 8 one-hot MFMAs, the 6 coefficient MFMAs
+// (16-dimensional contraction, bf16 high/low parts) and the 16 PV MFMAs, against
+// 16 + 6 + 16 when the centroid rows are gathered into a 128-wide K tile.
+//
+// Ordering: a stable counting sort by block (block = min(a, C - 1) / CL_BLK) per head,
+// in three launches: per-chunk block counts, per-head prefix sums (block offsets,
+// each chunk's first destination per block, and the tile table: a block's keys are
+// cut into 64-key tiles, the last one ragged), and a scatter that copies each key's K
+// coefficient row and V row to its sorted place (rank within a chunk from wave
+// ballots, so equal blocks keep token order and the result is deterministic).
+constexpr int CL_BLK = 32;        // centroids per block (one 32 x 32 MFMA tile)
+constexpr int CL_CHUNK = 2048;    // keys per counting / scatter workgroup
+constexpr int CL_THREADS = 256;
+constexpr int CL_MAXNB = 128;     // blocks at most (C <= 4096)
+
+struct ClusterParams {
+  int64_t n;                      // keys per head
+  int H, nb, nchunk, tmax;
+  Src k, v;                       // source stores (rows h * cap + i)
+  uint32_t* kcodes;               // cluster-ordered copies, rows h * n + j
+  uint32_t* ksz;
+  uint8_t* kidx;
+  uint32_t* vcodes;
+  uint32_t* vsz;
+  uint8_t* vidx;
+  int* cnt;                       // [H][nchunk][nb]: counts, then first destinations
+  int2* tiles;                    // [H][tmax]: (first sorted position, block | keys << 8
+                                  //   | first tile of its block << 16)
+  int* ntiles;                    // [H]
+};
+
+__device__ __forceinline__ int cl_index(const Src& s, int64_t row) {
+  return s.idxb == 1 ? (int)reinterpret_cast<const uint8_t*>(s.index)[row]
+                     : (int)reinterpret_cast<const uint16_t*>(s.index)[row];
+}
+__device__ __forceinline__ int cl_bin(const ClusterParams& c, int h, int64_t i) {
+  return min(cl_index(c.k, (int64_t)h * c.k.cap + i), c.k.C - 1) / CL_BLK;
+}
+
+__global__ __launch_bounds__(CL_THREADS) void cluster_count_kernel(ClusterParams c) {
+  __shared__ int hist[CL_MAXNB];
+  const int chunk = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  for (int b = tid; b < c.nb; b += CL_THREADS) hist[b] = 0;
+  __syncthreads();
+  const int64_t i0 = (int64_t)chunk * CL_CHUNK;
+  for (int j = tid; j < CL_CHUNK; j += CL_THREADS)
+    if (i0 + j < c.n) atomicAdd(&hist[cl_bin(c, h, i0 + j)], 1);
+  __syncthreads();
+  for (int b = tid; b < c.nb; b += CL_THREADS)
+    c.cnt[((int64_t)h * c.nchunk + chunk) * c.nb + b] = hist[b];
+}
+
+__global__ __launch_bounds__(CL_THREADS) void cluster_scan_kernel(ClusterParams c) {
+  __shared__ int boff[CL_MAXNB + 1];
+  __shared__ int tbase[CL_MAXNB + 1];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  int* cnt = c.cnt + (int64_t)h * c.nchunk * c.nb;
+  for (int b = tid; b < c.nb; b += CL_THREADS) {   // per block: prefix over chunks
+    int run = 0;
+    for (int k0 = 0; k0 < c.nchunk; k0 += 8) {      // 8 loads in flight
+      int v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = k0 + j < c.nchunk ? cnt[(k0 + j) * c.nb + b] : 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (k0 + j < c.nchunk) cnt[(k0 + j) * c.nb + b] = run;
+        run += v[j];
+      }
+    }
+    boff[b] = run;   // the block's size for now
+  }
+  __syncthreads();
+  if (tid == 0) {   // block offsets and first tiles (at most CL_MAXNB steps)
+    int off = 0, tb = 0;
+    for (int b = 0; b < c.nb; ++b) {
+      const int sz = boff[b];
+      boff[b] = off;
+      tbase[b] = tb;
+      off += sz;
+      tb += (sz + BK - 1) / BK;
+    }
+    boff[c.nb] = off;
+    tbase[c.nb] = tb;
+    c.ntiles[h] = tb;
+  }
+  __syncthreads();
+  for (int e = tid; e < c.nchunk * c.nb; e += CL_THREADS) cnt[e] += boff[e % c.nb];
+  const int T = tbase[c.nb];
+  for (int t = tid; t < T; t += CL_THREADS) {
+    int lo = 0, hi = c.nb - 1;   // the last block with tbase <= t (it holds tile t)
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tbase[mid] <= t) lo = mid;
+      else hi = mid - 1;
+    }
+    const int st = boff[lo] + (t - tbase[lo]) * BK;
+    const int cnt = min(BK, boff[lo + 1] - st);
+    c.tiles[(int64_t)h * c.tmax + t] = make_int2(st, lo | (cnt << 8) | ((t == tbase[lo]) << 16));
+  }
+}
+
+__device__ __forceinline__ void cl_copy_words(uint32_t* dst, const uint32_t* src, int n) {
+  if ((n & 3) == 0) {
+    for (int w = 0; w < n; w += 4)
+      *reinterpret_cast<uint4*>(dst + w) = *reinterpret_cast<const uint4*>(src + w);
+  } else if ((n & 1) == 0) {
+    for (int w = 0; w < n; w += 2)
+      *reinterpret_cast<uint2*>(dst + w) = *reinterpret_cast<const uint2*>(src + w);
+  } else {
+    for (int w = 0; w < n; ++w) dst[w] = src[w];
+  }
+}
+
+__global__ __launch_bounds__(CL_THREADS) void cluster_scatter_kernel(ClusterParams c) {
+  constexpr int NWV = CL_THREADS / 64;
+  __shared__ int run[CL_MAXNB];
+  __shared__ int wh[NWV][CL_MAXNB];
+  const int chunk = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  for (int b = tid; b < c.nb; b += CL_THREADS) {
+    run[b] = c.cnt[((int64_t)h * c.nchunk + chunk) * c.nb + b];
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) wh[w][b] = 0;
+  }
+  __syncthreads();
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+  for (int r = 0; r < CL_CHUNK / CL_THREADS; ++r) {
+    const int64_t i = (int64_t)chunk * CL_CHUNK + r * CL_THREADS + tid;
+    const bool live = i < c.n;
+    const int bin = live ? cl_bin(c, h, i) : CL_MAXNB;   // 8 bits
+    uint64_t same = ~0ull;   // lanes of the wave with this lane's block
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint64_t bk = __ballot((bin >> k) & 1);
+      same &= ((bin >> k) & 1) ? bk : ~bk;
+    }
+    const int rank = __popcll(same & below);
+    if (live && rank == 0) wh[wave][bin] = __popcll(same);
+    __syncthreads();
+    if (live) {
+      int j = run[bin] + rank;
+      for (int w = 0; w < wave; ++w) j += wh[w][bin];
+      const int64_t src = (int64_t)h * c.k.cap + i, dk = (int64_t)h * c.n + j;
+      const int64_t vsrc = (int64_t)h * c.v.cap + i;
+      cl_copy_words(c.kcodes + dk * c.k.words, c.k.codes + src * c.k.words, c.k.words);
+      cl_copy_words(c.ksz + dk * c.k.groups, c.k.sz + src * c.k.groups, c.k.groups);
+      cl_copy_words(c.vcodes + dk * c.v.words, c.v.codes + vsrc * c.v.words, c.v.words);
+      cl_copy_words(c.vsz + dk * c.v.groups, c.v.sz + vsrc * c.v.groups, c.v.groups);
+      if (c.k.idxb == 1) c.kidx[dk] = reinterpret_cast<const uint8_t*>(c.k.index)[src];
+      else reinterpret_cast<uint16_t*>(c.kidx)[dk] = reinterpret_cast<const uint16_t*>(c.k.index)[src];
+      if (c.v.idxb == 1) c.vidx[dk] = reinterpret_cast<const uint8_t*>(c.v.index)[vsrc];
+      else if (c.v.idxb == 2)
+        reinterpret_cast<uint16_t*>(c.vidx)[dk] = reinterpret_cast<const uint16_t*>(c.v.index)[vsrc];
+    }
+    __syncthreads();
+    for (int b = tid; b < c.nb; b += CL_THREADS) {
+      int add = 0;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) {
+        add += wh[w][b];
+        wh[w][b] = 0;
+      }
+      run[b] += add;
+    }
+    __syncthreads();
+  }
+}
+
+// The tile table of the ordered history.
+struct ClusterTabs {
+  const int2* tiles;   // [H][tmax], as ClusterParams::tiles
+  const int* ntiles;   // [H]
+  int tmax;
+};
+constexpr int MWIN = 1024;   // tile records a workgroup stages in LDS at a time
+
+// One workgroup = 8 waves x 32 queries of one head, as attend_bf16_kernel; p.k and p.v
+// are the cluster-ordered stores (capacity n), p.k.cen the key centroid table.
+template <int KBITS, int VBITS, bool VCEN>
+__global__ __launch_bounds__(NT, 1) void attend_mixed_cl_kernel(AttnParams p, ClusterTabs ct) {
+  // K tile row: 16 high + 16 low coefficient parts, the one-hot row over the block's 32
+  // centroids, pad
+  constexpr int KR = 32 + CL_BLK + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BK * KR];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][DM * VROW];
+  __shared__ __attribute__((aligned(16))) uint16_t c_lds[2][CL_BLK * KROW];
+  __shared__ int2 m_lds[MWIN];   // the tile records of the current window
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int nqb = (int)((p.nq + BQ - 1) / BQ);
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = tile % p.splits, hq = tile / p.splits;
+  const int h = hq / nqb;
+  const int64_t myq = (int64_t)(hq % nqb) * BQ + wave * QW + col;
+  const int nth = ct.ntiles[h];
+  // this workgroup's tiles of the head's table (none for a late split of a head with
+  // fewer tiles than the longest)
+  const int tb = min(nth, split * p.tps), te = min(nth, tb + p.tps);
+  const int2* tab = ct.tiles + (int64_t)h * ct.tmax;
+  int w0 = tb, w1 = tb;   // the window of tile records in m_lds
+
+  auto rsrc = [](const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+  };
+  const int64_t n = p.nk;
+  const int kwb = p.k.words * 4;
+  const int vwb = p.v.words * 4, vgb = p.v.groups * 4;
+  const int64_t hr = (int64_t)h * n;   // the ordered stores have capacity n
+  const auto rk_code = rsrc(p.k.codes + hr * p.k.words, n * kwb);
+  const auto rk_sz = rsrc(p.k.sz + hr, n * 4);
+  const auto rk_idx = rsrc(reinterpret_cast<const uint8_t*>(p.k.index) + hr * p.k.idxb, n * p.k.idxb);
+  const auto rv_code = rsrc(p.v.codes + hr * p.v.words, n * vwb);
+  const auto rv_sz = rsrc(p.v.sz + hr * p.v.groups, n * vgb);
+  const auto rv_idx = rsrc(reinterpret_cast<const uint8_t*>(p.v.index) + hr * p.v.idxb,
+                           VCEN ? n * p.v.idxb : 0);
+  const auto rk_cen = rsrc(reinterpret_cast<const uint16_t*>(p.k.cen) + (int64_t)h * p.k.C * DM,
+                           (int64_t)p.k.C * DM * 2);
+  const auto rv_cen = rsrc(reinterpret_cast<const uint16_t*>(p.v.cen) + (int64_t)h * p.v.C * DM,
+                           VCEN ? (int64_t)p.v.C * DM * 2 : 0);
+
+  // roles: 8 lanes per K row (lanes kw < 2 decode 8 coefficients each, kw == 0 also the
+  // table offset), 16 lanes per V row pair (8 channels each), 16 lanes per centroid row
+  const int kk = tid >> 3, kw = tid & 7;
+  const int c8 = tid & 15, kp = tid >> 4;
+  const int kword = (8 * min(kw, 1) * KBITS) >> 5;
+  const int kcsh = (8 * min(kw, 1) * KBITS) & 31;
+  const int vword = (8 * c8 * VBITS) >> 5;
+  const int vgrp = (8 * c8) / p.v.group;
+  const int vsh = (8 * c8 * VBITS) & 31;
+  const uint32_t vsel = vsh ? 0x07060302u : 0x05040100u;
+  auto load_index = [](__amdgpu_buffer_rsrc_t r, uint32_t key, int idxb) -> int {
+    return idxb == 1 ? (int)__builtin_amdgcn_raw_buffer_load_b8(r, key, 0, 0)
+                     : (int)__builtin_amdgcn_raw_buffer_load_b16(r, 2u * key, 0, 0);
+  };
+
+  struct Pre {
+    uint32_t kcode, ksz;
+    int kidx;
+    uint32_t vcode[2], vsz[2];
+    uint4 vc[2];
+    uint4 crow;
+  };
+  // a tile record of the window: first sorted position, block, keys of the block in it,
+  // and whether the block's Q C^T table has to be formed (its first tile, or the
+  // window's); the records of tiles t+1 .. t+4 ride in registers, one LDS read per tile
+  struct Meta {
+    int st, blk, cnt;
+    bool fresh;
+  };
+  auto meta_of = [&](int2 e, int t) {
+    Meta m;
+    m.st = __builtin_amdgcn_readfirstlane(e.x);
+    const int y = __builtin_amdgcn_readfirstlane(e.y);
+    m.blk = y & 0xFF;
+    m.cnt = (y >> 8) & 0xFF;
+    m.fresh = t == w0 || ((y >> 16) & 1);
+    return m;
+  };
+  auto meta = [&](int t) { return meta_of(m_lds[t - w0], t); };
+  auto load_vidx = [&](const Meta& mt, int (&vi)[2]) {
+    const uint32_t st = (uint32_t)mt.st;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) vi[j] = VCEN ? load_index(rv_idx, st + 2 * kp + j, p.v.idxb) : 0;
+  };
+  auto load_data = [&](const Meta& mt, const int (&vi)[2], Pre& pr) {
+    const int st = mt.st, blk = mt.blk;
+    const bool fresh = mt.fresh;
+    const uint32_t key = (uint32_t)st + kk;
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    pr.kcode = __builtin_amdgcn_raw_buffer_load_b32(rk_code, key * kwb + kword * 4, 0, 0);
+    pr.ksz = __builtin_amdgcn_raw_buffer_load_b32(rk_sz, key * 4, 0, 0);
+    pr.kidx = load_index(rk_idx, key, p.k.idxb);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t m = (uint32_t)st + 2 * kp + j;
+      pr.vcode[j] = __builtin_amdgcn_raw_buffer_load_b32(rv_code, m * vwb + vword * 4, 0, 0);
+      pr.vsz[j] = __builtin_amdgcn_raw_buffer_load_b32(rv_sz, m * vgb + vgrp * 4, 0, 0);
+      if constexpr (VCEN) {
+        const uint32_t off = min((uint32_t)vi[j], (uint32_t)(p.v.C - 1)) * (DM * 2) + 16 * c8;
+        const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rv_cen, off, 0, 0);
+        pr.vc[j] = uint4{a.x, a.y, a.z, a.w};
+      } else {
+        pr.vc[j] = uint4{0u, 0u, 0u, 0u};
+      }
+    }
+    if (fresh) {   // the block's centroid rows, zero past C (the range check)
+      const uint32_t row = (uint32_t)(CL_BLK * blk) + (tid >> 4);
+      const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rk_cen, row * (DM * 2) + 16 * (tid & 15), 0, 0);
+      pr.crow = uint4{a.x, a.y, a.z, a.w};
+    }
+  };
+  auto dequant = [&](const Meta& mt, const Pre& pr, int buf) {
+    const int blk = mt.blk;
+    const bool fresh = mt.fresh;
+    // ---- K: coefficients (hi, lo) and the key's row in the wave's Q C^T table
+    if (kw < 2) {
+      const float sc = f16_bits_to_f32(pr.ksz & 0xFFFFu), ze = f16_bits_to_f32(pr.ksz >> 16);
+      const uint32_t w = pr.kcode >> kcsh;
+      float cv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        cv[i] = __builtin_fmaf((float)((w >> (KBITS * i)) & ((1u << KBITS) - 1u)), sc, ze);
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hi[i] = pk_bf16(cv[2 * i], cv[2 * i + 1]);
+        lo[i] = pk_bf16(cv[2 * i] - lo_bf16(hi[i]), cv[2 * i + 1] - hi_bf16(hi[i]));
+      }
+      *reinterpret_cast<uint4*>(&k_lds[buf][kk * KR + 8 * kw]) = uint4{hi[0], hi[1], hi[2], hi[3]};
+      *reinterpret_cast<uint4*>(&k_lds[buf][kk * KR + 16 + 8 * kw]) = uint4{lo[0], lo[1], lo[2], lo[3]};
+    }
+    {   // one-hot row: centroids 4kw..4kw+3 of the block (keys of the next block, which
+        // are masked, get a row inside the block)
+      const int a = min(max(min(pr.kidx, p.k.C - 1) - CL_BLK * blk, 0), CL_BLK - 1) - 4 * kw;
+      const uint32_t o0 = (a == 0 ? 0x3F80u : 0u) | (a == 1 ? 0x3F800000u : 0u);
+      const uint32_t o1 = (a == 2 ? 0x3F80u : 0u) | (a == 3 ? 0x3F800000u : 0u);
+      *reinterpret_cast<uint2*>(&k_lds[buf][kk * KR + 32 + 4 * kw]) = make_uint2(o0, o1);
+    }
+    if (fresh)
+      *reinterpret_cast<uint4*>(&c_lds[buf][(tid >> 4) * KROW + 8 * (tid & 15)]) = pr.crow;
+    // ---- V: channels 8c8..8c8+7 of keys 2kp, 2kp+1 -> transposed fp16 (swizzled)
+    float x[2][8];
+    float dq[2][8];
+    float s24[2], ze2[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      s24[j] = f16_bits_to_f32(pr.vsz[j] & 0xFFFFu) * 0x1p24f;
+      ze2[j] = f16_bits_to_f32(pr.vsz[j] >> 16);
+    }
+    if constexpr (VBITS == 2) {
+      const uint32_t w = __builtin_amdgcn_perm(pr.vcode[1], pr.vcode[0], vsel);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const uint32_t b = (w >> (2 * r)) & 0x00030003u;
+        dq[0][r] = __builtin_fmaf(code_lo(b), s24[0], ze2[0]);
+        dq[1][r] = __builtin_fmaf(code_hi(b), s24[1], ze2[1]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t b = (pr.vcode[j] >> (4 * r)) & 0x000F000Fu;
+          dq[j][r] = __builtin_fmaf(code_lo(b), s24[j], ze2[j]);
+          dq[j][r + 4] = __builtin_fmaf(code_hi(b), s24[j], ze2[j]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t cw[4] = {pr.vc[j].x, pr.vc[j].y, pr.vc[j].z, pr.vc[j].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[j][2 * i] = lo_bf16(cw[i]) + dq[j][2 * i];
+        x[j][2 * i + 1] = hi_bf16(cw[i]) + dq[j][2 * i + 1];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int row = 8 * c8 + c;
+      const uint32_t w = bf16x2_to_f16x2(pk_bf16(x[0][c], x[1][c]));
+      *reinterpret_cast<uint32_t*>(&v_lds[buf][row * VROW + vpos(row, 2 * kp)]) = w;
+    }
+  };
+
+  // Q^T operand: lane holds Q[myq][16*ks + 8*half .. +7] for ks = 0..7
+  bf16x8_t qreg[8];
+  {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + (myq * p.H + h) * DM + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (myq < p.nq) qreg[ks] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * ks);
+      else qreg[ks] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+  // (B^T q) for the lane's query as bf16 high / low parts, k-slice 8*half..+7
+  bf16x8_t phi, plo;
+  {
+    uint16_t* bst = &v_lds[1][0];   // the basis is staged in the not yet used V buffer
+    for (int e = tid; e < DM * 16 / 8; e += NT)
+      *reinterpret_cast<uint4*>(&bst[8 * e]) = *reinterpret_cast<const uint4*>(p.basis + 8 * e);
+    __syncthreads();
+    float part[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) part[j] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = 16 * ks + 8 * half + e;
+        const float qv = bf16_bits_to_f32((uint16_t)qreg[ks][e]);
+        const uint4 b0 = *reinterpret_cast<const uint4*>(&bst[16 * i]);
+        const uint4 b1 = *reinterpret_cast<const uint4*>(&bst[16 * i + 8]);
+        const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          part[2 * jj] = __builtin_fmaf(qv, lo_bf16(bw[jj]), part[2 * jj]);
+          part[2 * jj + 1] = __builtin_fmaf(qv, hi_bf16(bw[jj]), part[2 * jj + 1]);
+        }
+      }
+    float pj[8];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float full = part[j] + other_half(part[j], half);
+      if ((j >> 3) == half) pj[j & 7] = full;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t h2 = pk_bf16(pj[2 * i], pj[2 * i + 1]);
+      const uint32_t l2 = pk_bf16(pj[2 * i] - lo_bf16(h2), pj[2 * i + 1] - hi_bf16(h2));
+      phi[2 * i] = (short)(h2 & 0xFFFFu); phi[2 * i + 1] = (short)(h2 >> 16);
+      plo[2 * i] = (short)(l2 & 0xFFFFu); plo[2 * i + 1] = (short)(l2 >> 16);
+    }
+    __syncthreads();
+  }
+
+  f32x16_t oacc[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[d][r] = 0.0f;
+  float m_run = -__builtin_inff();
+  float l_run = 0.0f;
+  const float c2 = p.scale_log2;
+  // Q C_blk^T of this wave's queries as the B operand of the one-hot MFMAs: k-step s
+  // covers the block's centroids 16 s .. 16 s + 15, high and low bf16 parts
+  bf16x8_t qch[2], qcl[2];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    qch[s2] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    qcl[s2] = qch[s2];
+  }
+
+  auto compute = [&](const Meta& mt, int buf) {
+    const int cnt = mt.cnt;
+    const bool fresh = mt.fresh;
+    if (fresh) {   // Q C_blk^T of this wave's queries (uniform over the workgroup)
+      f32x16_t qc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) qc[r] = 0.0f;
+      const uint16_t* crow = &c_lds[buf][col * KROW + 8 * half];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        qc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t*>(crow + 16 * ks),
+                                                      qreg[ks], qc, 0, 0, 0);
+      // accumulator row m = 8 (r / 4) + 4 half + r % 4 (a centroid), column = the lane's
+      // query; the B operand of k-step s wants rows 16 s + 8 half .. + 7 in the lane:
+      // trading rows 4..7 of half 1 for rows 8..11 of half 0 (and so on) between the
+      // register pairs (r, r + 4) puts them there
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(qc[8 * s2 + j]),
+                                                           __float_as_uint(qc[8 * s2 + 4 + j]), false, false);
+          v[j] = __uint_as_float(sw[0]);
+          v[4 + j] = __uint_as_float(sw[1]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t h2 = pk_bf16(v[2 * i], v[2 * i + 1]);
+          const uint32_t l2 = pk_bf16(v[2 * i] - lo_bf16(h2), v[2 * i + 1] - hi_bf16(h2));
+          qch[s2][2 * i] = (short)(h2 & 0xFFFFu); qch[s2][2 * i + 1] = (short)(h2 >> 16);
+          qcl[s2][2 * i] = (short)(l2 & 0xFFFFu); qcl[s2][2 * i + 1] = (short)(l2 >> 16);
+        }
+      }
+    }
+    // S^T = one-hot(a) (Q C_blk^T) + the coefficient part (hi*hi + hi*lo + lo*hi)
+    f32x16_t sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+      const uint16_t* r0 = &k_lds[buf][(kb * 32 + col) * KR + 8 * half];
+      const bf16x8_t ch = *reinterpret_cast<const bf16x8_t*>(r0);
+      const bf16x8_t cl = *reinterpret_cast<const bf16x8_t*>(r0 + 16);
+      const bf16x8_t oh0 = *reinterpret_cast<const bf16x8_t*>(r0 + 32);
+      const bf16x8_t oh1 = *reinterpret_cast<const bf16x8_t*>(r0 + 48);
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oh0, qch[0], sacc[kb], 0, 0, 0);
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oh1, qch[1], sacc[kb], 0, 0, 0);
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oh0, qcl[0], sacc[kb], 0, 0, 0);
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oh1, qcl[1], sacc[kb], 0, 0, 0);
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ch, phi, sacc[kb], 0, 0, 0);
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ch, plo, sacc[kb], 0, 0, 0);
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cl, phi, sacc[kb], 0, 0, 0);
+    }
+    f16x8_t vf[4][4];
+    const uint16_t* vbase = &v_lds[buf][col * VROW + 8 * (half ^ (col >> 4))];
+    auto read_vf = [&](int d) {
+#pragma unroll
+      for (int kh = 0; kh < 4; ++kh)
+        vf[d][kh] = *reinterpret_cast<const f16x8_t*>(vbase + 32 * d * VROW + 16 * (kh ^ d));
+    };
+    read_vf(0);   // the other channel blocks are read during the PV MFMAs (registers)
+    if (cnt < BK) {   // the block's last, partial tile: keys of the next block are masked
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= cnt) sacc[kb][r] = -__builtin_inff();
+    }
+    float mloc = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[kb][r]);
+    mloc = fmaxf(mloc, other_half(mloc, half));
+    if (__builtin_expect(__any(mloc * c2 > m_run + 8.0f), 0)) {   // lazy rescaling (2^8)
+      const float m_new = fmaxf(m_run, mloc * c2);
+      const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= corr;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[d][r] *= corr;
+      m_run = m_new;
+    }
+    const float negm = -m_run;
+    f16x8_t pb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        f16x8_t t8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          t8[j] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * hf + j], c2, negm));
+        pb[kb][hf] = t8;
+      }
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kh = 0; kh < 4; ++kh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const h2 pr = {pb[kh >> 1][kh & 1][2 * i], pb[kh >> 1][kh & 1][2 * i + 1]};
+        ls[kh] = __builtin_amdgcn_fdot2(pr, one2, ls[kh], false);
+      }
+    float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    lsum += other_half(lsum, half);
+    l_run = l_run + lsum;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      if (d + 1 < 4) read_vf(d + 1);
+#pragma unroll
+      for (int kh = 0; kh < 4; ++kh)
+        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[d][kh], pb[kh >> 1][kh & 1], oacc[d], 0, 0, 0);
+    }
+  };
+
+  // ---- prologue / main loop: decode tile t+1 into the other buffer and prefetch tile
+  //      t+2's rows (t+3's value indices) while tile t is attended
+  Pre pre;
+  int vidx[2] = {0, 0};
+  for (w0 = tb; w0 < te; w0 = w1) {   // windows of MWIN tiles, each its own pipeline
+    w1 = min(te, w0 + MWIN);
+    for (int i = tid; i < w1 - w0; i += NT) m_lds[i] = tab[w0 + i];
+    __syncthreads();
+    Meta m0 = meta(w0), m1 = m0, m2 = m0, m3 = m0;
+    if (w0 + 1 < w1) m1 = meta(w0 + 1);
+    if (w0 + 2 < w1) m2 = meta(w0 + 2);
+    if (w0 + 3 < w1) m3 = meta(w0 + 3);
+    load_vidx(m0, vidx);
+    load_data(m0, vidx, pre);
+    if (w0 + 1 < w1) load_vidx(m1, vidx);
+    dequant(m0, pre, 0);
+    if (w0 + 1 < w1) load_data(m1, vidx, pre);
+    if (w0 + 2 < w1) load_vidx(m2, vidx);
+    __syncthreads();
+    for (int t = w0; t < w1; ++t) {
+      const int buf = (t - w0) & 1;
+      const int2 r4 = m_lds[min(t + 4, w1 - 1) - w0];   // decoded at the end of the tile
+      if (t + 1 < w1) {
+        dequant(m1, pre, buf ^ 1);
+        if (t + 2 < w1) load_data(m2, vidx, pre);
+        if (t + 3 < w1) load_vidx(m3, vidx);
+      }
+      compute(m0, buf);
+      __syncthreads();
+      m0 = m1;
+      m1 = m2;
+      m2 = m3;
+      if (t + 4 < w1) m3 = meta_of(r4, t + 4);
+    }
+  }
+
+  // ---- epilogue (a split without tiles writes O = 0 with log-sum-exp -inf)
+  float* const outp = p.splits > 1 ? p.part_o + (int64_t)split * p.nq * p.H * DM : p.out;
+  float* const lsep = p.splits > 1 ? p.part_lse + (int64_t)split * p.H * p.nq : p.lse;
+  if (myq < p.nq) {
+    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+    float* op = outp + (myq * p.H + h) * DM;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float4 o;
+        o.x = oacc[d][4 * g + 0] * inv;
+        o.y = oacc[d][4 * g + 1] * inv;
+        o.z = oacc[d][4 * g + 2] * inv;
+        o.w = oacc[d][4 * g + 3] * inv;
+        *reinterpret_cast<float4*>(op + d * 32 + 8 * g + 4 * half) = o;
+      }
+    if (lsep && half == 0)
+      lsep[(int64_t)h * p.nq + myq] =
+          l_run > 0.0f ? (m_run + __log2f(l_run)) * 0.69314718055994531f : -__builtin_inff();
+  }
+}
+
+// ----------------------------------------------------------------------------
 // fp32 path: one lane per query, 32-key tiles decoded into LDS as fp32
 // ----------------------------------------------------------------------------
 template <int D>
@@ -1090,23 +1717,23 @@ Src make_src(const CodecArgs& c, const StoreArgs& st, const BaseArgs& b) {
 // Key splits of the bf16 path.  One workgroup fills a CU (its registers), so a launch of
 // W workgroups takes ceil(W / CUs) rounds of equal length; splitting the keys s ways
 // shortens a workgroup's run s-fold but multiplies the workgroups by s and adds a partial
-// output per split.  The count kept minimizes rounds x key tiles per split, and splits
-// only when that is at least 5% shorter than one pass (so a (head, query block) grid
-// that fills the chip runs unsplit): at most 8 splits, at least 8 key tiles each, none
-// empty.
+// output per split.  The count kept minimizes rounds x key tiles per split: at most 8
+// splits, at least 8 key tiles each, none empty.
+int even_cost(int64_t base, int ntiles, int64_t cus, int s) {
+  const int64_t tps = (ntiles + s - 1) / s;
+  return (int)(((base * s + cus - 1) / cus) * tps);
+}
+
 int choose_splits(int H, int64_t nq, int64_t nk) {
   const int64_t base = (int64_t)H * ((nq + BQ - 1) / BQ);
   const int ntiles = (int)((nk + BK - 1) / BK);
   const int64_t cus = cu_count();
-  auto cost = [&](int s) {
-    const int64_t tps = (ntiles + s - 1) / s;
-    return ((base * s + cus - 1) / cus) * tps;
-  };
   const int smax = std::max(1, std::min(8, ntiles / 8));
   int sp = 1;
   for (int s = 2; s <= smax; ++s)
-    if (cost(s) < cost(sp)) sp = s;
-  if (sp > 1 && cost(sp) * 20 > cost(1) * 19) sp = 1;
+    if (even_cost(base, ntiles, cus, s) < even_cost(base, ntiles, cus, sp)) sp = s;
+  // a split pays a partial output and a merge: keep one pass unless 5% shorter
+  if (sp > 1 && (int64_t)even_cost(base, ntiles, cus, sp) * 20 > (int64_t)ntiles * 19) sp = 1;
   const int tps = (ntiles + sp - 1) / sp;
   return (ntiles + tps - 1) / tps;
 }
@@ -1285,6 +1912,57 @@ hipError_t launch_attend_chunk(const AttendLaunch& a, const void* chunk_k, const
   return launch_combine(pm, s);
 }
 
+namespace {
+
+// Workspace of the cluster-ordered mixed path: the tables, the ordered K and V copies
+// (V sized for the widest value codec: 16 code words, 8 scale/zero words and 2-byte
+// indices per row), then the key splits' partial results.
+struct MixedLayout {
+  size_t cnt, tiles, ntiles, kcodes, ksz, kidx, vcodes, vsz, vidx, part, total;
+  int nb, nchunk, tmax, splits;
+};
+
+bool mixed_clusterable(const CodecArgs& kc) {
+  return kc.base == KVC_BASE_COEFF && kc.x_dtype == KVC_BF16 && kc.D == DM && kc.m == 16 &&
+         kc.groups == 1 && kc.C >= 1 && kc.C <= CL_BLK * CL_MAXNB;
+}
+
+MixedLayout mixed_layout(const CodecArgs& kc, int64_t n, int64_t nq) {
+  MixedLayout L{};
+  L.nb = (kc.C + CL_BLK - 1) / CL_BLK;
+  L.nchunk = (int)((n + CL_CHUNK - 1) / CL_CHUNK);
+  L.tmax = (int)((n + BK - 1) / BK) + L.nb;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t H = (size_t)kc.H, rows = H * (size_t)n;
+  size_t o = 0;
+  L.cnt = o;    o = al(o + H * L.nchunk * L.nb * 4);
+  L.tiles = o;  o = al(o + H * L.tmax * 8);
+  L.ntiles = o; o = al(o + H * 4);
+  L.kcodes = o; o = al(o + rows * kc.code_words * 4);
+  L.ksz = o;    o = al(o + rows * 4);
+  L.kidx = o;   o = al(o + rows * kc.index_bytes);
+  L.vcodes = o; o = al(o + rows * 16 * 4);
+  L.vsz = o;    o = al(o + rows * 8 * 4);
+  L.vidx = o;   o = al(o + rows * 2);
+  L.splits = choose_splits(kc.H, nq, (int64_t)L.tmax * BK);
+  L.part = o;
+  if (L.splits > 1) o = al(o + (size_t)L.splits * nq * H * (DM + 1) * 4);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+size_t attend_mixed_workspace_bytes(const CodecArgs& kc, int64_t n_keys, int64_t n_queries) {
+  if (n_queries <= 0 || n_keys <= 0) return 0;
+  if (!mixed_clusterable(kc)) return attend_workspace_bytes(kc, n_keys, n_queries);
+  return mixed_layout(kc, n_keys, n_queries).total;
+}
+
+// With a workspace of attend_mixed_workspace_bytes: order the keys by centroid block
+// (three small launches), attend the ordered copies with attend_mixed_cl_kernel, merge
+// the key splits.  Otherwise the centroid rows are gathered into the K tiles
+// (attend_bf16_kernel<..., MIXED>).
 hipError_t launch_attend_mixed(const AttendLaunch& a, hipStream_t s) {
   if (a.n_queries == 0) return hipSuccess;
   if (a.kc.m != 16 || a.kc.groups != 1) return hipErrorInvalidValue;
@@ -1301,10 +1979,69 @@ hipError_t launch_attend_mixed(const AttendLaunch& a, hipStream_t s) {
   p.v = make_src(a.vc, a.vs, a.vb);
   p.jensen = a.jensen;
   p.basis = reinterpret_cast<const uint16_t*>(a.kb.basis);
-  plan_splits(a, p);
-  const int nqb = (int)((a.n_queries + BQ - 1) / BQ);
-  const dim3 grid(nqb * a.kc.H * p.splits), block(NT);
   const bool vc = p.v.mode == SRC_CENTROID;
+  const int nqb = (int)((a.n_queries + BQ - 1) / BQ);
+  if (mixed_clusterable(a.kc) && vc && a.vc.code_words <= 16 && a.vc.groups <= 8 && a.vc.index_bytes <= 2 &&
+      a.workspace && a.workspace_bytes >= attend_mixed_workspace_bytes(a.kc, a.n_keys, a.n_queries)) {
+    const MixedLayout L = mixed_layout(a.kc, a.n_keys, a.n_queries);
+    char* ws = reinterpret_cast<char*>(a.workspace);
+    ClusterParams c{};
+    c.n = a.n_keys;
+    c.H = a.kc.H;
+    c.nb = L.nb;
+    c.nchunk = L.nchunk;
+    c.tmax = L.tmax;
+    c.k = p.k;
+    c.v = p.v;
+    c.cnt = reinterpret_cast<int*>(ws + L.cnt);
+    c.tiles = reinterpret_cast<int2*>(ws + L.tiles);
+    c.ntiles = reinterpret_cast<int*>(ws + L.ntiles);
+    c.kcodes = reinterpret_cast<uint32_t*>(ws + L.kcodes);
+    c.ksz = reinterpret_cast<uint32_t*>(ws + L.ksz);
+    c.kidx = reinterpret_cast<uint8_t*>(ws + L.kidx);
+    c.vcodes = reinterpret_cast<uint32_t*>(ws + L.vcodes);
+    c.vsz = reinterpret_cast<uint32_t*>(ws + L.vsz);
+    c.vidx = reinterpret_cast<uint8_t*>(ws + L.vidx);
+    const dim3 cg((unsigned)L.nchunk, (unsigned)a.kc.H);
+    hipLaunchKernelGGL(cluster_count_kernel, cg, dim3(CL_THREADS), 0, s, c);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(cluster_scan_kernel, dim3((unsigned)a.kc.H), dim3(CL_THREADS), 0, s, c);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(cluster_scatter_kernel, cg, dim3(CL_THREADS), 0, s, c);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    AttnParams pc = p;
+    pc.k.codes = c.kcodes;
+    pc.k.sz = c.ksz;
+    pc.k.index = c.kidx;
+    pc.k.cap = a.n_keys;
+    pc.v.codes = c.vcodes;
+    pc.v.sz = c.vsz;
+    pc.v.index = c.vidx;
+    pc.v.cap = a.n_keys;
+    pc.splits = L.splits;
+    pc.tps = (L.tmax + L.splits - 1) / L.splits;
+    if (pc.splits > 1) {
+      pc.part_o = reinterpret_cast<float*>(ws + L.part);
+      pc.part_lse = pc.part_o + (int64_t)pc.splits * a.n_queries * a.kc.H * DM;
+    }
+    ClusterTabs ct{c.tiles, c.ntiles, L.tmax};
+    const dim3 grid((unsigned)(nqb * a.kc.H * pc.splits)), block(NT);
+#define KVC_MIXCL(KB_, VB_)                                                               \
+    if (a.kc.bits == KB_ && a.vc.bits == VB_) {                                           \
+      hipLaunchKernelGGL((attend_mixed_cl_kernel<KB_, VB_, true>), grid, block, 0, s, pc, ct); \
+      e = hipGetLastError();                                                              \
+      if (e != hipSuccess) return e;                                                      \
+      return launch_combine(pc, s);                                                       \
+    }
+    KVC_MIXCL(4, 2) KVC_MIXCL(4, 4) KVC_MIXCL(2, 2) KVC_MIXCL(2, 4)
+#undef KVC_MIXCL
+    return hipErrorInvalidValue;
+  }
+  plan_splits(a, p);
+  const dim3 grid(nqb * a.kc.H * p.splits), block(NT);
 #define KVC_MIX(KB_, VB_, VC_)                                                           \
   if (a.kc.bits == KB_ && a.vc.bits == VB_ && vc == VC_) {                              \
     hipLaunchKernelGGL((attend_bf16_kernel<KB_, VB_, true, VC_, true>), grid, block, 0, s, p); \

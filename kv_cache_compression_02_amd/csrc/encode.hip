@@ -44,6 +44,15 @@ struct EncodeParams {
   void* index;
   void* recon;
   float* pred;
+  // a second tensor encoded by the same launch (the keys and the values of a chunk):
+  // its input, centroid table and store; same codec, token count, stride and offset
+  int pair;
+  const void* x2;
+  const void* centroids2;
+  uint32_t* codes2;
+  uint32_t* sz2;
+  void* index2;
+  int64_t capacity2;
 };
 
 template <typename XT, int D>
@@ -1047,18 +1056,26 @@ __global__ __launch_bounds__(64 * c16_waves(CM), 4) void encode_c16_kernel(Encod
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = lane & 15, q = lane >> 4;
   const int ntile = (int)((p.n_tokens + TT - 1) / TT);
-  const int wph = (int)gridDim.x / p.H;   // workgroups per head
+  const int wph = (int)gridDim.x / (p.pair ? 2 * p.H : p.H);   // workgroups per head
   const int b = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = b / wph, first = b % wph;
+  const int hs = b / wph, first = b % wph;
+  // a paired launch: head slots H .. 2H - 1 are the second tensor's heads
+  const bool second = hs >= p.H;
+  const int h = second ? hs - p.H : hs;
+  const void* const px = second ? p.x2 : p.x;
+  uint32_t* const pcodes = second ? p.codes2 : p.codes;
+  uint32_t* const psz = second ? p.sz2 : p.sz;
+  void* const pidx = second ? p.index2 : p.index;
+  const int64_t pcap = second ? p.capacity2 : p.capacity;
   const int C = p.C;
   const int nb = (C + 15) >> 4;
-  const uint16_t* cen = reinterpret_cast<const uint16_t*>(p.centroids) + (int64_t)h * C * D;
+  const uint16_t* cen = reinterpret_cast<const uint16_t*>(second ? p.centroids2 : p.centroids) + (int64_t)h * C * D;
 
   // this lane's quarter row of a tile's token (zeros past the last token)
   auto load_quarter = [&](int tl, uint4 (&dst)[4]) {
     const int64_t nn = (int64_t)tl * TT + wave * 16 + t;
     const bool lv = tl < ntile && nn < p.n_tokens;
-    const uint16_t* src = reinterpret_cast<const uint16_t*>(p.x) + (lv ? nn : 0) * p.x_stride +
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(px) + (lv ? nn : 0) * p.x_stride +
                           (int64_t)h * D + 8 * q;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
@@ -1282,7 +1299,7 @@ __global__ __launch_bounds__(64 * c16_waves(CM), 4) void encode_c16_kernel(Encod
         const uint32_t tk = qt[lane];
         const int j = (int)(tk & 0x3FFu);
         const int64_t nt = nw0 + (int)((tk >> 10) & 15u);
-        const uint16_t* xr = reinterpret_cast<const uint16_t*>(p.x) + nt * p.x_stride + (int64_t)h * D;
+        const uint16_t* xr = reinterpret_cast<const uint16_t*>(px) + nt * p.x_stride + (int64_t)h * D;
         const uint16_t* crow = &tab[j * ROW];
         float acc = 0.0f;
 #pragma unroll
@@ -1323,7 +1340,7 @@ __global__ __launch_bounds__(64 * c16_waves(CM), 4) void encode_c16_kernel(Encod
 
   // 4. residual, group scale/zero, codes of the lane's quarter row
   const uint16_t* crow = &tab[best * ROW + 8 * q];
-  const int64_t row = (int64_t)h * p.capacity + p.token_offset + n;
+  const int64_t row = (int64_t)h * pcap + p.token_offset + n;
   constexpr int KG = G == 64 ? 2 : 1;   // k-steps of one group
 #pragma unroll
   for (int kg = 0; kg < 4; kg += KG) {
@@ -1360,16 +1377,16 @@ __global__ __launch_bounds__(64 * c16_waves(CM), 4) void encode_c16_kernel(Encod
       const float rinv = __builtin_amdgcn_rcpf(gq.s);
       const float nzr = -(gq.z * rinv);
       const float thr = 0.5f - (fabsf(nzr) + (float)(L + 2)) * 0x1p-19f;
-      bool bad = false;
+      float dev = 0.0f;   // largest |y - rint(y)| of the group
 #pragma unroll
       for (int i = 0; i < 8 * KG; ++i) {
         const float y = __builtin_fmaf(r[i], rinv, nzr);
         const float k = __builtin_rintf(y);
-        bad |= fabsf(y - k) > thr;
+        dev = fmaxf(dev, fabsf(y - k));
         const uint32_t code = (uint32_t)__builtin_amdgcn_fmed3f(k, 0.0f, (float)L);
         cw[i >> 3] |= code << (BITS * (i & 7));
       }
-      if (bad) {
+      if (dev > thr) {
 #pragma unroll
         for (int u = 0; u < KG; ++u) cw[u] = 0u;
 #pragma unroll
@@ -1381,20 +1398,20 @@ __global__ __launch_bounds__(64 * c16_waves(CM), 4) void encode_c16_kernel(Encod
     for (int u = 0; u < KG; ++u) {
       const int ks = kg + u;
       if constexpr (BITS == 4) {
-        if (live) p.codes[row * 16 + 4 * ks + q] = cw[u];
+        if (live) pcodes[row * 16 + 4 * ks + q] = cw[u];
       } else {
         const uint32_t pw = xqi(cw[u], 16);   // the partner quarter's 16 bits
-        if (live && (q & 1) == 0) p.codes[row * 8 + 2 * ks + (q >> 1)] = cw[u] | (pw << 16);
+        if (live && (q & 1) == 0) pcodes[row * 8 + 2 * ks + (q >> 1)] = cw[u] | (pw << 16);
       }
     }
     // scale/zero word of the group (one lane per group)
     const int gi = G == 16 ? 2 * kg + (q >> 1) : (G == 32 ? kg : kg >> 1);
     const bool owner = G == 16 ? (q & 1) == 0 : q == 0;
-    if (live && owner) p.sz[row * (D / G) + gi] = gq.word;
+    if (live && owner) psz[row * (D / G) + gi] = gq.word;
   }
   if (live && q == 0) {
-    if (p.index_bytes == 2) reinterpret_cast<uint16_t*>(p.index)[row] = (uint16_t)best;
-    else reinterpret_cast<uint8_t*>(p.index)[row] = (uint8_t)best;
+    if (p.index_bytes == 2) reinterpret_cast<uint16_t*>(pidx)[row] = (uint16_t)best;
+    else reinterpret_cast<uint8_t*>(pidx)[row] = (uint8_t)best;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) xv[i] = xnext[i];
@@ -1410,8 +1427,9 @@ hipError_t launch_c16_t(const EncodeParams& p, hipStream_t s) {
   if (e != hipSuccess) return e;
   const int64_t ntile = (p.n_tokens + TT - 1) / TT;
   const int64_t resident = (int64_t)std::max(1, occ) * cu_count();
-  const int wph = (int)std::max<int64_t>(1, std::min<int64_t>(ntile, resident / p.H));
-  hipLaunchKernelGGL(k, dim3((unsigned)(wph * p.H)), dim3(NT), 0, s, p);
+  const int slots = p.pair ? 2 * p.H : p.H;
+  const int wph = (int)std::max<int64_t>(1, std::min<int64_t>(ntile, resident / slots));
+  hipLaunchKernelGGL(k, dim3((unsigned)(wph * slots)), dim3(NT), 0, s, p);
   return hipGetLastError();
 }
 
@@ -1439,19 +1457,8 @@ hipError_t launch_encode_t(const EncodeParams& p, int H, hipStream_t s) {
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_predict(const EncodeLaunch& a, float* base_out, hipStream_t s);
-
-hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s) {
-  if (a.n_tokens == 0) return hipSuccess;
-  {
-    hipError_t e = hipSuccess;
-    if (launch_encode_fused(a, s, &e)) return e;
-  }
-  // rotated predictor and plain codecs are encoded by the fused predictor + quantizer
-  // only; refuse before any prediction kernel is launched
-  if (a.c.rot != 0 && a.c.base != KVC_BASE_CENTROID) return hipErrorInvalidValue;
+// The fields of EncodeParams that come straight from the validated call.
+EncodeParams encode_params(const EncodeLaunch& a) {
   EncodeParams p{};
   p.x = a.x;
   p.n_tokens = a.n_tokens;
@@ -1479,6 +1486,49 @@ hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s) {
   p.index = a.st.index;
   p.recon = a.recon;
   p.pred = a.pred;
+  return p;
+}
+
+// The 16-token-wave centroid encoder, if it serves the codec (bf16 d = 128, <= 512
+// centroids, group 16 / 32 / 64, no reconstruction or prediction output, input stride a
+// multiple of 8): launches it and sets *done.
+hipError_t dispatch_c16(const EncodeParams& p, const CodecArgs& c, hipStream_t s, bool* done) {
+  *done = false;
+  if (!(c.x_dtype == KVC_BF16 && c.D == 128 && p.mode == MODE_CENTROID && !p.recon && !p.pred &&
+        c.C <= 512 && p.x_stride % 8 == 0 && (c.group == 16 || c.group == 32 || c.group == 64)))
+    return hipSuccess;
+#define KVC_ENC_C16(B, G, CM, R)                                                         \
+  if (c.bits == B && c.group == G && (c.C <= 256) == (CM == 256) && c.rot == R) {       \
+    *done = true;                                                                       \
+    return launch_c16_t<B, G, CM, R>(p, s);                                             \
+  }
+#define KVC_ENC_C16_CM(CM)                                                                \
+  KVC_ENC_C16(2, 16, CM, 0) KVC_ENC_C16(2, 32, CM, 0) KVC_ENC_C16(2, 64, CM, 0)          \
+  KVC_ENC_C16(4, 16, CM, 0) KVC_ENC_C16(4, 32, CM, 0) KVC_ENC_C16(4, 64, CM, 0)          \
+  KVC_ENC_C16(2, 16, CM, 16) KVC_ENC_C16(2, 32, CM, 16) KVC_ENC_C16(2, 64, CM, 16)       \
+  KVC_ENC_C16(4, 16, CM, 16) KVC_ENC_C16(4, 32, CM, 16) KVC_ENC_C16(4, 64, CM, 16)       \
+  KVC_ENC_C16(2, 64, CM, 64) KVC_ENC_C16(4, 64, CM, 64)
+  KVC_ENC_C16_CM(256)
+  KVC_ENC_C16_CM(512)
+#undef KVC_ENC_C16_CM
+#undef KVC_ENC_C16
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_predict(const EncodeLaunch& a, float* base_out, hipStream_t s);
+
+hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s) {
+  if (a.n_tokens == 0) return hipSuccess;
+  {
+    hipError_t e = hipSuccess;
+    if (launch_encode_fused(a, s, &e)) return e;
+  }
+  // rotated predictor and plain codecs are encoded by the fused predictor + quantizer
+  // only; refuse before any prediction kernel is launched
+  if (a.c.rot != 0 && a.c.base != KVC_BASE_CENTROID) return hipErrorInvalidValue;
+  EncodeParams p = encode_params(a);
   switch (a.c.base) {
     case KVC_BASE_NONE: p.mode = MODE_NONE; break;
     case KVC_BASE_CENTROID: p.mode = MODE_CENTROID; break;
@@ -1506,20 +1556,10 @@ hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s) {
   // register-resident MFMA assignment, persistent workgroups per head
   const bool cen_ok = p.mode == MODE_CENTROID && (a.c.group == 16 || a.c.group == 32 || a.c.group == 64);
   const bool coeff_ok = p.mode == MODE_COEFF && a.c.m == 16 && a.c.group == 16 && a.c.bits == 4;
-  if (bf16 && a.c.D == 128 && cen_ok && !p.recon && !p.pred && a.c.C <= 512 && p.x_stride % 8 == 0) {
-#define KVC_ENC_C16(B, G, CM, R)                                                         \
-    if (a.c.bits == B && a.c.group == G && (a.c.C <= 256) == (CM == 256) && a.c.rot == R) \
-      return launch_c16_t<B, G, CM, R>(p, s);
-#define KVC_ENC_C16_CM(CM)                                                                \
-    KVC_ENC_C16(2, 16, CM, 0) KVC_ENC_C16(2, 32, CM, 0) KVC_ENC_C16(2, 64, CM, 0)          \
-    KVC_ENC_C16(4, 16, CM, 0) KVC_ENC_C16(4, 32, CM, 0) KVC_ENC_C16(4, 64, CM, 0)          \
-    KVC_ENC_C16(2, 16, CM, 16) KVC_ENC_C16(2, 32, CM, 16) KVC_ENC_C16(2, 64, CM, 16)       \
-    KVC_ENC_C16(4, 16, CM, 16) KVC_ENC_C16(4, 32, CM, 16) KVC_ENC_C16(4, 64, CM, 16)       \
-    KVC_ENC_C16(2, 64, CM, 64) KVC_ENC_C16(4, 64, CM, 64)
-    KVC_ENC_C16_CM(256)
-    KVC_ENC_C16_CM(512)
-#undef KVC_ENC_C16_CM
-#undef KVC_ENC_C16
+  {
+    bool done = false;
+    const hipError_t e = dispatch_c16(p, a.c, s, &done);
+    if (done || e != hipSuccess) return e;
   }
   if (a.c.rot != 0) return hipErrorInvalidValue;   // a width / group pair without a kernel
   if (bf16 && a.c.D == 128 && (cen_ok || coeff_ok) && a.c.C <= 512 && p.x_stride % 8 == 0) {
@@ -1549,6 +1589,30 @@ hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s) {
     return bf16 ? launch_encode_t<uint16_t, 128>(p, a.c.H, s) : launch_encode_t<float, 128>(p, a.c.H, s);
   }
   return bf16 ? launch_encode_t<uint16_t, 64>(p, a.c.H, s) : launch_encode_t<float, 64>(p, a.c.H, s);
+}
+
+// The keys and the values of a chunk (same codec, token count, stride and offset): one
+// launch of the 16-token-wave centroid encoder over both tensors' heads when it serves
+// the codec, else the two tensors one after the other.
+hipError_t launch_encode_pair(const EncodeLaunch& a, const EncodeLaunch& b, hipStream_t s) {
+  if (a.n_tokens == 0) return hipSuccess;
+  if (a.c.base == KVC_BASE_CENTROID) {
+    EncodeParams p = encode_params(a);
+    p.mode = MODE_CENTROID;
+    p.pair = 1;
+    p.x2 = b.x;
+    p.centroids2 = b.b.centroids;
+    p.codes2 = b.st.codes;
+    p.sz2 = b.st.sz;
+    p.index2 = b.st.index;
+    p.capacity2 = b.st.capacity;
+    bool done = false;
+    const hipError_t e = dispatch_c16(p, a.c, s, &done);
+    if (done || e != hipSuccess) return e;
+  }
+  const hipError_t e = launch_encode(a, s);
+  if (e != hipSuccess) return e;
+  return launch_encode(b, s);
 }
 
 }  // namespace kvc

@@ -138,16 +138,16 @@ __device__ __forceinline__ GroupQ quantize_with(const float (&r)[G], float mn, f
     const float rinv = __builtin_amdgcn_rcpf(q.s);
     const float nzr = -(q.z * rinv);
     const float thr = 0.5f - (fabsf(nzr) + (float)(L + 2)) * 0x1p-19f;
-    bool bad = false;
+    float dev = 0.0f;   // largest |y - rint(y)| of the group
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       const float y = __builtin_fmaf(r[i], rinv, nzr);
       const float k = __builtin_rintf(y);
-      bad |= fabsf(y - k) > thr;
+      dev = fmaxf(dev, fabsf(y - k));
       const uint32_t code = (uint32_t)__builtin_amdgcn_fmed3f(k, 0.0f, (float)L);
       cw[i / PER] |= code << (BITS * (i % PER));
     }
-    if (bad) {
+    if (dev > thr) {
 #pragma unroll
       for (int w = 0; w < GW; ++w) cw[w] = 0u;
 #pragma unroll

@@ -81,6 +81,7 @@ struct AttendLaunch {
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s);
+hipError_t launch_encode_pair(const EncodeLaunch& a, const EncodeLaunch& b, hipStream_t s);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t s);
 hipError_t launch_attend(const AttendLaunch& a, hipStream_t s);
 hipError_t launch_attend_mixed(const AttendLaunch& a, hipStream_t s);
@@ -103,6 +104,7 @@ bool predict_available();
 // pass is used anyway).
 size_t attend_workspace_bytes(const CodecArgs& kc, int64_t n_keys, int64_t n_queries);
 size_t attend_chunk_workspace_bytes(const CodecArgs& kc, int64_t n_keys, int64_t n_queries);
+size_t attend_mixed_workspace_bytes(const CodecArgs& kc, int64_t n_keys, int64_t n_queries);
 // Online centroid fitting: `iterations` Lloyd steps on a.x (n_tokens rows) updating the
 // table a.b.centroids in place; a.workspace holds a scratch store of n_tokens rows.
 size_t fit_workspace_bytes(const CodecArgs& c, int64_t n_tokens);

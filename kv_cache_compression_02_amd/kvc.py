@@ -28,7 +28,8 @@ ATTEND_JENSEN = 1
 # bytes of the fixed per-device scratch of kvc_encode_noalloc (KVC_NOALLOC_SCRATCH_BYTES)
 KVC_NOALLOC_SCRATCH_BYTES = 16 << 20
 
-EXPORTED = ("kvc_store_bytes", "kvc_encode", "kvc_encode_noalloc", "kvc_decode", "kvc_fit_centroids",
+EXPORTED = ("kvc_store_bytes", "kvc_encode", "kvc_encode_kv", "kvc_encode_noalloc", "kvc_decode",
+            "kvc_fit_centroids",
             "kvc_attend_compressed",
             "kvc_attend_compressed_chunk", "kvc_attend_mixed_dim", "kvc_workspace_bytes",
             "kvc_status_str", "kvc_abi_version")
@@ -77,6 +78,9 @@ def lib():
     L.kvc_encode.restype = I32
     L.kvc_encode_noalloc.argtypes = [P(_Codec), VP, I64, I64, P(_Base), P(_Store), I64, VP, VP, VP]
     L.kvc_encode_noalloc.restype = I32
+    L.kvc_encode_kv.argtypes = [P(_Codec), VP, VP, I64, I64, P(_Base), P(_Base), P(_Store), P(_Store),
+                                I64, VP]
+    L.kvc_encode_kv.restype = I32
     L.kvc_decode.argtypes = [P(_Codec), P(_Store), I64, I64, P(_Base), VP, I32, VP, VP, SZ, VP]
     L.kvc_decode.restype = I32
     L.kvc_fit_centroids.argtypes = [P(_Codec), VP, I64, I64, VP, I32, VP, SZ, VP]
@@ -250,6 +254,24 @@ def kvc_encode(codec: Codec, x: torch.Tensor, store: Store, token_offset: int = 
                             x_token_stride, ctypes.byref(b), ctypes.byref(store.c()), token_offset,
                             _p(recon_out, "recon_out"), _p(pred_out, "pred_out"),
                             _p(workspace, "workspace"), ws_bytes, _stream()), "kvc_encode")
+
+
+def kvc_encode_kv(codec: Codec, xk: torch.Tensor, xv: torch.Tensor, kstore: Store, vstore: Store,
+                  token_offset: int = 0, kbase: Optional[BaseParams] = None,
+                  vbase: Optional[BaseParams] = None, x_token_stride: int = 0) -> None:
+    """Compress the keys xk and the values xv [n][H][d] of one chunk (same codec, shape and
+    row stride) into their stores at rows [token_offset, token_offset + n)."""
+    if xk.shape != xv.shape:
+        raise ValueError("xk and xv must have the same shape")
+    kb, vb = (kbase or BaseParams()).c(), (vbase or BaseParams()).c()
+    if not x_token_stride:
+        x_token_stride = _row_stride(xk, "xk")
+        if _row_stride(xv, "xv") != x_token_stride:
+            raise ValueError("xk and xv must have the same token stride")
+    _check(lib().kvc_encode_kv(ctypes.byref(codec.c()), ctypes.c_void_p(xk.data_ptr()),
+                               ctypes.c_void_p(xv.data_ptr()), xk.shape[0], x_token_stride,
+                               ctypes.byref(kb), ctypes.byref(vb), ctypes.byref(kstore.c()),
+                               ctypes.byref(vstore.c()), token_offset, _stream()), "kvc_encode_kv")
 
 
 def kvc_encode_noalloc(codec: Codec, x: torch.Tensor, store: Store, token_offset: int = 0,

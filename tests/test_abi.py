@@ -56,6 +56,34 @@ def _enc(codec, x=FAKE, n=4, stride=0, base=None, store=None, off=0):
                         ctypes.byref(b), ctypes.byref(st), off, None, None, None, 0, None)
 
 
+def test_encode_kv_validation_errors():
+    """The paired encode validates both tensors as kvc_encode does, refuses bases that
+    need a workspace and stores that share a buffer - all before any launch."""
+    L = _lib()
+    FAKE2 = FAKE + (1 << 20)
+
+    def enc_kv(codec, kstore, vstore, kbase=None, vbase=None, n=4):
+        return L.kvc_encode_kv(ctypes.byref(codec.c()), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE2),
+                               n, 0, ctypes.byref(kbase or kvc._Base()), ctypes.byref(vbase or kvc._Base()),
+                               ctypes.byref(kstore), ctypes.byref(vstore), 0, None)
+
+    plain = kvc.Codec(2, 128, 2, 32, kvc.BASE_NONE)
+    ks = kvc._Store(FAKE, FAKE, None, 16)
+    vs = kvc._Store(FAKE2, FAKE2, None, 16)
+    assert enc_kv(plain, ks, ks) == kvc.KVC_E_SHAPE                     # the stores overlap
+    assert enc_kv(plain, ks, vs, n=0) == kvc.KVC_OK                     # empty: nothing launched
+    assert enc_kv(plain, ks, kvc._Store(FAKE2, FAKE2, None, 2)) == kvc.KVC_E_SHAPE   # 4 > capacity
+    cen = kvc.Codec(2, 128, 2, 32, kvc.BASE_CENTROID, 16)
+    b = kvc._Base()
+    b.centroids = FAKE
+    assert enc_kv(cen, kvc._Store(FAKE, FAKE, FAKE, 16), kvc._Store(FAKE2, FAKE2, FAKE2, 16),
+                  kbase=b) == kvc.KVC_E_NULL                            # no value centroids
+    dplr = kvc.Codec(2, 128, 2, 32, kvc.BASE_DPLR, rank=16, n_inputs=1)
+    d = kvc._Base()
+    d.prev0 = d.w_block = d.u = d.v_lr = FAKE
+    assert enc_kv(dplr, ks, vs, kbase=d, vbase=d) == kvc.KVC_E_UNSUPPORTED   # needs a workspace
+
+
 def test_encode_validation_errors():
     ok_codec = kvc.Codec(2, 64, 4, 32, kvc.BASE_NONE, x_dtype=kvc.F32)
     assert _enc(ok_codec, x=0) == kvc.KVC_E_NULL

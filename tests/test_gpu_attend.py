@@ -164,7 +164,7 @@ def test_cfg1_full_size_attention_sampled():
     (kc, ks, kb), (vc, vs, vb) = _compress(d, 12, 128, 2, 32, 256, kvc.BF16, dev)
     q = to_dev(d["Q"], dev)
     # the benchmark's configuration: whatever workspace the library asks for (none here:
-    # the 228 (head, query block) workgroups fill the chip, so the keys run unsplit)
+    # splitting 228 (head, query block) workgroups over 256 CUs would take two rounds)
     ws = kvc.kvc.workspace_for(kvc.kvc.OP_ATTEND, kc, d["K"].shape[0], dev, n_queries=q.shape[0])
     out = kvc.kvc_attend_compressed(kc, ks, kb, vc, vs, vb, d["K"].shape[0], q, d["scale"],
                                     workspace=ws)

@@ -85,18 +85,58 @@ def _oracle_mixed(d, q_rows, n_keys=None, bits=4):
                                 e["chat"], vh, d["scale"], return_lse=True)
 
 
-@pytest.mark.parametrize("n_keys", [300, 1, 77])
-def test_mixed_attention_small_ragged(n_keys):
+@pytest.mark.parametrize("n_keys,ordered", [(300, False), (1, False), (77, False),
+                                            (300, True), (1, True), (77, True)])
+def test_mixed_attention_small_ragged(n_keys, ordered):
+    """ordered: with the workspace the keys are put in centroid-block order first (40
+    centroids: a full block of 32 and a partial one; ragged 64-key tiles at each block's
+    end); without it the centroid rows are gathered per key."""
     dev = device()
     d = _small(seed=22)
     kc, ks, kb = _encode_keys(d, dev)
     vc, vs, vb = _encode_values(d, dev)
     q = to_dev(d["Q"], dev)
+    ws = kvc.kvc.workspace_for(kvc.kvc.OP_ATTEND_MIXED, kc, n_keys, dev, n_queries=q.shape[0]) \
+        if ordered else None
+    assert (ws is not None) == ordered
+    print(f"mixed attention n_keys={n_keys} ordered={ordered}", flush=True)
     out, lse = kvc.kvc_attend_mixed_dim(kc, ks, kb, vc, vs, vb, n_keys, q, d["scale"],
-                                        want_lse=True)
+                                        want_lse=True, workspace=ws)
     torch.cuda.synchronize()
     ref, rlse = _oracle_mixed(d, slice(None), n_keys)
     assert np.abs(out.cpu().numpy() - ref).max() <= 2e-2
+    assert np.abs(lse.cpu().numpy() - rlse).max() <= 2e-2
+
+
+@pytest.mark.parametrize("n_centroids,bits,vbits,n_keys", [(300, 4, 2, 1957), (512, 2, 4, 3000),
+                                                          (33, 4, 2, 700), (64, 4, 4, 64)])
+def test_mixed_attention_ordered_shapes(n_centroids, bits, vbits, n_keys):
+    """The centroid-block order across shapes: 300 centroids (10 blocks, the last
+    partial), 512 (16 full blocks, INT2 coefficients, INT4 values), 33 (a block of one
+    centroid), 64 keys (one tile); against the oracle and against the gather path."""
+    dev = device()
+    d = synth.cfg4(seed=23, hist_frames=max(1, (n_keys + 99) // 100), query_frames=1, tokens=100,
+                   heads=3, n_centroids=n_centroids)
+    d["v_bits"] = vbits
+    kc, ks, kb = _encode_keys(d, dev, bits)
+    vc, vs, vb = _encode_values(d, dev)
+    q = to_dev(d["Q"], dev)
+    ws = kvc.kvc.workspace_for(kvc.kvc.OP_ATTEND_MIXED, kc, n_keys, dev, n_queries=q.shape[0])
+    assert ws is not None
+    print(f"ordered mixed attention C={n_centroids} bits={bits}/{vbits} n_keys={n_keys}", flush=True)
+    out, lse = kvc.kvc_attend_mixed_dim(kc, ks, kb, vc, vs, vb, n_keys, q, d["scale"],
+                                        want_lse=True, workspace=ws)
+    g_out, g_lse = kvc.kvc_attend_mixed_dim(kc, ks, kb, vc, vs, vb, n_keys, q, d["scale"],
+                                            want_lse=True)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(np.isfinite(o))
+    # the two paths sum the keys in different orders, and P is rounded to fp16 against
+    # a running maximum that moves differently: they agree to a few fp16 ulps of P
+    assert np.abs(o - g_out.cpu().numpy()).max() <= 1e-2
+    assert np.abs(lse.cpu().numpy() - g_lse.cpu().numpy()).max() <= 1e-3
+    ref, rlse = _oracle_mixed(d, slice(None), n_keys, bits)
+    assert np.abs(o - ref).max() <= 2e-2
     assert np.abs(lse.cpu().numpy() - rlse).max() <= 2e-2
 
 
