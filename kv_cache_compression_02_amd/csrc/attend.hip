@@ -773,8 +773,9 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      if (t + 2 < te) load_k(t + 2, kidx, kpre);
-      if (t + 3 < te) load_kidx(t + 3, kidx);
+      // past the last tile the prefetches repeat it (valid rows, no branches)
+      load_k(min(t + 2, te - 1), kidx, kpre);
+      load_kidx(min(t + 3, te - 1), kidx);
     } else {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {   // g: (kb, ks half) = (g >> 1, g & 1)
@@ -918,8 +919,8 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
     for (; t < min(tfull, te - 1); ++t) {
       const int buf = (t - tb) & 1;
       dequant(kpre, vpre, buf ^ 1, false);
-      if (t + 2 < te) load_v(t + 2, vidx, vpre);
-      if (t + 3 < te) load_vidx(t + 3, vidx);
+      load_v(min(t + 2, te - 1), vidx, vpre);
+      load_vidx(min(t + 3, te - 1), vidx);
       compute(t, buf, std::false_type{}, std::true_type{});
       __syncthreads();
     }
@@ -930,11 +931,11 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
   } else {
     for (int t = tb; t < tfull; ++t) {
       const int buf = (t - tb) & 1;
-      if (t + 1 < te) {
-        dequant(kpre, vpre, buf ^ 1);
-        if (t + 2 < te) load_data(t + 2, kidx, vidx, kpre, vpre);
-        if (t + 3 < te) load_idx(t + 3, kidx, vidx);
-      }
+      // past the last tile the decode and the prefetches repeat it into the buffer
+      // nobody reads (valid rows, no branches)
+      dequant(kpre, vpre, buf ^ 1);
+      load_data(min(t + 2, te - 1), kidx, vidx, kpre, vpre);
+      load_idx(min(t + 3, te - 1), kidx, vidx);
       compute(t, buf, std::false_type{}, std::false_type{});
       __syncthreads();
     }
@@ -1280,7 +1281,6 @@ __global__ __launch_bounds__(NT, 1) void attend_mixed_cl_kernel(AttnParams p, Cl
   };
   auto load_data = [&](const Meta& mt, const int (&vi)[2], Pre& pr) {
     const int st = mt.st, blk = mt.blk;
-    const bool fresh = mt.fresh;
     const uint32_t key = (uint32_t)st + kk;
     typedef uint32_t u4 __attribute__((ext_vector_type(4)));
     pr.kcode = __builtin_amdgcn_raw_buffer_load_b32(rk_code, key * kwb + kword * 4, 0, 0);
@@ -1299,7 +1299,8 @@ __global__ __launch_bounds__(NT, 1) void attend_mixed_cl_kernel(AttnParams p, Cl
         pr.vc[j] = uint4{0u, 0u, 0u, 0u};
       }
     }
-    if (fresh) {   // the block's centroid rows, zero past C (the range check)
+    {   // the block's centroid rows, zero past C (the range check); staged every tile,
+        // used on a block's first (branch-free prefetch)
       const uint32_t row = (uint32_t)(CL_BLK * blk) + (tid >> 4);
       const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rk_cen, row * (DM * 2) + 16 * (tid & 15), 0, 0);
       pr.crow = uint4{a.x, a.y, a.z, a.w};
@@ -1307,7 +1308,6 @@ __global__ __launch_bounds__(NT, 1) void attend_mixed_cl_kernel(AttnParams p, Cl
   };
   auto dequant = [&](const Meta& mt, const Pre& pr, int buf) {
     const int blk = mt.blk;
-    const bool fresh = mt.fresh;
     // ---- K: coefficients (hi, lo) and the key's row in the wave's Q C^T table
     if (kw < 2) {
       const float sc = f16_bits_to_f32(pr.ksz & 0xFFFFu), ze = f16_bits_to_f32(pr.ksz >> 16);
@@ -1332,8 +1332,7 @@ __global__ __launch_bounds__(NT, 1) void attend_mixed_cl_kernel(AttnParams p, Cl
       const uint32_t o1 = (a == 2 ? 0x3F80u : 0u) | (a == 3 ? 0x3F800000u : 0u);
       *reinterpret_cast<uint2*>(&k_lds[buf][kk * KR + 32 + 4 * kw]) = make_uint2(o0, o1);
     }
-    if (fresh)
-      *reinterpret_cast<uint4*>(&c_lds[buf][(tid >> 4) * KROW + 8 * (tid & 15)]) = pr.crow;
+    *reinterpret_cast<uint4*>(&c_lds[buf][(tid >> 4) * KROW + 8 * (tid & 15)]) = pr.crow;
     // ---- V: channels 8c8..8c8+7 of keys 2kp, 2kp+1 -> transposed fp16 (swizzled)
     float x[2][8];
     float dq[2][8];
@@ -1573,31 +1572,31 @@ __global__ __launch_bounds__(NT, 1) void attend_mixed_cl_kernel(AttnParams p, Cl
     w1 = min(te, w0 + MWIN);
     for (int i = tid; i < w1 - w0; i += NT) m_lds[i] = tab[w0 + i];
     __syncthreads();
-    Meta m0 = meta(w0), m1 = m0, m2 = m0, m3 = m0;
-    if (w0 + 1 < w1) m1 = meta(w0 + 1);
-    if (w0 + 2 < w1) m2 = meta(w0 + 2);
-    if (w0 + 3 < w1) m3 = meta(w0 + 3);
+    // past the window's last tile the pipeline repeats that tile's loads and decode into
+    // the buffer nobody reads (valid rows, no branches in the loop)
+    const int wl = w1 - 1;
+    Meta m0 = meta(w0), m1 = meta(min(w0 + 1, wl)), m2 = meta(min(w0 + 2, wl)),
+         m3 = meta(min(w0 + 3, wl));
     load_vidx(m0, vidx);
     load_data(m0, vidx, pre);
-    if (w0 + 1 < w1) load_vidx(m1, vidx);
+    load_vidx(m1, vidx);
     dequant(m0, pre, 0);
-    if (w0 + 1 < w1) load_data(m1, vidx, pre);
-    if (w0 + 2 < w1) load_vidx(m2, vidx);
+    load_data(m1, vidx, pre);
+    load_vidx(m2, vidx);
     __syncthreads();
     for (int t = w0; t < w1; ++t) {
       const int buf = (t - w0) & 1;
-      const int2 r4 = m_lds[min(t + 4, w1 - 1) - w0];   // decoded at the end of the tile
-      if (t + 1 < w1) {
-        dequant(m1, pre, buf ^ 1);
-        if (t + 2 < w1) load_data(m2, vidx, pre);
-        if (t + 3 < w1) load_vidx(m3, vidx);
-      }
+      const int t4 = min(t + 4, wl);
+      const int2 r4 = m_lds[t4 - w0];   // decoded at the end of the tile
+      dequant(m1, pre, buf ^ 1);
+      load_data(m2, vidx, pre);
+      load_vidx(m3, vidx);
       compute(m0, buf);
       __syncthreads();
       m0 = m1;
       m1 = m2;
       m2 = m3;
-      if (t + 4 < w1) m3 = meta_of(r4, t + 4);
+      m3 = meta_of(r4, t4);
     }
   }
 
