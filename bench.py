@@ -646,10 +646,11 @@ def main() -> int:
     kb = kvc.BaseParams(centroids=dev_bf16(d["Ck"]))
     vb = kvc.BaseParams(centroids=dev_bf16(d["Cv"]))
     out = torch.empty((nq, H, D), dtype=torch.float32, device=dev)
-    # history before the timed chunk, encoded once
-    if lo:
-        kvc.kvc_encode(codec, K[:lo], ks, 0, kb)
-        kvc.kvc_encode(codec, V[:lo], vs, 0, vb)
+    # history before the timed chunk, encoded once, chunk by chunk as a cache fills
+    # (every encode launch of the run then has the timed launch's shape)
+    for c0 in range(0, lo, hi - lo):
+        c1 = min(lo, c0 + (hi - lo))
+        kvc.kvc_encode_kv(codec, K[c0:c1], V[c0:c1], ks, vs, c0, kb, vb)
     Kc, Vc = K[lo:hi].contiguous(), V[lo:hi].contiguous()
     att_ws = kvc.kvc.workspace_for(kvc.kvc.OP_ATTEND, codec, nk, dev, n_queries=nq)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]

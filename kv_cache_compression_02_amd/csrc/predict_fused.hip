@@ -5,15 +5,15 @@
 // * Temporal values (TempoKV arXiv 2610.15324, Fig. 2b): pred[h] = M_h aux_h + beta_h * in0_h.
 // * Temporal keys: pred = (a * in0) + (b * in1) per channel; anchors: pred = 0.
 //
-// rank_kernel forms t (fp32) for 64 tokens per workgroup, the contraction split over
-// four waves and the partial sums added in a fixed order, so every call with the same
-// inputs gives the same t.  pred_kernel keeps one head's W_h and U_h in LDS and walks
-// that head's 32-token tiles; in a wave, lane (t, hf) owns channels 64 hf .. 64 hf + 63 of
-// token t.  The MFMA rows of the weight operand are permuted (row 8q + 4hf + s of block
-// ob holds output channel 64 hf + 16 ob + 4 q + s) so that accumulator r of block ob is
-// channel 64 hf + 16 ob + r of the lane's own token: the prediction reaches the group
-// quantizer from registers.  The contraction index is permuted the same way on both
-// operands, so each lane also feeds only its own half rows.  t enters as bf16 high and
+// rank_kernel forms t (fp32), 16 tokens per wave, each element one MFMA accumulation
+// chain over the whole contraction in ascending order, so every call with the same
+// inputs gives the same t.  pred_kernel keeps one head's W_h (and U_h) in LDS and walks
+// that head's 16-token tiles; in a wave, lane (t, q) = (lane & 15, lane >> 4) owns
+// channels 32 q .. 32 q + 31 of token t.  The MFMA rows of the weight operand are
+// permuted (row 4 q + s of output block ob holds channel 32 q + 4 ob + s), so accumulator
+// s of block ob is a channel of the lane's own quarter row: the prediction reaches the
+// group quantizer from registers.  The contraction runs in natural channel order, lane q
+// feeding channels 32 ks + 8 q .. + 7 of k-step ks.  t enters as bf16 high and
 // low parts (about 2^-16 relative).  With no input to encode the same kernel only
 // writes the prediction, for the decoder: encoder and decoder see identical bases.
 #include "kvc_device.h"
@@ -41,9 +41,12 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 // t = v_lr [in0 ; in1] on v_mfma_f32_16x16x32_bf16.  A workgroup of eight waves takes
 // 128 tokens, each wave 16 of them over the whole contraction, so every t element is one
 // MFMA accumulation chain in ascending k and the same on every call.  v_lr is staged
-// through LDS in chunks of 128 columns shared by the eight waves (double-buffered: the
-// next chunk and the waves' next input fragments are in flight while the current chunk's
-// MFMAs run); every global load reads 64 contiguous bytes of 16 rows.
+// through LDS in chunks of 128 columns shared by the eight waves; every global load
+// reads 64 contiguous bytes of 16 rows.  The pass only streams its inputs, so it is
+// bound by how many bytes are in flight: each wave keeps the next three chunks of its
+// input fragments in registers (a ring of three), and the v_lr chunk for the LDS buffer
+// two chunks ahead is requested an iteration before it is stored.  Past the last chunk
+// the requests repeat it (valid addresses, no branches around the loads).
 constexpr int RK_KC = 128;              // contraction chunk
 constexpr int RK_ROW = RK_KC + 8;       // padded LDS row (bf16)
 constexpr int RK_TOK = 128;             // tokens per workgroup
@@ -56,24 +59,26 @@ __global__ __launch_bounds__(512) void rank_kernel(RankParams p) {
   const int col = lane & 15, q = lane >> 4;
   const int n = blockIdx.x * RK_TOK + wave * 16 + col;   // token of B-operand column col
   const bool tok = n < p.n;
-  const int64_t trow = (int64_t)(tok ? n : 0) * p.ps;
+  // Rows past the last token and v_lr rows past r are read from the last valid row: they
+  // only feed t columns and rows that are never stored, and every load stays unconditional
+  // (no divergent branch makes the compiler drain the loads in flight).
+  const int64_t trow = (int64_t)min(n, p.n - 1) * p.ps;
   const int K = p.nin * p.hd, nch = K / RK_KC;           // hd is a multiple of 128
-  const bf16x8_t zero = {0, 0, 0, 0, 0, 0, 0, 0};
-  auto load_stage = [&](int c, uint4 (&v)[PPT]) {
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int e = tid + 512 * i, row = e >> 4, pc = e & 15;
-      v[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (e < PIECES && row < p.r)
-        v[i] = *reinterpret_cast<const uint4*>(p.vlr + (int64_t)row * K + c * RK_KC + 8 * pc);
-    }
+  static_assert(PIECES % 512 == 0 && PPT <= 2, "whole chunk pieces per thread");
+  // a chunk's v_lr pieces of this thread on their way to LDS (one or two 16-byte pieces)
+  struct Stage { uint4 a, b; };
+  auto load_stage = [&](int c, Stage& v) {
+    auto piece = [&](int e) {
+      const int row = min(e >> 4, p.r - 1), pc = e & 15;
+      return *reinterpret_cast<const uint4*>(p.vlr + (int64_t)row * K + c * RK_KC + 8 * pc);
+    };
+    v.a = piece(tid);
+    if constexpr (PPT == 2) v.b = piece(tid + 512);
   };
-  auto store_stage = [&](int b, const uint4 (&v)[PPT]) {
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int e = tid + 512 * i, row = e >> 4, pc = e & 15;
-      if (e < PIECES) *reinterpret_cast<uint4*>(&vl[b][row * RK_ROW + 8 * pc]) = v[i];
-    }
+  auto store_stage = [&](int b, const Stage& v) {
+    *reinterpret_cast<uint4*>(&vl[b][(tid >> 4) * RK_ROW + 8 * (tid & 15)]) = v.a;
+    if constexpr (PPT == 2)
+      *reinterpret_cast<uint4*>(&vl[b][((tid + 512) >> 4) * RK_ROW + 8 * (tid & 15)]) = v.b;
   };
   auto load_b = [&](int c, bf16x8_t (&bx)[4]) {
     const int k0 = c * RK_KC;
@@ -81,43 +86,56 @@ __global__ __launch_bounds__(512) void rank_kernel(RankParams p) {
     const uint16_t* src = (j ? p.in1 : p.in0) + (k0 - j * p.hd) + trow + 8 * q;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      bx[ks] = tok ? *reinterpret_cast<const bf16x8_t*>(src + 32 * ks) : zero;
+      bx[ks] = *reinterpret_cast<const bf16x8_t*>(src + 32 * ks);
   };
   f32x4_t acc[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  bf16x8_t bcur[4];
-  {
-    uint4 v[PPT];
-    load_stage(0, v);
-    load_b(0, bcur);
-    store_stage(0, v);
-  }
+  // sa / sb: the v_lr chunk of even / odd index on its way to LDS; b0, b1, b2: the input
+  // fragments of chunk c with c % 3 == 0, 1, 2
+  Stage sa, sb;
+  bf16x8_t b0[4], b1[4], b2[4];
+  load_stage(0, sa);
+  load_stage(min(1, nch - 1), sb);
+  load_b(0, b0);
+  load_b(min(1, nch - 1), b1);
+  load_b(min(2, nch - 1), b2);
+  store_stage(0, sa);
   __syncthreads();
-#pragma unroll 1
-  for (int c = 0; c < nch; ++c) {
-    const int b = c & 1;
-    uint4 v[PPT];
-    bf16x8_t bnxt[4];
-    const bool more = c + 1 < nch;
-    if (more) {
-      load_stage(c + 1, v);
-      load_b(c + 1, bnxt);
-    }
+  // chunk c: LDS buffer lb = c & 1 holds it, sfree (same parity) is free, snext holds
+  // chunk c + 1, bcur holds its input fragments
+  auto step = [&](int c, int lb, Stage& sfree, Stage& snext,
+                  bf16x8_t (&bcur)[4]) __attribute__((always_inline)) {
+    load_stage(min(c + 2, nch - 1), sfree);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&vl[b][(16 * rb + col) * RK_ROW + 32 * ks + 8 * q]);
+        const bf16x8_t a =
+            *reinterpret_cast<const bf16x8_t*>(&vl[lb][(16 * rb + col) * RK_ROW + 32 * ks + 8 * q]);
         acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bcur[ks], acc[rb], 0, 0, 0);
       }
-    if (more) store_stage(b ^ 1, v);
+    load_b(min(c + 3, nch - 1), bcur);
+    store_stage(lb ^ 1, snext);
     __syncthreads();
-    if (more) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) bcur[ks] = bnxt[ks];
-    }
+  };
+  // six chunks per pass, so that both rings are indexed statically; the passes have no
+  // branches inside, the chunks of a last partial pass (nch % 6) follow
+  int c0 = 0;
+#pragma unroll 1
+  for (; c0 + 6 <= nch; c0 += 6) {
+    step(c0, 0, sa, sb, b0);
+    step(c0 + 1, 1, sb, sa, b1);
+    step(c0 + 2, 0, sa, sb, b2);
+    step(c0 + 3, 1, sb, sa, b0);
+    step(c0 + 4, 0, sa, sb, b1);
+    step(c0 + 5, 1, sb, sa, b2);
   }
+  if (c0 < nch) step(c0, 0, sa, sb, b0);
+  if (c0 + 1 < nch) step(c0 + 1, 1, sb, sa, b1);
+  if (c0 + 2 < nch) step(c0 + 2, 0, sa, sb, b2);
+  if (c0 + 3 < nch) step(c0 + 3, 1, sb, sa, b0);
+  if (c0 + 4 < nch) step(c0 + 4, 0, sa, sb, b1);
   // lane (col, q) holds t[n][16 rb + 4 q + i]: 64 contiguous bytes per token and block
   if (tok) {
     float* trow_out = p.t + (int64_t)n * p.r;
@@ -237,7 +255,7 @@ __global__ __launch_bounds__(512) void pred_kernel(PredParams p) {
   const int ct = lane >> 4, cc = lane & 15;
   // matrix modes: workgroup = (head, segment) with the head's weights in LDS, its waves
   // walking that head's tiles; other modes walk the flattened (head, tile) list
-  const int hw = MAT ? blockIdx.x / p.segs : 0, seg = blockIdx.x % p.segs;
+  const int hw = MAT ? blockIdx.x / p.segs : 0, seg = MAT ? blockIdx.x % p.segs : (int)blockIdx.x;
   uint16_t* wl = lds;                                   // [128][WROW], permuted rows
   uint16_t* ul = lds + (MAT ? w_elems(NIN) : 0);        // [128][URW]
   uint16_t* stg = lds + (MAT ? w_elems(NIN) : 0) + (LR ? 128 * URW : 0) + wave * STG;
@@ -325,7 +343,7 @@ __global__ __launch_bounds__(512) void pred_kernel(PredParams p) {
   };
 
   TileIn cur;
-  const int first = (MAT ? seg : (int)blockIdx.x) * 8 + wave;
+  const int first = seg * 8 + wave;
   load_tile(first, cur);
 #pragma unroll 1
   for (int item = first; item < items; item += istride) {

@@ -141,3 +141,31 @@ def test_fit_does_not_depend_on_the_codec_rotation():
     kvc.kvc_fit_centroids(kvc.Codec(3, 128, 2, 64, kvc.BASE_CENTROID, 40, rotation=64), x, Cb, 2)
     torch.cuda.synchronize()
     assert np.array_equal(_bits(Ca), _bits(Cb))
+
+
+@pytest.mark.parametrize("iterations", [3, 6])
+def test_fit_free_running_against_the_oracle(iterations):
+    """Several iterations in one call against the oracle's own free-running fit from the
+    same table (600 tokens, 3 heads, 40 centroids).  The two trajectories may part where
+    a 1-ulp difference moves a token across a boundary, so the bar is on what the fit is
+    for: the objective (sum of squared distances to the nearest centroid, fp64) of the
+    GPU table within 0.1% of the oracle table's, no higher than the starting table's, and
+    at least 95% of the fitted values within one bf16 ulp of the oracle's."""
+    dev = device()
+    d = synth.cfg1(seed=35, hist_frames=6, query_frames=1, tokens=100, heads=3, dim=128,
+                   n_centroids=40)
+    xb = d["K"]
+    x32 = nm.bf16_to_f32(xb)
+    C0 = _init(xb, 40, 13)
+    C = to_dev(C0, dev)
+    codec = kvc.Codec(3, 128, 2, 32, kvc.BASE_CENTROID, 40)
+    print(f"free-running fit, {iterations} iterations", flush=True)
+    kvc.kvc_fit_centroids(codec, to_dev(xb, dev), C, iterations)
+    torch.cuda.synchronize()
+    got = nm.bf16_to_f32(_bits(C))
+    want = ofit.fit(x32, nm.bf16_to_f32(C0), iterations)
+    f_got, f_want = ofit.objective(x32, got), ofit.objective(x32, want)
+    assert f_got <= ofit.objective(x32, nm.bf16_to_f32(C0))
+    assert abs(f_got - f_want) <= 1e-3 * f_want, (f_got, f_want)
+    ulp = np.spacing(np.abs(want).astype(np.float32)) * 65536.0
+    assert np.mean(np.abs(got - want) <= ulp + 1e-38) >= 0.95
