@@ -306,8 +306,8 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
   const int kk = tid >> 3, kw = tid & 7;          // K: key kk, channels 16kw..16kw+15
   const int c8 = tid & 15, kp = tid >> 4;         // V: keys 2kp, 2kp+1, channels 8c8..8c8+7
   // first code word of the thread's 16 channels (MIXED: of coefficients 8kw..8kw+7)
-  const int kword = MIXED ? (8 * min(kw, 1) * BITS) >> 5 : (16 * kw * BITS) >> 5;
-  const int kcsh = MIXED ? (8 * min(kw, 1) * BITS) & 31 : 0;
+  const int kword = MIXED ? (2 * kw * BITS) >> 5 : (16 * kw * BITS) >> 5;
+  const int kcsh = MIXED ? (2 * kw * BITS) & 31 : 0;
   const int kgrp = MIXED ? 0 : (16 * kw) / p.k.group;   // coefficients: one group per key
   const int vword = (8 * c8 * VBITS) >> 5;
   const int vgrp = (8 * c8) / p.v.group;
@@ -474,24 +474,19 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
       return;
     }
     if constexpr (MIXED) {
-      // ---- K: centroid row chunk as is; lanes kw < 2 add 8 coefficients (hi, lo)
+      // ---- K: centroid row chunk as is; lane kw adds coefficients 2 kw, 2 kw + 1 (hi, lo)
       uint4* dst = reinterpret_cast<uint4*>(&k_lds[buf][kk * KR + 16 * kw]);
       dst[0] = kpr.c0;
       dst[1] = kpr.c1;
-      if (kw < 2) {
+      {
         const float sc = f16_bits_to_f32(kpr.sz & 0xFFFFu), ze = f16_bits_to_f32(kpr.sz >> 16);
         const uint32_t w = kpr.code[0] >> kcsh;
-        float cv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) cv[i] = __builtin_fmaf((float)((w >> (BITS * i)) & ((1u << BITS) - 1u)), sc, ze);
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          hi[i] = pk_bf16(cv[2 * i], cv[2 * i + 1]);
-          lo[i] = pk_bf16(cv[2 * i] - lo_bf16(hi[i]), cv[2 * i + 1] - hi_bf16(hi[i]));
-        }
-        *reinterpret_cast<uint4*>(&k_lds[buf][kk * KR + DM + 8 * kw]) = uint4{hi[0], hi[1], hi[2], hi[3]};
-        *reinterpret_cast<uint4*>(&k_lds[buf][kk * KR + DM + 16 + 8 * kw]) = uint4{lo[0], lo[1], lo[2], lo[3]};
+        const float c0 = __builtin_fmaf((float)(w & ((1u << BITS) - 1u)), sc, ze);
+        const float c1 = __builtin_fmaf((float)((w >> BITS) & ((1u << BITS) - 1u)), sc, ze);
+        const uint32_t hi = pk_bf16(c0, c1);
+        const uint32_t lo = pk_bf16(c0 - lo_bf16(hi), c1 - hi_bf16(hi));
+        *reinterpret_cast<uint32_t*>(&k_lds[buf][kk * KR + DM + 2 * kw]) = hi;
+        *reinterpret_cast<uint32_t*>(&k_lds[buf][kk * KR + DM + 16 + 2 * kw]) = lo;
       }
     } else {
     // ---- K: 16 consecutive channels of key kk -> row-major bf16
@@ -1243,12 +1238,12 @@ __global__ __launch_bounds__(NT, 1) void attend_mixed_cl_kernel(AttnParams p, Cl
   const auto rv_cen = rsrc(reinterpret_cast<const uint16_t*>(p.v.cen) + (int64_t)h * p.v.C * DM,
                            VCEN ? (int64_t)p.v.C * DM * 2 : 0);
 
-  // roles: 8 lanes per K row (lanes kw < 2 decode 8 coefficients each, kw == 0 also the
-  // table offset), 16 lanes per V row pair (8 channels each), 16 lanes per centroid row
+  // roles: 8 lanes per K row (2 coefficients and 4 one-hot columns each), 16 lanes per V
+  // row pair (8 channels each), 16 lanes per centroid row
   const int kk = tid >> 3, kw = tid & 7;
   const int c8 = tid & 15, kp = tid >> 4;
-  const int kword = (8 * min(kw, 1) * KBITS) >> 5;
-  const int kcsh = (8 * min(kw, 1) * KBITS) & 31;
+  const int kword = (2 * kw * KBITS) >> 5;
+  const int kcsh = (2 * kw * KBITS) & 31;
   const int vword = (8 * c8 * VBITS) >> 5;
   const int vgrp = (8 * c8) / p.v.group;
   const int vsh = (8 * c8 * VBITS) & 31;
@@ -1316,22 +1311,17 @@ __global__ __launch_bounds__(NT, 1) void attend_mixed_cl_kernel(AttnParams p, Cl
   };
   auto dequant = [&](const Meta& mt, const Pre& pr, int buf) {
     const int blk = mt.blk;
-    // ---- K: coefficients (hi, lo) and the key's row in the wave's Q C^T table
-    if (kw < 2) {
+    // ---- K: coefficients 2 kw, 2 kw + 1 (hi, lo) and the key's row in the wave's Q C^T
+    //      table
+    {
       const float sc = f16_bits_to_f32(pr.ksz & 0xFFFFu), ze = f16_bits_to_f32(pr.ksz >> 16);
       const uint32_t w = pr.kcode >> kcsh;
-      float cv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        cv[i] = __builtin_fmaf((float)((w >> (KBITS * i)) & ((1u << KBITS) - 1u)), sc, ze);
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        hi[i] = pk_bf16(cv[2 * i], cv[2 * i + 1]);
-        lo[i] = pk_bf16(cv[2 * i] - lo_bf16(hi[i]), cv[2 * i + 1] - hi_bf16(hi[i]));
-      }
-      *reinterpret_cast<uint4*>(&k_lds[buf][kk * KR + 8 * kw]) = uint4{hi[0], hi[1], hi[2], hi[3]};
-      *reinterpret_cast<uint4*>(&k_lds[buf][kk * KR + 16 + 8 * kw]) = uint4{lo[0], lo[1], lo[2], lo[3]};
+      const float c0 = __builtin_fmaf((float)(w & ((1u << KBITS) - 1u)), sc, ze);
+      const float c1 = __builtin_fmaf((float)((w >> KBITS) & ((1u << KBITS) - 1u)), sc, ze);
+      const uint32_t hi = pk_bf16(c0, c1);
+      const uint32_t lo = pk_bf16(c0 - lo_bf16(hi), c1 - hi_bf16(hi));
+      *reinterpret_cast<uint32_t*>(&k_lds[buf][kk * KR + 2 * kw]) = hi;
+      *reinterpret_cast<uint32_t*>(&k_lds[buf][kk * KR + 16 + 2 * kw]) = lo;
     }
     {   // one-hot row: centroids 4kw..4kw+3 of the block (keys of the next block, which
         // are masked, get a row inside the block)
