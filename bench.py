@@ -263,7 +263,9 @@ def bench_dplr(args, torch, kvc, synth, dev):
                                   "x 128, 32760 tokens, rank 64, INT2 g32 (INT4 g32 layer 0)",
                                   "layers": layers, "tokens": n, "heads": H, "rank": r},
                  {"bound": "hbm", "achieved": v_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                  "frac": v_gbs / HBM_PEAK_GBS, "traffic": None,
+                  "frac": v_gbs / HBM_PEAK_GBS,
+                  "traffic": recorded_traffic("pred_kernel_dplr_chain_30x12x128_32760tok.md",
+                                              "kv_cache_compression_02_amd/csrc/predict_fused.hip"),
                   "kernel": "value encode call (rank_kernel + pred_kernel)", "ms": t_v * 1e3},
                  chain_ms=t_ev * 1e3, chain_frac_hbm=gbs / HBM_PEAK_GBS,
                  predictor_tflops=flops / t_ev / 1e12, algorithmic_bytes=alg, flops=flops)
@@ -473,9 +475,10 @@ def bench_mixed(args, torch, kvc, synth, dev):
                           "heads": H, "keys": nk, "queries": nq, "centroids": C, "coeff_dim": m},
                  {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                   "frac": achieved / BF16_PEAK_TFLOPS,
-                  "traffic": recorded_traffic("attend_bf16_kernel_mixed_12x128_4680q_65520k.md",
+                  "traffic": recorded_traffic("attend_mixed_cl_kernel_mixed_12x128_4680q_65520k.md",
                                               "kv_cache_compression_02_amd/csrc/attend.hip"),
-                  "kernel": "attend_bf16_kernel (mixed)", "ms": t_ev * 1e3},
+                  "kernel": "attend_mixed_cl_kernel (+ the centroid-block sort of the history: "
+                            "one kvc_attend_mixed_dim call)", "ms": t_ev * 1e3},
                  full_attention_equivalent_tflops=attention_flops(nq, nk, D, H) / t_ev / 1e12,
                  encode={"keys_ms": t_k * 1e3, "values_ms": t_v * 1e3, "bytes": enc_k + enc_v,
                          "GB/s": (enc_k + enc_v) / (t_k + t_v) / 1e9,
