@@ -391,6 +391,8 @@ def bench_chunk(args, torch, kvc, synth, dev, jensen: bool = False):
     vb = kvc.BaseParams(centroids=b16(d["Cv"]))
     kvc.kvc_encode(codec, b16(d["K"][:lo]), ks, 0, kb)
     kvc.kvc_encode(codec, b16(d["V"][:lo]), vs, 0, vb)
+    kb.centroid_tables = kvc.kvc_centroid_tables(codec, kb.centroids)   # fp16 images (or None)
+    vb.centroid_tables = kvc.kvc_centroid_tables(codec, vb.centroids)
     Kc, Vc, Q = b16(d["K"][lo:hi]), b16(d["V"][lo:hi]), b16(d["Q"])
     out = torch.empty((nq, H, D), dtype=torch.float32, device=dev)
     ws = kvc.kvc.workspace_for(kvc.kvc.OP_ATTEND_CHUNK, codec, lo, dev, n_queries=nq)
@@ -656,13 +658,19 @@ def main() -> int:
         kvc.kvc_encode_kv(codec, K[c0:c1], V[c0:c1], ks, vs, c0, kb, vb)
     Kc, Vc = K[lo:hi].contiguous(), V[lo:hi].contiguous()
     att_ws = kvc.kvc.workspace_for(kvc.kvc.OP_ATTEND, codec, nk, dev, n_queries=nq)
+    # fp16 images of the centroid tables for the tile decode, made once per table like the
+    # tables themselves (None where a table has no exact image: the bf16 table is used)
+    ka = kvc.BaseParams(centroids=kb.centroids,
+                        centroid_tables=kvc.kvc_centroid_tables(codec, kb.centroids))
+    va = kvc.BaseParams(centroids=vb.centroids,
+                        centroid_tables=kvc.kvc_centroid_tables(codec, vb.centroids))
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
 
     def step(e=None):
         if e: e[0].record()
         kvc.kvc_encode_kv(codec, Kc, Vc, ks, vs, lo, kb, vb)   # the chunk's K and V, one launch
         if e: e[1].record()
-        kvc.kvc_attend_compressed(codec, ks, kb, codec, vs, vb, nk, Q, d["scale"], out=out,
+        kvc.kvc_attend_compressed(codec, ks, ka, codec, vs, va, nk, Q, d["scale"], out=out,
                                   workspace=att_ws)
         if e: e[2].record()
 
@@ -698,7 +706,9 @@ def main() -> int:
         "config": {"workload": "centroid+INT2 g32 codec, 12 heads x 128, 256 centroids/head; "
                                "encode 4680-token chunk (K,V) + attention 4680 q x 32760 keys",
                    "heads": H, "head_dim": D, "history_tokens": nk, "queries": nq,
-                   "chunk_tokens": hi - lo, "bits": bits, "group": group, "centroids": C},
+                   "chunk_tokens": hi - lo, "bits": bits, "group": group, "centroids": C,
+                   "centroid_tables": "fp16 images" if ka.centroid_tables is not None
+                                      and va.centroid_tables is not None else "bf16"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
                      "traffic": recorded_traffic("attend_bf16_kernel_centroid_int2_12x128_4680q_32760k.md",

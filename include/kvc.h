@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 3
+#define KVC_ABI_VERSION 4
 
 typedef enum {
   KVC_OK = 0,
@@ -142,7 +142,11 @@ typedef struct {
  *   (0 = H*d; a multiple of 8, else KVC_E_ALIGN: the inputs are read in 16-byte pieces).
  * Matrix-product bases (DPLR, temporal values) compute an fp32 prediction first: it
  * goes to pred_out when given, else to the workspace; DPLR always needs the workspace
- * (kvc_workspace_bytes) for its rank-r intermediate. */
+ * (kvc_workspace_bytes) for its rank-r intermediate.
+ *   centroid_tables: optional, attention only (NULL elsewhere is fine, and ignored by
+ *   every other call): the buffer a successful kvc_centroid_tables call filled from
+ *   these same centroids.  The bf16 decode-fused attention then adds the centroid rows
+ *   from that fp16 image (identical results, fewer instructions per decoded value). */
 typedef struct {
   const void* centroids;
   const void* basis;
@@ -155,6 +159,7 @@ typedef struct {
   const float* coef_a;
   const float* coef_b;
   int64_t prev_token_stride;
+  const void* centroid_tables;
 } kvc_base_params;
 
 /* Device bytes a store of `capacity` tokens needs (host-side helper). */
@@ -275,6 +280,28 @@ kvc_status kvc_decode(const kvc_codec* codec, const kvc_store* src, int64_t toke
  *   query term rounded to bf16).  Needs the bf16 path with centroid K and V. */
 enum { KVC_ATTEND_JENSEN = 1 };
 
+/* kvc_centroid_tables - the fp16 image of a bf16 centroid table [H][C][d] that the
+ * decode-fused attention reads in place of the table (kvc_base_params.centroid_tables).
+ * The tile decode adds a key's centroid row to its dequantized residual in fp32; from a
+ * bf16 table that takes an unpack and an add per value, from fp16 one mixed-precision
+ * FMA, c16 * 2^-k + r with a single rounding, i.e. exactly the fp32 sum c + r.  Each
+ * head h gets the power of two 2^k_h that brings its largest |c| closest below 65504,
+ * and every c * 2^k_h must be an fp16 value exactly; then attention with the image
+ * returns bit for bit what it returns with the bf16 table.
+ *   codec: KVC_BASE_CENTROID or KVC_BASE_COEFF, bf16, d = 128 (the layout is that of
+ *     the bf16 attention path; other codecs: KVC_E_UNSUPPORTED).
+ *   centroids: [H][C][d] bf16 (C = codec->n_centroids).
+ *   tables: device buffer of kvc_centroid_tables_bytes(codec) bytes, 16-byte aligned:
+ *     [H] int32 k_h, [H] int32 exact flags, padding to 256 bytes, then [H][C][d] fp16.
+ *   Synchronous: the call waits for `stream` to read the per-head checks back.
+ * Returns KVC_OK when every head's image is exact; KVC_E_UNSUPPORTED when some entry is
+ * not a finite value that fits (a table whose nonzero magnitudes span more than fp16's
+ * range, about 2^30); the buffer must then not be passed to attention.  Errors:
+ * KVC_E_NULL, KVC_E_SHAPE (tables_bytes too small), KVC_E_ALIGN, KVC_E_DEVICE. */
+size_t kvc_centroid_tables_bytes(const kvc_codec* codec);
+kvc_status kvc_centroid_tables(const kvc_codec* codec, const void* centroids, void* tables,
+                               size_t tables_bytes, void* stream);
+
 /* kvc_attend_compressed - O = softmax(Q K^T * softmax_scale) V per head, no mask,
  * over n_keys keys held compressed in stores k and v (rows 0..n_keys-1); K and V
  * tiles are decoded on the fly (NanoKV abstract: repeated attention over the
@@ -302,6 +329,9 @@ enum { KVC_ATTEND_JENSEN = 1 };
  *     decoded tile rotates its dequantized residuals back before the centroid is added,
  *     with the decoder's arithmetic, so the tiles hold exactly what kvc_decode returns
  *     (rounded to bf16).  K and V must then both use KVC_BASE_CENTROID.
+ *   kp->centroid_tables and vp->centroid_tables (both given, centroid K and V, not
+ *     rotated, no flags): the tile decode reads the fp16 images (kvc_centroid_tables);
+ *     same results.  Otherwise they are ignored.
  * Errors: KVC_E_NULL, KVC_E_SHAPE (n_keys > capacity, n_keys < 1, mismatched
  * heads/d, softmax_scale not finite and positive; bf16 path: a store whose per-head
  * code or scale/zero rows span 2 GiB or more, or a dense cache of 2 GiB or more - the

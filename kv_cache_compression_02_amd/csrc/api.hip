@@ -10,6 +10,8 @@
 #include "kvc.h"
 #include "kvc_internal.h"
 
+#include <vector>
+
 using namespace kvc;
 
 namespace {
@@ -121,6 +123,7 @@ kvc_status resolve_base(const kvc_base_params* b, const CodecArgs& c, BaseArgs* 
   a.v_lr = b->v_lr;
   a.coef_a = b->coef_a;
   a.coef_b = b->coef_b;
+  a.centroid_tables = b->centroid_tables;
   a.prev_stride = b->prev_token_stride ? b->prev_token_stride : (int64_t)c.H * c.D;
   if (a.prev_stride < (int64_t)c.H * c.D) return KVC_E_SHAPE;
   switch (c.base) {
@@ -373,6 +376,39 @@ kvc_status kvc_fit_centroids(const kvc_codec* codec, const void* x, int64_t n_to
   return from_hip(launch_fit(a, iterations, reinterpret_cast<hipStream_t>(stream)));
 }
 
+size_t kvc_centroid_tables_bytes(const kvc_codec* codec) {
+  CodecArgs c;
+  if (resolve_codec(codec, &c) != KVC_OK) return 0;
+  if ((c.base != KVC_BASE_CENTROID && c.base != KVC_BASE_COEFF) || c.x_dtype != KVC_BF16 ||
+      c.D != 128)
+    return 0;
+  return centroid_tables_header_bytes(c.H) + (size_t)c.H * c.C * c.D * 2;
+}
+
+kvc_status kvc_centroid_tables(const kvc_codec* codec, const void* centroids, void* tables,
+                               size_t tables_bytes, void* stream) {
+  CodecArgs c;
+  kvc_status st = resolve_codec(codec, &c);
+  if (st != KVC_OK) return st;
+  if ((c.base != KVC_BASE_CENTROID && c.base != KVC_BASE_COEFF) || c.x_dtype != KVC_BF16 ||
+      c.D != 128)
+    return KVC_E_UNSUPPORTED;
+  if (!centroids || !tables) return KVC_E_NULL;
+  if (!aligned16(centroids) || !aligned16(tables)) return KVC_E_ALIGN;
+  if (tables_bytes < kvc_centroid_tables_bytes(codec)) return KVC_E_SHAPE;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_centroid_tables(centroids, c.H, c.C, c.D, tables, s);
+  if (e != hipSuccess) return KVC_E_DEVICE;
+  std::vector<int32_t> exact((size_t)c.H);
+  e = hipMemcpyAsync(exact.data(), reinterpret_cast<const int32_t*>(tables) + c.H,
+                     sizeof(int32_t) * c.H, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return KVC_E_DEVICE;
+  for (int32_t v : exact)
+    if (v != 1) return KVC_E_UNSUPPORTED;
+  return KVC_OK;
+}
+
 kvc_status kvc_decode(const kvc_codec* codec, const kvc_store* src, int64_t token_offset,
                       int64_t n_tokens, const kvc_base_params* base, void* out, int32_t out_dtype,
                       float* pred_out, void* workspace, size_t workspace_bytes, void* stream) {
@@ -433,6 +469,9 @@ static kvc_status check_attend(const kvc_codec* kc, const kvc_store* k, const kv
   if (st != KVC_OK) return st;
   st = resolve_base(vp, a->vc, &a->vb, false);
   if (st != KVC_OK) return st;
+  if ((a->kb.centroid_tables && !aligned16(a->kb.centroid_tables)) ||
+      (a->vb.centroid_tables && !aligned16(a->vb.centroid_tables)))
+    return KVC_E_ALIGN;
   a->n_keys = n_keys;
   a->n_queries = n_queries;
   a->q = q;

@@ -38,6 +38,8 @@ struct Src {
   const uint32_t* sz;
   const void* index;
   const void* cen;     // [H][C][D] cache dtype
+  const uint16_t* cen16;   // fp16 image of cen (c * 2^cexp[h]), or null
+  const int32_t* cexp;     // [H] per-head exponents of cen16
   int64_t cap;
   int bits, group, groups, words, idxb, C, mode;
   int rot;             // Hn residual transform width: 0, 16 or 64
@@ -117,6 +119,18 @@ constexpr int VROW = BK + 16;    // V^T tile row (fp16 elements), padded to 40 d
 
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+// c + d for c the fp16 value in the low / high half of w scaled by sc (a power of two):
+// one v_fma_mix_f32, c * sc + d with a single rounding, i.e. exactly fl(c * sc + d)
+__device__ __forceinline__ float add_f16lo(uint32_t w, float sc, float d) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(sc), "v"(d));
+  return r;
+}
+__device__ __forceinline__ float add_f16hi(uint32_t w, float sc, float d) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(sc), "v"(d));
+  return r;
+}
 __device__ __forceinline__ float byte_f(uint32_t x, int k) { return (float)((x >> (8 * k)) & 0xFFu); }
 // A code held in a 16-bit half of w, read as the f16 denormal q * 2^-24.  v_fma_mix_f32
 // widens it exactly, so fma(code_lo(w), s * 2^24, z) == fma(q, s, z) bit for bit (s an
@@ -250,7 +264,7 @@ __device__ __forceinline__ void hn_back(float (&v)[W], int piece, int n) {
 // every lane holds -(scale / 24) ||q_g||^2 of its query as a B operand (k = g), so one
 // more v_mfma_f32_32x32x16_bf16 per 32-key block adds the correction to the raw scores.
 template <int BITS, int VBITS, bool KCEN, bool VCEN, bool MIXED, bool DENSE = false, bool ROT = false,
-          bool JB = false>
+          bool JB = false, bool CF16 = false>
 __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
   constexpr int KR = MIXED ? DM + 32 + 8 : (JB ? DM + 16 + 8 : KROW);   // K tile row (bf16 elements)
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BK * KR];     // bf16
@@ -291,10 +305,23 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
                            KCEN ? nkr * p.k.idxb : 0);
   const auto rv_idx = rsrc(reinterpret_cast<const uint8_t*>(p.v.index) + vhrow * p.v.idxb,
                            VCEN ? nkr * p.v.idxb : 0);
-  const auto rk_cen = rsrc(reinterpret_cast<const uint16_t*>(p.k.cen) + (int64_t)h * p.k.C * DM,
-                           KCEN ? (int64_t)p.k.C * DM * 2 : 0);
-  const auto rv_cen = rsrc(reinterpret_cast<const uint16_t*>(p.v.cen) + (int64_t)h * p.v.C * DM,
-                           VCEN ? (int64_t)p.v.C * DM * 2 : 0);
+  // CF16: the tables' fp16 images (c * 2^e_h, same layout and size) and the per-head
+  // powers of two 2^-e_h that restore c inside the centroid add
+  const uint16_t* kcen = CF16 ? p.k.cen16 : reinterpret_cast<const uint16_t*>(p.k.cen);
+  const uint16_t* vcen = CF16 ? p.v.cen16 : reinterpret_cast<const uint16_t*>(p.v.cen);
+  const auto rk_cen = rsrc(kcen + (int64_t)h * p.k.C * DM, KCEN ? (int64_t)p.k.C * DM * 2 : 0);
+  const auto rv_cen = rsrc(vcen + (int64_t)h * p.v.C * DM, VCEN ? (int64_t)p.v.C * DM * 2 : 0);
+  const float ksc = CF16 ? __int_as_float((127 - p.k.cexp[h]) << 23) : 1.0f;
+  const float vsc = CF16 ? __int_as_float((127 - p.v.cexp[h]) << 23) : 1.0f;
+  // centroid + dequantized residual (fp32, one rounding), channel pair in word w
+  auto cadd_lo = [&](uint32_t w, float sc, float d) {
+    if constexpr (CF16) return add_f16lo(w, sc, d);
+    else return lo_bf16(w) + d;
+  };
+  auto cadd_hi = [&](uint32_t w, float sc, float d) {
+    if constexpr (CF16) return add_f16hi(w, sc, d);
+    else return hi_bf16(w) + d;
+  };
 
   // DENSE: one resource over the whole token-major cache, rows H*d apart
   const int hdb = p.H * DM * 2;
@@ -522,8 +549,8 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
       uint32_t o[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float x0 = lo_bf16(cw[i]) + dq[2 * i];
-        const float x1 = hi_bf16(cw[i]) + dq[2 * i + 1];
+        const float x0 = cadd_lo(cw[i], ksc, dq[2 * i]);
+        const float x1 = cadd_hi(cw[i], ksc, dq[2 * i + 1]);
         o[i] = pk_bf16(x0, x1);
       }
       uint4* dst = reinterpret_cast<uint4*>(&k_lds[buf][kk * KR + 16 * kw]);
@@ -577,8 +604,8 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
         const uint32_t cw[4] = {vp.c[j].x, vp.c[j].y, vp.c[j].z, vp.c[j].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          x[j][2 * i] = lo_bf16(cw[i]) + dq[j][2 * i];
-          x[j][2 * i + 1] = hi_bf16(cw[i]) + dq[j][2 * i + 1];
+          x[j][2 * i] = cadd_lo(cw[i], vsc, dq[j][2 * i]);
+          x[j][2 * i + 1] = cadd_hi(cw[i], vsc, dq[j][2 * i + 1]);
         }
       }
 #pragma unroll
@@ -726,7 +753,7 @@ __global__ __launch_bounds__(NT, 1) void attend_bf16_kernel(AttnParams p) {
       const int i = j - 8;
       const uint32_t cwi = (i < 4) ? (i == 0 ? kpr.c0.x : i == 1 ? kpr.c0.y : i == 2 ? kpr.c0.z : kpr.c0.w)
                                    : (i == 4 ? kpr.c1.x : i == 5 ? kpr.c1.y : i == 6 ? kpr.c1.z : kpr.c1.w);
-      st.o[i] = pk_bf16(lo_bf16(cwi) + st.dq[2 * i], hi_bf16(cwi) + st.dq[2 * i + 1]);
+      st.o[i] = pk_bf16(cadd_lo(cwi, ksc, st.dq[2 * i]), cadd_hi(cwi, ksc, st.dq[2 * i + 1]));
       if (j == 15) {
         uint4* dst = reinterpret_cast<uint4*>(&k_lds[dbuf][kk * KR + 16 * kw]);
         dst[0] = uint4{st.o[0], st.o[1], st.o[2], st.o[3]};
@@ -1708,7 +1735,64 @@ Src make_src(const CodecArgs& c, const StoreArgs& st, const BaseArgs& b) {
   s.C = c.C;
   s.mode = (c.base == KVC_BASE_CENTROID || c.base == KVC_BASE_COEFF) ? SRC_CENTROID : SRC_NONE;
   s.rot = c.rot;
+  if (b.centroid_tables && s.mode == SRC_CENTROID && c.x_dtype == KVC_BF16) {
+    s.cexp = reinterpret_cast<const int32_t*>(b.centroid_tables);
+    s.cen16 = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(b.centroid_tables) +
+                                                centroid_tables_header_bytes(c.H));
+  }
   return s;
+}
+
+// fp16 image of a bf16 centroid table, one workgroup per head: the head's largest |c|
+// picks the power of two 2^k that brings it closest below 65504, every c * 2^k is
+// rounded to fp16 and checked for exactness (non-finite entries fail the check).  The
+// header holds k per head, then 1 / 0 per head for exact / not.
+constexpr int CT_THREADS = 256;
+__global__ __launch_bounds__(CT_THREADS) void centroid_tables_kernel(const uint16_t* cen, int H,
+                                                                      int n, int32_t* hdr,
+                                                                      uint16_t* out) {
+  __shared__ float red[CT_THREADS / 64];
+  __shared__ int okw[CT_THREADS / 64];
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint16_t* src = cen + (int64_t)h * n;
+  uint16_t* dst = out + (int64_t)h * n;
+  float m = 0.0f;
+  int ok = 1;
+  for (int i = tid; i < n; i += CT_THREADS) {
+    const float c = __uint_as_float((uint32_t)src[i] << 16);
+    if (!(fabsf(c) <= 3.0e38f)) ok = 0;   // inf / nan
+    m = fmaxf(m, fabsf(c));
+  }
+#pragma unroll
+  for (int o = 32; o; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  m = red[0];
+#pragma unroll
+  for (int w = 1; w < CT_THREADS / 64; ++w) m = fmaxf(m, red[w]);
+  int k = 0;
+  if (m > 0.0f && m <= 3.0e38f) {
+    int e;
+    const float f = frexpf(m, &e);            // m = f 2^e, f in [0.5, 1)
+    k = (f * 65536.0f <= 65504.0f) ? 16 - e : 15 - e;
+    k = max(-100, min(100, k));
+  }
+  const float sc = __int_as_float((127 + k) << 23);
+  for (int i = tid; i < n; i += CT_THREADS) {
+    const float y = __uint_as_float((uint32_t)src[i] << 16) * sc;   // exact: a power of two
+    const _Float16 hv = (_Float16)y;
+    if (!((float)hv == y)) ok = 0;
+    dst[i] = __builtin_bit_cast(uint16_t, hv);
+  }
+  ok = __all(ok) ? 1 : 0;
+  if (lane == 0) okw[wave] = ok;
+  __syncthreads();
+  if (tid == 0) {
+    int all = 1;
+    for (int w = 0; w < CT_THREADS / 64; ++w) all &= okw[w];
+    hdr[h] = k;
+    hdr[H + h] = all;
+  }
 }
 
 // Key splits of the bf16 path.  One workgroup fills a CU (its registers), so a launch of
@@ -1779,6 +1863,17 @@ hipError_t launch_compressed_bf16(const AttnParams& p, int kbits, int vbits, dim
 #undef KVC_ATT_RJ
     return hipErrorInvalidValue;
   }
+  if (kc && vc && p.k.cen16 && p.v.cen16) {   // both tables' fp16 images given
+#define KVC_ATT16(KB_, VB_)                                                                       \
+    if (kbits == KB_ && vbits == VB_) {                                                           \
+      hipLaunchKernelGGL((attend_bf16_kernel<KB_, VB_, true, true, false, false, false, false, true>), \
+                         grid, block, 0, s, p);                                                   \
+      return hipGetLastError();                                                                   \
+    }
+    KVC_ATT16(2, 2) KVC_ATT16(2, 4) KVC_ATT16(4, 2) KVC_ATT16(4, 4)
+#undef KVC_ATT16
+    return hipErrorInvalidValue;
+  }
 #define KVC_ATT(KB_, VB_, KC_, VC_)                                                       \
   if (kbits == KB_ && vbits == VB_ && kc == KC_ && vc == VC_) {                         \
     hipLaunchKernelGGL((attend_bf16_kernel<KB_, VB_, KC_, VC_, false>), grid, block, 0, s, p); \
@@ -1805,6 +1900,18 @@ int chunk_history_splits(int H, int64_t nq, int64_t nk) {
 }
 
 }  // namespace
+
+size_t centroid_tables_header_bytes(int H) { return ((size_t)8 * H + 255) / 256 * 256; }
+
+hipError_t launch_centroid_tables(const void* centroids, int H, int C, int D, void* tables,
+                                  hipStream_t s) {
+  int32_t* hdr = reinterpret_cast<int32_t*>(tables);
+  uint16_t* out = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(tables) +
+                                              centroid_tables_header_bytes(H));
+  hipLaunchKernelGGL(centroid_tables_kernel, dim3((unsigned)H), dim3(CT_THREADS), 0, s,
+                     reinterpret_cast<const uint16_t*>(centroids), H, C * D, hdr, out);
+  return hipGetLastError();
+}
 
 size_t attend_workspace_bytes(const CodecArgs& kc, int64_t n_keys, int64_t n_queries) {
   if (kc.x_dtype != KVC_BF16 || kc.D != DM || n_queries <= 0 || n_keys <= 0) return 0;

@@ -40,6 +40,7 @@ struct BaseArgs {
   const float* coef_a = nullptr;
   const float* coef_b = nullptr;
   int64_t prev_stride = 0;
+  const void* centroid_tables = nullptr;   // fp16 image of centroids (attention only)
 };
 
 struct EncodeLaunch {
@@ -105,6 +106,11 @@ bool predict_available();
 size_t attend_workspace_bytes(const CodecArgs& kc, int64_t n_keys, int64_t n_queries);
 size_t attend_chunk_workspace_bytes(const CodecArgs& kc, int64_t n_keys, int64_t n_queries);
 size_t attend_mixed_workspace_bytes(const CodecArgs& kc, int64_t n_keys, int64_t n_queries);
+// fp16 centroid images for the decode-fused attention: header (per-head exponents and
+// exactness flags, 256-byte padded) + [H][C][D] fp16
+size_t centroid_tables_header_bytes(int H);
+hipError_t launch_centroid_tables(const void* centroids, int H, int C, int D, void* tables,
+                                  hipStream_t s);
 // Online centroid fitting: `iterations` Lloyd steps on a.x (n_tokens rows) updating the
 // table a.b.centroids in place; a.workspace holds a scratch store of n_tokens rows.
 size_t fit_workspace_bytes(const CodecArgs& c, int64_t n_tokens);

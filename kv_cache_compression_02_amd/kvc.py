@@ -29,7 +29,7 @@ ATTEND_JENSEN = 1
 KVC_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 EXPORTED = ("kvc_store_bytes", "kvc_encode", "kvc_encode_kv", "kvc_encode_noalloc", "kvc_decode",
-            "kvc_fit_centroids",
+            "kvc_fit_centroids", "kvc_centroid_tables", "kvc_centroid_tables_bytes",
             "kvc_attend_compressed",
             "kvc_attend_compressed_chunk", "kvc_attend_mixed_dim", "kvc_workspace_bytes",
             "kvc_status_str", "kvc_abi_version")
@@ -55,7 +55,7 @@ class _Store(ctypes.Structure):
 class _Base(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("centroids", "basis", "prev0", "prev1", "aux",
                                                "w_block", "u", "v_lr", "coef_a", "coef_b")] \
-        + [("prev_token_stride", ctypes.c_int64)]
+        + [("prev_token_stride", ctypes.c_int64), ("centroid_tables", ctypes.c_void_p)]
 
 
 _lib = None
@@ -84,6 +84,10 @@ def lib():
     L.kvc_decode.argtypes = [P(_Codec), P(_Store), I64, I64, P(_Base), VP, I32, VP, VP, SZ, VP]
     L.kvc_decode.restype = I32
     L.kvc_fit_centroids.argtypes = [P(_Codec), VP, I64, I64, VP, I32, VP, SZ, VP]
+    L.kvc_centroid_tables_bytes.argtypes = [P(_Codec)]
+    L.kvc_centroid_tables_bytes.restype = SZ
+    L.kvc_centroid_tables.argtypes = [P(_Codec), VP, VP, SZ, VP]
+    L.kvc_centroid_tables.restype = I32
     L.kvc_fit_centroids.restype = I32
     U32 = ctypes.c_uint32
     att = [P(_Codec), P(_Store), P(_Base), P(_Codec), P(_Store), P(_Base), I64, VP, I64,
@@ -171,10 +175,12 @@ class BaseParams:
     coef_a: Optional[torch.Tensor] = None
     coef_b: Optional[torch.Tensor] = None
     prev_token_stride: int = 0
+    centroid_tables: Optional[torch.Tensor] = None
 
     def c(self) -> _Base:
         b = _Base()
-        for name in ("centroids", "basis", "w_block", "u", "v_lr", "coef_a", "coef_b"):
+        for name in ("centroids", "basis", "w_block", "u", "v_lr", "coef_a", "coef_b",
+                     "centroid_tables"):
             t = getattr(self, name)
             setattr(b, name, None if t is None else _p(t, name).value)
         # prev0, prev1 and aux share one token stride
@@ -347,6 +353,22 @@ def kvc_fit_centroids(codec: Codec, x: torch.Tensor, centroids: torch.Tensor, it
                                    _p(centroids, "centroids"), iterations,
                                    _p(workspace, "workspace"), ws_bytes, _stream()),
            "kvc_fit_centroids")
+
+
+def kvc_centroid_tables(codec: Codec, centroids: torch.Tensor) -> Optional[torch.Tensor]:
+    """The fp16 image of a bf16 centroid table [H][C][d] for the decode-fused attention
+    (pass it as BaseParams.centroid_tables), or None where some head's table is not an
+    exact fp16 image (that call then keeps the bf16 table).  Waits for the stream."""
+    n = int(lib().kvc_centroid_tables_bytes(ctypes.byref(codec.c())))
+    if n == 0:
+        raise KvcError(KVC_E_UNSUPPORTED, "kvc_centroid_tables")
+    out = torch.empty(n, dtype=torch.uint8, device=centroids.device)
+    st = lib().kvc_centroid_tables(ctypes.byref(codec.c()), _p(centroids, "centroids"),
+                                   ctypes.c_void_p(out.data_ptr()), n, _stream())
+    if st == KVC_E_UNSUPPORTED:
+        return None
+    _check(st, "kvc_centroid_tables")
+    return out
 
 
 def kvc_attend_compressed(kc: Codec, kstore: Store, kbase: Optional[BaseParams], vc: Codec,

@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
     assert declared == set(kvc.EXPORTED)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.kvc_abi_version() == 3
+    assert L.kvc_abi_version() == 4
 
 
 def test_status_strings():
@@ -46,6 +46,28 @@ def test_store_bytes():
 
 
 FAKE = 0x10000  # an aligned fake device address; validation never dereferences it
+
+
+def test_centroid_tables_validation():
+    """The fp16 table image: its size (256-byte header of per-head exponents and flags,
+    then [H][C][d] fp16), and the refusals that come before any device work."""
+    L = _lib()
+    c = kvc.Codec(12, 128, 2, 32, kvc.BASE_CENTROID, 256)
+    n = L.kvc_centroid_tables_bytes(ctypes.byref(c.c()))
+    assert n == 256 + 12 * 256 * 128 * 2
+    big = kvc.Codec(40, 128, 2, 64, kvc.BASE_CENTROID, 16)
+    assert L.kvc_centroid_tables_bytes(ctypes.byref(big.c())) == 512 + 40 * 16 * 128 * 2
+    for other in (kvc.Codec(2, 128, 2, 32, kvc.BASE_NONE),
+                  kvc.Codec(2, 64, 4, 32, kvc.BASE_CENTROID, 16, x_dtype=kvc.F32)):
+        assert L.kvc_centroid_tables_bytes(ctypes.byref(other.c())) == 0
+        assert L.kvc_centroid_tables(ctypes.byref(other.c()), ctypes.c_void_p(FAKE),
+                                     ctypes.c_void_p(FAKE), 1 << 30, None) == kvc.KVC_E_UNSUPPORTED
+    call = lambda cen, tab, nb: L.kvc_centroid_tables(ctypes.byref(c.c()), cen, tab, nb, None)
+    assert call(None, ctypes.c_void_p(FAKE), n) == kvc.KVC_E_NULL
+    assert call(ctypes.c_void_p(FAKE), None, n) == kvc.KVC_E_NULL
+    assert call(ctypes.c_void_p(FAKE + 2), ctypes.c_void_p(FAKE), n) == kvc.KVC_E_ALIGN
+    assert call(ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 8), n) == kvc.KVC_E_ALIGN
+    assert call(ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), n - 1) == kvc.KVC_E_SHAPE
 
 
 def _enc(codec, x=FAKE, n=4, stride=0, base=None, store=None, off=0):
