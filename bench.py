@@ -445,6 +445,7 @@ def bench_mixed(args, torch, kvc, synth, dev):
     Kx, Vx = b16(d["K"]), b16(d["V"])
     kvc.kvc_encode(kc, Kx, ks, 0, kb)
     kvc.kvc_encode(vc, Vx, vs, 0, vb)
+    vb.centroid_tables = kvc.kvc_centroid_tables(vc, vb.centroids)   # fp16 image (or None)
     # the encode of the whole 65520-token history (K: nearest of 512 centroids + INT4
     # coefficients of the residual on the basis; V: nearest centroid + INT2 g32), timed
     # with events apart from the attention steps
@@ -508,6 +509,8 @@ def bench_rotated(args, torch, kvc, synth, dev):
     vb = kvc.BaseParams(centroids=b16(d["Cv"]))
     kvc.kvc_encode(codec, K[:lo], ks, 0, kb)
     kvc.kvc_encode(codec, V[:lo], vs, 0, vb)
+    kb.centroid_tables = kvc.kvc_centroid_tables(codec, kb.centroids)   # fp16 images (or None)
+    vb.centroid_tables = kvc.kvc_centroid_tables(codec, vb.centroids)
     Kc, Vc = K[lo:hi].contiguous(), V[lo:hi].contiguous()
     out = torch.empty((nq, H, D), dtype=torch.float32, device=dev)
     ws = kvc.kvc.workspace_for(kvc.kvc.OP_ATTEND, codec, nk, dev, n_queries=nq)

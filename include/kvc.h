@@ -329,9 +329,9 @@ kvc_status kvc_centroid_tables(const kvc_codec* codec, const void* centroids, vo
  *     decoded tile rotates its dequantized residuals back before the centroid is added,
  *     with the decoder's arithmetic, so the tiles hold exactly what kvc_decode returns
  *     (rounded to bf16).  K and V must then both use KVC_BASE_CENTROID.
- *   kp->centroid_tables and vp->centroid_tables (both given, centroid K and V, not
- *     rotated, no flags): the tile decode reads the fp16 images (kvc_centroid_tables);
- *     same results.  Otherwise they are ignored.
+ *   kp->centroid_tables and vp->centroid_tables (both given, centroid K and V): the
+ *     tile decode reads the fp16 images (kvc_centroid_tables); same results.  One of
+ *     them alone is ignored.
  * Errors: KVC_E_NULL, KVC_E_SHAPE (n_keys > capacity, n_keys < 1, mismatched
  * heads/d, softmax_scale not finite and positive; bf16 path: a store whose per-head
  * code or scale/zero rows span 2 GiB or more, or a dense cache of 2 GiB or more - the
@@ -373,7 +373,9 @@ kvc_status kvc_attend_compressed_chunk(const kvc_codec* kc, const kvc_store* k,
  * is (q . C_k[a_n] + (B^T q) . c_n) * softmax_scale, c_n = dequantized coefficients;
  * softmax over all n_keys keys; values decoded from their centroid store.
  *   kc: KVC_BASE_COEFF (bf16, d = 128, m = 16); kp: centroids + basis.
- *   vc: KVC_BASE_CENTROID (bf16, d = 128, not rotated); vp: centroids.
+ *   vc: KVC_BASE_CENTROID (bf16, d = 128, not rotated); vp: centroids (and optionally
+ *     centroid_tables, the fp16 image kvc_centroid_tables made of them: the ordered path
+ *     then decodes V through it, same results).
  *   q, out, lse: as kvc_attend_compressed.
  *   workspace: optional.  With kvc_workspace_bytes(KVC_OP_ATTEND_MIXED, kc, n_keys,
  *     n_queries) bytes (and kc->n_centroids <= 4096) the call first copies the history

@@ -1218,7 +1218,7 @@ constexpr int MWIN = 1024;   // tile records a workgroup stages in LDS at a time
 
 // One workgroup = 8 waves x 32 queries of one head, as attend_bf16_kernel; p.k and p.v
 // are the cluster-ordered stores (capacity n), p.k.cen the key centroid table.
-template <int KBITS, int VBITS, bool VCEN>
+template <int KBITS, int VBITS, bool VCEN, bool CF16 = false>
 __global__ __launch_bounds__(NT, 1) void attend_mixed_cl_kernel(AttnParams p, ClusterTabs ct) {
   // K tile row: 16 high + 16 low coefficient parts, the one-hot row over the block's 32
   // centroids, pad
@@ -1262,8 +1262,10 @@ __global__ __launch_bounds__(NT, 1) void attend_mixed_cl_kernel(AttnParams p, Cl
                            VCEN ? n * p.v.idxb : 0);
   const auto rk_cen = rsrc(reinterpret_cast<const uint16_t*>(p.k.cen) + (int64_t)h * p.k.C * DM,
                            (int64_t)p.k.C * DM * 2);
-  const auto rv_cen = rsrc(reinterpret_cast<const uint16_t*>(p.v.cen) + (int64_t)h * p.v.C * DM,
-                           VCEN ? (int64_t)p.v.C * DM * 2 : 0);
+  // CF16: V's centroid rows from the table's fp16 image (c * 2^e_h), restored by 2^-e_h
+  const uint16_t* vcen = CF16 ? p.v.cen16 : reinterpret_cast<const uint16_t*>(p.v.cen);
+  const auto rv_cen = rsrc(vcen + (int64_t)h * p.v.C * DM, VCEN ? (int64_t)p.v.C * DM * 2 : 0);
+  const float vsc = CF16 ? __int_as_float((127 - p.v.cexp[h]) << 23) : 1.0f;
 
   // roles: 8 lanes per K row (2 coefficients and 4 one-hot columns each), 16 lanes per V
   // row pair (8 channels each), 16 lanes per centroid row
@@ -1390,8 +1392,13 @@ __global__ __launch_bounds__(NT, 1) void attend_mixed_cl_kernel(AttnParams p, Cl
       const uint32_t cw[4] = {pr.vc[j].x, pr.vc[j].y, pr.vc[j].z, pr.vc[j].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[j][2 * i] = lo_bf16(cw[i]) + dq[j][2 * i];
-        x[j][2 * i + 1] = hi_bf16(cw[i]) + dq[j][2 * i + 1];
+        if constexpr (CF16) {
+          x[j][2 * i] = add_f16lo(cw[i], vsc, dq[j][2 * i]);
+          x[j][2 * i + 1] = add_f16hi(cw[i], vsc, dq[j][2 * i + 1]);
+        } else {
+          x[j][2 * i] = lo_bf16(cw[i]) + dq[j][2 * i];
+          x[j][2 * i + 1] = hi_bf16(cw[i]) + dq[j][2 * i + 1];
+        }
       }
     }
 #pragma unroll
@@ -1847,11 +1854,16 @@ hipError_t launch_compressed_bf16(const AttnParams& p, int kbits, int vbits, dim
   const bool kc = p.k.mode == SRC_CENTROID, vc = p.v.mode == SRC_CENTROID;
   const dim3 block(NT);
   const bool rot = p.k.rot || p.v.rot, jb = p.jensen != 0;
+  const bool cf = kc && vc && p.k.cen16 && p.v.cen16;   // both tables' fp16 images given
   if (rot || jb) {   // rotated residuals / Jensen correction: centroid K and V (validated by the caller)
     if (!kc || !vc) return hipErrorInvalidValue;
 #define KVC_ATT_RJ(KB_, VB_, R_, J_)                                                             \
     if (kbits == KB_ && vbits == VB_ && rot == R_ && jb == J_) {                                 \
-      hipLaunchKernelGGL((attend_bf16_kernel<KB_, VB_, true, true, false, false, R_, J_>), grid, block, 0, s, p); \
+      if (cf)                                                                                    \
+        hipLaunchKernelGGL((attend_bf16_kernel<KB_, VB_, true, true, false, false, R_, J_, true>), \
+                           grid, block, 0, s, p);                                                \
+      else                                                                                       \
+        hipLaunchKernelGGL((attend_bf16_kernel<KB_, VB_, true, true, false, false, R_, J_>), grid, block, 0, s, p); \
       return hipGetLastError();                                                                  \
     }
 #define KVC_ATT_RJ_BITS(R_, J_) \
@@ -1863,7 +1875,7 @@ hipError_t launch_compressed_bf16(const AttnParams& p, int kbits, int vbits, dim
 #undef KVC_ATT_RJ
     return hipErrorInvalidValue;
   }
-  if (kc && vc && p.k.cen16 && p.v.cen16) {   // both tables' fp16 images given
+  if (cf) {
 #define KVC_ATT16(KB_, VB_)                                                                       \
     if (kbits == KB_ && vbits == VB_) {                                                           \
       hipLaunchKernelGGL((attend_bf16_kernel<KB_, VB_, true, true, false, false, false, false, true>), \
@@ -2135,7 +2147,10 @@ hipError_t launch_attend_mixed(const AttendLaunch& a, hipStream_t s) {
     const dim3 grid((unsigned)(nqb * a.kc.H * pc.splits)), block(NT);
 #define KVC_MIXCL(KB_, VB_)                                                               \
     if (a.kc.bits == KB_ && a.vc.bits == VB_) {                                           \
-      hipLaunchKernelGGL((attend_mixed_cl_kernel<KB_, VB_, true>), grid, block, 0, s, pc, ct); \
+      if (pc.v.cen16)                                                                     \
+        hipLaunchKernelGGL((attend_mixed_cl_kernel<KB_, VB_, true, true>), grid, block, 0, s, pc, ct); \
+      else                                                                                \
+        hipLaunchKernelGGL((attend_mixed_cl_kernel<KB_, VB_, true>), grid, block, 0, s, pc, ct); \
       e = hipGetLastError();                                                              \
       if (e != hipSuccess) return e;                                                      \
       return launch_combine(pc, s);                                                       \

@@ -158,3 +158,57 @@ def test_cfg1_full_size_with_images_is_identical():
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
     assert torch.isfinite(b[0]).all()
+
+
+@pytest.mark.parametrize("rotation,flags", [(64, 0), (0, 1), (16, 1)])
+def test_rotated_and_jensen_with_images_are_identical(rotation, flags):
+    """The rotated-residual and Jensen-corrected instances take the images too."""
+    dev = device()
+    d = synth.cfg1(seed=23, hist_frames=3, query_frames=1, tokens=100, heads=3, dim=128,
+                   n_centroids=40)
+    group = 64 if rotation == 64 else 32
+    enc = []
+    for name, cname in (("K", "Ck"), ("V", "Cv")):
+        codec = kvc.Codec(3, 128, 2, group, kvc.BASE_CENTROID, 40, rotation=rotation)
+        st = kvc.Store.allocate(codec, d[name].shape[0], dev)
+        cen = to_dev(d[cname], dev)
+        kvc.kvc_encode(codec, to_dev(d[name], dev), st, 0, kvc.BaseParams(centroids=cen))
+        enc.append((codec, st, cen, kvc.kvc_centroid_tables(codec, cen)))
+    (kc, ks, kcen, ktab), (vc, vs, vcen, vtab) = enc
+    q = to_dev(d["Q"], dev)
+    n = d["K"].shape[0]
+    a = kvc.kvc_attend_compressed(kc, ks, kvc.BaseParams(centroids=kcen), vc, vs,
+                                  kvc.BaseParams(centroids=vcen), n, q, d["scale"], flags=flags)
+    a = a.clone()
+    b = kvc.kvc_attend_compressed(kc, ks, kvc.BaseParams(centroids=kcen, centroid_tables=ktab),
+                                  vc, vs, kvc.BaseParams(centroids=vcen, centroid_tables=vtab),
+                                  n, q, d["scale"], flags=flags)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("n_keys", [1000, 333])
+def test_mixed_attention_with_value_images_is_identical(n_keys):
+    """The ordered mixed-dimensional kernel decodes V through the value table's image."""
+    dev = device()
+    d = synth.cfg4(seed=24, hist_frames=1, query_frames=1, tokens=1000, heads=2, n_centroids=64)
+    H, C, m = d["heads"], d["centroids"], d["coeff_dim"]
+    kc = kvc.Codec(H, 128, d["k_bits"], m, kvc.BASE_COEFF, C, coeff_dim=m)
+    vc = kvc.Codec(H, 128, d["v_bits"], d["v_group"], kvc.BASE_CENTROID, C)
+    ks, vs = kvc.Store.allocate(kc, n_keys, dev), kvc.Store.allocate(vc, n_keys, dev)
+    kb = kvc.BaseParams(centroids=to_dev(d["Ck"], dev), basis=to_dev(d["B"], dev))
+    vcen = to_dev(d["Cv"], dev)
+    kvc.kvc_encode(kc, to_dev(d["K"][:n_keys], dev), ks, 0, kb)
+    kvc.kvc_encode(vc, to_dev(d["V"][:n_keys], dev), vs, 0, kvc.BaseParams(centroids=vcen))
+    vtab = kvc.kvc_centroid_tables(vc, vcen)
+    assert vtab is not None
+    q = to_dev(d["Q"], dev)
+    ws = kvc.kvc.workspace_for(kvc.kvc.OP_ATTEND_MIXED, kc, n_keys, dev, n_queries=q.shape[0])
+    a = kvc.kvc_attend_mixed_dim(kc, ks, kb, vc, vs, kvc.BaseParams(centroids=vcen), n_keys, q,
+                                 d["scale"], workspace=ws)
+    a = a.clone()
+    b = kvc.kvc_attend_mixed_dim(kc, ks, kb, vc, vs,
+                                 kvc.BaseParams(centroids=vcen, centroid_tables=vtab), n_keys, q,
+                                 d["scale"], workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
