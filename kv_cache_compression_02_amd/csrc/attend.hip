@@ -1750,58 +1750,6 @@ Src make_src(const CodecArgs& c, const StoreArgs& st, const BaseArgs& b) {
   return s;
 }
 
-// fp16 image of a bf16 centroid table, one workgroup per head: the head's largest |c|
-// picks the power of two 2^k that brings it closest below 65504, every c * 2^k is
-// rounded to fp16 and checked for exactness (non-finite entries fail the check).  The
-// header holds k per head, then 1 / 0 per head for exact / not.
-constexpr int CT_THREADS = 256;
-__global__ __launch_bounds__(CT_THREADS) void centroid_tables_kernel(const uint16_t* cen, int H,
-                                                                      int n, int32_t* hdr,
-                                                                      uint16_t* out) {
-  __shared__ float red[CT_THREADS / 64];
-  __shared__ int okw[CT_THREADS / 64];
-  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint16_t* src = cen + (int64_t)h * n;
-  uint16_t* dst = out + (int64_t)h * n;
-  float m = 0.0f;
-  int ok = 1;
-  for (int i = tid; i < n; i += CT_THREADS) {
-    const float c = __uint_as_float((uint32_t)src[i] << 16);
-    if (!(fabsf(c) <= 3.0e38f)) ok = 0;   // inf / nan
-    m = fmaxf(m, fabsf(c));
-  }
-#pragma unroll
-  for (int o = 32; o; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if (lane == 0) red[wave] = m;
-  __syncthreads();
-  m = red[0];
-#pragma unroll
-  for (int w = 1; w < CT_THREADS / 64; ++w) m = fmaxf(m, red[w]);
-  int k = 0;
-  if (m > 0.0f && m <= 3.0e38f) {
-    int e;
-    const float f = frexpf(m, &e);            // m = f 2^e, f in [0.5, 1)
-    k = (f * 65536.0f <= 65504.0f) ? 16 - e : 15 - e;
-    k = max(-100, min(100, k));
-  }
-  const float sc = __int_as_float((127 + k) << 23);
-  for (int i = tid; i < n; i += CT_THREADS) {
-    const float y = __uint_as_float((uint32_t)src[i] << 16) * sc;   // exact: a power of two
-    const _Float16 hv = (_Float16)y;
-    if (!((float)hv == y)) ok = 0;
-    dst[i] = __builtin_bit_cast(uint16_t, hv);
-  }
-  ok = __all(ok) ? 1 : 0;
-  if (lane == 0) okw[wave] = ok;
-  __syncthreads();
-  if (tid == 0) {
-    int all = 1;
-    for (int w = 0; w < CT_THREADS / 64; ++w) all &= okw[w];
-    hdr[h] = k;
-    hdr[H + h] = all;
-  }
-}
-
 // Key splits of the bf16 path.  One workgroup fills a CU (its registers), so a launch of
 // W workgroups takes ceil(W / CUs) rounds of equal length; splitting the keys s ways
 // shortens a workgroup's run s-fold but multiplies the workgroups by s and adds a partial
@@ -1912,18 +1860,6 @@ int chunk_history_splits(int H, int64_t nq, int64_t nk) {
 }
 
 }  // namespace
-
-size_t centroid_tables_header_bytes(int H) { return ((size_t)8 * H + 255) / 256 * 256; }
-
-hipError_t launch_centroid_tables(const void* centroids, int H, int C, int D, void* tables,
-                                  hipStream_t s) {
-  int32_t* hdr = reinterpret_cast<int32_t*>(tables);
-  uint16_t* out = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(tables) +
-                                              centroid_tables_header_bytes(H));
-  hipLaunchKernelGGL(centroid_tables_kernel, dim3((unsigned)H), dim3(CT_THREADS), 0, s,
-                     reinterpret_cast<const uint16_t*>(centroids), H, C * D, hdr, out);
-  return hipGetLastError();
-}
 
 size_t attend_workspace_bytes(const CodecArgs& kc, int64_t n_keys, int64_t n_queries) {
   if (kc.x_dtype != KVC_BF16 || kc.D != DM || n_queries <= 0 || n_keys <= 0) return 0;
