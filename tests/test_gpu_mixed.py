@@ -157,7 +157,15 @@ def test_cfg4_full_size_sampled():
     ws = kvc.kvc.workspace_for(kvc.kvc.OP_ATTEND_MIXED, kc, d["K"].shape[0], dev, n_queries=q.shape[0])
     out = kvc.kvc_attend_mixed_dim(kc, ks, kb, vc, vs, vb, d["K"].shape[0], q, d["scale"],
                                    workspace=ws)
+    out = out.clone()
+    # the bench's configuration: V decoded through the value table's fp16 image, same bits
+    vtab = kvc.kvc_centroid_tables(vc, vb.centroids)
+    assert vtab is not None
+    out16 = kvc.kvc_attend_mixed_dim(kc, ks, kb, vc, vs,
+                                     kvc.BaseParams(centroids=vb.centroids, centroid_tables=vtab),
+                                     d["K"].shape[0], q, d["scale"], workspace=ws)
     torch.cuda.synchronize()
+    assert torch.equal(out, out16)
     got = store_np(ks)
     rng = np.random.default_rng(3)
     tok = np.sort(rng.choice(d["K"].shape[0], size=512, replace=False))

@@ -148,7 +148,14 @@ def test_cfg1_full_size_rotated_attention_sampled():
     ws = kvc.kvc.workspace_for(kvc.kvc.OP_ATTEND, kc, n, dev, n_queries=q.shape[0])
     print("rotated cfg1 attention", flush=True)
     out = kvc.kvc_attend_compressed(kc, ks, kb, vc, vs, vb, n, q, d["scale"], workspace=ws)
+    out = out.clone()
+    # the bench's configuration: centroid rows from the tables' fp16 images, same bits
+    ka = kvc.BaseParams(centroids=kb.centroids, centroid_tables=kvc.kvc_centroid_tables(kc, kb.centroids))
+    va = kvc.BaseParams(centroids=vb.centroids, centroid_tables=kvc.kvc_centroid_tables(vc, vb.centroids))
+    assert ka.centroid_tables is not None and va.centroid_tables is not None
+    out16 = kvc.kvc_attend_compressed(kc, ks, ka, vc, vs, va, n, q, d["scale"], workspace=ws)
     torch.cuda.synchronize()
+    assert torch.equal(out, out16)
     o = out.cpu().numpy()
     assert np.all(np.isfinite(o))
     rng = np.random.default_rng(3)
