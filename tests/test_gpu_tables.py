@@ -58,21 +58,23 @@ def _split_tables(tab: torch.Tensor, H: int):
     return hdr[:H], hdr[H:], img
 
 
-def test_table_image_matches_brute_force():
+@pytest.mark.parametrize("heads", [3, 40])
+def test_table_image_matches_brute_force(heads):
+    """40 heads: the header of exponents and flags spans two 256-byte blocks."""
     dev = device()
-    d = synth.cfg1(seed=3, hist_frames=1, query_frames=1, tokens=64, heads=3, dim=128,
+    d = synth.cfg1(seed=3, hist_frames=1, query_frames=1, tokens=64, heads=heads, dim=128,
                    n_centroids=40)
-    codec = kvc.Codec(3, 128, 2, 32, kvc.BASE_CENTROID, 40)
+    codec = kvc.Codec(heads, 128, 2, 32, kvc.BASE_CENTROID, 40)
     C = d["Ck"].copy()
     C[1] = 0                                               # an all-zero head: k = 0
     C[2] = nm.f32_to_bf16(nm.bf16_to_f32(C[2]) * np.float32(1e-3))   # another exponent
     tab = kvc.kvc_centroid_tables(codec, to_dev(C, dev))
     assert tab is not None
-    k, flags, img = _split_tables(tab, 3)
+    k, flags, img = _split_tables(tab, heads)
     ek, eimg, eok = _expected_image(C)
     assert all(eok)
     assert np.array_equal(k, ek), (k, ek)
-    assert np.array_equal(flags, [1, 1, 1])
+    assert np.array_equal(flags, np.ones(heads))
     assert np.array_equal(img.reshape(eimg.shape).view(np.uint16), eimg.view(np.uint16))
 
 
