@@ -87,3 +87,27 @@ def test_paired_encode_cfg1_chunk_full_size():
         ga, gb = store_np(a), store_np(b)
         for key in ga:
             assert np.array_equal(ga[key][:, lo:hi], gb[key][:, lo:hi]), key
+
+
+# every code width, group and rotation of the 16-token-wave encoder (rotations divide the group)
+TWO_ROUND = [(b, g, r) for b in (2, 4) for g in (16, 32, 64) for r in (0, 16)] + [(2, 64, 64), (4, 64, 64)]
+
+
+@pytest.mark.parametrize("bits,group,rot", TWO_ROUND)
+def test_paired_encode_two_round_grid(bits, group, rot):
+    """12 heads x 3000 tokens, 256 centroids: the paired launch walks two tile rounds of the
+    eight-wave grid and so runs sixteen-wave workgroups, the single-tensor calls run the
+    eight-wave grid; both give the same stores, which match the oracle on the first 96
+    rows and the ragged last 40."""
+    dev = device()
+    d = synth.cfg1(seed=44, hist_frames=2, query_frames=1, tokens=1500, heads=12, dim=128,
+                   n_centroids=256)
+    codec = kvc.Codec(12, 128, bits, group, kvc.BASE_CENTROID, 256, rotation=rot)
+    kb = kvc.BaseParams(centroids=to_dev(d["Ck"], dev))
+    vb = kvc.BaseParams(centroids=to_dev(d["Cv"], dev))
+    print(f"paired encode, two-round grid: bits={bits} group={group} rot={rot}", flush=True)
+    gk, gv = _pair_vs_single(codec, d, dev, kb, vb, 0, 3000, 3000)
+    for g, name, cname in ((gk, "K", "Ck"), (gv, "V", "Cv")):
+        for r0, r1 in ((0, 96), (2960, 3000)):
+            check_centroid_store(g, nm.bf16_to_f32(d[name][r0:r1]), nm.bf16_to_f32(d[cname]), bits,
+                                 group, rows=slice(r0, r1), rotation=rot)
