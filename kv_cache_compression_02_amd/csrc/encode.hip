@@ -53,6 +53,7 @@ struct EncodeParams {
   uint32_t* sz2;
   void* index2;
   int64_t capacity2;
+  int index_only;   // encode_c16_kernel: store the centroid index only
 };
 
 template <typename XT, int D>
@@ -1343,76 +1344,79 @@ __global__ __launch_bounds__(64 * NW, 4) void encode_c16_kernel(EncodeParams p) 
     if (!uniq) best = bj;
   }
 
-  // 4. residual, group scale/zero, codes of the lane's quarter row
+  // 4. residual, group scale/zero, codes of the lane's quarter row (none when only the
+  //    index is asked for)
   const uint16_t* crow = &tab[best * ROW + 8 * q];
   const int64_t row = (int64_t)h * pcap + p.token_offset + n;
   constexpr int KG = G == 64 ? 2 : 1;   // k-steps of one group
+  if (!p.index_only) {
 #pragma unroll
-  for (int kg = 0; kg < 4; kg += KG) {
-    float r[8 * KG];
+    for (int kg = 0; kg < 4; kg += KG) {
+      float r[8 * KG];
 #pragma unroll
-    for (int u = 0; u < KG; ++u) {
-      const uint4 cv = *reinterpret_cast<const uint4*>(crow + 32 * (kg + u));
-      const uint4 xw = xv[kg + u];
-      const uint32_t xa[4] = {xw.x, xw.y, xw.z, xw.w}, ca[4] = {cv.x, cv.y, cv.z, cv.w};
+      for (int u = 0; u < KG; ++u) {
+        const uint4 cv = *reinterpret_cast<const uint4*>(crow + 32 * (kg + u));
+        const uint4 xw = xv[kg + u];
+        const uint32_t xa[4] = {xw.x, xw.y, xw.z, xw.w}, ca[4] = {cv.x, cv.y, cv.z, cv.w};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        r[8 * u + 2 * k] = lo_bf16(xa[k]) - lo_bf16(ca[k]);
-        r[8 * u + 2 * k + 1] = hi_bf16(xa[k]) - hi_bf16(ca[k]);
+        for (int k = 0; k < 4; ++k) {
+          r[8 * u + 2 * k] = lo_bf16(xa[k]) - lo_bf16(ca[k]);
+          r[8 * u + 2 * k + 1] = hi_bf16(xa[k]) - hi_bf16(ca[k]);
+        }
       }
-    }
-    if constexpr (ROT != 0) hn_rotate_c16<ROT, KG>(r, q);
-    float mn = r[0], mx = r[0];
+      if constexpr (ROT != 0) hn_rotate_c16<ROT, KG>(r, q);
+      float mn = r[0], mx = r[0];
 #pragma unroll
-    for (int i = 1; i < 8 * KG; ++i) { mn = fminf(mn, r[i]); mx = fmaxf(mx, r[i]); }
-    // the group's other lanes: q ^ 1 (g = 16), all four (g = 32, 64)
-    mn = fminf(mn, xq(mn, 16));
-    mx = fmaxf(mx, xq(mx, 16));
-    if constexpr (G >= 32) {
-      mn = fminf(mn, xq(mn, 32));
-      mx = fmaxf(mx, xq(mx, 32));
-    }
-    const GroupQ gq = group_scale_zero(mn, mx, L);
-    // codes, 8 per k-step: the reciprocal quotient, redone with the IEEE division
-    // when an element lies within the bound of a rounding boundary (see quantize_with)
-    uint32_t cw[KG];
-#pragma unroll
-    for (int u = 0; u < KG; ++u) cw[u] = 0u;
-    if (gq.s != 0.0f) {
-      const float rinv = __builtin_amdgcn_rcpf(gq.s);
-      const float nzr = -(gq.z * rinv);
-      const float thr = 0.5f - (fabsf(nzr) + (float)(L + 2)) * 0x1p-19f;
-      float dev = 0.0f;   // largest |y - rint(y)| of the group
-#pragma unroll
-      for (int i = 0; i < 8 * KG; ++i) {
-        const float y = __builtin_fmaf(r[i], rinv, nzr);
-        const float k = __builtin_rintf(y);
-        dev = fmaxf(dev, fabsf(y - k));
-        const uint32_t code = (uint32_t)__builtin_amdgcn_fmed3f(k, 0.0f, (float)L);
-        cw[i >> 3] |= code << (BITS * (i & 7));
+      for (int i = 1; i < 8 * KG; ++i) { mn = fminf(mn, r[i]); mx = fmaxf(mx, r[i]); }
+      // the group's other lanes: q ^ 1 (g = 16), all four (g = 32, 64)
+      mn = fminf(mn, xq(mn, 16));
+      mx = fmaxf(mx, xq(mx, 16));
+      if constexpr (G >= 32) {
+        mn = fminf(mn, xq(mn, 32));
+        mx = fmaxf(mx, xq(mx, 32));
       }
-      if (dev > thr) {
+      const GroupQ gq = group_scale_zero(mn, mx, L);
+      // codes, 8 per k-step: the reciprocal quotient, redone with the IEEE division
+      // when an element lies within the bound of a rounding boundary (see quantize_with)
+      uint32_t cw[KG];
 #pragma unroll
-        for (int u = 0; u < KG; ++u) cw[u] = 0u;
+      for (int u = 0; u < KG; ++u) cw[u] = 0u;
+      if (gq.s != 0.0f) {
+        const float rinv = __builtin_amdgcn_rcpf(gq.s);
+        const float nzr = -(gq.z * rinv);
+        const float thr = 0.5f - (fabsf(nzr) + (float)(L + 2)) * 0x1p-19f;
+        float dev = 0.0f;   // largest |y - rint(y)| of the group
 #pragma unroll
-        for (int i = 0; i < 8 * KG; ++i) cw[i >> 3] |= quantize_one(r[i], gq, L) << (BITS * (i & 7));
+        for (int i = 0; i < 8 * KG; ++i) {
+          const float y = __builtin_fmaf(r[i], rinv, nzr);
+          const float k = __builtin_rintf(y);
+          dev = fmaxf(dev, fabsf(y - k));
+          const uint32_t code = (uint32_t)__builtin_amdgcn_fmed3f(k, 0.0f, (float)L);
+          cw[i >> 3] |= code << (BITS * (i & 7));
+        }
+        if (dev > thr) {
+#pragma unroll
+          for (int u = 0; u < KG; ++u) cw[u] = 0u;
+#pragma unroll
+          for (int i = 0; i < 8 * KG; ++i) cw[i >> 3] |= quantize_one(r[i], gq, L) << (BITS * (i & 7));
+        }
       }
-    }
-    // stores: channel piece (ks, q) holds bits 8 BITS (4 ks + q) .. of the token's row
+      // stores: channel piece (ks, q) holds bits 8 BITS (4 ks + q) .. of the token's row
 #pragma unroll
-    for (int u = 0; u < KG; ++u) {
-      const int ks = kg + u;
-      if constexpr (BITS == 4) {
-        if (live) pcodes[row * 16 + 4 * ks + q] = cw[u];
-      } else {
-        const uint32_t pw = xqi(cw[u], 16);   // the partner quarter's 16 bits
-        if (live && (q & 1) == 0) pcodes[row * 8 + 2 * ks + (q >> 1)] = cw[u] | (pw << 16);
+      for (int u = 0; u < KG; ++u) {
+        const int ks = kg + u;
+        if constexpr (BITS == 4) {
+          if (live) pcodes[row * 16 + 4 * ks + q] = cw[u];
+        } else {
+          const uint32_t pw = xqi(cw[u], 16);   // the partner quarter's 16 bits
+          if (live && (q & 1) == 0) pcodes[row * 8 + 2 * ks + (q >> 1)] = cw[u] | (pw << 16);
+        }
       }
+      // scale/zero word of the group (one lane per group)
+      const int gi = G == 16 ? 2 * kg + (q >> 1) : (G == 32 ? kg : kg >> 1);
+      const bool owner = G == 16 ? (q & 1) == 0 : q == 0;
+      if (live && owner) psz[row * (D / G) + gi] = gq.word;
     }
-    // scale/zero word of the group (one lane per group)
-    const int gi = G == 16 ? 2 * kg + (q >> 1) : (G == 32 ? kg : kg >> 1);
-    const bool owner = G == 16 ? (q & 1) == 0 : q == 0;
-    if (live && owner) psz[row * (D / G) + gi] = gq.word;
   }
   if (live && q == 0) {
     if (p.index_bytes == 2) reinterpret_cast<uint16_t*>(pidx)[row] = (uint16_t)best;
@@ -1521,6 +1525,7 @@ EncodeParams encode_params(const EncodeLaunch& a) {
   p.index = a.st.index;
   p.recon = a.recon;
   p.pred = a.pred;
+  p.index_only = a.index_only ? 1 : 0;
   return p;
 }
 

@@ -155,6 +155,7 @@ hipError_t launch_fit(const EncodeLaunch& a0, int iterations, hipStream_t s) {
   a.recon = nullptr;
   a.pred = nullptr;
   a.workspace = nullptr;
+  a.index_only = true;   // the update reads the assignment only
   uint16_t* table = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(a0.b.centroids));
   const dim3 grid((unsigned)(a0.c.H * ((a0.c.C + 3) / 4))), block(512);
   for (int it = 0; it < iterations; ++it) {

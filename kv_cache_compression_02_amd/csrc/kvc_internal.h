@@ -53,6 +53,9 @@ struct EncodeLaunch {
   float* pred = nullptr;
   void* workspace = nullptr;
   float* rank_buf = nullptr;   // DPLR rank-r intermediate [n][r] fp32; nullptr: in the workspace
+  // only the centroid index is read back (the fit's assignment pass): the 16-token-wave
+  // centroid encoder then writes the index alone; the other encoders write everything
+  bool index_only = false;
 };
 
 struct DecodeLaunch {
