@@ -985,12 +985,7 @@ __global__ __launch_bounds__(64 * cen_waves(CM, COEFF), 2 * 4 / cen_waves(CM, CO
 // (g = 16) or four (g = 32, 64) lanes, whose min and max are joined by lane exchanges.
 // With at most 128 registers per lane, four waves share a SIMD (two workgroups of
 // eight waves per CU with 256 centroids, one of sixteen with 512), which hides the
-// latency of small launches that one tile per workgroup cannot.  At 256 centroids a
-// launch whose eight-wave grid walks two tile rounds (the keys and values of one chunk
-// of a few thousand tokens in one launch) runs one workgroup of sixteen waves per CU
-// instead, in no more rounds: each CU then stages the head's table from L2 once instead
-// of twice (7% faster on such a chunk; a one-round launch, one tensor's chunk, is 10%
-// faster with the eight-wave grid, and long launches gain nothing).
+// latency of small launches that one tile per workgroup cannot.
 __host__ __device__ constexpr int c16_waves(int cm) { return cm == 512 ? 16 : 8; }
 
 // Hn residual transform (Coral-KV Fig. 5: each group of N residual channels is
@@ -1042,10 +1037,10 @@ __device__ __forceinline__ void hn_rotate_c16(float (&r)[8 * KG], int q) {
   for (int i = 0; i < 8 * KG; ++i) r[i] *= sc;
 }
 
-template <int BITS, int G, int CM, int ROT, int NW>
-__global__ __launch_bounds__(64 * NW, 4) void encode_c16_kernel(EncodeParams p) {
+template <int BITS, int G, int CM, int ROT>
+__global__ __launch_bounds__(64 * c16_waves(CM), 4) void encode_c16_kernel(EncodeParams p) {
   constexpr int D = 128, ROW = D + 8;
-  constexpr int NT = 64 * NW, TT = 16 * NW;   // threads, tokens per tile
+  constexpr int NW = c16_waves(CM), NT = 64 * NW, TT = 16 * NW;   // waves, threads, tokens
   constexpr int NBM = CM / 16;                 // centroid blocks at most
   constexpr int LOCB = CM == 256 ? 6 : 7;      // bits of a value's position in a lane
   constexpr uint32_t TAGM = (4u << LOCB) - 1u; // position + quarter
@@ -1427,49 +1422,19 @@ __global__ __launch_bounds__(64 * NW, 4) void encode_c16_kernel(EncodeParams p) 
   }   // tiles
 }
 
-// Persistent grid of NW-wave workgroups: workgroups per head slot = how many are
-// resident at once divided over the slots, at most one per tile; *rounds is the
-// largest number of tiles one workgroup walks.
-template <int BITS, int G, int CM, int ROT, int NW>
-hipError_t plan_c16(const EncodeParams& p, int* wph, int64_t* rounds) {
-  auto k = encode_c16_kernel<BITS, G, CM, ROT, NW>;
-  constexpr int NT = 64 * NW, TT = NT / 4;
+template <int BITS, int G, int CM, int ROT>
+hipError_t launch_c16_t(const EncodeParams& p, hipStream_t s) {
+  auto k = encode_c16_kernel<BITS, G, CM, ROT>;
+  constexpr int NT = 64 * c16_waves(CM), TT = NT / 4;
   int occ = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(k), NT, 0);
   if (e != hipSuccess) return e;
   const int64_t ntile = (p.n_tokens + TT - 1) / TT;
   const int64_t resident = (int64_t)std::max(1, occ) * cu_count();
   const int slots = p.pair ? 2 * p.H : p.H;
-  *wph = (int)std::max<int64_t>(1, std::min<int64_t>(ntile, resident / slots));
-  *rounds = (ntile + *wph - 1) / *wph;
-  return hipSuccess;
-}
-
-template <int BITS, int G, int CM, int ROT, int NW>
-hipError_t launch_c16_nw(const EncodeParams& p, int wph, hipStream_t s) {
-  const int slots = p.pair ? 2 * p.H : p.H;
-  hipLaunchKernelGGL((encode_c16_kernel<BITS, G, CM, ROT, NW>), dim3((unsigned)(wph * slots)),
-                     dim3(64 * NW), 0, s, p);
+  const int wph = (int)std::max<int64_t>(1, std::min<int64_t>(ntile, resident / slots));
+  hipLaunchKernelGGL(k, dim3((unsigned)(wph * slots)), dim3(NT), 0, s, p);
   return hipGetLastError();
-}
-
-template <int BITS, int G, int CM, int ROT>
-hipError_t launch_c16_t(const EncodeParams& p, hipStream_t s) {
-  constexpr int NW = c16_waves(CM);
-  int wph = 0;
-  int64_t rounds = 0;
-  hipError_t e = plan_c16<BITS, G, CM, ROT, NW>(p, &wph, &rounds);
-  if (e != hipSuccess) return e;
-  if constexpr (NW == 8) {   // two rounds: sixteen-wave workgroups, if no more rounds
-    if (rounds == 2) {
-      int wph16 = 0;
-      int64_t rounds16 = 0;
-      e = plan_c16<BITS, G, CM, ROT, 16>(p, &wph16, &rounds16);
-      if (e != hipSuccess) return e;
-      if (rounds16 <= 2) return launch_c16_nw<BITS, G, CM, ROT, 16>(p, wph16, s);
-    }
-  }
-  return launch_c16_nw<BITS, G, CM, ROT, NW>(p, wph, s);
 }
 
 // Persistent grid: workgroups per head = how many are resident at once (LDS and

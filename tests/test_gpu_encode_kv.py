@@ -95,10 +95,9 @@ TWO_ROUND = [(b, g, r) for b in (2, 4) for g in (16, 32, 64) for r in (0, 16)] +
 
 @pytest.mark.parametrize("bits,group,rot", TWO_ROUND)
 def test_paired_encode_two_round_grid(bits, group, rot):
-    """12 heads x 3000 tokens, 256 centroids: the paired launch walks two tile rounds of the
-    eight-wave grid and so runs sixteen-wave workgroups, the single-tensor calls run the
-    eight-wave grid; both give the same stores, which match the oracle on the first 96
-    rows and the ragged last 40."""
+    """12 heads x 3000 tokens, 256 centroids: the paired launch's workgroups walk two tiles
+    each, the single-tensor calls' one; both give the same stores, which match the oracle
+    on the first 96 rows and the ragged last 40."""
     dev = device()
     d = synth.cfg1(seed=44, hist_frames=2, query_frames=1, tokens=1500, heads=12, dim=128,
                    n_centroids=256)
