@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   if constexpr (sizeof(OT) == 2) {     // 16 bf16 (round to nearest even): two 16-byte stores
     uint32_t o[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) o[k] = f32_to_bf16_bits(v[2 * k]) | (f32_to_bf16_bits(v[2 * k + 1]) << 16);
+    for (int k = 0; k < 8; ++k) o[k] = pack_bf16x2(v[2 * k], v[2 * k + 1]);
     *reinterpret_cast<uint4*>(out) = make_uint4(o[0], o[1], o[2], o[3]);
     *reinterpret_cast<uint4*>(out + 8) = make_uint4(o[4], o[5], o[6], o[7]);
   } else {

@@ -934,7 +934,7 @@ __global__ __launch_bounds__(64 * cen_waves(CM, COEFF), 2 * 4 / cen_waves(CM, CO
             const uint32_t cw2 = crow[G * gi + i0] | ((uint32_t)crow[G * gi + i1] << 16);
             const float e0 = lo_bf16(cw2) + dequant_one(c0, q.s, q.z);
             const float e1 = hi_bf16(cw2) + dequant_one(c1, q.s, q.z);
-            o[k] = f32_to_bf16_bits(e0) | (f32_to_bf16_bits(e1) << 16);
+            o[k] = pack_bf16x2(e0, e1);
           }
           *reinterpret_cast<uint4*>(rec + i) = make_uint4(o[0], o[1], o[2], o[3]);
         }

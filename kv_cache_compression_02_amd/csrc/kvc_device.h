@@ -27,16 +27,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
-// float rounded to the nearest bf16 value, kept as float (finite inputs).
-__device__ __forceinline__ float round_bf16_f32(float f) {
-  uint32_t u = __float_as_uint(f);
-  u = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
-  return __uint_as_float(u);
-}
-
-// Two floats -> packed bf16 pair (lo in bits 0..15).
+// Two floats -> packed bf16 pair (lo in bits 0..15), round to nearest even: one
+// v_cvt_pk_bf16_f32, the same bits as f32_to_bf16_bits for every finite input, denormals
+// included (NaN payloads may differ). Inline asm, so that the compiler keeps one
+// instruction per pair also where the pair is unpacked again; f32_to_bf16_bits costs
+// three instructions per value.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  uint32_t r;
+  asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+  return r;
 }
 
 // fp16 conversions through clang's _Float16 (fptrunc is round-to-nearest-even).

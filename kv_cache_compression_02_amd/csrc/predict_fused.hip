@@ -411,10 +411,13 @@ __global__ __launch_bounds__(512) void pred_kernel(PredParams p) {
           const float4 a = cur.tv[ks][0], b = cur.tv[ks][1];
           const float tv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const uint32_t hb = f32_to_bf16_bits(tv[i]);
-            thi[ks][i] = (short)hb;
-            tlo[ks][i] = (short)f32_to_bf16_bits(tv[i] - bf16_bits_to_f32(hb));
+          for (int i = 0; i < 8; i += 2) {
+            const uint32_t hw = pack_bf16x2(tv[i], tv[i + 1]);
+            const uint32_t lw = pack_bf16x2(tv[i] - lo_bf16(hw), tv[i + 1] - hi_bf16(hw));
+            thi[ks][i] = (short)(hw & 0xFFFFu);
+            thi[ks][i + 1] = (short)(hw >> 16);
+            tlo[ks][i] = (short)(lw & 0xFFFFu);
+            tlo[ks][i + 1] = (short)(lw >> 16);
           }
         }
         const int rsteps = (p.r + 31) / 32;
@@ -512,7 +515,7 @@ __global__ __launch_bounds__(512) void pred_kernel(PredParams p) {
               const int i0 = i + 2 * k;
               const float v0 = pred[GL * gi + i0] + dq[i0];
               const float v1 = pred[GL * gi + i0 + 1] + dq[i0 + 1];
-              o[k] = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
+              o[k] = pack_bf16x2(v0, v1);
             }
             rq[(GL * gi + i) / 8] = make_uint4(o[0], o[1], o[2], o[3]);
           }
